@@ -1,0 +1,213 @@
+"""gated_delta_rule_gdr_amd: the gated delta rule forward pass on AMD MI355X.
+
+A thin ctypes binding over libgdr.so (include/gdr.h). Argument marshalling
+only: every step of the computation runs in the library's HIP kernels, torch
+supplies device memory and the current HIP stream. There is no CPU fallback:
+if the library is missing, importing the binding works but every call raises.
+
+    o = chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens)
+    o = recurrent_step(q, k, v, g, beta, pool, slot_idx)
+
+Layouts (torch tensors on the GPU):
+    q, k   [T, HK, DK]  bf16 or fp32 (a strided token dimension is allowed, e.g.
+           views into one fused qkv buffer; heads and dims must be contiguous)
+    v      [T, HV, DV]  same dtype as q, k
+    g      [T, HV] (scalar gate) | [T, HV, DK] (channel gate) | None, fp32, log alpha
+    beta   [T, HV] fp32 (delta rule) | None (linear rule)
+    pool   [num_slots, HV, DK, DV] fp32 or bf16, S^T per slot, updated in place
+    slot_idx [N] int32, cu_seqlens [N+1] int32 (prefill)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = ["chunk_fwd", "recurrent_step", "lib", "lib_path", "GdrError",
+           "abi_version", "Args", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK = 0
+_DT = {"f32": 0, "bf16": 1}
+_RULE = {"delta": 0, "linear": 1}
+_GATE = {"none": 0, "scalar": 1, "channel": 2}
+FLAG_ZERO_INIT = 1
+FLAG_DEBUG_CHECKS = 2
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gdr status {status}: {msg}")
+        self.status = status
+
+
+class Args(ctypes.Structure):
+    """Mirror of gdr_args (include/gdr.h)."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_stride_t", ctypes.c_int64), ("k_stride_t", ctypes.c_int64),
+        ("v_stride_t", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+        ("state_pool", ctypes.c_void_p), ("state_dtype", ctypes.c_int),
+        ("num_slots", ctypes.c_int64),
+        ("slot_idx", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("N", ctypes.c_int32), ("HK", ctypes.c_int32), ("HV", ctypes.c_int32),
+        ("DK", ctypes.c_int32), ("DV", ctypes.c_int32),
+        ("T_total", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("chunk_size", ctypes.c_int32),
+        ("rule", ctypes.c_int), ("gate", ctypes.c_int),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdr.so from this package directory (raises if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build it with `python -m gated_delta_rule_gdr_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    L.gdr_abi_version.restype = ctypes.c_int
+    L.gdr_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    L.gdr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
+    L.gdr_chunk_fwd.restype = ctypes.c_int
+    L.gdr_chunk_fwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p]
+    L.gdr_recurrent_step.restype = ctypes.c_int
+    L.gdr_recurrent_step.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
+    L.gdr_status_string.restype = ctypes.c_char_p
+    L.gdr_status_string.argtypes = [ctypes.c_int]
+    L.gdr_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def lib() -> ctypes.CDLL:
+    return load()
+
+
+def abi_version() -> int:
+    return load().gdr_abi_version()
+
+
+def _check(status: int):
+    if status != GDR_OK:
+        L = load()
+        raise GdrError(status, f"{L.gdr_status_string(status).decode()}: "
+                               f"{L.gdr_last_error().decode()}")
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _DT["bf16"]
+    if t.dtype == torch.float32:
+        return _DT["f32"]
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tok_stride(t, name: str) -> int:
+    """Token stride of a [T, H, D] tensor whose (H, D) block is contiguous."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [T, H, D], got {tuple(t.shape)}")
+    H, D = t.shape[1], t.shape[2]
+    if t.shape[0] > 0 and not (t.stride(2) == 1 and t.stride(1) == D):
+        raise ValueError(f"{name}: heads and dims must be contiguous")
+    return t.stride(0) if t.shape[0] > 1 else H * D
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
+             zero_init, debug_checks, chunk_size, out_dtype):
+    import torch
+    T, HK, DK = q.shape
+    HV, DV = v.shape[1], v.shape[2]
+    if gate is None:
+        gate = "none" if g is None else ("channel" if g.dim() == 3 else "scalar")
+    if scale is None:
+        scale = DK ** -0.5
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("pool", pool), ("slot_idx", slot_idx)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    if slot_idx.dtype != torch.int32 or not slot_idx.is_contiguous():
+        raise TypeError("slot_idx must be a contiguous int32 tensor")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous()):
+        raise TypeError("cu_seqlens must be a contiguous int32 tensor")
+    for name, t in (("g", g), ("beta", beta)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev):
+            raise TypeError(f"{name} must be a contiguous fp32 tensor on {dev}")
+    if not pool.is_contiguous():
+        raise ValueError("pool must be contiguous")
+    if o is None:
+        o = torch.empty((T, HV, DV), dtype=out_dtype, device=dev)
+    elif not o.is_contiguous() or tuple(o.shape) != (T, HV, DV):
+        raise ValueError("o must be a contiguous [T, HV, DV] tensor")
+    a = Args()
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.q_stride_t = _tok_stride(q, "q")
+    a.k_stride_t = _tok_stride(k, "k")
+    a.v_stride_t = _tok_stride(v, "v")
+    a.in_dtype = _dt(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    a.g, a.beta = _ptr(g), _ptr(beta)
+    a.o, a.out_dtype = _ptr(o), _dt(o)
+    a.state_pool, a.state_dtype = _ptr(pool), _dt(pool)
+    a.num_slots = pool.shape[0]
+    a.slot_idx = _ptr(slot_idx)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.N = slot_idx.shape[0]
+    a.HK, a.HV, a.DK, a.DV = HK, HV, DK, DV
+    a.T_total = T
+    a.scale = float(scale)
+    a.chunk_size = chunk_size
+    a.rule = _RULE[rule]
+    a.gate = _GATE[gate]
+    a.flags = (FLAG_ZERO_INIT if zero_init else 0) | (FLAG_DEBUG_CHECKS if debug_checks else 0)
+    if tuple(pool.shape[1:]) != (HV, DK, DV):
+        raise ValueError(f"pool must be [slots, {HV}, {DK}, {DV}], got {tuple(pool.shape)}")
+    return a, o
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk_size=64,
+              rule="delta", gate=None, out_dtype=None, zero_init=False, o=None,
+              debug_checks=False):
+    """Chunkwise prefill; returns o [T, HV, DV]; updates pool slots in place."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
+                    zero_init, debug_checks, chunk_size, out_dtype)
+    L = load()
+    _check(L.gdr_chunk_fwd(ctypes.byref(a), None, 0, _stream(q)))
+    return o
+
+
+def recurrent_step(q, k, v, g, beta, pool, slot_idx, *, scale=None, rule="delta", gate=None,
+                   out_dtype=None, zero_init=False, o=None, debug_checks=False):
+    """One token per sequence (q: [N, HK, DK]); returns o [N, HV, DV]."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, o = _prepare(q, k, v, g, beta, pool, slot_idx, None, o, scale, rule, gate,
+                    zero_init, debug_checks, 64, out_dtype)
+    L = load()
+    _check(L.gdr_recurrent_step(ctypes.byref(a), _stream(q)))
+    return o

@@ -1,0 +1,201 @@
+// Host side of libgdr: argument validation, dispatch, status strings.
+//
+// Validation reads only host-visible fields of gdr_args (never device memory)
+// and runs before anything is enqueued, so a rejected call has no side
+// effects. Device-side index arrays are checked only under
+// GDR_FLAG_DEBUG_CHECKS, by a small kernel whose verdict is copied back.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gdr_internal.h"
+
+#define GDR_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace gdr {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdr_status fail(gdr_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+size_t dtype_bytes(gdr_dtype d) { return d == GDR_BF16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == GDR_F32 || d == GDR_BF16; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void *p, int64_t rows, int64_t row_stride, int64_t row_len, size_t elem) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0) return {lo, lo};
+  return {lo, lo + static_cast<uintptr_t>(((rows - 1) * row_stride + row_len) * (int64_t)elem)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Checks shared by both entry points. `prefill` selects the chunk rules.
+gdr_status validate(const gdr_args *a, bool prefill) {
+  g_last_error[0] = '\0';
+  if (!a) return fail(GDR_E_INVALID, "args is NULL");
+  if (a->N < 0) return fail(GDR_E_INVALID, "N = %d < 0", a->N);
+  if (a->T_total < 0) return fail(GDR_E_INVALID, "T_total = %lld < 0", (long long)a->T_total);
+  if (a->HK <= 0 || a->HV <= 0) return fail(GDR_E_INVALID, "HK = %d, HV = %d must be positive", a->HK, a->HV);
+  if (a->HV % a->HK != 0) return fail(GDR_E_INVALID, "HV = %d is not a multiple of HK = %d", a->HV, a->HK);
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->out_dtype) || !dtype_ok(a->state_dtype))
+    return fail(GDR_E_INVALID, "unknown dtype code");
+  if (a->rule != GDR_RULE_DELTA && a->rule != GDR_RULE_LINEAR) return fail(GDR_E_INVALID, "unknown rule %d", (int)a->rule);
+  if (a->gate != GDR_GATE_NONE && a->gate != GDR_GATE_SCALAR && a->gate != GDR_GATE_CHANNEL)
+    return fail(GDR_E_INVALID, "unknown gate %d", (int)a->gate);
+  if (a->flags & ~(uint32_t)(GDR_FLAG_ZERO_INIT | GDR_FLAG_DEBUG_CHECKS))
+    return fail(GDR_E_INVALID, "unknown flag bits 0x%x", a->flags);
+  if (!std::isfinite(a->scale)) return fail(GDR_E_INVALID, "scale is not finite");
+  if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK))
+    return fail(GDR_E_UNSUPPORTED, "head dims DK = %d, DV = %d: built for DK = DV in {64, 128}", a->DK, a->DV);
+  if (!prefill && a->T_total != a->N)
+    return fail(GDR_E_INVALID, "recurrent step needs one token per sequence (T_total = %lld, N = %d)",
+                (long long)a->T_total, a->N);
+  if (prefill && a->chunk_size != 64)
+    return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: built for 64", a->chunk_size);
+  if (a->N == 0) return GDR_OK;  // nothing to do; pointers may be NULL
+
+  if (!a->state_pool || !a->slot_idx) return fail(GDR_E_INVALID, "state_pool / slot_idx is NULL");
+  if (prefill && !a->cu_seqlens) return fail(GDR_E_INVALID, "cu_seqlens is NULL");
+  if (a->num_slots < a->N) return fail(GDR_E_INVALID, "num_slots = %lld < N = %d (slots must be distinct)",
+                                       (long long)a->num_slots, a->N);
+  if (a->T_total > 0) {
+    if (!a->q || !a->k || !a->v || !a->o) return fail(GDR_E_INVALID, "q / k / v / o is NULL");
+    if (a->rule == GDR_RULE_DELTA && !a->beta) return fail(GDR_E_INVALID, "beta is NULL for the delta rule");
+    if (a->gate != GDR_GATE_NONE && !a->g) return fail(GDR_E_INVALID, "g is NULL for a gated call");
+    const int64_t kd = (int64_t)a->HK * a->DK, vd = (int64_t)a->HV * a->DV;
+    if (a->q_stride_t < kd || a->k_stride_t < kd || a->v_stride_t < vd)
+      return fail(GDR_E_INVALID, "token strides (%lld, %lld, %lld) shorter than a token (%lld, %lld)",
+                  (long long)a->q_stride_t, (long long)a->k_stride_t, (long long)a->v_stride_t,
+                  (long long)kd, (long long)vd);
+    const size_t ie = dtype_bytes(a->in_dtype);
+    const Range ro = span(a->o, a->T_total, vd, vd, dtype_bytes(a->out_dtype));
+    const Range ins[] = {
+        span(a->q, a->T_total, a->q_stride_t, kd, ie),
+        span(a->k, a->T_total, a->k_stride_t, kd, ie),
+        span(a->v, a->T_total, a->v_stride_t, vd, ie),
+        span(a->g, a->gate == GDR_GATE_NONE ? 0 : a->T_total, 1, 1,
+             4 * (size_t)a->HV * (a->gate == GDR_GATE_CHANNEL ? a->DK : 1)),
+        span(a->beta, a->rule == GDR_RULE_DELTA ? a->T_total : 0, 1, 1, 4 * (size_t)a->HV),
+        span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV, dtype_bytes(a->state_dtype)),
+    };
+    for (const Range &r : ins)
+      if (overlap(ro, r)) return fail(GDR_E_INVALID, "o overlaps an input or the state pool");
+  }
+  return GDR_OK;
+}
+
+gdr_status run_debug_checks(const gdr_args *a, bool prefill, hipStream_t stream) {
+  int *flag = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&flag), sizeof(int), stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
+  int h = -1;
+  e = launch_index_checks(*a, prefill, flag, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  (void)hipFreeAsync(flag, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
+  switch (h) {
+    case 0: return GDR_OK;
+    case 1: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens[0] != 0 or cu_seqlens[N] != T_total");
+    case 2: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens is not non-decreasing");
+    case 3: return fail(GDR_E_DEVICE_CHECK, "slot_idx out of [0, num_slots)");
+    case 4: return fail(GDR_E_DEVICE_CHECK, "slot_idx has duplicates");
+    default: return fail(GDR_E_DEVICE_CHECK, "device check code %d", h);
+  }
+}
+
+__global__ void index_check_kernel(const int32_t *cu, const int32_t *slots, int32_t N,
+                                   int64_t T_total, int64_t num_slots, int prefill, int *flag) {
+  __shared__ int code;
+  if (threadIdx.x == 0) code = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    if (prefill) {
+      if ((i == 0 && cu[0] != 0) || (i == N - 1 && cu[N] != T_total)) atomicMax(&code, 1);
+      if (cu[i + 1] < cu[i]) atomicMax(&code, 2);
+    }
+    const int32_t s = slots[i];
+    if (s < 0 || s >= num_slots) {
+      atomicMax(&code, 3);
+    } else {
+      for (int j = i + 1; j < N; ++j)
+        if (slots[j] == s) atomicMax(&code, 4);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = code;
+}
+
+}  // namespace
+
+hipError_t launch_index_checks(const gdr_args &a, bool prefill, int *flag_dev, hipStream_t stream) {
+  hipLaunchKernelGGL(index_check_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.slot_idx,
+                     a.N, (int64_t)a.T_total, (int64_t)a.num_slots, prefill ? 1 : 0, flag_dev);
+  return hipGetLastError();
+}
+
+}  // namespace gdr
+
+using namespace gdr;
+
+GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a) {
+  (void)a;
+  return 0;  // the fused chunk schedule keeps every intermediate on chip
+}
+
+GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  (void)workspace;
+  gdr_status s = validate(a, true);
+  if (s != GDR_OK) return s;
+  if (ws_bytes < gdr_chunk_fwd_workspace_bytes(a)) return fail(GDR_E_WORKSPACE, "workspace too small");
+  if (a->N == 0) return GDR_OK;
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_chunk_fwd(*a, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) {
+  gdr_status s = validate(a, false);
+  if (s != GDR_OK) return s;
+  if (a->N == 0) return GDR_OK;
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, false, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_recurrent_step(*a, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent_step launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+GDR_EXPORT const char *gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_E_INVALID: return "invalid argument";
+    case GDR_E_UNSUPPORTED: return "unsupported configuration";
+    case GDR_E_WORKSPACE: return "workspace too small";
+    case GDR_E_HIP: return "HIP runtime error";
+    case GDR_E_DEVICE_CHECK: return "device-side index check failed";
+    default: return "unknown status";
+  }
+}
+
+GDR_EXPORT const char *gdr_last_error(void) { return g_last_error; }

@@ -1,0 +1,45 @@
+// Internal declarations and device helpers shared by the HIP sources of
+// libgdr. Not part of the public ABI (include/gdr.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr.h"
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------
+// scalar conversions (bf16 carried as its 16-bit pattern)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// hi = bf16(x), lo = bf16(x - hi): hi + lo carries 16 significant bits of x.
+__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+// ---------------------------------------------------------------------------
+// launchers (defined next to their kernels)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_recurrent_step(const gdr_args &a, hipStream_t stream);
+hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
+// Writes 0 to *flag_dev when cu_seqlens (prefill) and slot_idx are valid,
+// else a nonzero code; flag_dev is a device int.
+hipError_t launch_index_checks(const gdr_args &a, bool prefill, int *flag_dev,
+                               hipStream_t stream);
+
+}  // namespace gdr

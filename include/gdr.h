@@ -1,0 +1,144 @@
+/*
+ * gdr.h - C ABI of the gated delta rule forward pass on AMD MI355X (gfx950).
+ *
+ * The method (per value head, state S in R^{d_v x d_k}, value-by-key):
+ *     S~  = S * alpha_t            (scalar gate)   or  S Diag(alpha_t) (channel gate)
+ *     e_t = beta_t (v_t - S~ k_t)
+ *     S   = S~ + e_t k_t^T
+ *     o_t = S (scale q_t)          read after the write
+ * as boxed in "You Could Have Come Up With Kimi Delta Attention" (opening
+ * display; sections 3 and 4) and listed as five steps on the "gated_delta"
+ * Mojo module page. The linear rule replaces the delta write by the additive
+ * write S = S~ + v_t k_t^T ("From Attention to Learned Memory", section 1).
+ * Gates arrive as g = log(alpha) <= 0 (the KDA page, section 4, notes that
+ * implementations store this form and exponentiate it).
+ *
+ * Two schedules compute the same result:
+ *   gdr_chunk_fwd       chunkwise prefill over a ragged batch (the chunk
+ *                       regrouping of section 6 of the KDA page and section 4
+ *                       of "From Attention to Learned Memory");
+ *   gdr_recurrent_step  one token per sequence (the tokenwise recurrence).
+ *
+ * Memory. Every pointer is device memory owned by the caller; the library
+ * neither allocates, frees nor keeps any of them after the call returns.
+ * Work is enqueued on `stream` and runs asynchronously: outputs and the state
+ * pool are ready once the stream has reached that point.
+ *
+ * Layouts (elements, row-major):
+ *   q, k        [T_total, HK, DK]   token t starts at t * {q,k}_stride_t; the
+ *                                   HK*DK values of one token are contiguous
+ *   v           [T_total, HV, DV]   token t starts at t * v_stride_t
+ *   g           [T_total, HV] (SCALAR) or [T_total, HV, DK] (CHANNEL), fp32
+ *   beta        [T_total, HV] fp32, in (0, 1]
+ *   o           [T_total, HV, DV]   contiguous, written (never read)
+ *   state_pool  [num_slots, HV, DK, DV]: S^T per slot and value head, updated
+ *               in place for the slots named by slot_idx; other slots are
+ *               never touched ("gated_delta" Mojo page, tensor shapes)
+ *   slot_idx    [N] int32, distinct, in [0, num_slots)
+ *   cu_seqlens  [N+1] int32, 0 = cu[0] <= cu[1] <= ... <= cu[N] = T_total;
+ *               sequence n is tokens cu[n] .. cu[n+1]-1 (prefill only)
+ * Value head h reads key head h / (HV / HK) (grouped heads, Mojo page).
+ *
+ * Errors. Everything checkable on the host is checked before any work is
+ * enqueued; on error nothing is launched and no memory is touched. Contents
+ * of device arrays (cu_seqlens monotone, slots in range and distinct, finite
+ * inputs) are the caller's contract; GDR_FLAG_DEBUG_CHECKS verifies the index
+ * arrays on the device first (this synchronises the stream).
+ *
+ * Thread safety: the library keeps no state besides a thread-local error
+ * message. Concurrent calls are safe when they write disjoint pool slots and
+ * outputs.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_E_INVALID = 1,      /* malformed arguments (null pointer, bad size, aliasing) */
+  GDR_E_UNSUPPORTED = 2,  /* well-formed but not built (head dim, chunk size, dtype) */
+  GDR_E_WORKSPACE = 3,    /* workspace smaller than gdr_chunk_fwd_workspace_bytes */
+  GDR_E_HIP = 4,          /* the HIP runtime reported an error at launch */
+  GDR_E_DEVICE_CHECK = 5  /* GDR_FLAG_DEBUG_CHECKS found a bad cu_seqlens or slot_idx */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* DELTA: the gated delta rule. LINEAR: S = S~ + v k^T (no prediction, no
+ * beta; with gate NONE this is plain linear attention, alpha = 1). */
+typedef enum gdr_rule { GDR_RULE_DELTA = 0, GDR_RULE_LINEAR = 1 } gdr_rule;
+
+/* NONE: alpha = 1 (g ignored). SCALAR: one g per token and value head.
+ * CHANNEL: one g per token, value head and key channel (KDA). */
+typedef enum gdr_gate { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gdr_gate;
+
+enum {
+  GDR_FLAG_ZERO_INIT = 1u,     /* start every sequence from S = 0 instead of its pool slot */
+  GDR_FLAG_DEBUG_CHECKS = 2u   /* verify cu_seqlens / slot_idx on the device first */
+};
+
+typedef struct gdr_args {
+  const void *q;                /* [T_total, HK, DK] in_dtype                              */
+  const void *k;                /* [T_total, HK, DK] in_dtype                              */
+  const void *v;                /* [T_total, HV, DV] in_dtype                              */
+  int64_t q_stride_t;           /* elements between tokens of q (>= HK*DK)                 */
+  int64_t k_stride_t;           /* elements between tokens of k (>= HK*DK)                 */
+  int64_t v_stride_t;           /* elements between tokens of v (>= HV*DV)                 */
+  gdr_dtype in_dtype;           /* type of q, k, v                                         */
+  const float *g;               /* log(alpha) <= 0; layout by gate; NULL for GATE_NONE     */
+  const float *beta;            /* [T_total, HV]; required for DELTA, ignored for LINEAR   */
+  void *o;                      /* [T_total, HV, DV] out_dtype; must not overlap any input */
+  gdr_dtype out_dtype;
+  void *state_pool;             /* [num_slots, HV, DK, DV] state_dtype, read and written   */
+  gdr_dtype state_dtype;
+  int64_t num_slots;
+  const int32_t *slot_idx;      /* [N]                                                     */
+  const int32_t *cu_seqlens;    /* [N+1] prefill; ignored (may be NULL) by the step        */
+  int32_t N;                    /* sequences                                               */
+  int32_t HK, HV;               /* key heads, value heads (HV % HK == 0)                   */
+  int32_t DK, DV;               /* head dims, each 64 or 128                               */
+  int64_t T_total;              /* tokens in q/k/v/o (the step requires T_total == N)      */
+  float scale;                  /* query scale; callers normally pass DK^-1/2              */
+  int32_t chunk_size;           /* prefill tile length in tokens: 64                       */
+  gdr_rule rule;
+  gdr_gate gate;
+  uint32_t flags;               /* GDR_FLAG_*                                              */
+} gdr_args;
+
+/* GDR_ABI_VERSION of the loaded library. */
+int gdr_abi_version(void);
+
+/* Bytes of device workspace gdr_chunk_fwd needs for these arguments (0 when
+ * the fused schedule needs none). Returns 0 for arguments it cannot size. */
+size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a);
+
+/* Chunkwise prefill over the ragged batch described by cu_seqlens: writes o
+ * for every token and the final state of each sequence into its pool slot.
+ * Zero-length sequences write their (initial) state back unchanged. N == 0 is
+ * a no-op. `workspace` may be NULL when ws_bytes == 0. */
+gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* One recurrent step: token n of q/k/v/g/beta belongs to sequence n
+ * (T_total == N); reads and writes pool slot slot_idx[n] in place. */
+gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *gdr_status_string(gdr_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *gdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H */

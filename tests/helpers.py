@@ -1,0 +1,92 @@
+"""Shared helpers for the GPU parity tests: move seeded inputs to the device,
+run the oracle on the same values, and apply the tolerance gate.
+
+Tolerance gate (stated once, used everywhere):
+  * fp32 inputs: max |o_gpu - o_ref| <= 1e-4 (absolute), same for an fp32 state;
+  * bf16 inputs: max |o_gpu - o_ref| <= 3e-3 * RMS(o_ref), same for an fp32
+    state relative to RMS(S_ref);
+  * a bf16 pool cannot hold the reference exactly: the GPU rounds its fp32
+    state and the oracle its fp64 state to bf16, and two values that straddle
+    a rounding midpoint land one bf16 step apart (a step is at most 2^-7 of
+    the value). Its entries are gated elementwise by
+    |S_gpu - S_ref| <= 2^-7 |S_ref| + 3e-3 RMS(S_ref);
+  * slots that no sequence names must come back bit-identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+
+def dev(x, dtype: str, device="cuda"):
+    import torch
+    if x is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def host(t, dtype: str) -> np.ndarray:
+    """Device tensor -> float64 numpy (exact widening)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        bits = t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        return synth.bf16_bits_to_f64(bits)
+    return t.detach().cpu().double().numpy()
+
+
+def to_device(w: synth.Workload, x: dict, device="cuda") -> dict:
+    return {
+        "q": dev(x["q"], w.in_dtype, device), "k": dev(x["k"], w.in_dtype, device),
+        "v": dev(x["v"], w.in_dtype, device),
+        "g": dev(x["g"], "f32", device), "beta": dev(x["beta"], "f32", device),
+        "pool": dev(x["pool"], w.state_dtype, device),
+        "slot_idx": dev(x["slot_idx"], "i32", device),
+        "cu_seqlens": dev(x["cu_seqlens"], "i32", device),
+    }
+
+
+def widened(w: synth.Workload, x: dict) -> dict:
+    return {
+        "q": synth.widen(x["q"], w.in_dtype), "k": synth.widen(x["k"], w.in_dtype),
+        "v": synth.widen(x["v"], w.in_dtype),
+        "g": None if x["g"] is None else x["g"].astype(np.float64),
+        "beta": None if x["beta"] is None else x["beta"].astype(np.float64),
+        "pool": synth.widen(x["pool"], w.state_dtype),
+    }
+
+
+def oracle_run(w: synth.Workload, xw: dict, slot_idx, cu_seqlens, scale):
+    return oracle.recurrent_fp64(xw["q"], xw["k"], xw["v"], xw["g"], xw["beta"], xw["pool"],
+                                 slot_idx, cu_seqlens, scale=scale, rule=w.rule, gate=w.gate,
+                                 zero_init=w.zero_init, state_dtype=w.state_dtype)
+
+
+def rms(x) -> float:
+    x = np.asarray(x, np.float64)
+    return float(np.sqrt(np.mean(x * x))) if x.size else 0.0
+
+
+def check_out(o_gpu: np.ndarray, o_ref: np.ndarray, in_dtype: str, what="o"):
+    err = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+    if in_dtype == "f32":
+        bound = 1e-4
+    else:
+        bound = 3e-3 * rms(o_ref)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
+    assert err <= bound, f"{what}: max|err| {err:.3e} > {bound:.3e} (rms {rms(o_ref):.3e})"
+    return err, bound
+
+
+def check_state(s_gpu: np.ndarray, s_ref: np.ndarray, in_dtype: str, state_dtype: str):
+    if state_dtype == "bf16":
+        bound = 2.0 ** -7 * np.abs(s_ref) + 3e-3 * rms(s_ref)
+        bad = np.abs(s_gpu - s_ref) > bound
+        assert not bad.any(), f"state: {bad.sum()} entries outside the bf16 gate"
+        return
+    check_out(s_gpu, s_ref, in_dtype, what="state")

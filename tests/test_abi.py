@@ -1,0 +1,144 @@
+"""The C ABI library loads, exports what include/gdr.h declares, and rejects
+malformed arguments on the host before touching the GPU (no compute here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+def _lib():
+    import gated_delta_rule_gdr_amd as gdr
+    if not os.path.exists(gdr.lib_path):
+        pytest.fail("libgdr.so is not built (python -m gated_delta_rule_gdr_amd.build)")
+    return gdr, gdr.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gdr_[a-z_0-9]+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["gdr_abi_version", "gdr_chunk_fwd_workspace_bytes", "gdr_chunk_fwd",
+                            "gdr_recurrent_step", "gdr_status_string", "gdr_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    gdr, L = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", gdr.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(gdr_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert L.gdr_abi_version() == 1
+
+
+def test_args_struct_matches_header_field_order():
+    import gated_delta_rule_gdr_amd as gdr
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct gdr_args {") + 25:text.index("} gdr_args;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        for part in decl.split(","):
+            ids = re.findall(r"\w+", part)
+            if ids:
+                fields.append(ids[-1])
+    names = [f[0] for f in gdr.Args._fields_]
+    assert fields == names
+
+
+def _valid_args(gdr):
+    a = gdr.Args()
+    a.q = a.k = a.v = 0x1000
+    a.o = 0x900000
+    a.g, a.beta = 0x2000, 0x3000
+    a.state_pool = 0x4000000
+    a.slot_idx, a.cu_seqlens = 0x5000, 0x6000
+    a.q_stride_t = a.k_stride_t = 2 * 128
+    a.v_stride_t = 4 * 128
+    a.in_dtype, a.out_dtype, a.state_dtype = 1, 0, 0
+    a.num_slots = 4
+    a.N, a.HK, a.HV, a.DK, a.DV = 2, 2, 4, 128, 128
+    a.T_total = 8
+    a.scale = 128 ** -0.5
+    a.chunk_size = 64
+    a.rule, a.gate, a.flags = 0, 1, 0
+    return a
+
+
+CASES = [
+    ("HV % HK", dict(HV=3), 1),
+    ("bad head dim", dict(DK=96, DV=96), 2),
+    ("DK != DV", dict(DV=64), 2),
+    ("chunk size", dict(chunk_size=32), 2),
+    ("null beta (delta)", dict(beta=None), 1),
+    ("null g (gated)", dict(g=None), 1),
+    ("null q", dict(q=None), 1),
+    ("null pool", dict(state_pool=None), 1),
+    ("null cu_seqlens", dict(cu_seqlens=None), 1),
+    ("short stride", dict(q_stride_t=100), 1),
+    ("too few slots", dict(num_slots=1), 1),
+    ("unknown dtype", dict(in_dtype=7), 1),
+    ("unknown rule", dict(rule=5), 1),
+    ("unknown gate", dict(gate=9), 1),
+    ("unknown flag", dict(flags=0x80), 1),
+    ("nan scale", dict(scale=float("nan")), 1),
+    ("negative N", dict(N=-1), 1),
+    ("o aliases q", dict(o=0x1000 + 64), 1),
+    ("o aliases pool", dict(o=0x4000000 + 4096), 1),
+]
+
+
+@pytest.mark.parametrize("name,change,status", CASES, ids=[c[0] for c in CASES])
+def test_chunk_fwd_rejects_on_host(name, change, status):
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    for k, v in change.items():
+        setattr(a, k, v)
+    s = L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None)
+    assert s == status, (name, L.gdr_last_error())
+    assert L.gdr_last_error().decode()
+
+
+def test_recurrent_step_rejects_on_host():
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    assert L.gdr_recurrent_step(ctypes.byref(a), None) == 1   # T_total != N
+    a.T_total = 2
+    a.HV = 3
+    assert L.gdr_recurrent_step(ctypes.byref(a), None) == 1
+    assert L.gdr_recurrent_step(None, None) == 1
+
+
+def test_empty_batch_is_a_no_op():
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    a.N, a.T_total = 0, 0
+    a.q = a.k = a.v = a.o = a.state_pool = a.slot_idx = a.cu_seqlens = None
+    assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 0
+    assert L.gdr_recurrent_step(ctypes.byref(a), None) == 0
+    assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_status_strings():
+    gdr, L = _lib()
+    for s in range(6):
+        assert L.gdr_status_string(s).decode()
+    assert L.gdr_status_string(0) == b"ok"
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import gated_delta_rule_gdr_amd as gdr
+    monkeypatch.setattr(gdr, "lib_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdr, "_lib", None)
+    with pytest.raises(ImportError):
+        gdr.load()

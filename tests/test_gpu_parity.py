@@ -1,0 +1,181 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle on
+small seeded inputs that span several chunks, ragged tails, empty sequences,
+grouped heads and every gate / rule / dtype combination."""
+import itertools
+
+import numpy as np
+import pytest
+
+import synth
+from helpers import (check_out, check_state, host, oracle_run, to_device, widened)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gdr():
+    import gated_delta_rule_gdr_amd as gdr
+    gdr.load()
+    return gdr
+
+
+def small_workload(D, in_dtype, gate, rule, state_dtype, zero_init, seqlens, HK=2, HV=4,
+                   slots=9, seed=11):
+    return synth.Workload(
+        name="small", seqlens=tuple(seqlens), HK=HK, HV=HV, DK=D, DV=D, in_dtype=in_dtype,
+        gate=gate, rule=rule, gate_shift=2.0 if gate != "channel" else 3.0,
+        state_dtype=state_dtype, num_slots=slots, zero_init=zero_init, seed=seed)
+
+
+RAGGED = (0, 1, 63, 64, 65, 130, 200)
+COMBOS = list(itertools.product([64, 128], ["bf16", "f32"], ["none", "scalar", "channel"],
+                                ["delta", "linear"]))
+
+
+@pytest.mark.parametrize("D,in_dtype,gate,rule", COMBOS,
+                         ids=[f"d{d}-{i}-{g}-{r}" for d, i, g, r in COMBOS])
+def test_chunk_fwd_matches_oracle(D, in_dtype, gate, rule):
+    gdr = _gdr()
+    state_dtype = "bf16" if (D == 128 and gate == "scalar") else "f32"
+    w = small_workload(D, in_dtype, gate, rule, state_dtype, zero_init=False, seqlens=RAGGED)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    pool_before = d["pool"].clone()
+    scale = D ** -0.5
+    print(f"chunk_fwd D={D} in={in_dtype} gate={gate} rule={rule} lens={RAGGED}", flush=True)
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      d["cu_seqlens"], scale=scale, rule=rule, gate=gate)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], scale)
+    check_out(host(o, in_dtype), o_ref, in_dtype)
+    pool = host(d["pool"], state_dtype)
+    for n, s in enumerate(x["slot_idx"]):
+        check_state(pool[s], pool_ref[s], in_dtype, state_dtype)
+    untouched = np.setdiff1d(np.arange(w.num_slots), x["slot_idx"])
+    assert torch.equal(d["pool"][untouched], pool_before[untouched])
+
+
+@pytest.mark.parametrize("zero_init", [True, False])
+def test_chunk_fwd_zero_init_and_bf16_output(zero_init):
+    gdr = _gdr()
+    w = small_workload(128, "bf16", "scalar", "delta", "f32", zero_init, seqlens=(100, 7, 64))
+    x = synth.generate(w)
+    d = to_device(w, x)
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      d["cu_seqlens"], zero_init=zero_init, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], 128 ** -0.5)
+    # a bf16 output carries its own rounding (2^-9 relative); gate it elementwise
+    og = host(o, "bf16")
+    assert np.all(np.abs(og - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + 3e-3 * np.sqrt(np.mean(o_ref ** 2)))
+    for s in x["slot_idx"]:
+        check_state(host(d["pool"], "f32")[s], pool_ref[s], "bf16", "f32")
+
+
+STEP_COMBOS = list(itertools.product([64, 128], ["bf16", "f32"], ["none", "scalar", "channel"],
+                                     ["delta", "linear"], ["f32", "bf16"]))
+
+
+@pytest.mark.parametrize("D,in_dtype,gate,rule,state_dtype", STEP_COMBOS,
+                         ids=[f"d{d}-{i}-{g}-{r}-pool{s}" for d, i, g, r, s in STEP_COMBOS])
+def test_recurrent_step_matches_oracle(D, in_dtype, gate, rule, state_dtype):
+    """Three consecutive steps chained through the pool."""
+    gdr = _gdr()
+    N, steps = 6, 3
+    w = small_workload(D, in_dtype, gate, rule, state_dtype, zero_init=False,
+                       seqlens=(1,) * N, slots=10).replace(steps=steps)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    xw = widened(w, x)
+    pool_ref = xw["pool"]
+    scale = D ** -0.5
+    print(f"recurrent_step D={D} in={in_dtype} gate={gate} rule={rule} pool={state_dtype}", flush=True)
+    for s in range(steps):
+        sl = slice(s * N, (s + 1) * N)
+        o = gdr.recurrent_step(d["q"][sl], d["k"][sl], d["v"][sl],
+                               None if d["g"] is None else d["g"][sl],
+                               None if d["beta"] is None else d["beta"][sl],
+                               d["pool"], d["slot_idx"], scale=scale, rule=rule, gate=gate)
+        torch.cuda.synchronize()
+        xs = {k: (None if v is None else v[sl]) for k, v in xw.items() if k != "pool"}
+        xs["pool"] = pool_ref
+        o_ref, pool_ref = oracle_run(w.replace(zero_init=False), xs, x["slot_idx"],
+                                     np.arange(N + 1), scale)
+        check_out(host(o, in_dtype), o_ref, in_dtype)
+    pool = host(d["pool"], state_dtype)
+    for s in x["slot_idx"]:
+        check_state(pool[s], pool_ref[s], in_dtype, state_dtype)
+    untouched = np.setdiff1d(np.arange(w.num_slots), x["slot_idx"])
+    np.testing.assert_array_equal(pool[untouched], xw["pool"][untouched])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_chunk_equals_repeated_steps(gate):
+    """The two schedules agree: one chunk_fwd over T tokens = T recurrent steps."""
+    gdr = _gdr()
+    N, T, D = 3, 150, 128
+    w = small_workload(D, "bf16", gate, "delta", "f32", zero_init=False, seqlens=(T,) * N)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    pool0 = d["pool"].clone()
+    o_chunk = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"],
+                            d["slot_idx"], d["cu_seqlens"])
+    pool_chunk = d["pool"].clone()
+    d["pool"].copy_(pool0)
+    outs = []
+    for t in range(T):
+        idx = torch.arange(N, device="cuda") * T + t
+        outs.append(gdr.recurrent_step(d["q"][idx], d["k"][idx], d["v"][idx], d["g"][idx],
+                                       d["beta"][idx], d["pool"], d["slot_idx"]))
+    o_step = torch.stack(outs, 1).reshape(N * T, w.HV, D)
+    torch.cuda.synchronize()
+    ref = host(o_step, "f32")
+    check_out(host(o_chunk, "f32"), ref, "bf16")
+    for s in x["slot_idx"]:
+        check_state(host(pool_chunk, "f32")[s], host(d["pool"], "f32")[s], "bf16", "f32")
+
+
+def test_fused_qkv_strides():
+    """q, k, v may be views into one fused [T, 2 HK DK + HV DV] buffer (the
+    channel layout of the Mojo gated_delta module)."""
+    gdr = _gdr()
+    w = small_workload(128, "bf16", "scalar", "delta", "f32", False, seqlens=(70, 33))
+    x = synth.generate(w)
+    d = to_device(w, x)
+    T = w.T_total
+    kd, vd = w.HK * w.DK, w.HV * w.DV
+    fused = torch.cat([d["q"].reshape(T, kd), d["k"].reshape(T, kd), d["v"].reshape(T, vd)], 1)
+    q = fused[:, :kd].view(T, w.HK, w.DK)
+    k = fused[:, kd:2 * kd].view(T, w.HK, w.DK)
+    v = fused[:, 2 * kd:].view(T, w.HV, w.DV)
+    pool2 = d["pool"].clone()
+    o1 = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                       d["cu_seqlens"])
+    o2 = gdr.chunk_fwd(q, k, v, d["g"], d["beta"], pool2, d["slot_idx"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(d["pool"], pool2)
+
+
+def test_debug_checks_reject_bad_indices():
+    gdr = _gdr()
+    w = small_workload(64, "bf16", "scalar", "delta", "f32", False, seqlens=(5, 6))
+    x = synth.generate(w)
+    d = to_device(w, x)
+    bad = d["slot_idx"].clone()
+    bad[1] = bad[0]
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], bad,
+                      d["cu_seqlens"], debug_checks=True)
+    assert e.value.status == 5
+    cu = d["cu_seqlens"].clone()
+    cu[1] = 9   # beyond cu[2] = 11? keep monotone break explicit
+    cu[2] = 8
+    with pytest.raises(gdr.GdrError):
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      cu, debug_checks=True)
+    # valid indices pass and compute
+    gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                  d["cu_seqlens"], debug_checks=True)
+    torch.cuda.synchronize()
