@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one gdr_chunk_fwd call (the whole prefill path: loads, gate sums,
+Gram matrices, triangular solve, corrected values, outputs, state scan and
+write-back) over the workload's full batch, with inputs already resident in
+HBM. Three copies of the inputs/outputs are used in rotation so that no step
+reads what the previous one left in the 256 MB last-level cache. The decode
+path is timed alongside: 1000 consecutive gdr_recurrent_step launches over
+the 256-sequence decode workload, each step with a new token per sequence
+(64 distinct token sets in rotation; the state pool carries over).
+
+Prints one JSON line. `value` is prefill tokens per second for one layer (all
+heads); `roofline` describes the prefill kernel against HBM bandwidth (its
+binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
+fraction alongside; `decode` gives steps/s and HBM fraction of the step
+kernel; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", "chunk_fwd.hip")
+STEP_SRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", "recurrent_step.hip")
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (per launch)
+# ----------------------------------------------------------------------------
+
+def _isz(dtype: str) -> int:
+    return 2 if dtype == "bf16" else 4
+
+
+def prefill_bytes(w: synth.Workload, out_dtype="f32") -> int:
+    """q, k (per key head), v, g, beta read once; o written once; the state
+    read at sequence starts (unless zero-initialised) and written at ends."""
+    T, ie = w.T_total, _isz(w.in_dtype)
+    b = 2 * T * w.HK * w.DK * ie + T * w.HV * w.DV * ie
+    if w.gate == "scalar":
+        b += T * w.HV * 4
+    elif w.gate == "channel":
+        b += T * w.HV * w.DK * 4
+    if w.rule == "delta":
+        b += T * w.HV * 4
+    b += T * w.HV * w.DV * _isz(out_dtype)
+    st = w.N * w.HV * w.DK * w.DV * _isz(w.state_dtype)
+    b += st if w.zero_init else 2 * st
+    return b
+
+
+def prefill_flops(w: synth.Workload, C=64) -> int:
+    """Dense C x C tiles, no recompute (per token and value head):
+    delta 4C(dk + dv) + 6 dk dv, linear 2C(dk + dv) + 4 dk dv."""
+    if w.rule == "delta":
+        per = 4 * C * (w.DK + w.DV) + 6 * w.DK * w.DV
+    else:
+        per = 2 * C * (w.DK + w.DV) + 4 * w.DK * w.DV
+    return per * w.T_total * w.HV
+
+
+def step_bytes(w: synth.Workload, out_dtype="f32") -> int:
+    N, ie = w.N, _isz(w.in_dtype)
+    b = 2 * N * w.HV * w.DK * w.DV * _isz(w.state_dtype)
+    b += 2 * N * w.HK * w.DK * ie + N * w.HV * w.DV * ie
+    b += N * w.HV * 4 * (2 if w.rule == "delta" else 1)
+    b += N * w.HV * w.DV * _isz(out_dtype)
+    return b
+
+
+def _sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != _sha(src):
+        return None
+    return float(m.group(1))
+
+
+# ----------------------------------------------------------------------------
+# GPU legs
+# ----------------------------------------------------------------------------
+
+def _dev(x, dtype, device):
+    import torch
+    if x is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def bench_prefill(w: synth.Workload, steps: int, warmup: int, copies: int = 3):
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    gdr.load()
+    dev = torch.device("cuda", 0)
+    x = synth.generate(w)
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(
+            q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
+            v=_dev(x["v"], w.in_dtype, dev), g=_dev(x["g"], "f32", dev),
+            beta=_dev(x["beta"], "f32", dev), pool=_dev(x["pool"], w.state_dtype, dev),
+            o=torch.empty((w.T_total, w.HV, w.DV), dtype=torch.float32, device=dev)))
+    slot = _dev(x["slot_idx"], "i32", dev)
+    cu = _dev(x["cu_seqlens"], "i32", dev)
+    del x
+
+    def run(i):
+        s = sets[i % copies]
+        gdr.chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["pool"], slot, cu,
+                      rule=w.rule, gate=w.gate, zero_init=w.zero_init, o=s["o"],
+                      chunk_size=w.chunk_size)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        run(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in ev]
+    return wall / steps, float(np.mean(kms)), float(np.median(kms))
+
+
+def bench_decode(w: synth.Workload, steps: int, warmup: int = 10):
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    distinct = min(steps, 64)      # distinct token sets, used in rotation
+    ws = w.replace(steps=distinct)
+    x = synth.generate(ws)
+    N = w.N
+    q = _dev(x["q"], w.in_dtype, dev)
+    k = _dev(x["k"], w.in_dtype, dev)
+    v = _dev(x["v"], w.in_dtype, dev)
+    g = _dev(x["g"], "f32", dev)
+    beta = _dev(x["beta"], "f32", dev)
+    pool = _dev(x["pool"], w.state_dtype, dev)
+    slot = _dev(x["slot_idx"], "i32", dev)
+    o = torch.empty((N, w.HV, w.DV), dtype=torch.float32, device=dev)
+    del x
+
+    def run(s):
+        s %= distinct
+        sl = slice(s * N, (s + 1) * N)
+        gdr.recurrent_step(q[sl], k[sl], v[sl], g[sl], beta[sl], pool, slot, o=o,
+                           rule=w.rule, gate=w.gate)
+
+    for s in range(warmup):
+        run(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(steps):
+        run(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, e0.elapsed_time(e1) / steps
+
+
+# ----------------------------------------------------------------------------
+# CPU leg: the fp64 oracle on a bounded sample
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w: synth.Workload, budget_s: float = 15.0):
+    """Time the oracle (single BLAS thread) on the first sequence's first
+    tokens for all value heads; report tokens/s/layer for that sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    tok = 64
+    x = None
+    elapsed = 0.0
+    while True:
+        ws = w.replace(seqlens=(tok,))
+        x = synth.generate(ws)
+        args = dict(q=synth.widen(x["q"], w.in_dtype), k=synth.widen(x["k"], w.in_dtype),
+                    v=synth.widen(x["v"], w.in_dtype),
+                    g=None if x["g"] is None else x["g"].astype(np.float64),
+                    beta=None if x["beta"] is None else x["beta"].astype(np.float64),
+                    pool=synth.widen(x["pool"], w.state_dtype))
+        ctx = threadpool_limits(1) if threadpool_limits else None
+        t0 = time.perf_counter()
+        if ctx:
+            with ctx:
+                oracle.recurrent_fp64(**args, slot_idx=x["slot_idx"], cu_seqlens=[0, tok],
+                                      scale=w.DK ** -0.5, rule=w.rule, gate=w.gate,
+                                      zero_init=w.zero_init, state_dtype=w.state_dtype)
+        else:
+            oracle.recurrent_fp64(**args, slot_idx=x["slot_idx"], cu_seqlens=[0, tok],
+                                  scale=w.DK ** -0.5, rule=w.rule, gate=w.gate,
+                                  zero_init=w.zero_init, state_dtype=w.state_dtype)
+        elapsed = time.perf_counter() - t0
+        if elapsed > budget_s / 3 or tok >= w.seqlens[0]:
+            break
+        tok = min(w.seqlens[0], tok * 4)
+    return {"value": tok / elapsed, "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 tokenwise recurrence, first {tok} tokens of sequence 0, all "
+                      f"{w.HV} value heads, one BLAS thread; {elapsed:.2f} s"}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=synth.HEADLINE)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the gated delta rule "
+                                   "shards by (sequence, head) with no communication and "
+                                   "multi-GPU runs are not part of it"}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    w = synth.workload(args.workload)
+    torch.cuda.synchronize()
+    step_s, kernel_ms, kernel_med = bench_prefill(w, args.steps, args.warmup)
+    tokens_per_s = w.T_total / step_s
+    nbytes = prefill_bytes(w)
+    nflops = prefill_flops(w, w.chunk_size)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    traffic = committed_traffic("chunk_fwd", w.name, KERNEL_SRC)
+    result = {
+        "metric": "prefill tokens/s/layer + decode steps/s; % MFMA peak / % HBM BW",
+        "value": tokens_per_s,
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
+                "g=-softplus(N(0,1)-shift))",
+        "config": {"workload": w.name, "batch": w.N, "seq_len": int(w.seqlens[0]),
+                   "tokens": w.T_total, "key_heads": w.HK, "value_heads": w.HV,
+                   "head_dim": w.DK, "chunk": w.chunk_size, "gate": w.gate, "rule": w.rule,
+                   "in_dtype": w.in_dtype, "out_dtype": "f32", "state_dtype": w.state_dtype},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel", "kernel_ms_mean": kernel_ms,
+                     "kernel_ms_median": kernel_med, "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": nflops,
+                     "mfma_tflops": nflops / (kernel_ms * 1e-3) / 1e12,
+                     "mfma_frac": nflops / (kernel_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+    if not args.no_decode:
+        dw = synth.workload("decode_n256_hk16_hv32_d128")
+        d_step, d_kernel = bench_decode(dw, args.decode_steps)
+        db = step_bytes(dw)
+        result["decode"] = {
+            "workload": dw.name, "steps": args.decode_steps, "steps_per_s": 1.0 / d_step,
+            "us_per_step": d_step * 1e6, "kernel_us_per_step": d_kernel * 1e3,
+            "algorithmic_bytes_per_step": db,
+            "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
+            "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": committed_traffic("recurrent_step", dw.name, STEP_SRC)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

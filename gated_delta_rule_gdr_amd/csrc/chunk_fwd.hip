@@ -6,9 +6,8 @@
 // cumulative log-decay G_i (per key channel for the channel gate):
 //   R   = strict-lower( beta_i k_i^T D_{j+1:i} k_j )       key-key coefficients
 //   A   = lower( s q_i^T D_{j+1:i} k_j )                    query-key coefficients
-//   T   = (I + R)^-1                                        unit lower triangular
 //   X   = (D_{0:i} k_i)^T S^T  rows                         prediction of the incoming state
-//   Vb  = T (beta (V - X))                                  solved errors e_i
+//   Vb  = (I + R)^-1 (beta (V - X))                         solved errors e_i
 //   O   = s (D_{0:i} q_i)^T S^T + A Vb                      outputs (read after write)
 //   S' = S D_{0:C-1} + sum_j e_j (D_{j+1:C-1} k_j)^T       chunk-end state
 // The linear rule drops R, T and X (Vb = V, no beta).
@@ -19,10 +18,13 @@
 // the MFMA that updates it, so it never leaves the chip between chunks: HBM
 // sees q, k, v, g, beta once, o once, and the state at sequence ends only.
 // Per chunk: cooperative loads into LDS; gate prefix sums; the two Gram
-// matrices on MFMA; the 64x64 unit-lower inverse (forward substitution on the
-// 16x16 diagonal blocks, then the block merges T21 = -T22 A21 T11 of
-// section 4 of "From Attention to Learned Memory", 16 -> 32 -> 64); then each
-// wave's state-dependent products on MFMA.
+// matrices on MFMA; the inverses T_II of the four 16x16 diagonal blocks of
+// I + R by forward substitution (section 4 of "From Attention to Learned
+// Memory" builds the 64x64 inverse from these blocks); then each wave's
+// state-dependent products on MFMA, where the 64-row unit lower triangular
+// system is solved blockwise on the right-hand side itself,
+// Vb_I = T_II (R_v,I - sum_{J<I} R_IJ Vb_J), so the full inverse is never
+// formed.
 //
 // Precision. MFMA runs on bf16 operands with fp32 accumulation. Inputs that
 // are bf16 are exact operands. Every computed operand (state, T, A, the
@@ -124,6 +126,63 @@ __device__ __forceinline__ void chainfrag(const f32x4 &t0, const f32x4 &t1, Frag
   split8(x, f);
 }
 
+// 16x16x16 products (k = 4g .. 4g+3 per lane): the accumulator layout of a
+// 16-row tile is directly a B fragment, so block-triangular chains need no
+// reordering.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+struct Frag4 {
+  bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(const f32x4 &x, Frag4 &f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    f.hi[j] = h;
+    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  }
+}
+
+// acc += a * b, both split (three passes, lo terms first)
+__device__ __forceinline__ f32x4 mm16(const Frag4 &a, const Frag4 &b, f32x4 c) {
+  c = mfma16(a.lo, b.hi, c);
+  c = mfma16(a.hi, b.lo, c);
+  return mfma16(a.hi, b.hi, c);
+}
+
+// A fragment of a 16x16 block of an fp32 LDS matrix: row `row`, columns
+// col0 + 4g .. col0 + 4g + 3.
+__device__ __forceinline__ void ldfrag4(const float *base, int pitch, int row, int col0, int g,
+                                        Frag4 &f) {
+  const float4 a = *reinterpret_cast<const float4 *>(base + row * pitch + col0 + 4 * g);
+  const f32x4 x = {a.x, a.y, a.z, a.w};
+  split4(x, f);
+}
+
+
+// Split fragment of a 16x16 block of a pre-split bf16 plane pair: row `row`,
+// columns col0 + 4g .. col0 + 4g + 3.
+__device__ __forceinline__ void ldsplit4(const uint16_t *hi, const uint16_t *lo, int pitch, int row,
+                                         int col0, int g, Frag4 &f) {
+  const int o = row * pitch + col0 + 4 * g;
+  f.hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi + o));
+  f.lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo + o));
+}
+
+__device__ __forceinline__ void store_split(uint16_t *hi, uint16_t *lo, int idx, float x) {
+  const __bf16 h = static_cast<__bf16>(x);
+  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
+  hi[idx] = __builtin_bit_cast(uint16_t, h);
+  lo[idx] = __builtin_bit_cast(uint16_t, l);
+}
+
 // ---------------------------------------------------------------------------
 // LDS layout
 // ---------------------------------------------------------------------------
@@ -139,7 +198,7 @@ struct Smem {
   static constexpr int PK = D + (OPF32 ? 4 : 8);   // token-major rows
   static constexpr int PT = C + (OPF32 ? 4 : 8);   // key-major rows (transposed keys)
   static constexpr int PV = BV + (IN_F32 ? 4 : 8);
-  static constexpr int PF = C + 4;                 // fp32 C x C
+  static constexpr int PB = C + 8;                 // bf16 C x C planes
   Op kk[C][PK];   // keys (channel: e^{G} k) - A operand of X, rows of R
   Op qq[C][PK];   // queries (channel: e^{G} q)
   // Transposed keys for the state update (channel: e^{-G} k). For the channel
@@ -149,11 +208,15 @@ struct Smem {
     Op kinv[C][PK];
   };
   In vv[C][PV];   // this workgroup's value columns
-  // R then T (delta rule); during the channel-gate prep also the g staging.
+  // The C x C coefficient matrices, already split into bf16 hi / lo planes:
+  // R's off-diagonal blocks and the diagonal-block inverses T_II share rt*,
+  // A sits in aq*. rdT holds R's diagonal blocks in fp32, transposed, for the
+  // solve. During the channel-gate prep the same storage stages g.
   union {
     struct {
-      float rt[C][PF];
-      float aq[C][PF];
+      uint16_t rth[C][PB], rtl[C][PB];
+      uint16_t aqh[C][PB], aql[C][PB];
+      float rdT[4][16][17];
     };
     float gstage[C][D];
   };
@@ -217,10 +280,181 @@ __device__ __forceinline__ void copy8(const void *base, int64_t off, bool valid,
   }
 }
 
+// Registers holding one chunk's keys, queries, values and gates between its
+// global loads and its LDS stores, so that the loads of chunk c+1 are in
+// flight while chunk c computes.
+// (Vector types, not arrays: they stay in registers as SSA values.)
+template <int N>
+struct U32Vec {
+  typedef unsigned int type __attribute__((ext_vector_type(N)));
+};
+
+template <bool IN_F32, int D>
+struct Prefetch {
+  static constexpr int E = IN_F32 ? 4 : 8;       // elements per 16-byte unit
+  static constexpr int KU = C * D / E / 256;     // units per thread, keys (and queries)
+  static constexpr int VU = C * BV / E / 256;    // units per thread, values
+  typename U32Vec<4 * KU>::type k, q;
+  typename U32Vec<4 * VU>::type v;
+  float g, beta;                                 // wave 0: token `lane`
+};
+
+template <class Vec>
+__device__ __forceinline__ void put4(Vec &v, int u, const uint4 x) {
+  v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
+}
+template <class Vec>
+__device__ __forceinline__ uint4 get4(const Vec &v, int u) {
+  return make_uint4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+}
+
+// Where each lane's prefetch units sit inside a chunk: unit u of the keys is
+// row krow + u * krs, 16-byte column block kc (same for queries); values
+// likewise with vrow / vrs / vc.
+struct LaneOffsets {
+  int krow, krs, kc;
+  int vrow, vrs, vc;
+};
+
+template <bool IN_F32, int D>
+__device__ __forceinline__ LaneOffsets lane_offsets() {
+  using PF = Prefetch<IN_F32, D>;
+  constexpr int E = PF::E;
+  const int tid = threadIdx.x;
+  LaneOffsets o;
+  o.krow = tid / (D / E);
+  o.krs = 256 / (D / E);
+  o.kc = (tid % (D / E)) * 16;
+  o.vrow = tid / (BV / E);
+  o.vrs = 256 / (BV / E);
+  o.vc = (tid % (BV / E)) * 16;
+  return o;
+}
+
+// Issue the global loads of the chunk starting at token t0 (L valid rows).
+// Rows past the chunk's end are clamped to its last row so every load is in
+// bounds and unconditional; they are zeroed when stored to LDS. No load is
+// waited for here: the registers are consumed by the next chunk's LDS stores.
+template <bool IN_F32, int GATE, bool DELTA, int D>
+__device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkParams &p,
+                                           const LaneOffsets &lo, int64_t t0, int L, int h,
+                                           int hk, int vb) {
+  using PF = Prefetch<IN_F32, D>;
+  constexpr int es = IN_F32 ? 4 : 2;
+  const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * es;
+  const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * es;
+  const char *vb_ = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BV) * es;
+  const uint32_t ks = (uint32_t)(p.k_stride * es), qs = (uint32_t)(p.q_stride * es),
+                 vs = (uint32_t)(p.v_stride * es);
+  const int last = L - 1;
+#pragma unroll
+  for (int u = 0; u < PF::KU; ++u) {
+    const uint32_t row = (uint32_t)min(lo.krow + u * lo.krs, last);
+    put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + lo.kc)));
+    put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (row * qs + lo.kc)));
+  }
+#pragma unroll
+  for (int u = 0; u < PF::VU; ++u) {
+    const uint32_t row = (uint32_t)min(lo.vrow + u * lo.vrs, last);
+    put4(pf.v, u, *reinterpret_cast<const uint4 *>(vb_ + (row * vs + lo.vc)));
+  }
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int64_t th = (t0 + min(tid, last)) * p.HV + h;
+    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
+    if constexpr (DELTA) pf.beta = p.beta[th];
+  }
+}
+
+// Gram matrices of one chunk, lower 16x16 tiles (I >= J). Delta rule: waves
+// 0-1 form K K^T (-> R), waves 2-3 form Q K^T (-> A); each wave owns row
+// blocks {a, 3-a} (five tiles, its A fragments loaded once, five independent
+// MFMA chains). Linear rule: wave w forms the Q K^T tiles of row block w. The
+// wave's role is a template argument so each role is straight-line code.
+template <int W, bool IN_F32, int GATE, bool DELTA, int D, class SM>
+__device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g) {
+  constexpr bool OPF32 = SM::OPF32;
+  constexpr int NS = D / 32;
+  constexpr bool ISQ = DELTA ? (W >= 2) : true;
+  constexpr int IA = DELTA ? (W & 1) : W;
+  constexpr int NRB = DELTA ? 2 : 1;
+  constexpr int IB = DELTA ? 3 - IA : IA;
+  constexpr int JMAX = IB > IA ? IB : IA;
+  using Op = typename SM::Op;
+  const Op *arow = ISQ ? &sm.qq[0][0] : &sm.kk[0][0];
+
+  Frag fa[NRB][NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    ldfrag(arow, SM::PK, 16 * IA + r, 32 * s, g, fa[0][s]);
+    if constexpr (DELTA) ldfrag(arow, SM::PK, 16 * IB + r, 32 * s, g, fa[NRB - 1][s]);
+  }
+  f32x4 acc[NRB][4];
+#pragma unroll
+  for (int J = 0; J <= JMAX; ++J) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag fb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (GATE == GDR_GATE_CHANNEL && !DELTA) {
+        // e^{-G} k is only held transposed for the linear rule
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kcol = 32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+          x[j] = sm.kt[kcol][16 * J + r];
+        }
+        split8(x, fb[s]);
+      } else if constexpr (GATE == GDR_GATE_CHANNEL) {
+        ldfrag(&sm.kinv[0][0], SM::PK, 16 * J + r, 32 * s, g, fb[s]);
+      } else {
+        ldfrag(&sm.kk[0][0], SM::PK, 16 * J + r, 32 * s, g, fb[s]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int I = rb ? IB : IA;
+      if (J <= I) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<OPF32, OPF32>(fa[rb][s], fb[s], acc[rb][J]);
+      }
+    }
+  }
+  // decay, write strength, mask; store split planes (+ R's diagonal in fp32)
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int I = rb ? IB : IA;
+    const float4 Gi = *reinterpret_cast<const float4 *>(&sm.G[16 * I + 4 * g]);
+    const float4 Bi = *reinterpret_cast<const float4 *>(&sm.beta[16 * I + 4 * g]);
+    const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      const int jj = 16 * J + r;
+      const float Gj = sm.G[jj];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 16 * I + 4 * g + i;
+        float gam = 1.f;
+        if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(gi[i] - Gj);
+        if constexpr (ISQ) {
+          const float val = (jj <= ii) ? p.scale * acc[rb][J][i] * gam : 0.f;
+          store_split(&sm.aqh[0][0], &sm.aql[0][0], ii * SM::PB + jj, val);
+        } else {
+          const float val = (jj < ii) ? bi[i] * acc[rb][J][i] * gam : 0.f;
+          if (J < I) store_split(&sm.rth[0][0], &sm.rtl[0][0], ii * SM::PB + jj, val);
+          else sm.rdT[I][r][4 * g + i] = val;   // transposed diagonal block
+        }
+      }
+    }
+  }
+}
+
 template <bool IN_F32, int GATE, bool DELTA, int D>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using SM = Smem<IN_F32, GATE, DELTA, D>;
-  using Op = typename SM::Op;
+  using In = typename SM::In;
+  using PF = Prefetch<IN_F32, D>;
   constexpr bool OPF32 = SM::OPF32;
   constexpr int NB = D / BV;
   constexpr int NT = D / 16;   // 16-row tiles over the key dim
@@ -239,60 +473,99 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 
   const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
   const int64_t slot = p.slot_idx[n];
-  const int64_t sbase = (slot * p.HV + h) * (int64_t)(D * D);
 
   // ---- initial state: st[m][i] = S^T[16m + 4g + i][col] ----
   f32x4 st[NT];
+  {
+    const int64_t sbase = (slot * p.HV + h) * (int64_t)(D * D) + col;
 #pragma unroll
-  for (int m = 0; m < NT; ++m) {
+    for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!p.zero_init) {
+      if (p.st_bf16) {
+        const uint16_t *sp = static_cast<const uint16_t *>(p.pool) + sbase;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t e = sbase + (int64_t)(16 * m + 4 * g + i) * D + col;
-      float x = 0.f;
-      if (!p.zero_init)
-        x = p.st_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(p.pool)[e])
-                      : static_cast<const float *>(p.pool)[e];
-      st[m][i] = x;
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[m][i] = bf16_to_f32(sp[(16 * m + 4 * g + i) * D]);
+      } else {
+        const float *sp = static_cast<const float *>(p.pool) + sbase;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[m][i] = sp[(16 * m + 4 * g + i) * D];
+      }
     }
+  }
+
+  PF pf;
+  pf.g = pf.beta = 0.f;
+  const LaneOffsets lo = lane_offsets<IN_F32, D>();
+  if constexpr (GATE != GDR_GATE_CHANNEL) {
+    if (bos < eos)
+      load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, bos, (int)min<int64_t>(C, eos - bos), h, hk, vb);
   }
 
   const int64_t HVD = (int64_t)p.HV * D;
   for (int64_t t0 = bos; t0 < eos; t0 += C) {
     const int L = (int)((eos - t0) < C ? (eos - t0) : C);
 
-    // ================= phase 0: loads =================
-    // values of this workgroup's column block
-    for (int it = tid; it < C * (BV / 8); it += 256) {
-      const int row = it / (BV / 8), c8 = 8 * (it % (BV / 8));
-      copy8<IN_F32>(p.v, (t0 + row) * p.v_stride + (int64_t)h * D + vb * BV + c8, row < L,
-                    &sm.vv[row][c8]);
-    }
+    // ================= phase 0: inputs into LDS =================
     if constexpr (GATE != GDR_GATE_CHANNEL) {
-      // keys and queries, plus transposed keys for the state update
-      for (int it = tid; it < C * (D / 8); it += 256) {
-        const int row = it / (D / 8), c8 = 8 * (it % (D / 8));
-        const bool ok = row < L;
-        copy8<IN_F32>(p.k, (t0 + row) * p.k_stride + (int64_t)hk * D + c8, ok, &sm.kk[row][c8]);
-        copy8<IN_F32>(p.q, (t0 + row) * p.q_stride + (int64_t)hk * D + c8, ok, &sm.qq[row][c8]);
+      const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.kt[c8 + j][row] = sm.kk[row][c8 + j];
+      for (int u = 0; u < PF::KU; ++u) {
+        const int row = lo.krow + u * lo.krs, c = lo.kc / (int)sizeof(In);
+        const bool ok = row < L;
+        *reinterpret_cast<uint4 *>(&sm.kk[row][c]) = ok ? get4(pf.k, u) : z;
+        *reinterpret_cast<uint4 *>(&sm.qq[row][c]) = ok ? get4(pf.q, u) : z;
+      }
+#pragma unroll
+      for (int u = 0; u < PF::VU; ++u) {
+        const int row = lo.vrow + u * lo.vrs, c = lo.vc / (int)sizeof(In);
+        *reinterpret_cast<uint4 *>(&sm.vv[row][c]) = row < L ? get4(pf.v, u) : z;
       }
       if (w == 0) {
         const bool ok = lane < L;
-        const int64_t th = (t0 + lane) * p.HV + h;
-        float gi = 0.f;
-        if constexpr (GATE == GDR_GATE_SCALAR) gi = ok ? p.g[th] : 0.f;
-        const float Gi = wave_scan(gi);
+        float gl = 0.f;
+        if constexpr (GATE == GDR_GATE_SCALAR) gl = ok ? pf.g : 0.f;
+        const float Gi = wave_scan(gl);
         const float Gl = __shfl(Gi, 63, 64);
         sm.G[lane] = Gi;
         sm.eG[lane] = __expf(Gi);
         sm.eGl[lane] = __expf(Gl - Gi);
         if (lane == 0) sm.eGlast = __expf(Gl);
-        if constexpr (DELTA) sm.beta[lane] = ok ? p.beta[th] : 0.f;
+        sm.beta[lane] = ok ? pf.beta : 0.f;
+      }
+      // next chunk's loads stay in flight while this one computes
+      if (t0 + C < eos)
+        load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, t0 + C, (int)min<int64_t>(C, eos - t0 - C), h,
+                                           hk, vb);
+      __syncthreads();
+      // transposed keys for the state update (read only at the end of the chunk)
+      constexpr int E = PF::E;
+      constexpr int RG = C / E;   // row groups of E tokens
+#pragma unroll
+      for (int u = 0; u < D * RG / 256; ++u) {
+        const int it = tid + 256 * u, dk = it % D, rg = it / D;
+        uint32_t wv[4];
+        if constexpr (IN_F32) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wv[j] = __float_as_uint(sm.kk[E * rg + j][dk]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            wv[j] = (uint32_t)sm.kk[E * rg + 2 * j][dk] | ((uint32_t)sm.kk[E * rg + 2 * j + 1][dk] << 16);
+        }
+        *reinterpret_cast<uint4 *>(&sm.kt[dk][E * rg]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
     } else {
       // channel gate: stage g, prefix-sum each key channel over the chunk,
       // then form e^{G} k, e^{G} q and e^{-G} k.
+      for (int it = tid; it < C * (BV / 8); it += 256) {
+        const int row = it / (BV / 8), c8 = 8 * (it % (BV / 8));
+        copy8<IN_F32>(p.v, (t0 + row) * p.v_stride + (int64_t)h * D + vb * BV + c8, row < L,
+                      &sm.vv[row][c8]);
+      }
       for (int it = tid; it < C * (D / 4); it += 256) {
         const int row = it / (D / 4), c4 = 4 * (it % (D / 4));
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -300,8 +573,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           x = *reinterpret_cast<const float4 *>(p.g + ((t0 + row) * p.HV + h) * (int64_t)D + c4);
         *reinterpret_cast<float4 *>(&sm.gstage[row][c4]) = x;
       }
-      if constexpr (DELTA) {
-        if (w == 0) sm.beta[lane] = lane < L ? p.beta[(t0 + lane) * p.HV + h] : 0.f;
+      if (w == 0) {
+        sm.G[lane] = 0.f;   // decay sits inside the channel-gate operands
+        float bl = 0.f;
+        if constexpr (DELTA) bl = lane < L ? p.beta[(t0 + lane) * p.HV + h] : 0.f;
+        sm.beta[lane] = bl;
       }
       __syncthreads();
       if (tid < D) {
@@ -329,76 +605,20 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           else sm.kt[c8 + j][row] = kx[j] * ei;   // linear rule: no Gram needs kinv
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
 
     // ================= phase 1: Gram matrices =================
-    // Lower 16x16 tiles (I >= J): KK^T feeds R (delta rule), QK^T feeds A.
-    {
-      constexpr int NTASK = DELTA ? 20 : 10;
-      for (int task = w; task < NTASK; task += 4) {
-        const bool isq = DELTA ? (task >= 10) : true;
-        const int tt = DELTA ? task % 10 : task;
-        int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
-        const int J = tt - I * (I + 1) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const Op *arow = isq ? &sm.qq[0][0] : &sm.kk[0][0];
-        const Op *bsrc;
-        if constexpr (GATE == GDR_GATE_CHANNEL && DELTA) bsrc = &sm.kinv[0][0];
-        else bsrc = &sm.kk[0][0];
-        // channel gate, linear rule: B operand e^{-G} k is only held transposed
-        if constexpr (GATE == GDR_GATE_CHANNEL && !DELTA) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            Frag fa, fb;
-            ldfrag(arow, SM::PK, 16 * I + r, 32 * s, g, fa);
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int kcol = 32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-              x[j] = sm.kt[kcol][16 * J + r];
-            }
-            split8(x, fb);
-            acc = mm<true, true>(fa, fb, acc);
-          }
-        } else {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            Frag fa, fb;
-            ldfrag(arow, SM::PK, 16 * I + r, 32 * s, g, fa);
-            ldfrag(bsrc, SM::PK, 16 * J + r, 32 * s, g, fb);
-            acc = mm<OPF32, OPF32>(fa, fb, acc);
-          }
-        }
-        const int jj = 16 * J + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ii = 16 * I + 4 * g + i;
-          float gam = 1.f;
-          if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(sm.G[ii] - sm.G[jj]);
-          if (isq) {
-            sm.aq[ii][jj] = (jj <= ii) ? p.scale * acc[i] * gam : 0.f;
-          } else if constexpr (DELTA) {
-            sm.rt[ii][jj] = (jj < ii) ? sm.beta[ii] * acc[i] * gam : 0.f;
-          }
-        }
-      }
-      // zero the strictly upper tiles (read by the 32-wide k steps below)
-      for (int e = tid; e < 6 * 256; e += 256) {
-        const int tu = e / 256, el = e % 256;
-        // upper tiles (I, J), I < J: (0,1),(0,2),(0,3),(1,2),(1,3),(2,3)
-        const int I = tu < 3 ? 0 : (tu < 5 ? 1 : 2);
-        const int J = tu < 3 ? tu + 1 : (tu < 5 ? tu - 1 : 3);
-        const int ii = 16 * I + el / 16, jj = 16 * J + el % 16;
-        sm.aq[ii][jj] = 0.f;
-        if constexpr (DELTA) sm.rt[ii][jj] = 0.f;
-      }
+    switch (w) {
+      case 0: grams<0, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+      case 1: grams<1, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+      case 2: grams<2, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+      default: grams<3, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
     }
-    __syncthreads();
 
     if constexpr (GATE == GDR_GATE_CHANNEL && DELTA) {
       // e^{-G} k: token-major (Gram operand) -> key-major (update operand)
+      __syncthreads();
       float tmp[C * D / 256];
 #pragma unroll
       for (int e = 0; e < C * D / 256; ++e) {
@@ -413,69 +633,59 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
     }
 
-    // ================= phase 2: T = (I + R)^-1 =================
+    // ============ phase 2 (per wave): X = K S^T and Q S^T, eight chains ============
+    // They read only keys, queries and this wave's state, so they run before
+    // the barrier that publishes the Gram results.
+    f32x4 xa[4], qa[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) xa[I] = qa[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      Frag sf;   // state B fragment over key rows 32s .. 32s+31
+      chainfrag(st[2 * s], st[2 * s + 1], sf);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        Frag fq;
+        ldfrag(&sm.qq[0][0], SM::PK, 16 * I + r, 32 * s, g, fq);
+        qa[I] = mm<OPF32, true>(fq, sf, qa[I]);
+        if constexpr (DELTA) {
+          Frag fk;
+          ldfrag(&sm.kk[0][0], SM::PK, 16 * I + r, 32 * s, g, fk);
+          xa[I] = mm<OPF32, true>(fk, sf, xa[I]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ======== phase 3: inverses of the diagonal blocks of I + R (wave w: block w) ========
     if constexpr (DELTA) {
-      if (tid < 64) {
-        // forward substitution, one column of one 16x16 diagonal block per lane
-        const int bb = tid >> 4, c = tid & 15, o = 16 * bb;
-        float x[16];
+      // Right-looking forward substitution; the four lane groups of a wave
+      // solve the same column c redundantly (branch free) and each stores a
+      // quarter of its rows.
+      const int c = lane & 15, q = lane >> 4, o = 16 * w;
+      float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc = (i == c) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
-          for (int j = 0; j < i; ++j) acc -= sm.rt[o + i][o + j] * x[j];
-          x[i] = acc;
+      for (int j = 0; j < 15; ++j) {
+        float colj[16];   // column j of the block: R[o + i][o + j]
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rdT[w][j][4 * i4]);
+          colj[4 * i4] = v4.x; colj[4 * i4 + 1] = v4.y; colj[4 * i4 + 2] = v4.z; colj[4 * i4 + 3] = v4.w;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.rt[o + i][o + c] = x[i];
+        for (int i = j + 1; i < 16; ++i) x[i] -= colj[i] * x[j];
       }
-      __syncthreads();
-      // merges T21 = -T22 R21 T11: 16 -> 32 (two blocks), then 32 -> 64
 #pragma unroll
-      for (int lvl = 0; lvl < 2; ++lvl) {
-        const int nb = lvl == 0 ? 16 : 32;   // size of T11 / T22
-        const int per = lvl == 0 ? 2 : 4;    // outputs per thread
-        float pv[4];
-        int pi[4], pj[4], po[4];
-        // P = R21 T11
-#pragma unroll
-        for (int u = 0; u < per; ++u) {
-          const int e = tid + 256 * u;
-          int base, i, j;
-          if (lvl == 0) { base = 32 * (e / 256); i = (e % 256) / 16; j = e % 16; }
-          else { base = 0; i = e / 32; j = e % 32; }
-          pi[u] = i; pj[u] = j; po[u] = base;
-          float acc = 0.f;
-          for (int kx = j; kx < nb; ++kx) acc += sm.rt[base + nb + i][base + kx] * sm.rt[base + kx][base + j];
-          pv[u] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < per; ++u) sm.rt[po[u] + nb + pi[u]][po[u] + pj[u]] = pv[u];
-        __syncthreads();
-        // T21 = -T22 P
-#pragma unroll
-        for (int u = 0; u < per; ++u) {
-          const int base = po[u], i = pi[u], j = pj[u];
-          float acc = 0.f;
-          for (int kx = 0; kx <= i; ++kx) acc += sm.rt[base + nb + i][base + nb + kx] * sm.rt[base + nb + kx][base + j];
-          pv[u] = -acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < per; ++u) sm.rt[po[u] + nb + pi[u]][po[u] + pj[u]] = pv[u];
-        __syncthreads();
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float v = q == 0 ? x[i4] : q == 1 ? x[4 + i4] : q == 2 ? x[8 + i4] : x[12 + i4];
+        store_split(&sm.rth[0][0], &sm.rtl[0][0], (o + 4 * q + i4) * SM::PB + o + c, v);
       }
-    } else {
       __syncthreads();
     }
 
-    // ================= phase 3: state-dependent products (per wave) =================
-    // state B fragments over the key dim
-    Frag sf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) chainfrag(st[2 * s], st[2 * s + 1], sf[s]);
-
+    // ================= phase 4: corrected values, outputs, state (per wave) =================
     // value tiles of this wave: vt[I][i] = V[16I + 4g + i][col]
     f32x4 vt[4];
 #pragma unroll
@@ -488,80 +698,90 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
 
     f32x4 vbar[4];   // corrected values (delta) or values (linear)
+    Frag4 vsp[4];    // their split B fragments
     if constexpr (DELTA) {
-      // X = K_l S^T, then R_v = beta (V - X)
-      f32x4 rv[4];
+      // Vb = (I + R)^-1 R_v by block forward substitution over 16-row blocks:
+      // Vb_I = T_II (R_v,I - sum_{J<I} R_IJ Vb_J), with T_II the diagonal
+      // inverses and R_IJ the off-diagonal blocks.
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          Frag fa;
-          ldfrag(&sm.kk[0][0], SM::PK, 16 * I + r, 32 * s, g, fa);
-          acc = mm<OPF32, true>(fa, sf[s], acc);
-        }
+        const float4 Bi = *reinterpret_cast<const float4 *>(&sm.beta[16 * I + 4 * g]);
+        const float bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+        f32x4 rv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int ii = 16 * I + 4 * g + i;
-          float x = acc[i];
-          if constexpr (GATE == GDR_GATE_SCALAR) x *= sm.eG[ii];
-          rv[I][i] = sm.beta[ii] * (vt[I][i] - x);
+          float x = xa[I][i];
+          if constexpr (GATE == GDR_GATE_SCALAR) x *= sm.eG[16 * I + 4 * g + i];
+          rv[i] = bi[i] * (vt[I][i] - x);
         }
-      }
-      // Vb = T R_v (T lower triangular: row tile I needs k steps s <= I/2)
-      Frag rf[2];
-      chainfrag(rv[0], rv[1], rf[0]);
-      chainfrag(rv[2], rv[3], rf[1]);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s <= I / 2; ++s) {
-          Frag fa;
-          ldfrag(&sm.rt[0][0], SM::PF, 16 * I + r, 32 * s, g, fa);
-          acc = mm<true, true>(fa, rf[s], acc);
+        for (int J = 0; J < I; ++J) {
+          Frag4 fr;
+          ldsplit4(&sm.rth[0][0], &sm.rtl[0][0], SM::PB, 16 * I + r, 16 * J, g, fr);
+          acc = mm16(fr, vsp[J], acc);
         }
-        vbar[I] = acc;
+        Frag4 fy, ft;
+        split4(rv - acc, fy);
+        ldsplit4(&sm.rth[0][0], &sm.rtl[0][0], SM::PB, 16 * I + r, 16 * I, g, ft);
+        vbar[I] = mm16(ft, fy, f32x4{0.f, 0.f, 0.f, 0.f});
+        split4(vbar[I], vsp[I]);
       }
     } else {
 #pragma unroll
-      for (int I = 0; I < 4; ++I) vbar[I] = vt[I];
+      for (int I = 0; I < 4; ++I) {
+        vbar[I] = vt[I];
+        split4(vbar[I], vsp[I]);
+      }
     }
 
-    // O = s e^{G} (.) Q S^T + A Vb
+    // O = s e^{G} (.) Q S^T + A Vb   (A lower triangular: blocks J <= I)
+    f32x4 oa[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 acc = qa[I];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sc = p.scale;
+        if constexpr (GATE == GDR_GATE_SCALAR) sc *= sm.eG[16 * I + 4 * g + i];
+        acc[i] *= sc;
+      }
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        Frag4 fa;
+        ldsplit4(&sm.aqh[0][0], &sm.aql[0][0], SM::PB, 16 * I + r, 16 * J, g, fa);
+        acc = mm16(fa, vsp[J], acc);
+      }
+      oa[I] = acc;
+    }
     {
-      Frag vf[2];
-      chainfrag(vbar[0], vbar[1], vf[0]);
-      chainfrag(vbar[2], vbar[3], vf[1]);
+      // row (16I + 4g + i) of this chunk, column col: 32-bit offsets from the
+      // chunk's first output row
+      const uint32_t HVDu = (uint32_t)HVD;
+      if (p.out_bf16) {
+        uint16_t *ob = static_cast<uint16_t *>(p.o) + t0 * HVD + (int64_t)h * D + col;
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          Frag fa;
-          ldfrag(&sm.qq[0][0], SM::PK, 16 * I + r, 32 * s, g, fa);
-          acc = mm<OPF32, true>(fa, sf[s], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sc = p.scale;
-          if constexpr (GATE == GDR_GATE_SCALAR) sc *= sm.eG[16 * I + 4 * g + i];
-          acc[i] *= sc;
-        }
-#pragma unroll
-        for (int s = 0; s <= I / 2; ++s) {
-          Frag fa;
-          ldfrag(&sm.aq[0][0], SM::PF, 16 * I + r, 32 * s, g, fa);
-          acc = mm<true, (DELTA || IN_F32)>(fa, vf[s], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ii = 16 * I + 4 * g + i;
-          if (ii < L) {
-            const int64_t oe = (t0 + ii) * HVD + (int64_t)h * D + col;
-            if (p.out_bf16) static_cast<uint16_t *>(p.o)[oe] = f32_to_bf16(acc[i]);
-            else static_cast<float *>(p.o)[oe] = acc[i];
+          for (int i = 0; i < 4; ++i) {
+            const int ii = 16 * I + 4 * g + i;
+            if (L == C || ii < L) ob[(uint32_t)ii * HVDu] = f32_to_bf16(oa[I][i]);
           }
+      } else {
+        float *ob = static_cast<float *>(p.o) + t0 * HVD + (int64_t)h * D + col;
+        if (L == C) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[(uint32_t)(16 * I + 4 * g + i) * HVDu] = oa[I][i];
+        } else {
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ii = 16 * I + 4 * g + i;
+              if (ii < L) ob[(uint32_t)ii * HVDu] = oa[I][i];
+            }
         }
       }
     }
@@ -604,17 +824,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 
   // ---- final state back to the pool slot ----
+  {
+    const int64_t sbase = (slot * p.HV + h) * (int64_t)(D * D) + col;
+    if (p.st_bf16) {
+      uint16_t *sp = static_cast<uint16_t *>(p.pool) + sbase;
 #pragma unroll
-  for (int m = 0; m < NT; ++m) {
+      for (int m = 0; m < NT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t e = sbase + (int64_t)(16 * m + 4 * g + i) * D + col;
-      if (p.st_bf16) static_cast<uint16_t *>(p.pool)[e] = f32_to_bf16(st[m][i]);
-      else static_cast<float *>(p.pool)[e] = st[m][i];
+        for (int i = 0; i < 4; ++i) sp[(16 * m + 4 * g + i) * D] = f32_to_bf16(st[m][i]);
+    } else {
+      float *sp = static_cast<float *>(p.pool) + sbase;
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[(16 * m + 4 * g + i) * D] = st[m][i];
     }
   }
 }
-
 template <bool IN_F32, int GATE, bool DELTA, int D>
 hipError_t launch_t(const ChunkParams &p, int N, hipStream_t stream) {
   const int blocks = N * p.HV * (D / BV);

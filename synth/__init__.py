@@ -6,19 +6,20 @@ Both the fp64 oracle (through tests and the bench's CPU leg) and the HIP path
 consume exactly the arrays produced here.
 
 Recipe (the same for every workload):
-  * one ``numpy.random.SeedSequence(seed)`` spawns one child stream per tensor,
-    in the order q, k, v, beta-logits, g-logits, extras;
-  * q, k ~ N(0, 1) per token and head, L2-normalised over the key dimension in
-    fp64, then cast (fp64 -> fp32 -> bf16, round to nearest even) when the
-    workload's input type is bf16;
+  * each tensor (q, k, v, beta-logits, g-logits) is drawn in blocks of 4096
+    tokens, block b from SeedSequence([seed, tensor id, b]); initial
+    states slot by slot from SeedSequence([seed, 98, slot]) and slot indices
+    from SeedSequence([seed, 99]);
+  * draws are fp32 N(0, 1);
+  * q, k are L2-normalised over the key dimension (norm accumulated in fp64),
+    then cast to bf16 (round to nearest even) when the workload's input type
+    is bf16;
   * v ~ N(0, 1), cast the same way;
-  * beta = sigmoid(N(0, 1)) and g = -softplus(N(0, 1) - shift) in fp64, then
-    rounded to fp32 (g = log alpha <= 0; channel gates draw one value per key
-    channel);
+  * beta = sigmoid(N(0, 1)) and g = -softplus(N(0, 1) - shift) in fp32
+    (g = log alpha <= 0; channel gates draw one value per key channel);
   * initial states ~ N(0, 0.02^2) cast to the pool's storage type; slot indices
     are a seeded choice of distinct slots.
-Draws go token-major, so generating a token range in blocks yields the same
-values as one draw of the whole range.
+Any token range reproduces the values of the whole tensor.
 
 bf16 arrays are carried as numpy ``uint16`` bit patterns; ``widen`` turns any
 stored array into float64 exactly.
@@ -26,7 +27,7 @@ stored array into float64 exactly.
 from __future__ import annotations
 
 import dataclasses
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, Optional
 
 import numpy as np
@@ -135,9 +136,13 @@ def workload(name: str, **overrides) -> Workload:
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp64 -> fp32 (RNE) -> bf16 (RNE) bit patterns as uint16 (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u          # no overflow for finite inputs
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -163,25 +168,33 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 # generation
 # ----------------------------------------------------------------------------
 
-_STREAMS = ("q", "k", "v", "beta", "g", "extra")
+_TENSORS = {"q": 1, "k": 2, "v": 3, "beta": 4, "g": 5}
+BLOCK = 4096   # tokens per independently seeded block
 
 
-def _streams(seed: int):
-    ss = np.random.SeedSequence(seed)
-    return {name: np.random.Generator(np.random.PCG64(c))
-            for name, c in zip(_STREAMS, ss.spawn(len(_STREAMS)))}
-
-
-def _skip_normals(rng: np.random.Generator, count: int, block: int = 1 << 22):
-    while count > 0:
-        n = min(count, block)
-        rng.standard_normal(n)
-        count -= n
+def _block(w: Workload, seed: int, name: str, b: int, T: int):
+    """Stored values of tensor `name` for token block b (tokens b*BLOCK ...)."""
+    n = min(BLOCK, T - b * BLOCK)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TENSORS[name], b])))
+    HK, HV, DK, DV = w.HK, w.HV, w.DK, w.DV
+    f32 = np.float32
+    if name in ("q", "k"):
+        x = rng.standard_normal((n, HK, DK), dtype=f32)
+        x /= np.sqrt(np.sum(np.square(x, dtype=np.float64), axis=-1, keepdims=True)).astype(f32)
+        return _cast(x, w.in_dtype)
+    if name == "v":
+        return _cast(rng.standard_normal((n, HV, DV), dtype=f32), w.in_dtype)
+    if name == "beta":
+        b_ = rng.standard_normal((n, HV), dtype=f32)
+        return (1.0 / (1.0 + np.exp(-b_))).astype(f32)
+    x = rng.standard_normal((n, HV, DK) if w.gate == "channel" else (n, HV), dtype=f32)
+    z = x - f32(w.gate_shift)
+    return (-(np.maximum(z, f32(0)) + np.log1p(np.exp(-np.abs(z))))).astype(f32)
 
 
 def generate(w: Workload, seed: Optional[int] = None, t0: int = 0,
              t1: Optional[int] = None, heads: Optional[np.ndarray] = None,
-             block_tokens: int = 8192) -> dict:
+             threads: Optional[int] = None) -> dict:
     """Draw the workload's token inputs for tokens [t0, t1) plus its extras.
 
     Returns a dict with q, k [T, HK, DK], v [T, HV, DV] in storage form, beta
@@ -189,51 +202,41 @@ def generate(w: Workload, seed: Optional[int] = None, t0: int = 0,
     for gate "none"), pool [num_slots, HV, DK, DV] in storage form, slot_idx
     [N] int32 and cu_seqlens [N+1] int32. Decode workloads with ``steps`` > 1
     lay the steps out as consecutive token blocks of N tokens.
+    Each tensor is drawn in blocks of BLOCK tokens, block b from its own
+    stream SeedSequence([seed, tensor, b]), so any token range reproduces the
+    values of the whole tensor and blocks can be drawn in parallel.
     ``heads`` optionally keeps only some value heads (and the key heads they
-    read) of the returned token arrays; draws still cover every head so the
-    values equal those of the full tensors.
+    read) of the returned token arrays.
     """
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+
     seed = w.seed if seed is None else seed
     T = w.T_total * w.steps
     t1 = T if t1 is None else t1
     assert 0 <= t0 <= t1 <= T
-    rs = _streams(seed)
+    names = ["q", "k", "v"]
+    if w.rule == "delta":
+        names.append("beta")
+    if w.gate != "none":
+        names.append("g")
+    b0, b1 = t0 // BLOCK, (t1 + BLOCK - 1) // BLOCK
+    jobs = [(nm, b) for nm in names for b in range(b0, b1)]
+    threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(lambda j: _block(w, seed, j[0], j[1], T), jobs))
+    res = {"beta": None, "g": None}
     HK, HV, DK, DV = w.HK, w.HV, w.DK, w.DV
-    per_tok = {"q": HK * DK, "k": HK * DK, "v": HV * DV, "beta": HV,
-               "g": HV * (DK if w.gate == "channel" else 1)}
-    for name in per_tok:
-        _skip_normals(rs[name], t0 * per_tok[name])
-
-    out = {n: [] for n in per_tok}
-    t = t0
-    while t < t1:
-        n = min(block_tokens, t1 - t)
-        for name in ("q", "k"):
-            x = rs[name].standard_normal((n, HK, DK))
-            x /= np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
-            out[name].append(_cast(x, w.in_dtype))
-        out["v"].append(_cast(rs["v"].standard_normal((n, HV, DV)), w.in_dtype))
-        b = rs["beta"].standard_normal((n, HV))
-        out["beta"].append((1.0 / (1.0 + np.exp(-b))).astype(np.float32))
-        if w.gate == "channel":
-            x = rs["g"].standard_normal((n, HV, DK))
+    empty = {"q": (0, HK, DK), "k": (0, HK, DK), "v": (0, HV, DV), "beta": (0, HV),
+             "g": (0, HV, DK) if w.gate == "channel" else (0, HV)}
+    for nm in names:
+        blocks = [p for (n_, _), p in zip(jobs, parts) if n_ == nm]
+        if blocks:
+            full = np.concatenate(blocks, axis=0) if len(blocks) > 1 else blocks[0]
+            res[nm] = full[t0 - b0 * BLOCK:t1 - b0 * BLOCK]
         else:
-            x = rs["g"].standard_normal((n, HV))
-        z = x - w.gate_shift
-        softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
-        out["g"].append((-softplus).astype(np.float32))
-        t += n
-    res = {n: (np.concatenate(v, axis=0) if v else None) for n, v in out.items()}
-    if res["q"] is None:
-        res["q"] = _cast(np.zeros((0, HK, DK)), w.in_dtype)
-        res["k"] = _cast(np.zeros((0, HK, DK)), w.in_dtype)
-        res["v"] = _cast(np.zeros((0, HV, DV)), w.in_dtype)
-        res["beta"] = np.zeros((0, HV), np.float32)
-        res["g"] = np.zeros((0, HV) + ((DK,) if w.gate == "channel" else ()), np.float32)
-    if w.rule == "linear":
-        res["beta"] = None
-    if w.gate == "none":
-        res["g"] = None
+            dt = np.float32 if nm in ("beta", "g") or w.in_dtype == "f32" else np.uint16
+            res[nm] = np.zeros(empty[nm], dt)
 
     if heads is not None:
         heads = np.asarray(heads)
@@ -247,13 +250,18 @@ def generate(w: Workload, seed: Optional[int] = None, t0: int = 0,
         if res["g"] is not None:
             res["g"] = res["g"][:, heads]
 
-    ex = rs["extra"]
-    slot_idx = ex.choice(w.num_slots, size=w.N, replace=False).astype(np.int32)
+    ex_rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    slot_idx = ex_rng.choice(w.num_slots, size=w.N, replace=False).astype(np.int32)
     if w.zero_init:
-        pool = np.zeros((w.num_slots, HV, DK, DV))
+        res["pool"] = _cast(np.zeros((w.num_slots, HV, DK, DV), np.float32), w.state_dtype)
     else:
-        pool = 0.02 * ex.standard_normal((w.num_slots, HV, DK, DV))
-    res["pool"] = _cast(pool, w.state_dtype)
+        def slot_state(sl):
+            r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 98, sl])))
+            x = r.standard_normal((HV, DK, DV), dtype=np.float32)
+            x *= np.float32(0.02)
+            return _cast(x, w.state_dtype)
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            res["pool"] = np.stack(list(ex.map(slot_state, range(w.num_slots))))
     res["slot_idx"] = slot_idx
     res["cu_seqlens"] = w.cu_seqlens()
     return res

@@ -1,0 +1,136 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times. The GPU computes every sequence and head; the fp64 oracle
+recomputes a sample of (sequence, head) chains end to end and those outputs
+and final states are compared under the same gate as the small tests."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import check_out, check_state, host, to_device, widened
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gdr():
+    import gated_delta_rule_gdr_amd as gdr
+    gdr.load()
+    return gdr
+
+
+def subset(w, x, heads):
+    """Stored inputs of whole groups of value heads (and their key heads)."""
+    heads = np.asarray(heads)
+    ratio = w.HV // w.HK
+    kh = np.unique(heads // ratio)
+    assert ratio == 1 or len(heads) == len(kh) * ratio, "sample whole head groups"
+    return dict(q=x["q"][:, kh], k=x["k"][:, kh], v=x["v"][:, heads],
+                g=None if x["g"] is None else x["g"][:, heads],
+                beta=None if x["beta"] is None else x["beta"][:, heads],
+                pool=x["pool"][:, heads])
+
+
+def run_prefill(gdr, w, d):
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      d["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init,
+                      chunk_size=w.chunk_size)
+    torch.cuda.synchronize()
+    return o
+
+
+def check_sampled(w, x, o, pool_gpu, heads):
+    xs = widened(w, subset(w, x, heads))
+    o_ref, pool_ref = oracle.recurrent_fp64(
+        xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["pool"], x["slot_idx"],
+        x["cu_seqlens"], scale=w.DK ** -0.5, rule=w.rule, gate=w.gate,
+        zero_init=w.zero_init, state_dtype=w.state_dtype)
+    og = host(o[:, torch.as_tensor(heads, device=o.device)], "f32")
+    err, bound = check_out(og, o_ref, w.in_dtype)
+    pg = host(pool_gpu, w.state_dtype)[:, heads]
+    for s in x["slot_idx"]:
+        check_state(pg[s], pool_ref[s], w.in_dtype, w.state_dtype)
+    print(f"{w.name}: heads {list(heads)} max|err| {err:.3e} <= {bound:.3e}", flush=True)
+
+
+def test_gdr_fp32_t256_d64_all_outputs():
+    gdr = _gdr()
+    w = synth.workload("gdr_fp32_t256_h1_d64")
+    x = synth.generate(w)
+    d = to_device(w, x)
+    print(f"launch {w.name}", flush=True)
+    o = run_prefill(gdr, w, d)
+    check_sampled(w, x, o, d["pool"], [0])
+
+
+@pytest.mark.parametrize("name", ["gdn_prefill_b4_t4096_h16_d128", "la_prefill_b4_t4096_h16_d128"])
+def test_gdn_prefill_b4_t4096_h16(name):
+    gdr = _gdr()
+    w = synth.workload(name)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    print(f"launch {w.name}", flush=True)
+    o = run_prefill(gdr, w, d)
+    assert torch.isfinite(o).all()
+    check_sampled(w, x, o, d["pool"], [0, 9])
+
+
+def test_ragged_gqa_prefill_bf16_pool():
+    gdr = _gdr()
+    w = synth.workload("ragged_gqa_prefill_n8_hk16_hv32_d128")
+    x = synth.generate(w)
+    d = to_device(w, x)
+    pool0 = d["pool"].clone()
+    print(f"launch {w.name} lens {w.seqlens}", flush=True)
+    o = run_prefill(gdr, w, d)
+    untouched = np.setdiff1d(np.arange(w.num_slots), x["slot_idx"])
+    assert torch.equal(d["pool"][untouched], pool0[untouched])
+    check_sampled(w, x, o, d["pool"], [0, 1, 30, 31])
+
+
+def test_decode_n256_steps():
+    """The full batch for 4 steps against the oracle on every sequence and
+    head, then 60 more steps with a 16-sequence sample followed end to end."""
+    gdr = _gdr()
+    w = synth.workload("decode_n256_hk16_hv32_d128")
+    steps_full, steps_more = 4, 60
+    ws = w.replace(steps=steps_full + steps_more)
+    x = synth.generate(ws)
+    d = to_device(ws, x)
+    xw = widened(ws, x)
+    N = w.N
+    pool_ref = xw["pool"]
+    sample = np.arange(0, N, 16)
+    sub_slots = x["slot_idx"][sample]
+    print(f"launch {w.name}", flush=True)
+    for s in range(steps_full + steps_more):
+        sl = slice(s * N, (s + 1) * N)
+        o = gdr.recurrent_step(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["beta"][sl],
+                               d["pool"], d["slot_idx"])
+        torch.cuda.synchronize()
+        if s < steps_full:
+            o_ref, pool_ref = oracle.recurrent_fp64(
+                xw["q"][sl], xw["k"][sl], xw["v"][sl], xw["g"][sl], xw["beta"][sl], pool_ref,
+                x["slot_idx"], np.arange(N + 1), scale=w.DK ** -0.5)
+            check_out(host(o, "f32"), o_ref, "bf16")
+        else:
+            idx = s * N + sample
+            o_ref, pool_ref = oracle.recurrent_fp64(
+                xw["q"][idx], xw["k"][idx], xw["v"][idx], xw["g"][idx], xw["beta"][idx],
+                pool_ref, sub_slots, np.arange(len(sample) + 1), scale=w.DK ** -0.5)
+            check_out(host(o[torch.as_tensor(sample, device=o.device)], "f32"), o_ref, "bf16")
+    pool = host(d["pool"], "f32")
+    for s in sub_slots:
+        check_state(pool[s], pool_ref[s], "bf16", "f32")
+
+
+def test_kda_prefill_t131072_h32():
+    gdr = _gdr()
+    w = synth.workload("kda_prefill_t131072_h32_d128")
+    x = synth.generate(w)
+    d = to_device(w, x)
+    print(f"launch {w.name}", flush=True)
+    o = run_prefill(gdr, w, d)
+    assert torch.isfinite(o).all()
+    check_sampled(w, x, o, d["pool"], [5])
