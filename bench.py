@@ -253,6 +253,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain device copies of a known size (scales the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -265,6 +268,17 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+
+    if args.calibrate_copy:
+        nbytes = 512 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes,
+                          "bytes_written_per_copy": nbytes, "copies": 3}), flush=True)
+        return
 
     w = synth.workload(args.workload)
     torch.cuda.synchronize()

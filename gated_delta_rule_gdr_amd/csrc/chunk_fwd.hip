@@ -71,7 +71,7 @@ struct ChunkParams {
   void *o;
   void *pool;
   const int32_t *slot_idx, *cu_seqlens;
-  int32_t HV, ratio;
+  int32_t N, HK, HV, ratio;
   float scale;
   int zero_init, st_bf16, out_bf16;
 };
@@ -461,12 +461,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   constexpr int NS = D / 32;   // 32-wide k steps over the key dim
   __shared__ SM sm;
 
-  int b = blockIdx.x;
-  const int vb = b % NB;
-  b /= NB;
-  const int h = b % p.HV;
-  const int n = b / p.HV;
-  const int hk = h / p.ratio;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2). All workgroups that read the same keys and queries - the value
+  // blocks of the value heads sharing one key head of one sequence - get ids
+  // that are equal modulo 8, so they run on one XCD and share those reads.
+  const int GRP = p.ratio * NB;                 // workgroups per (sequence, key head)
+  const int b = blockIdx.x;
+  const int gi = (b / (8 * GRP)) * 8 + (b & 7);  // (sequence, key head) group
+  if (gi >= p.N * p.HK) return;                 // padding of the last XCD round
+  const int j = (b >> 3) % GRP;
+  const int n = gi / p.HK;
+  const int hk = gi - n * p.HK;
+  const int h = hk * p.ratio + j / NB;
+  const int vb = j % NB;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int col = vb * BV + 16 * w + r;   // value column this lane owns in C tiles
@@ -843,7 +850,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 }
 template <bool IN_F32, int GATE, bool DELTA, int D>
 hipError_t launch_t(const ChunkParams &p, int N, hipStream_t stream) {
-  const int blocks = N * p.HV * (D / BV);
+  // one XCD round covers 8 groups of ratio * NB workgroups
+  const int grp = p.ratio * (D / BV);
+  const int blocks = ((N * p.HK + 7) / 8) * 8 * grp;
   hipLaunchKernelGGL((chunk_fwd_kernel<IN_F32, GATE, DELTA, D>), dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -877,7 +886,7 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
   p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;
   p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
-  p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.N = a.N; p.HK = a.HK; p.HV = a.HV; p.ratio = a.HV / a.HK;
   p.scale = a.scale;
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   p.st_bf16 = a.state_dtype == GDR_BF16;
