@@ -1,0 +1,197 @@
+// Types and MFMA helpers shared by the chunk-prefill kernels (gfx950).
+// Internal to libgdr.
+#pragma once
+
+#include <stdint.h>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace chunk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;    // tokens per chunk
+constexpr int BV = 64;   // value columns per workgroup (16 per wave)
+
+struct ChunkParams {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  const float *g, *beta;
+  void *o;
+  void *pool;
+  const int32_t *slot_idx, *cu_seqlens;
+  int32_t N, HK, HV, ratio;
+  float scale;
+  int zero_init, st_bf16, out_bf16;
+};
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Frag {
+  bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ void split8(const float (&x)[8], Frag &f) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    f.hi[j] = h;
+    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  }
+}
+
+// acc += a * b with the passes the operands need (lo terms first).
+template <bool A_SPLIT, bool B_SPLIT>
+__device__ __forceinline__ f32x4 mm(const Frag &a, const Frag &b, f32x4 c) {
+  if constexpr (A_SPLIT) c = mfma(a.lo, b.hi, c);
+  if constexpr (B_SPLIT) c = mfma(a.hi, b.lo, c);
+  return mfma(a.hi, b.hi, c);
+}
+
+// Operand arrays in LDS store each 32-wide block of their contraction axis
+// permuted so that a lane's slot set K(g) = {4g..4g+3, 16+4g..16+4g+3} is the
+// contiguous physical range 8g .. 8g+7: logical index c sits at perm32(c).
+__device__ __forceinline__ int perm32(int c) {
+  const int a = (c >> 2) & 7;
+  return (c & ~31) + 8 * (a & 3) + 4 * (a >> 2) + (c & 3);
+}
+
+// Fragment of row `row`, k step starting at (logical = physical) column col0
+// of a permuted operand array: one 16-byte (bf16) or 32-byte (fp32) read.
+__device__ __forceinline__ void ldfrag(const uint16_t *base, int pitch, int row, int col0, int g,
+                                       Frag &f) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(base + row * pitch + col0 + 8 * g);
+  f.hi = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void ldfrag(const float *base, int pitch, int row, int col0, int g,
+                                       Frag &f) {
+  const float *p = base + row * pitch + col0 + 8 * g;
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  split8(x, f);
+}
+
+// B fragment over 32 rows built from two stacked accumulator tiles.
+__device__ __forceinline__ void chainfrag(const f32x4 &t0, const f32x4 &t1, Frag &f) {
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  split8(x, f);
+}
+
+// 16x16x16 products (k = 4g .. 4g+3 per lane): the accumulator layout of a
+// 16-row tile is directly a B fragment, so block-triangular chains need no
+// reordering.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+struct Frag4 {
+  bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(const f32x4 &x, Frag4 &f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    f.hi[j] = h;
+    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  }
+}
+
+// acc += a * b, both split (three passes, lo terms first)
+__device__ __forceinline__ f32x4 mm16(const Frag4 &a, const Frag4 &b, f32x4 c) {
+  c = mfma16(a.lo, b.hi, c);
+  c = mfma16(a.hi, b.lo, c);
+  return mfma16(a.hi, b.hi, c);
+}
+
+// A fragment of a 16x16 block of an fp32 LDS matrix: row `row`, columns
+// col0 + 4g .. col0 + 4g + 3.
+__device__ __forceinline__ void ldfrag4(const float *base, int pitch, int row, int col0, int g,
+                                        Frag4 &f) {
+  const float4 a = *reinterpret_cast<const float4 *>(base + row * pitch + col0 + 4 * g);
+  const f32x4 x = {a.x, a.y, a.z, a.w};
+  split4(x, f);
+}
+
+
+// Split fragment of a 16x16 block of a pre-split bf16 plane pair: row `row`,
+// columns col0 + 4g .. col0 + 4g + 3.
+__device__ __forceinline__ void ldsplit4(const uint16_t *hi, const uint16_t *lo, int pitch, int row,
+                                         int col0, int g, Frag4 &f) {
+  const int o = row * pitch + col0 + 4 * g;
+  f.hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi + o));
+  f.lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo + o));
+}
+
+__device__ __forceinline__ void store_split(uint16_t *hi, uint16_t *lo, int idx, float x) {
+  const __bf16 h = static_cast<__bf16>(x);
+  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
+  hi[idx] = __builtin_bit_cast(uint16_t, h);
+  lo[idx] = __builtin_bit_cast(uint16_t, l);
+}
+
+// Inclusive scan across the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (no LDS traffic): shifts 1, 2, 4, 8 scan each row of 16 lanes,
+// then lane 15 of row 0/2 is added into row 1/3 and lane 31 into rows 2-3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false);
+  return v + __builtin_bit_cast(float, s);
+}
+
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+  x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Inclusive scan across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// (Vector types, not arrays: prefetched data stays in registers as SSA values.)
+template <int N>
+struct U32Vec {
+  typedef unsigned int type __attribute__((ext_vector_type(N)));
+};
+
+template <class Vec>
+__device__ __forceinline__ void put4(Vec &v, int u, const uint4 x) {
+  v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
+}
+template <class Vec>
+__device__ __forceinline__ uint4 get4(const Vec &v, int u) {
+  return make_uint4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+}
+
+
+}  // namespace chunk
+
+hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream);
+
+}  // namespace gdr

@@ -50,138 +50,16 @@
 // C[4g + i][r], i = 0..3. With K(g) so chosen, two stacked 16-row accumulator
 // tiles are directly the B fragment of the next product that contracts over
 // those rows: no data movement between chained products.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
-#include "gdr_internal.h"
+#include "chunk_common.h"
 
 namespace gdr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int C = 64;    // tokens per chunk
-constexpr int BV = 64;   // value columns per workgroup (16 per wave)
-
-struct ChunkParams {
-  const void *q, *k, *v;
-  int64_t q_stride, k_stride, v_stride;
-  const float *g, *beta;
-  void *o;
-  void *pool;
-  const int32_t *slot_idx, *cu_seqlens;
-  int32_t N, HK, HV, ratio;
-  float scale;
-  int zero_init, st_bf16, out_bf16;
-};
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-struct Frag {
-  bf16x8 hi, lo;
-};
-
-__device__ __forceinline__ void split8(const float (&x)[8], Frag &f) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    f.hi[j] = h;
-    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-  }
-}
-
-// acc += a * b with the passes the operands need (lo terms first).
-template <bool A_SPLIT, bool B_SPLIT>
-__device__ __forceinline__ f32x4 mm(const Frag &a, const Frag &b, f32x4 c) {
-  if constexpr (A_SPLIT) c = mfma(a.lo, b.hi, c);
-  if constexpr (B_SPLIT) c = mfma(a.hi, b.lo, c);
-  return mfma(a.hi, b.hi, c);
-}
-
-// Fragment of row `row`, k step starting at column col0, from a row-major LDS
-// array: columns col0 + 4g + 0..3 and col0 + 16 + 4g + 0..3.
-__device__ __forceinline__ void ldfrag(const uint16_t *base, int pitch, int row, int col0, int g,
-                                       Frag &f) {
-  const uint16_t *p = base + row * pitch + col0 + 4 * g;
-  const uint2 a = *reinterpret_cast<const uint2 *>(p);
-  const uint2 b = *reinterpret_cast<const uint2 *>(p + 16);
-  const u32x4 u = {a.x, a.y, b.x, b.y};
-  f.hi = __builtin_bit_cast(bf16x8, u);
-}
-__device__ __forceinline__ void ldfrag(const float *base, int pitch, int row, int col0, int g,
-                                       Frag &f) {
-  const float *p = base + row * pitch + col0 + 4 * g;
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 16);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  split8(x, f);
-}
-
-// B fragment over 32 rows built from two stacked accumulator tiles.
-__device__ __forceinline__ void chainfrag(const f32x4 &t0, const f32x4 &t1, Frag &f) {
-  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-  split8(x, f);
-}
-
-// 16x16x16 products (k = 4g .. 4g+3 per lane): the accumulator layout of a
-// 16-row tile is directly a B fragment, so block-triangular chains need no
-// reordering.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-struct Frag4 {
-  bf16x4 hi, lo;
-};
-
-__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void split4(const f32x4 &x, Frag4 &f) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    f.hi[j] = h;
-    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-  }
-}
-
-// acc += a * b, both split (three passes, lo terms first)
-__device__ __forceinline__ f32x4 mm16(const Frag4 &a, const Frag4 &b, f32x4 c) {
-  c = mfma16(a.lo, b.hi, c);
-  c = mfma16(a.hi, b.lo, c);
-  return mfma16(a.hi, b.hi, c);
-}
-
-// A fragment of a 16x16 block of an fp32 LDS matrix: row `row`, columns
-// col0 + 4g .. col0 + 4g + 3.
-__device__ __forceinline__ void ldfrag4(const float *base, int pitch, int row, int col0, int g,
-                                        Frag4 &f) {
-  const float4 a = *reinterpret_cast<const float4 *>(base + row * pitch + col0 + 4 * g);
-  const f32x4 x = {a.x, a.y, a.z, a.w};
-  split4(x, f);
-}
-
-
-// Split fragment of a 16x16 block of a pre-split bf16 plane pair: row `row`,
-// columns col0 + 4g .. col0 + 4g + 3.
-__device__ __forceinline__ void ldsplit4(const uint16_t *hi, const uint16_t *lo, int pitch, int row,
-                                         int col0, int g, Frag4 &f) {
-  const int o = row * pitch + col0 + 4 * g;
-  f.hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi + o));
-  f.lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo + o));
-}
-
-__device__ __forceinline__ void store_split(uint16_t *hi, uint16_t *lo, int idx, float x) {
-  const __bf16 h = static_cast<__bf16>(x);
-  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
-  hi[idx] = __builtin_bit_cast(uint16_t, h);
-  lo[idx] = __builtin_bit_cast(uint16_t, l);
-}
+using namespace chunk;
 
 // ---------------------------------------------------------------------------
 // LDS layout
@@ -210,13 +88,12 @@ struct Smem {
   In vv[C][PV];   // this workgroup's value columns
   // The C x C coefficient matrices, already split into bf16 hi / lo planes:
   // R's off-diagonal blocks and the diagonal-block inverses T_II share rt*,
-  // A sits in aq*. rdT holds R's diagonal blocks in fp32, transposed, for the
-  // solve. During the channel-gate prep the same storage stages g.
+  // A sits in aq*. rd holds R's diagonal blocks in fp32 for the solve. During the channel-gate prep the same storage stages g.
   union {
     struct {
       uint16_t rth[C][PB], rtl[C][PB];
       uint16_t aqh[C][PB], aql[C][PB];
-      float rdT[4][16][17];
+      float rd[4][16][20];
     };
     float gstage[C][D];
   };
@@ -224,17 +101,6 @@ struct Smem {
   float eGlastc[D];
   float eGlast;
 };
-
-// Inclusive scan across the 64 lanes of a wave.
-__device__ __forceinline__ float wave_scan(float x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
 
 template <bool IN_F32>
 __device__ __forceinline__ void load8(const void *base, int64_t off, bool valid, float (&x)[8]) {
@@ -283,12 +149,6 @@ __device__ __forceinline__ void copy8(const void *base, int64_t off, bool valid,
 // Registers holding one chunk's keys, queries, values and gates between its
 // global loads and its LDS stores, so that the loads of chunk c+1 are in
 // flight while chunk c computes.
-// (Vector types, not arrays: they stay in registers as SSA values.)
-template <int N>
-struct U32Vec {
-  typedef unsigned int type __attribute__((ext_vector_type(N)));
-};
-
 template <bool IN_F32, int D>
 struct Prefetch {
   static constexpr int E = IN_F32 ? 4 : 8;       // elements per 16-byte unit
@@ -298,15 +158,6 @@ struct Prefetch {
   typename U32Vec<4 * VU>::type v;
   float g, beta;                                 // wave 0: token `lane`
 };
-
-template <class Vec>
-__device__ __forceinline__ void put4(Vec &v, int u, const uint4 x) {
-  v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
-}
-template <class Vec>
-__device__ __forceinline__ uint4 get4(const Vec &v, int u) {
-  return make_uint4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
-}
 
 // Where each lane's prefetch units sit inside a chunk: unit u of the keys is
 // row krow + u * krs, 16-byte column block kc (same for queries); values
@@ -368,9 +219,13 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
 
 // Gram matrices of one chunk, lower 16x16 tiles (I >= J). Delta rule: waves
 // 0-1 form K K^T (-> R), waves 2-3 form Q K^T (-> A); each wave owns row
-// blocks {a, 3-a} (five tiles, its A fragments loaded once, five independent
+// blocks {a, 3-a} (five tiles, their fragments loaded once, five independent
 // MFMA chains). Linear rule: wave w forms the Q K^T tiles of row block w. The
 // wave's role is a template argument so each role is straight-line code.
+// Each tile is computed transposed (keys of block J as the M operand, rows of
+// block I as N), so a lane ends up holding row ii = 16I + r, columns
+// jj = 16J + 4g .. +3: exactly the A-fragment layout of the 16x16x16 products
+// that consume R and A, stored with one 8-byte write per plane.
 template <int W, bool IN_F32, int GATE, bool DELTA, int D, class SM>
 __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g) {
   constexpr bool OPF32 = SM::OPF32;
@@ -381,35 +236,33 @@ __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g
   constexpr int IB = DELTA ? 3 - IA : IA;
   constexpr int JMAX = IB > IA ? IB : IA;
   using Op = typename SM::Op;
-  const Op *arow = ISQ ? &sm.qq[0][0] : &sm.kk[0][0];
+  const Op *nrow = ISQ ? &sm.qq[0][0] : &sm.kk[0][0];
 
-  Frag fa[NRB][NS];
+  Frag fn[NRB][NS];   // rows of blocks IA, IB (N operand)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    ldfrag(arow, SM::PK, 16 * IA + r, 32 * s, g, fa[0][s]);
-    if constexpr (DELTA) ldfrag(arow, SM::PK, 16 * IB + r, 32 * s, g, fa[NRB - 1][s]);
+    ldfrag(nrow, SM::PK, 16 * IA + r, 32 * s, g, fn[0][s]);
+    if constexpr (DELTA) ldfrag(nrow, SM::PK, 16 * IB + r, 32 * s, g, fn[NRB - 1][s]);
   }
   f32x4 acc[NRB][4];
 #pragma unroll
   for (int J = 0; J <= JMAX; ++J) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Frag fb[NS];
+    Frag fm[NS];   // keys of block J (M operand)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if constexpr (GATE == GDR_GATE_CHANNEL && !DELTA) {
         // e^{-G} k is only held transposed for the linear rule
         float x[8];
+        const int tok = perm32(16 * J + r);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kcol = 32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-          x[j] = sm.kt[kcol][16 * J + r];
-        }
-        split8(x, fb[s]);
+        for (int j = 0; j < 8; ++j) x[j] = sm.kt[32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4)][tok];
+        split8(x, fm[s]);
       } else if constexpr (GATE == GDR_GATE_CHANNEL) {
-        ldfrag(&sm.kinv[0][0], SM::PK, 16 * J + r, 32 * s, g, fb[s]);
+        ldfrag(&sm.kinv[0][0], SM::PK, 16 * J + r, 32 * s, g, fm[s]);
       } else {
-        ldfrag(&sm.kk[0][0], SM::PK, 16 * J + r, 32 * s, g, fb[s]);
+        ldfrag(&sm.kk[0][0], SM::PK, 16 * J + r, 32 * s, g, fm[s]);
       }
     }
 #pragma unroll
@@ -417,7 +270,7 @@ __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g
       const int I = rb ? IB : IA;
       if (J <= I) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<OPF32, OPF32>(fa[rb][s], fb[s], acc[rb][J]);
+        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<OPF32, OPF32>(fm[s], fn[rb][s], acc[rb][J]);
       }
     }
   }
@@ -425,26 +278,37 @@ __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int I = rb ? IB : IA;
-    const float4 Gi = *reinterpret_cast<const float4 *>(&sm.G[16 * I + 4 * g]);
-    const float4 Bi = *reinterpret_cast<const float4 *>(&sm.beta[16 * I + 4 * g]);
-    const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+    const int ii = 16 * I + r;
+    const float Gi = sm.G[ii], bi = sm.beta[ii];
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
-      const int jj = 16 * J + r;
-      const float Gj = sm.G[jj];
+      const float4 Gj4 = *reinterpret_cast<const float4 *>(&sm.G[16 * J + 4 * g]);
+      const float Gj[4] = {Gj4.x, Gj4.y, Gj4.z, Gj4.w};
+      float val[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ii = 16 * I + 4 * g + i;
+        const int jj = 16 * J + 4 * g + i;
         float gam = 1.f;
-        if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(gi[i] - Gj);
-        if constexpr (ISQ) {
-          const float val = (jj <= ii) ? p.scale * acc[rb][J][i] * gam : 0.f;
-          store_split(&sm.aqh[0][0], &sm.aql[0][0], ii * SM::PB + jj, val);
-        } else {
-          const float val = (jj < ii) ? bi[i] * acc[rb][J][i] * gam : 0.f;
-          if (J < I) store_split(&sm.rth[0][0], &sm.rtl[0][0], ii * SM::PB + jj, val);
-          else sm.rdT[I][r][4 * g + i] = val;   // transposed diagonal block
+        if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(Gi - Gj[i]);
+        if constexpr (ISQ) val[i] = (jj <= ii) ? p.scale * acc[rb][J][i] * gam : 0.f;
+        else val[i] = (jj < ii) ? bi * acc[rb][J][i] * gam : 0.f;
+      }
+      if (!ISQ && J == I) {
+        *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
+      } else {
+        uint16_t hb[4], lb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 hh = static_cast<__bf16>(val[i]);
+          hb[i] = __builtin_bit_cast(uint16_t, hh);
+          lb[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val[i] - static_cast<float>(hh)));
         }
+        const uint2 hw = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+        const uint2 lw = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
+        uint16_t *ph = ISQ ? &sm.aqh[0][0] : &sm.rth[0][0];
+        uint16_t *pl = ISQ ? &sm.aql[0][0] : &sm.rtl[0][0];
+        *reinterpret_cast<uint2 *>(ph + ii * SM::PB + 16 * J + 4 * g) = hw;
+        *reinterpret_cast<uint2 *>(pl + ii * SM::PB + 16 * J + 4 * g) = lw;
       }
     }
   }
@@ -523,8 +387,16 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       for (int u = 0; u < PF::KU; ++u) {
         const int row = lo.krow + u * lo.krs, c = lo.kc / (int)sizeof(In);
         const bool ok = row < L;
-        *reinterpret_cast<uint4 *>(&sm.kk[row][c]) = ok ? get4(pf.k, u) : z;
-        *reinterpret_cast<uint4 *>(&sm.qq[row][c]) = ok ? get4(pf.q, u) : z;
+        const uint4 kx = ok ? get4(pf.k, u) : z, qx = ok ? get4(pf.q, u) : z;
+        if constexpr (IN_F32) {   // 4 columns: one permuted group
+          *reinterpret_cast<uint4 *>(&sm.kk[row][perm32(c)]) = kx;
+          *reinterpret_cast<uint4 *>(&sm.qq[row][perm32(c)]) = qx;
+        } else {                  // 8 columns: two permuted groups of 4
+          *reinterpret_cast<uint2 *>(&sm.kk[row][perm32(c)]) = make_uint2(kx.x, kx.y);
+          *reinterpret_cast<uint2 *>(&sm.kk[row][perm32(c + 4)]) = make_uint2(kx.z, kx.w);
+          *reinterpret_cast<uint2 *>(&sm.qq[row][perm32(c)]) = make_uint2(qx.x, qx.y);
+          *reinterpret_cast<uint2 *>(&sm.qq[row][perm32(c + 4)]) = make_uint2(qx.z, qx.w);
+        }
       }
 #pragma unroll
       for (int u = 0; u < PF::VU; ++u) {
@@ -554,16 +426,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int u = 0; u < D * RG / 256; ++u) {
         const int it = tid + 256 * u, dk = it % D, rg = it / D;
+        const int pdk = perm32(dk);
         uint32_t wv[4];
         if constexpr (IN_F32) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) wv[j] = __float_as_uint(sm.kk[E * rg + j][dk]);
+          for (int j = 0; j < 4; ++j) wv[j] = __float_as_uint(sm.kk[E * rg + j][pdk]);
+          *reinterpret_cast<uint4 *>(&sm.kt[dk][perm32(E * rg)]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            wv[j] = (uint32_t)sm.kk[E * rg + 2 * j][dk] | ((uint32_t)sm.kk[E * rg + 2 * j + 1][dk] << 16);
+            wv[j] = (uint32_t)sm.kk[E * rg + 2 * j][pdk] | ((uint32_t)sm.kk[E * rg + 2 * j + 1][pdk] << 16);
+          *reinterpret_cast<uint2 *>(&sm.kt[dk][perm32(E * rg)]) = make_uint2(wv[0], wv[1]);
+          *reinterpret_cast<uint2 *>(&sm.kt[dk][perm32(E * rg + 4)]) = make_uint2(wv[2], wv[3]);
         }
-        *reinterpret_cast<uint4 *>(&sm.kt[dk][E * rg]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
     } else {
       // channel gate: stage g, prefix-sum each key channel over the chunk,
@@ -606,10 +481,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         for (int j = 0; j < 8; ++j) {
           const float Gv = sm.gstage[row][c8 + j];
           const float e = __expf(Gv), ei = __expf(-Gv);
-          sm.kk[row][c8 + j] = kx[j] * e;
-          sm.qq[row][c8 + j] = qx[j] * e;
-          if constexpr (DELTA) sm.kinv[row][c8 + j] = kx[j] * ei;
-          else sm.kt[c8 + j][row] = kx[j] * ei;   // linear rule: no Gram needs kinv
+          const int pc = perm32(c8 + j);
+          sm.kk[row][pc] = kx[j] * e;
+          sm.qq[row][pc] = qx[j] * e;
+          if constexpr (DELTA) sm.kinv[row][pc] = kx[j] * ei;
+          else sm.kt[c8 + j][perm32(row)] = kx[j] * ei;   // linear rule: no Gram needs kinv
         }
       }
       __syncthreads();
@@ -630,13 +506,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int e = 0; e < C * D / 256; ++e) {
         const int idx = tid + 256 * e;
-        tmp[e] = sm.kinv[idx / D][idx % D];
+        tmp[e] = sm.kinv[idx / D][perm32(idx % D)];
       }
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < C * D / 256; ++e) {
         const int idx = tid + 256 * e;
-        sm.kt[idx % D][idx / D] = tmp[e];
+        sm.kt[idx % D][perm32(idx / D)] = tmp[e];
       }
     }
 
@@ -666,23 +542,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 
     // ======== phase 3: inverses of the diagonal blocks of I + R (wave w: block w) ========
     if constexpr (DELTA) {
-      // Right-looking forward substitution; the four lane groups of a wave
-      // solve the same column c redundantly (branch free) and each stores a
-      // quarter of its rows.
+      // Forward substitution down the rows of block w (x = column c of T_ww);
+      // the four lane groups of a wave solve the same column redundantly
+      // (branch free) and each stores a quarter of its rows.
       const int c = lane & 15, q = lane >> 4, o = 16 * w;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) {
-        float colj[16];   // column j of the block: R[o + i][o + j]
+      for (int i = 0; i < 16; ++i) {
+        float row[16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rdT[w][j][4 * i4]);
-          colj[4 * i4] = v4.x; colj[4 * i4 + 1] = v4.y; colj[4 * i4 + 2] = v4.z; colj[4 * i4 + 3] = v4.w;
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rd[w][i][4 * i4]);
+          row[4 * i4] = v4.x; row[4 * i4 + 1] = v4.y; row[4 * i4 + 2] = v4.z; row[4 * i4 + 3] = v4.w;
         }
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] -= colj[i] * x[j];
+        for (int j = 0; j < i; ++j) a4[j & 3] += row[j] * x[j];
+        x[i] = ((i == c) ? 1.f : 0.f) - ((a4[0] + a4[1]) + (a4[2] + a4[3]));
       }
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -881,6 +757,15 @@ hipError_t by_gate(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
+  // bf16 inputs without a channel gate take the warp-specialised kernel;
+  // GDR_PREFILL_KERNEL=generic selects this file's kernel for every case
+  // (used to compare the two).
+  static const bool force_generic = [] {
+    const char *e = getenv("GDR_PREFILL_KERNEL");
+    return e && strcmp(e, "generic") == 0;
+  }();
+  if (!force_generic && a.in_dtype == GDR_BF16 && a.gate != GDR_GATE_CHANNEL)
+    return launch_chunk_fwd_ws(a, stream);
   ChunkParams p;
   p.q = a.q; p.k = a.k; p.v = a.v;
   p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
