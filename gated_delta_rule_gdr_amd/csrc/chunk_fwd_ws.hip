@@ -205,73 +205,17 @@ __device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, 
   f.hi = __builtin_bit_cast(bf16x8, ab);
 }
 
+// Prep role (waves 4-7): stages chunk c+1 while the state waves run chunk c.
 template <int GATE, bool DELTA, int D>
-__global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
+__device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D> &sm, int pw, int ptid,
+                                                int lane, int r, int g, int h, int hk, int64_t bos,
+                                                int64_t eos, int nc) {
   using SM = SmemWS<D>;
   using PF = PrefWS<D>;
-  constexpr int NB = D / BV;
-  constexpr int NT = D / 16;
-  constexpr int NS = D / 32;
   constexpr int PK = SM::PK, PB = SM::PB;
-  __shared__ SM sm;
-
-  // XCD-aware decomposition (see chunk_fwd.hip)
-  const int GRP = p.ratio * NB;
-  const int b = blockIdx.x;
-  const int gi = (b / (8 * GRP)) * 8 + (b & 7);
-  if (gi >= p.N * p.HK) return;
-  const int j = (b >> 3) % GRP;
-  const int n = gi / p.HK;
-  const int hk = gi - n * p.HK;
-  const int h = hk * p.ratio + j / NB;
-  const int vb = j % NB;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const bool is_state = w < 4;
-  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
-  const int nc = (int)((eos - bos + C - 1) / C);
-  const int64_t HVD = (int64_t)p.HV * D;
-  if (tid == 0) sm.kcount = 0;
-
-  // state waves: this lane's value column and resident state
-  const int col = vb * BV + 16 * (w & 3) + r;
-  f32x4 st[NT];
-#pragma unroll
-  for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  typename U32Vec<16>::type vreg;   // this lane's 16 values of the next chunk (bf16 bits)
-  if (is_state && !p.zero_init) {
-    const int64_t sbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + col;
-    if (p.st_bf16) {
-      const uint16_t *sp = static_cast<const uint16_t *>(p.pool) + sbase;
-#pragma unroll
-      for (int m = 0; m < NT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[m][i] = bf16_to_f32(sp[(16 * m + 4 * g + i) * D]);
-    } else {
-      const float *sp = static_cast<const float *>(p.pool) + sbase;
-#pragma unroll
-      for (int m = 0; m < NT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[m][i] = sp[(16 * m + 4 * g + i) * D];
-    }
-  }
-  auto load_v = [&](int ci) {
-    const int64_t t0 = bos + (int64_t)ci * C;
-    const int last = (int)min<int64_t>(C, eos - t0) - 1;
-    const uint16_t *vp = static_cast<const uint16_t *>(p.v) + t0 * p.v_stride + (int64_t)h * D + col;
-    const uint32_t vs = (uint32_t)p.v_stride;
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vreg[4 * I + i] = vp[(uint32_t)min(16 * I + 4 * g + i, last) * vs];
-  };
-
-  // prep waves: work for chunk ci into set ci % 2
-  const int ptid = tid - 256, pw = w - 4;
   PF pf;
   pf.g = pf.beta = 0.f;
+  // work for chunk ci into set ci % 2
   auto prep = [&](int ci) {
     auto &S = sm.set[ci & 1];
     const int64_t t0 = bos + (int64_t)ci * C;
@@ -333,25 +277,97 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
     }
   };
 
+  if (nc == 0) return;
+  prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
+  prep(0);
+  __syncthreads();   // chunk 0 staged
+  for (int c = 0; c < nc; ++c) {
+    if (c + 1 < nc) prep(c + 1);
+    __syncthreads();   // set c % 2 is free again once the state waves are done with it
+  }
+}
+
+template <int GATE, bool DELTA, int D>
+__global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
+  using SM = SmemWS<D>;
+  constexpr int NB = D / BV;
+  constexpr int NT = D / 16;
+  constexpr int NS = D / 32;
+  constexpr int PK = SM::PK, PB = SM::PB;
+  __shared__ SM sm;
+
+  // XCD-aware decomposition (see chunk_fwd.hip)
+  const int GRP = p.ratio * NB;
+  const int b = blockIdx.x;
+  const int gi = (b / (8 * GRP)) * 8 + (b & 7);
+  if (gi >= p.N * p.HK) return;
+  const int j = (b >> 3) % GRP;
+  const int n = gi / p.HK;
+  const int hk = gi - n * p.HK;
+  const int h = hk * p.ratio + j / NB;
+  const int vb = j % NB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+  // the wave index through readfirstlane is provably uniform, so the role
+  // branch below is a scalar branch and each role runs its own loop
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  const int nc = (int)((eos - bos + C - 1) / C);
+  const int64_t HVD = (int64_t)p.HV * D;
+  if (tid == 0) sm.kcount = 0;
   __syncthreads();   // kcount initialised
-  if (nc > 0) {
-    if (is_state) {
-      load_v(0);
+
+  // Both roles pass the same barriers: one after the prologue and one at the
+  // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
+  if (w >= 4) {
+    chunk_prep_role<GATE, DELTA, D>(p, sm, w - 4, tid - 256, lane, r, g, h, hk, bos, eos, nc);
+    return;
+  }
+
+  // state waves: this lane's value column and resident state
+  const int col = vb * BV + 16 * w + r;
+  f32x4 st[NT];
+#pragma unroll
+  for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  typename U32Vec<16>::type vreg;   // this lane's 16 values of the next chunk (bf16 bits)
+  if (!p.zero_init) {
+    const int64_t sbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + col;
+    if (p.st_bf16) {
+      const uint16_t *sp = static_cast<const uint16_t *>(p.pool) + sbase;
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[m][i] = bf16_to_f32(sp[(16 * m + 4 * g + i) * D]);
     } else {
-      prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
-      prep(0);
+      const float *sp = static_cast<const float *>(p.pool) + sbase;
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[m][i] = sp[(16 * m + 4 * g + i) * D];
     }
   }
-  __syncthreads();
+  auto load_v = [&](int ci) {
+    const int64_t t0 = bos + (int64_t)ci * C;
+    const int last = (int)min<int64_t>(C, eos - t0) - 1;
+    const uint16_t *vp = static_cast<const uint16_t *>(p.v) + t0 * p.v_stride + (int64_t)h * D + col;
+    const uint32_t vs = (uint32_t)p.v_stride;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vreg[4 * I + i] = vp[(uint32_t)min(16 * I + 4 * g + i, last) * vs];
+  };
+
+  if (nc == 0) return;
+  load_v(0);
+  __syncthreads();   // chunk 0 staged by the prep waves
 
   for (int c = 0; c < nc; ++c) {
-    if (!is_state) {
-      if (c + 1 < nc) prep(c + 1);
-    } else {
+    {
       const auto &S = sm.set[c & 1];
       const int64_t t0 = bos + (int64_t)c * C;
       const int L = (int)min<int64_t>(C, eos - t0);
-      const int sw = w;   // state wave 0..3
 
       // this chunk's values, then the next chunk's loads go in flight
       f32x4 vt[4];
@@ -504,13 +520,12 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
           }
         }
       }
-      (void)sw;
     }
     __syncthreads();   // set c % 2 is refilled by the prep waves next
   }
 
   // ---- final state back to the pool slot ----
-  if (is_state) {
+  {
     const int64_t sbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + col;
     if (p.st_bf16) {
       uint16_t *sp = static_cast<uint16_t *>(p.pool) + sbase;
