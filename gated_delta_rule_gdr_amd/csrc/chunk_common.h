@@ -159,6 +159,30 @@ __device__ __forceinline__ float wave_scan_dpp(float x) {
   return x;
 }
 
+// Lane J of every row of 16 lanes, broadcast to that row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast16(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, false));
+}
+
+// Right-looking substitution for the inverse of a unit lower triangular
+// 16x16 matrix I + N (N strictly lower, exact zeros on and above the
+// diagonal). Lane (r, g) holds row r of N in n[] and row r, columns
+// 4g .. 4g+3 of the inverse in t[] (start: row r of I). At step J row J of
+// the inverse is final; every row below subtracts N[r][J] times it.
+template <int J>
+__device__ __forceinline__ void unit_lower_inverse16(float (&t)[4], const float (&n)[16]) {
+  if constexpr (J < 16) {
+    float tj[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tj[i] = row_bcast16<J>(t[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = fmaf(-n[J], tj[i], t[i]);
+    unit_lower_inverse16<J + 1>(t, n);
+  }
+}
+
 __device__ __forceinline__ float lane_value(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }

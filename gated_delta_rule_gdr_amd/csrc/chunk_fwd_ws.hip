@@ -12,14 +12,14 @@
 //   * prep waves 4-7 do everything that does not, one chunk ahead: write
 //     chunk c+1's keys and queries into LDS (from registers loaded one more
 //     chunk ahead), the gate prefix sums, the Gram matrices R and A, and the
-//     16x16 diagonal inverses of I + R.
+//     16x16 diagonal inverses of I + R (in registers, by the waves that
+//     formed those blocks of R).
 //
 // Keys, queries, the coefficient planes and the gate factors are double
 // buffered in LDS (set c % 2 is read by the state waves while the prep waves
 // fill set (c+1) % 2), so one workgroup barrier per chunk suffices. The prep
-// waves synchronise among themselves through an LDS counter (their key and
-// query stores must land before their Gram matrices read them, and R must be
-// complete before each of them inverts one diagonal block).
+// waves synchronise among themselves through an LDS counter: their key and
+// query stores must land before their Gram matrices read them.
 //
 // The state update reads K^T fragments straight from the token-major key
 // array with the transposing LDS read of gfx950 (ds_read_b64_tr_b16), so no
@@ -46,7 +46,7 @@ struct SmemWS {
     float eGlast, pad_[3];
   };
   Set set[2];
-  float rd[4][16][20];   // R's diagonal blocks in fp32 (prep waves only)
+  float rd[4][16][20];   // R's diagonal blocks in fp32, each read back only by the wave that wrote it
   int kcount;            // prep-wave store counter (monotonic)
 };
 
@@ -82,8 +82,8 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
 
 // Gram matrices of one chunk (see grams() in chunk_fwd.hip for the tile
 // assignment): tile (I, J) is computed transposed so that a lane holds row
-// ii = 16I + r, columns 16J + 4g .. +3, stored as split bf16 planes (R's
-// diagonal blocks in fp32 into rd).
+// ii = 16I + r, columns 16J + 4g .. +3, stored as split bf16 planes. R's
+// diagonal blocks are replaced by their unit lower triangular inverses.
 template <int W, int GATE, bool DELTA, int D, class Set>
 __device__ __forceinline__ void grams_ws(Set &S, float (*rd)[16][20], float scale, int r, int g,
                                          int pitch_k, int pitch_b) {
@@ -155,34 +155,34 @@ __device__ __forceinline__ void grams_ws(Set &S, float (*rd)[16][20], float scal
       }
     }
   }
-}
-
-// Inverse of the unit lower triangular 16x16 block I + R_bb (R_bb from rd)
-// by forward substitution down its rows: lane column c = r; the four lane
-// groups solve the same column redundantly and each stores 4 of its rows
-// (rows 4g .. 4g+3) into the diagonal block of the planes.
-template <class Set>
-__device__ __forceinline__ void solve_diag(Set &S, const float (*rd)[16][20], int bb, int r, int g,
-                                           int pitch_b) {
-  float x[16];
+  if constexpr (!ISQ) {
+    // T_II = (I + R_II)^{-1} in registers; rd[I] (this wave's own rows)
+    // hands every lane its full row of R_II
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float row[16];
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int I = rb ? IB : IA;
+      float nrow[16], t[4];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 v4 = *reinterpret_cast<const float4 *>(&rd[bb][i][4 * i4]);
-      row[4 * i4] = v4.x; row[4 * i4 + 1] = v4.y; row[4 * i4 + 2] = v4.z; row[4 * i4 + 3] = v4.w;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(&rd[I][r][4 * i4]);
+        nrow[4 * i4] = v4.x; nrow[4 * i4 + 1] = v4.y; nrow[4 * i4 + 2] = v4.z; nrow[4 * i4 + 3] = v4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = (r == 4 * g + i) ? 1.f : 0.f;
+      unit_lower_inverse16<0>(t, nrow);
+      uint16_t hb[4], lb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 hh = static_cast<__bf16>(t[i]);
+        hb[i] = __builtin_bit_cast(uint16_t, hh);
+        lb[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(t[i] - static_cast<float>(hh)));
+      }
+      const int idx = (16 * I + r) * pitch_b + 16 * I + 4 * g;
+      *reinterpret_cast<uint2 *>(&S.rth[0][0] + idx) =
+          make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+      *reinterpret_cast<uint2 *>(&S.rtl[0][0] + idx) =
+          make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
     }
-    float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < i; ++j) a4[j & 3] += row[j] * x[j];
-    x[i] = ((i == r) ? 1.f : 0.f) - ((a4[0] + a4[1]) + (a4[2] + a4[3]));
-  }
-  const int o = 16 * bb;
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const float v = g == 0 ? x[i4] : g == 1 ? x[4 + i4] : g == 2 ? x[8 + i4] : x[12 + i4];
-    store_split(&S.rth[0][0], &S.rtl[0][0], (o + 4 * g + i4) * pitch_b + o + r, v);
   }
 }
 
@@ -248,32 +248,26 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D> 
       const int64_t tn = t0 + C;
       prep_load<GATE, DELTA, D>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
     }
-    // all prep waves' stores land before any prep wave reads them
-    __threadfence_block();
+    // all prep waves' key/query stores land before any prep wave reads them:
+    // wait for this wave's LDS stores only (the prefetch stays in flight),
+    // then count in and spin on the counter (bounded)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (lane == 0) atomicAdd(&sm.kcount, 1);
-    const int target = (DELTA ? 8 : 4) * ci + 4;   // two arrivals per chunk under the delta rule
+    // an LDS-typed pointer: a generic one compiles to a flat load, which
+    // would also wait for the prefetch in flight
+    typedef __attribute__((address_space(3))) volatile int lds_vint;
+    const lds_vint *kcount_lds = (const lds_vint *)&sm.kcount;
+    const int target = 4 * ci + 4;
     for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (*reinterpret_cast<volatile int *>(&sm.kcount) >= target) break;
+      if (*kcount_lds >= target) break;
       __builtin_amdgcn_s_sleep(1);
     }
-    __threadfence_block();
+    asm volatile("" ::: "memory");
     switch (pw) {
       case 0: grams_ws<0, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
       case 1: grams_ws<1, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
       case 2: grams_ws<2, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
       default: grams_ws<3, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
-    }
-    if constexpr (DELTA) {
-      // every prep wave inverts one diagonal block once all of R is formed
-      __threadfence_block();
-      if (lane == 0) atomicAdd(&sm.kcount, 1);
-      const int target2 = 8 * ci + 8;
-      for (int spin = 0; spin < (1 << 24); ++spin) {
-        if (*reinterpret_cast<volatile int *>(&sm.kcount) >= target2) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      __threadfence_block();
-      solve_diag(S, sm.rd, pw, r, g, PB);
     }
   };
 
