@@ -47,6 +47,7 @@ struct SmemWS {
   };
   Set set[2];
   float rd[4][16][20];   // R's diagonal blocks in fp32, each read back only by the wave that wrote it
+  uint16_t vx[4][C][16];  // per state wave: its 16 value columns of the chunk, token-major (swizzled halves)
   int kcount;            // prep-wave store counter (monotonic)
 };
 
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
   f32x4 st[NT];
 #pragma unroll
   for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  typename U32Vec<16>::type vreg;   // this lane's 16 values of the next chunk (bf16 bits)
+  typename U32Vec<8>::type vreg;   // next chunk: token `lane`, this wave's 16 value columns (bf16)
   if (!p.zero_init) {
     const int64_t sbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + col;
     if (p.st_bf16) {
@@ -344,18 +345,17 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
   auto load_v = [&](int ci) {
     const int64_t t0 = bos + (int64_t)ci * C;
     const int last = (int)min<int64_t>(C, eos - t0) - 1;
-    const uint16_t *vp = static_cast<const uint16_t *>(p.v) + t0 * p.v_stride + (int64_t)h * D + col;
-    const uint32_t vs = (uint32_t)p.v_stride;
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vreg[4 * I + i] = vp[(uint32_t)min(16 * I + 4 * g + i, last) * vs];
+    const char *vbase = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BV + 16 * w) * 2;
+    const uint32_t off = (uint32_t)min(lane, last) * (uint32_t)(p.v_stride * 2);
+    put4(vreg, 0, *reinterpret_cast<const uint4 *>(vbase + off));
+    put4(vreg, 1, *reinterpret_cast<const uint4 *>(vbase + off + 16));
   };
-
-  if (nc == 0) return;
-  load_v(0);
-  __syncthreads();   // chunk 0 staged by the prep waves
+  // A zero-length sequence has no rows to read and its prep waves have
+  // already left, so it goes straight to the write-back of its initial state.
+  if (nc > 0) {
+    load_v(0);
+    __syncthreads();   // chunk 0 staged by the prep waves
+  }
 
   for (int c = 0; c < nc; ++c) {
     {
@@ -364,13 +364,30 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
       const int L = (int)min<int64_t>(C, eos - t0);
 
       // this chunk's values, then the next chunk's loads go in flight
+      // Token-major values go through this wave's LDS tile (16-byte halves
+      // swapped on rows with bit 3 set, so the row writes do not collide) and
+      // come back in the accumulator layout: lane (r, g), slot i of block I
+      // holds V[16I + 4g + i][r]. Tokens past the sequence end are zero.
       f32x4 vt[4];
+      {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        uint16_t *vx = &sm.vx[w][0][0];
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const bool okv = lane < L;
+        const int sw = (lane >> 3) & 1;
+        *reinterpret_cast<uint4 *>(vx + lane * 16 + 8 * sw) = okv ? get4(vreg, 0) : z;
+        *reinterpret_cast<uint4 *>(vx + lane * 16 + 8 * (sw ^ 1)) = okv ? get4(vreg, 1) : z;
+        if (c + 1 < nc) load_v(c + 1);
 #pragma unroll
-      for (int I = 0; I < 4; ++I)
+        for (int I = 0; I < 4; ++I) {
+          const int row = 16 * I + 4 * g + (r >> 2);
+          const int half = ((r & 3) >> 1) ^ ((row >> 3) & 1);
+          const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(vx + row * 16 + 8 * half + 4 * (r & 1)));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vt[I][i] = (16 * I + 4 * g + i < L) ? bf16_to_f32((uint16_t)vreg[4 * I + i]) : 0.f;
-      if (c + 1 < nc) load_v(c + 1);
+          for (int i = 0; i < 4; ++i) vt[I][i] = bf16_to_f32((uint16_t)t[i]);
+        }
+      }
 
       // X = K S^T (delta rule) and Q S^T
       f32x4 xa[4], qa[4];
@@ -452,33 +469,28 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         oa[I] = acc;
       }
       {
+        // Buffer stores against a descriptor over this chunk's 64 output
+        // rows: row 16I + i is a scalar offset, the lane part (row group 4g,
+        // column) a fixed 32-bit offset, so no per-store address arithmetic.
         const uint32_t HVDu = (uint32_t)HVD;
-        if (p.out_bf16) {
-          uint16_t *ob = static_cast<uint16_t *>(p.o) + t0 * HVD + (int64_t)h * D + col;
+        const uint32_t osz = p.out_bf16 ? 2u : 4u;
+        char *obase = static_cast<char *>(p.o) + (t0 * HVD + (int64_t)h * D) * osz;
+        const uint32_t orow = HVDu * osz;
+        const __amdgpu_buffer_rsrc_t ors =
+            __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)(C * orow), 0x00020000);
+        const uint32_t olane = ((uint32_t)(4 * g) * HVDu + (uint32_t)col) * osz;
 #pragma unroll
-          for (int I = 0; I < 4; ++I)
+        for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int ii = 16 * I + 4 * g + i;
-              if (L == C || ii < L) ob[(uint32_t)ii * HVDu] = f32_to_bf16(oa[I][i]);
+          for (int i = 0; i < 4; ++i) {
+            const int srow = (16 * I + i) * (int)orow;
+            const bool ok = L == C || 16 * I + 4 * g + i < L;
+            if (p.out_bf16) {
+              if (ok) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), ors, olane, srow, 0);
+            } else {
+              if (ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][i]), ors, olane, srow, 0);
             }
-        } else {
-          float *ob = static_cast<float *>(p.o) + t0 * HVD + (int64_t)h * D + col;
-          if (L == C) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) ob[(uint32_t)(16 * I + 4 * g + i) * HVDu] = oa[I][i];
-          } else {
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int ii = 16 * I + 4 * g + i;
-                if (ii < L) ob[(uint32_t)ii * HVDu] = oa[I][i];
-              }
           }
-        }
       }
 
       // S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j)

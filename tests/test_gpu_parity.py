@@ -59,7 +59,7 @@ def test_chunk_fwd_matches_oracle(D, in_dtype, gate, rule):
 @pytest.mark.parametrize("zero_init", [True, False])
 def test_chunk_fwd_zero_init_and_bf16_output(zero_init):
     gdr = _gdr()
-    w = small_workload(128, "bf16", "scalar", "delta", "f32", zero_init, seqlens=(100, 7, 64))
+    w = small_workload(128, "bf16", "scalar", "delta", "f32", zero_init, seqlens=(100, 0, 7, 64))
     x = synth.generate(w)
     d = to_device(w, x)
     o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
