@@ -36,13 +36,30 @@ struct Frag {
   bf16x8 hi, lo;
 };
 
+// Split of two fp32 values into bf16 pairs hi + lo: hi = bf16(x) (nearest
+// even, one packed conversion for the pair), lo = bf16(x - hi) of the exact
+// fp32 remainder (one more packed conversion). hi + lo carries about 17
+// significant bits of the value.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  const bf16x2 h = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const bf16x2 l = {static_cast<__bf16>(x0 - __uint_as_float(hi << 16)),
+                    static_cast<__bf16>(x1 - __uint_as_float(hi & 0xffff0000u))};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 __device__ __forceinline__ void split8(const float (&x)[8], Frag &f) {
+  u32x4 h, l;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    f.hi[j] = h;
-    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  for (int j = 0; j < 4; ++j) {
+    uint32_t hh, ll;
+    split_pair(x[2 * j], x[2 * j + 1], hh, ll);
+    h[j] = hh;
+    l[j] = ll;
   }
+  f.hi = __builtin_bit_cast(bf16x8, h);
+  f.lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // acc += a * b with the passes the operands need (lo terms first).
@@ -99,12 +116,11 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, f32x4 
 }
 
 __device__ __forceinline__ void split4(const f32x4 &x, Frag4 &f) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    f.hi[j] = h;
-    f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-  }
+  uint32_t h0, l0, h1, l1;
+  split_pair(x[0], x[1], h0, l0);
+  split_pair(x[2], x[3], h1, l1);
+  f.hi = __builtin_bit_cast(bf16x4, make_uint2(h0, h1));
+  f.lo = __builtin_bit_cast(bf16x4, make_uint2(l0, l1));
 }
 
 // acc += a * b, both split (three passes, lo terms first)

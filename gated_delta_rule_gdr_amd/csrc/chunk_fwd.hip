@@ -368,6 +368,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
   }
 
+  // The initial state loads complete here, so that the chunk loop never
+  // waits on them (and hence on everything issued after them). 0x0F70
+  // encodes vmcnt(0) alone.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
   PF pf;
   pf.g = pf.beta = 0.f;
   const LaneOffsets lo = lane_offsets<IN_F32, D>();

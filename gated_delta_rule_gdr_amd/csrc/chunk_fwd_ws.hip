@@ -1,29 +1,39 @@
 // Warp-specialised chunkwise prefill (bf16 q/k/v, no gate or a scalar gate).
 //
 // Same mathematics as chunk_fwd.hip (section 6 of "You Could Have Come Up With
-// Kimi Delta Attention"; section 4 of "From Attention to Learned Memory"), but
-// the work of a chunk is split between two groups of waves that run
-// concurrently on every SIMD:
+// Kimi Delta Attention"; section 4 of "From Attention to Learned Memory"): per
+// chunk of C = 64 tokens with incoming state S (S^T resident in registers),
 //
-//   * state waves 0-3 own 16 value columns each (state S^T[DK, 16] resident in
-//     MFMA accumulators) and do everything that depends on the state for
-//     chunk c: X = K S^T, Q S^T, the block triangular solve of the corrected
-//     values, the outputs and the state update;
-//   * prep waves 4-7 do everything that does not, one chunk ahead: write
-//     chunk c+1's keys and queries into LDS (from registers loaded one more
-//     chunk ahead), the gate prefix sums, the Gram matrices R and A, and the
-//     16x16 diagonal inverses of I + R (in registers, by the waves that
-//     formed those blocks of R).
+//   R  = strict-lower(beta_i (k_i . k_j) e^{G_i - G_j}),  T = (I + R)^{-1}
+//   A  = lower(scale (q_i . k_j) e^{G_i - G_j})
+//   Vb = T (beta (V - e^{G} (K S^T)))          (delta rule; Vb = V for the linear rule)
+//   O  = scale e^{G} (Q S^T) + A Vb
+//   S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j)
 //
-// Keys, queries, the coefficient planes and the gate factors are double
-// buffered in LDS (set c % 2 is read by the state waves while the prep waves
-// fill set (c+1) % 2), so one workgroup barrier per chunk suffices. The prep
-// waves synchronise among themselves through an LDS counter: their key and
-// query stores must land before their Gram matrices read them.
+// The work of a chunk is split between two groups of waves that run
+// concurrently; a workgroup covers BVW = 16 * NSW value columns of one
+// (sequence, value head):
+//
+//   * state waves 0 .. NSW-1 own 16 value columns each (S^T[DK, 16] in MFMA
+//     accumulators) and do everything that depends on the state: the products
+//     with the state, Vb, the outputs and the state update. Every product is a
+//     16x16x32 MFMA, and the LDS fragments of the next step are in flight
+//     while the current one multiplies;
+//   * prep waves NSW .. NSW+3 do everything that does not, one chunk ahead:
+//     write the next chunk's keys and queries into LDS (from registers loaded
+//     one more chunk ahead), the gate prefix sums, R and A, the 16x16
+//     diagonal inverses of I + R, and then the whole of T by block forward
+//     substitution, one 16-column block of T per prep wave. T and A stay in
+//     registers across the end-of-chunk barrier and go to LDS right after it.
+//
+// Keys, queries and gate factors are double buffered in LDS (set c % 2 is read
+// by the state waves while the prep waves fill set (c+1) % 2). T and A are
+// single buffered: the prep waves store them after the barrier that ends the
+// previous chunk and count their stores on an LDS counter, on which the state
+// waves wait just before their first use. One workgroup barrier per chunk.
 //
 // The state update reads K^T fragments straight from the token-major key
-// array with the transposing LDS read of gfx950 (ds_read_b64_tr_b16), so no
-// transposed copy of the keys is kept.
+// array with the transposing LDS read of gfx950 (ds_read_b64_tr_b16).
 #include "chunk_common.h"
 
 namespace gdr {
@@ -31,39 +41,103 @@ namespace {
 
 using namespace chunk;
 
-constexpr int NTH = 512;   // 8 waves
+constexpr int NPW = 4;            // prep waves
+constexpr int SPIN = 1 << 20;     // bound of every LDS-counter wait
 
-template <int D>
+template <int D, int NSW>
 struct SmemWS {
-  static constexpr int PK = D + 8;   // bf16 token-major rows (permuted k blocks)
-  static constexpr int PB = C + 8;   // bf16 C x C planes
+  // bf16 token-major key and query rows (permuted k blocks): a row pitch of
+  // 32 bytes modulo 128 keeps the 16-byte fragment reads free of bank conflicts
+  static constexpr int PK = D + 16;
+  static constexpr int PT = C + 16;   // bf16 rows of T and A (permuted 32-token blocks)
+  static constexpr int PR = C + 8;    // bf16 rows of R (8-byte fragment reads)
   struct Set {
     uint16_t kk[C][PK];
     uint16_t qq[C][PK];
-    uint16_t rth[C][PB], rtl[C][PB];   // R off-diagonal blocks, T_II on the diagonal
-    uint16_t aqh[C][PB], aql[C][PB];   // A
     float G[C], eG[C], eGl[C], beta[C];
     float eGlast, pad_[3];
   };
+  // The fixed-address arrays come first and stay within the 64 KiB that an
+  // LDS instruction's immediate offset reaches, so their many access sites
+  // share a few base registers; the sets are addressed from a per-chunk base.
+  int kcount;    // prep waves: key/query stores done (4 per chunk)
+  int scount;    // prep waves: R and the diagonal inverses done (4 per chunk)
+  int tacount;   // prep waves: T and A stored (4 per chunk)
+  int pad2_;
+  uint16_t th[C][PT], tl[C][PT];   // T of the chunk the state waves are on (split bf16)
+  uint16_t ah[C][PT], al[C][PT];   // A of that chunk
+  uint16_t rh[C][PR], rl[C][PR];   // R's off-diagonal blocks (prep waves only)
+  float rd[4][16][20];             // R's diagonal blocks, then their inverses (prep waves only)
+  uint16_t vx[NSW][C][16];         // per state wave: its value columns, token-major (swizzled halves)
   Set set[2];
-  float rd[4][16][20];   // R's diagonal blocks in fp32, each read back only by the wave that wrote it
-  uint16_t vx[4][C][16];  // per state wave: its 16 value columns of the chunk, token-major (swizzled halves)
-  int kcount;            // prep-wave store counter (monotonic)
 };
 
 // Prep-wave registers for one chunk's keys, queries and gates.
 template <int D>
 struct PrefWS {
-  static constexpr int KU = C * D / 8 / 256;   // 16-byte units per prep thread
+  static constexpr int KU = C * D / 8 / (64 * NPW);   // 16-byte units per prep thread
   typename U32Vec<4 * KU>::type k, q;
   float g, beta;
 };
+
+// Registers a prep wave carries across the end-of-chunk barrier: its block
+// column of T (the diagonal block in row layout, the blocks below it in
+// accumulator layout) and its tiles of A (row layout).
+struct HoldWS {
+  f32x4 tdiag;      // T_JJ[r][4g .. 4g+3]
+  f32x4 toff[4];    // T_IJ[4g + i][r] for I > J
+  f32x4 a[4];       // A tile (I, J) of this wave's A row block I: [16I + r][16J + 4g .. +3]
+};
+
+__device__ __forceinline__ void spin_until(const int *ctr, int target) {
+  // an LDS-typed pointer: a generic one compiles to a flat load, which would
+  // also wait for global loads in flight
+  typedef __attribute__((address_space(3))) volatile int lds_vint;
+  const lds_vint *p = (const lds_vint *)ctr;
+  for (int spin = 0; spin < SPIN; ++spin) {
+    if (*p >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// This wave's LDS stores land, then one lane counts the wave in.
+__device__ __forceinline__ void count_in(int *ctr, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) atomicAdd(ctr, 1);
+}
+
+// LDS stores of 8 and 16 bytes at addresses known to be that aligned (so
+// they compile to single ds_write_b64 / ds_write_b128 instructions).
+__device__ __forceinline__ void st8(void *p, uint2 v) {
+  *static_cast<uint2 *>(__builtin_assume_aligned(p, 8)) = v;
+}
+__device__ __forceinline__ void st16(void *p, uint4 v) {
+  *static_cast<uint4 *>(__builtin_assume_aligned(p, 16)) = v;
+}
+
+// Four values split into packed bf16 hi and lo (see split_pair).
+__device__ __forceinline__ uint2 pack_hi(const f32x4 &x, uint2 &lo) {
+  uint32_t h0, l0, h1, l1;
+  split_pair(x[0], x[1], h0, l0);
+  split_pair(x[2], x[3], h1, l1);
+  lo = make_uint2(l0, l1);
+  return make_uint2(h0, h1);
+}
+
+// 16x16x32 A fragment of a split bf16 plane pair: row `row`, k step `s`.
+__device__ __forceinline__ void ldfrag2(const uint16_t *hi, const uint16_t *lo, int pitch, int row,
+                                        int s, int g, Frag &f) {
+  const int o = row * pitch + 32 * s + 8 * g;
+  f.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(hi + o));
+  f.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(lo + o));
+}
 
 template <int GATE, bool DELTA, int D>
 __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, int64_t t0, int L,
                                           int h, int hk, int ptid) {
   constexpr int KU = PrefWS<D>::KU;
-  const int krow = ptid / (D / 8), krs = 256 / (D / 8), kc = (ptid % (D / 8)) * 16;
+  const int krow = ptid / (D / 8), krs = 64 * NPW / (D / 8), kc = (ptid % (D / 8)) * 16;
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * 2;
   const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * 2;
   const uint32_t ks = (uint32_t)(p.k_stride * 2), qs = (uint32_t)(p.q_stride * 2);
@@ -81,108 +155,187 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
   }
 }
 
-// Gram matrices of one chunk (see grams() in chunk_fwd.hip for the tile
-// assignment): tile (I, J) is computed transposed so that a lane holds row
-// ii = 16I + r, columns 16J + 4g .. +3, stored as split bf16 planes. R's
-// diagonal blocks are replaced by their unit lower triangular inverses.
-template <int W, int GATE, bool DELTA, int D, class Set>
-__device__ __forceinline__ void grams_ws(Set &S, float (*rd)[16][20], float scale, int r, int g,
-                                         int pitch_k, int pitch_b) {
+// Row blocks of R and A that prep wave W forms. The first two prep waves
+// have a SIMD without a state wave when there are two state waves, so they
+// take the longer rows: delta rule, R rows 3, 2, 1, 0 and A rows 2, 3, 0, 1
+// (7, 7, 3, 3 tiles); linear rule, A rows 3, 2, 1, 0.
+template <int W> struct RowsWS {
+  static constexpr int R = 3 - W;
+  static constexpr int A_DELTA = W ^ 2;
+  static constexpr int A_LINEAR = 3 - W;
+};
+
+// Gram tiles of one chunk (rows RowsWS<W>). Tile (I, J) is computed
+// transposed (keys of block J as the M operand), so a lane ends with row
+// ii = 16I + r, columns 16J + 4g .. +3. R's off-diagonal tiles go to the R
+// planes and its diagonal block, in fp32, to rd, where this wave then
+// replaces it by its inverse (row r of the block read back by lane (r, g)
+// from the rows its own wave wrote). A's tiles stay in registers (h.a).
+template <int W, int GATE, bool DELTA, int D, class SM>
+__device__ __forceinline__ void grams_ws(SM &sm, const typename SM::Set &S, float scale, int r, int g,
+                                         HoldWS &h) {
   constexpr int NS = D / 32;
-  constexpr bool ISQ = DELTA ? (W >= 2) : true;
-  constexpr int IA = DELTA ? (W & 1) : W;
+  constexpr int PK = SM::PK, PR = SM::PR;
+  // row block rb = 0: R (delta) or A (linear) rows IA; rb = 1: A rows IB
+  constexpr int IA = DELTA ? RowsWS<W>::R : RowsWS<W>::A_LINEAR;
   constexpr int NRB = DELTA ? 2 : 1;
-  constexpr int IB = DELTA ? 3 - IA : IA;
+  constexpr int IB = DELTA ? RowsWS<W>::A_DELTA : IA;
   constexpr int JMAX = IB > IA ? IB : IA;
-  const uint16_t *nrow = ISQ ? &S.qq[0][0] : &S.kk[0][0];
 
   Frag fn[NRB][NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    ldfrag(nrow, pitch_k, 16 * IA + r, 32 * s, g, fn[0][s]);
-    if constexpr (DELTA) ldfrag(nrow, pitch_k, 16 * IB + r, 32 * s, g, fn[NRB - 1][s]);
+    ldfrag(DELTA ? &S.kk[0][0] : &S.qq[0][0], PK, 16 * IA + r, 32 * s, g, fn[0][s]);
+    if constexpr (DELTA) ldfrag(&S.qq[0][0], PK, 16 * IB + r, 32 * s, g, fn[1][s]);
   }
   f32x4 acc[NRB][4];
+  Frag fm[2][NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, r, 32 * s, g, fm[0][s]);
 #pragma unroll
   for (int J = 0; J <= JMAX; ++J) {
+    if (J < JMAX) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Frag fm[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], pitch_k, 16 * J + r, 32 * s, g, fm[s]);
+      for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, 16 * (J + 1) + r, 32 * s, g, fm[(J + 1) & 1][s]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
+      acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int I = rb ? IB : IA;
       if (J <= I) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<false, false>(fm[s], fn[rb][s], acc[rb][J]);
+        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<false, false>(fm[J & 1][s], fn[rb][s], acc[rb][J]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int I = rb ? IB : IA;
+    const bool ISQ = !DELTA || rb == 1;
     const int ii = 16 * I + r;
     const float Gi = S.G[ii], bi = S.beta[ii];
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       const float4 Gj4 = *reinterpret_cast<const float4 *>(&S.G[16 * J + 4 * g]);
       const float Gj[4] = {Gj4.x, Gj4.y, Gj4.z, Gj4.w};
-      float val[4];
+      f32x4 val;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jj = 16 * J + 4 * g + i;
         float gam = 1.f;
         if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(Gi - Gj[i]);
-        if constexpr (ISQ) val[i] = (jj <= ii) ? scale * acc[rb][J][i] * gam : 0.f;
+        if (ISQ) val[i] = (jj <= ii) ? scale * acc[rb][J][i] * gam : 0.f;
         else val[i] = (jj < ii) ? bi * acc[rb][J][i] * gam : 0.f;
       }
-      if (!ISQ && J == I) {
-        *reinterpret_cast<float4 *>(&rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
+      if (ISQ) {
+        h.a[J] = val;
+      } else if (J == I) {
+        *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
       } else {
-        uint16_t hb[4], lb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const __bf16 hh = static_cast<__bf16>(val[i]);
-          hb[i] = __builtin_bit_cast(uint16_t, hh);
-          lb[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val[i] - static_cast<float>(hh)));
-        }
-        const uint2 hw = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
-        const uint2 lw = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
-        uint16_t *ph = ISQ ? &S.aqh[0][0] : &S.rth[0][0];
-        uint16_t *pl = ISQ ? &S.aql[0][0] : &S.rtl[0][0];
-        *reinterpret_cast<uint2 *>(ph + ii * pitch_b + 16 * J + 4 * g) = hw;
-        *reinterpret_cast<uint2 *>(pl + ii * pitch_b + 16 * J + 4 * g) = lw;
+        uint2 lo;
+        const uint2 hi = pack_hi(val, lo);
+        st8(&sm.rh[ii][16 * J + 4 * g], hi);
+        st8(&sm.rl[ii][16 * J + 4 * g], lo);
       }
     }
   }
-  if constexpr (!ISQ) {
-    // T_II = (I + R_II)^{-1} in registers; rd[I] (this wave's own rows)
-    // hands every lane its full row of R_II
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int I = rb ? IB : IA;
-      float nrow[16], t[4];
+  if constexpr (DELTA) {
+    // T_II = (I + R_II)^{-1} for this wave's R row block I: lane (r, g)
+    // reads row r of R_II (written by lanes (r, 0..3) of this wave), inverts
+    // in registers, writes back its four entries of row r of T_II
+    {
+      constexpr int I = IA;
+      float nrow16[16], t[4];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(&rd[I][r][4 * i4]);
-        nrow[4 * i4] = v4.x; nrow[4 * i4 + 1] = v4.y; nrow[4 * i4 + 2] = v4.z; nrow[4 * i4 + 3] = v4.w;
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * i4]);
+        nrow16[4 * i4] = v4.x; nrow16[4 * i4 + 1] = v4.y; nrow16[4 * i4 + 2] = v4.z; nrow16[4 * i4 + 3] = v4.w;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) t[i] = (r == 4 * g + i) ? 1.f : 0.f;
-      unit_lower_inverse16<0>(t, nrow);
-      uint16_t hb[4], lb[4];
+      unit_lower_inverse16<0>(t, nrow16);
+      *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(t[0], t[1], t[2], t[3]);
+    }
+  }
+}
+
+// Block column J of T = (I + R)^{-1} by forward substitution over 16-row
+// blocks: T_JJ from rd, then for I > J
+//     T_IJ = -T_II (sum_{K=J}^{I-1} R_IK T_KJ)
+// (16x16x16 products; R_IK and T_II in row layout as A operands, T_KJ in
+// accumulator layout, which is the B operand layout).
+template <int J, class SM>
+__device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h) {
+  constexpr int PR = SM::PR;
+  {
+    const float4 d = *reinterpret_cast<const float4 *>(&sm.rd[J][r][4 * g]);
+    h.tdiag = f32x4{d.x, d.y, d.z, d.w};
+  }
+  Frag4 tcol[4];
+  {
+    f32x4 c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = sm.rd[J][4 * g + i][r];   // column r of T_JJ
+    split4(c, tcol[J]);
+  }
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = J; K < I; ++K) {
+      Frag4 fr;
+      ldsplit4(&sm.rh[0][0], &sm.rl[0][0], PR, 16 * I + r, 16 * K, g, fr);
+      acc = mm16(fr, tcol[K], acc);
+    }
+    Frag4 ft, fy;
+    const float4 d = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * g]);
+    split4(f32x4{d.x, d.y, d.z, d.w}, ft);
+    split4(acc, fy);
+    const f32x4 t = -mm16(ft, fy, f32x4{0.f, 0.f, 0.f, 0.f});
+    h.toff[I] = t;
+    if (I < 3) split4(t, tcol[I]);
+  }
+}
+
+// Store a prep wave's T block column and A tiles (held across the barrier)
+// into the single-buffered planes: row-major, token columns of each 32-block
+// permuted (perm32) so that a state wave's A fragment is one 16-byte read.
+template <int W, bool DELTA, class SM>
+__device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g) {
+  constexpr int PT = SM::PT;
+  if constexpr (DELTA) {
+    constexpr int J = W;
+    {
+      uint2 lo;
+      const uint2 hi = pack_hi(h.tdiag, lo);
+      const int o = (16 * J + r) * PT + perm32(16 * J + 4 * g);
+      st8(&sm.th[0][0] + o, hi);
+      st8(&sm.tl[0][0] + o, lo);
+    }
+#pragma unroll
+    for (int I = J + 1; I < 4; ++I) {
+      const int c = perm32(16 * J + r);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 hh = static_cast<__bf16>(t[i]);
-        hb[i] = __builtin_bit_cast(uint16_t, hh);
-        lb[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(t[i] - static_cast<float>(hh)));
+        const float x = h.toff[I][i];
+        const __bf16 hh = static_cast<__bf16>(x);
+        const int o = (16 * I + 4 * g + i) * PT + c;
+        sm.th[0][o] = __builtin_bit_cast(uint16_t, hh);
+        sm.tl[0][o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x - static_cast<float>(hh)));
       }
-      const int idx = (16 * I + r) * pitch_b + 16 * I + 4 * g;
-      *reinterpret_cast<uint2 *>(&S.rth[0][0] + idx) =
-          make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
-      *reinterpret_cast<uint2 *>(&S.rtl[0][0] + idx) =
-          make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
+    }
+  }
+  {
+    constexpr int I = DELTA ? RowsWS<W>::A_DELTA : RowsWS<W>::A_LINEAR;   // this wave's row block of A
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      uint2 lo;
+      const uint2 hi = pack_hi(h.a[J], lo);
+      const int o = (16 * I + r) * PT + perm32(16 * J + 4 * g);
+      st8(&sm.ah[0][0] + o, hi);
+      st8(&sm.al[0][0] + o, lo);
     }
   }
 }
@@ -206,34 +359,42 @@ __device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, 
   f.hi = __builtin_bit_cast(bf16x8, ab);
 }
 
-// Prep role (waves 4-7): stages chunk c+1 while the state waves run chunk c.
-template <int GATE, bool DELTA, int D>
-__device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D> &sm, int pw, int ptid,
+// Prep role of prep wave PW (the whole loop is instantiated per wave, so
+// every register it carries across the barrier has a fixed place): stages
+// chunk c+1 while the state waves run chunk c. Per chunk: store the held T
+// and A of chunk c, stage the keys and queries of chunk c+1 (and issue the
+// loads of chunk c+2), then count both in with one wait, so the store
+// latency overlaps the staging; then R and A, the diagonal inverse, and one
+// block column of T of chunk c+1.
+template <int PW, int GATE, bool DELTA, int D, int NSW>
+__device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int ptid,
                                                 int lane, int r, int g, int h, int hk, int64_t bos,
                                                 int64_t eos, int nc) {
-  using SM = SmemWS<D>;
   using PF = PrefWS<D>;
-  constexpr int PK = SM::PK, PB = SM::PB;
   PF pf;
   pf.g = pf.beta = 0.f;
-  // work for chunk ci into set ci % 2
-  auto prep = [&](int ci) {
+  HoldWS hold;
+
+  // keys and queries of chunk ci into set ci % 2 (from pf), its gate
+  // factors (first prep wave), and the loads of chunk ci + 1 into pf
+  auto stage = [&](int ci) {
     auto &S = sm.set[ci & 1];
     const int64_t t0 = bos + (int64_t)ci * C;
     const int L = (int)min<int64_t>(C, eos - t0);
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const int krow = ptid / (D / 8), krs = 256 / (D / 8), c8 = 8 * (ptid % (D / 8));
+    const int krow = ptid / (D / 8), krs = 64 * NPW / (D / 8), c8 = 8 * (ptid % (D / 8));
 #pragma unroll
     for (int u = 0; u < PF::KU; ++u) {
       const int row = krow + u * krs;
       const bool ok = row < L;
       const uint4 kx = ok ? get4(pf.k, u) : z, qx = ok ? get4(pf.q, u) : z;
-      *reinterpret_cast<uint2 *>(&S.kk[row][perm32(c8)]) = make_uint2(kx.x, kx.y);
-      *reinterpret_cast<uint2 *>(&S.kk[row][perm32(c8 + 4)]) = make_uint2(kx.z, kx.w);
-      *reinterpret_cast<uint2 *>(&S.qq[row][perm32(c8)]) = make_uint2(qx.x, qx.y);
-      *reinterpret_cast<uint2 *>(&S.qq[row][perm32(c8 + 4)]) = make_uint2(qx.z, qx.w);
+      // (8-byte aligned: rows are 16-byte multiples and perm32 keeps groups of 4)
+      st8(&S.kk[row][perm32(c8)], make_uint2(kx.x, kx.y));
+      st8(&S.kk[row][perm32(c8 + 4)], make_uint2(kx.z, kx.w));
+      st8(&S.qq[row][perm32(c8)], make_uint2(qx.x, qx.y));
+      st8(&S.qq[row][perm32(c8 + 4)], make_uint2(qx.z, qx.w));
     }
-    if (pw == 0) {
+    if constexpr (PW == 0) {
       const bool ok = lane < L;
       float gl = 0.f;
       if constexpr (GATE == GDR_GATE_SCALAR) gl = ok ? pf.g : 0.f;
@@ -249,46 +410,54 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D> 
       const int64_t tn = t0 + C;
       prep_load<GATE, DELTA, D>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
     }
-    // all prep waves' key/query stores land before any prep wave reads them:
-    // wait for this wave's LDS stores only (the prefetch stays in flight),
-    // then count in and spin on the counter (bounded)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) atomicAdd(&sm.kcount, 1);
-    // an LDS-typed pointer: a generic one compiles to a flat load, which
-    // would also wait for the prefetch in flight
-    typedef __attribute__((address_space(3))) volatile int lds_vint;
-    const lds_vint *kcount_lds = (const lds_vint *)&sm.kcount;
-    const int target = 4 * ci + 4;
-    for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (*kcount_lds >= target) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
-    switch (pw) {
-      case 0: grams_ws<0, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
-      case 1: grams_ws<1, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
-      case 2: grams_ws<2, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
-      default: grams_ws<3, GATE, DELTA, D>(S, sm.rd, p.scale, r, g, PK, PB); break;
+  };
+
+  // R, A, the diagonal inverse and T's block column PW of chunk ci, once
+  // every prep wave's key/query stores of that chunk have landed
+  auto compute = [&](int ci) {
+    const auto &S = sm.set[ci & 1];
+    spin_until(&sm.kcount, NPW * (ci + 1));
+    grams_ws<PW, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
+    if constexpr (DELTA) {
+      // R's off-diagonal blocks and the diagonal inverses are complete once
+      // every prep wave has counted in; then this wave solves block column
+      // PW of T (the longest, column 0, goes to the first prep wave, which
+      // with two state waves has a SIMD of its own)
+      count_in(&sm.scount, lane);
+      spin_until(&sm.scount, NPW * (ci + 1));
+      solve_col<PW>(sm, r, g, hold);
     }
   };
 
   if (nc == 0) return;
   prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
-  prep(0);
+  stage(0);
+  count_in(&sm.kcount, lane);
+  compute(0);
   __syncthreads();   // chunk 0 staged
   for (int c = 0; c < nc; ++c) {
-    if (c + 1 < nc) prep(c + 1);
-    __syncthreads();   // set c % 2 is free again once the state waves are done with it
+    // T and A of chunk c: the state waves finished chunk c-1 at the barrier
+    store_hold<PW, DELTA>(sm, hold, r, g);
+    const bool more = c + 1 < nc;
+    if (more) stage(c + 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) {
+      atomicAdd(&sm.tacount, 1);
+      if (more) atomicAdd(&sm.kcount, 1);
+    }
+    if (more) compute(c + 1);
+    __syncthreads();   // set c % 2, T and A are free again once the state waves are done with them
   }
 }
 
-template <int GATE, bool DELTA, int D>
-__global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
-  using SM = SmemWS<D>;
-  constexpr int NB = D / BV;
+template <int GATE, bool DELTA, int D, int NSW>
+__global__ __launch_bounds__(64 * (NSW + NPW)) void chunk_fwd_ws_kernel(ChunkParams p) {
+  using SM = SmemWS<D, NSW>;
+  constexpr int BVW = 16 * NSW;
+  constexpr int NB = D / BVW;
   constexpr int NT = D / 16;
   constexpr int NS = D / 32;
-  constexpr int PK = SM::PK, PB = SM::PB;
+  constexpr int PK = SM::PK, PT = SM::PT;
   __shared__ SM sm;
 
   // XCD-aware decomposition (see chunk_fwd.hip)
@@ -310,18 +479,31 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
   const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
   const int nc = (int)((eos - bos + C - 1) / C);
   const int64_t HVD = (int64_t)p.HV * D;
-  if (tid == 0) sm.kcount = 0;
-  __syncthreads();   // kcount initialised
+  if (tid == 0) sm.kcount = sm.scount = sm.tacount = 0;
+  {
+    // T and A are lower triangular: the blocks above the diagonal that their
+    // fragments still read (block rows 0 and 2, next block column) stay zero
+    uint4 *tz = reinterpret_cast<uint4 *>(&sm.th[0][0]);
+    constexpr int NZ = 4 * C * PT * 2 / 16;   // th, tl, ah, al are contiguous
+    for (int i = tid; i < NZ; i += 64 * (NSW + NPW)) tz[i] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();   // counters and planes initialised
 
   // Both roles pass the same barriers: one after the prologue and one at the
   // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
-  if (w >= 4) {
-    chunk_prep_role<GATE, DELTA, D>(p, sm, w - 4, tid - 256, lane, r, g, h, hk, bos, eos, nc);
+  if (w >= NSW) {
+    const int ptid = tid - 64 * NSW;
+    switch (w - NSW) {
+      case 0: chunk_prep_role<0, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
+      case 1: chunk_prep_role<1, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
+      case 2: chunk_prep_role<2, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
+      default: chunk_prep_role<3, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
+    }
     return;
   }
 
   // state waves: this lane's value column and resident state
-  const int col = vb * BV + 16 * w + r;
+  const int col = vb * BVW + 16 * w + r;
   f32x4 st[NT];
 #pragma unroll
   for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -342,10 +524,15 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         for (int i = 0; i < 4; ++i) st[m][i] = sp[(16 * m + 4 * g + i) * D];
     }
   }
+  // The initial state loads complete here. Left in flight, they would make
+  // the compiler wait inside the chunk loop for every outstanding memory
+  // operation (the next chunk's value loads and this chunk's output stores)
+  // before the state is first used. 0x0F70 encodes vmcnt(0) alone.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   auto load_v = [&](int ci) {
     const int64_t t0 = bos + (int64_t)ci * C;
     const int last = (int)min<int64_t>(C, eos - t0) - 1;
-    const char *vbase = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BV + 16 * w) * 2;
+    const char *vbase = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
     const uint32_t off = (uint32_t)min(lane, last) * (uint32_t)(p.v_stride * 2);
     put4(vreg, 0, *reinterpret_cast<const uint4 *>(vbase + off));
     put4(vreg, 1, *reinterpret_cast<const uint4 *>(vbase + off + 16));
@@ -375,8 +562,8 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         const uint4 z = make_uint4(0, 0, 0, 0);
         const bool okv = lane < L;
         const int sw = (lane >> 3) & 1;
-        *reinterpret_cast<uint4 *>(vx + lane * 16 + 8 * sw) = okv ? get4(vreg, 0) : z;
-        *reinterpret_cast<uint4 *>(vx + lane * 16 + 8 * (sw ^ 1)) = okv ? get4(vreg, 1) : z;
+        st16(vx + lane * 16 + 8 * sw, okv ? get4(vreg, 0) : z);
+        st16(vx + lane * 16 + 8 * (sw ^ 1), okv ? get4(vreg, 1) : z);
         if (c + 1 < nc) load_v(c + 1);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -389,65 +576,102 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         }
       }
 
-      // X = K S^T (delta rule) and Q S^T
+      // X = K S^T (delta rule) and Q S^T over the NS key steps; the key and
+      // query fragments of step s+1 load while step s multiplies
       f32x4 xa[4], qa[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) xa[I] = qa[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        Frag sf;
-        chainfrag(st[2 * s], st[2 * s + 1], sf);
+      {
+        Frag fq[2][4], fk[2][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          Frag fq;
-          ldfrag(&S.qq[0][0], PK, 16 * I + r, 32 * s, g, fq);
-          qa[I] = mm<false, true>(fq, sf, qa[I]);
-          if constexpr (DELTA) {
-            Frag fk;
-            ldfrag(&S.kk[0][0], PK, 16 * I + r, 32 * s, g, fk);
-            xa[I] = mm<false, true>(fk, sf, xa[I]);
+          ldfrag(&S.qq[0][0], PK, 16 * I + r, 0, g, fq[0][I]);
+          if constexpr (DELTA) ldfrag(&S.kk[0][0], PK, 16 * I + r, 0, g, fk[0][I]);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          if (s + 1 < NS) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+              ldfrag(&S.qq[0][0], PK, 16 * I + r, 32 * (s + 1), g, fq[(s + 1) & 1][I]);
+              if constexpr (DELTA) ldfrag(&S.kk[0][0], PK, 16 * I + r, 32 * (s + 1), g, fk[(s + 1) & 1][I]);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
+          Frag sf;
+          chainfrag(st[2 * s], st[2 * s + 1], sf);
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            qa[I] = mm<false, true>(fq[s & 1][I], sf, qa[I]);
+            if constexpr (DELTA) xa[I] = mm<false, true>(fk[s & 1][I], sf, xa[I]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
+      // T and A of this chunk are in LDS once every prep wave has stored them
+      spin_until(&sm.tacount, NPW * (c + 1));
+
+      // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule)
       f32x4 vbar[4];
-      Frag4 vsp[4];
+      Frag af[4][2];
       if constexpr (DELTA) {
-        // Vb_I = T_II (beta (V - e^{G} X)_I - sum_{J<I} R_IJ Vb_J)
+        Frag tf[4][2];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.th[0][0], &sm.tl[0][0], PT, 16 * I + r, s, g, tf[I][s]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 rv[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           const float4 Bi = *reinterpret_cast<const float4 *>(&S.beta[16 * I + 4 * g]);
           const float4 Ei = *reinterpret_cast<const float4 *>(&S.eG[16 * I + 4 * g]);
           const float bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w}, ei[4] = {Ei.x, Ei.y, Ei.z, Ei.w};
-          f32x4 rv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float x = xa[I][i];
             if constexpr (GATE == GDR_GATE_SCALAR) x *= ei[i];
-            rv[i] = bi[i] * (vt[I][i] - x);
+            rv[I][i] = bi[i] * (vt[I][i] - x);
           }
+        }
+        Frag rb[2];
+        chainfrag(rv[0], rv[1], rb[0]);
+        chainfrag(rv[2], rv[3], rb[1]);
+        // A's fragments load while Vb multiplies
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int J = 0; J < I; ++J) {
-            Frag4 fr;
-            ldsplit4(&S.rth[0][0], &S.rtl[0][0], PB, 16 * I + r, 16 * J, g, fr);
-            acc = mm16(fr, vsp[J], acc);
-          }
-          Frag4 fy, ft;
-          split4(rv - acc, fy);
-          ldsplit4(&S.rth[0][0], &S.rtl[0][0], PB, 16 * I + r, 16 * I, g, ft);
-          vbar[I] = mm16(ft, fy, f32x4{0.f, 0.f, 0.f, 0.f});
-          split4(vbar[I], vsp[I]);
+          for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, true>(tf[I][s], rb[s], acc);
+          vbar[I] = acc;
         }
+        __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           vbar[I] = vt[I];
-          split4(vbar[I], vsp[I]);
+#pragma unroll
+          for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
         }
       }
 
-      // O = s e^{G} (.) Q S^T + A Vb
+      // O = s e^{G} (.) Q S^T + A Vb; the key fragments of the state update
+      // load while it multiplies
+      Frag vbf[2];
+      chainfrag(vbar[0], vbar[1], vbf[0]);
+      chainfrag(vbar[2], vbar[3], vbf[1]);
+      Frag kt[NT][2];
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ldfrag_kt(&S.kk[0][0], PK, m, s, r, g, kt[m][s]);
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 oa[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
@@ -461,11 +685,7 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
           acc[i] *= sc;
         }
 #pragma unroll
-        for (int J = 0; J <= I; ++J) {
-          Frag4 fa;
-          ldsplit4(&S.aqh[0][0], &S.aql[0][0], PB, 16 * I + r, 16 * J, g, fa);
-          acc = mm16(fa, vsp[J], acc);
-        }
+        for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, DELTA>(af[I][s], vbf[s], acc);
         oa[I] = acc;
       }
       {
@@ -479,19 +699,36 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         const __amdgpu_buffer_rsrc_t ors =
             __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)(C * orow), 0x00020000);
         const uint32_t olane = ((uint32_t)(4 * g) * HVDu + (uint32_t)col) * osz;
+        // (uniform branches: a full chunk stores unmasked; rows past a
+        // partial chunk's end are skipped)
+        if (!p.out_bf16) {
+          if (L == C) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int srow = (16 * I + i) * (int)orow;
-            const bool ok = L == C || 16 * I + 4 * g + i < L;
-            if (p.out_bf16) {
-              if (ok) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), ors, olane, srow, 0);
-            } else {
-              if (ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][i]), ors, olane, srow, 0);
-            }
+              for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][i]), ors, olane,
+                                                      (16 * I + i) * (int)orow, 0);
+          } else {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * I + 4 * g + i < L)
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][i]), ors, olane,
+                                                        (16 * I + i) * (int)orow, 0);
           }
+        } else {
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (L == C || 16 * I + 4 * g + i < L)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), ors, olane,
+                                                      (16 * I + i) * (int)orow, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
 
       // S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j)
       {
@@ -517,17 +754,12 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
         }
         constexpr bool USPLIT = DELTA || GATE == GDR_GATE_SCALAR;
 #pragma unroll
-        for (int m = 0; m < NT; ++m) {
+        for (int m = 0; m < NT; ++m)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            Frag fa;
-            ldfrag_kt(&S.kk[0][0], PK, m, s, r, g, fa);
-            st[m] = mm<false, USPLIT>(fa, uf[s], st[m]);
-          }
-        }
+          for (int s = 0; s < 2; ++s) st[m] = mm<false, USPLIT>(kt[m][s], uf[s], st[m]);
       }
     }
-    __syncthreads();   // set c % 2 is refilled by the prep waves next
+    __syncthreads();   // set c % 2, T and A are refilled by the prep waves next
   }
 
   // ---- final state back to the pool slot ----
@@ -549,18 +781,41 @@ __global__ __launch_bounds__(NTH) void chunk_fwd_ws_kernel(ChunkParams p) {
   }
 }
 
-template <int GATE, bool DELTA, int D>
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int GATE, bool DELTA, int D, int NSW>
 hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
-  const int grp = p.ratio * (D / BV);
+  const int grp = p.ratio * (D / (16 * NSW));
   const int blocks = ((p.N * p.HK + 7) / 8) * 8 * grp;
-  hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D>), dim3(blocks), dim3(NTH), 0, stream, p);
+  hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW>), dim3(blocks), dim3(64 * (NSW + NPW)), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+// 64 value columns per workgroup when that already gives every compute unit
+// a workgroup, else 32 (twice the workgroups, each with half the state work).
+template <int GATE, bool DELTA, int D>
+hipError_t ws_by_width(const ChunkParams &p, hipStream_t s) {
+  const int64_t wide = (int64_t)p.N * p.HV * (D / 64);
+  if (wide >= cu_count()) return launch_ws<GATE, DELTA, D, 4>(p, s);
+  return launch_ws<GATE, DELTA, D, 2>(p, s);
 }
 
 template <int GATE, bool DELTA>
 hipError_t ws_by_dim(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
-  if (a.DK == 128) return launch_ws<GATE, DELTA, 128>(p, s);
-  return launch_ws<GATE, DELTA, 64>(p, s);
+  if (a.DK == 128) return ws_by_width<GATE, DELTA, 128>(p, s);
+  return ws_by_width<GATE, DELTA, 64>(p, s);
 }
 
 template <int GATE>
