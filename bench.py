@@ -38,8 +38,18 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", "chunk_fwd.hip")
-STEP_SRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc", "recurrent_step.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc")
+STEP_SRC = [os.path.join(CSRC, "recurrent_step.hip"), os.path.join(CSRC, "gdr_internal.h")]
+
+
+def prefill_kernel(w: synth.Workload):
+    """(kernel name, its source files) of the prefill kernel the library runs
+    for this workload: the warp-specialised kernel for bf16 inputs without a
+    channel gate, the general one otherwise (the dispatch in chunk_fwd.hip)."""
+    common = [os.path.join(CSRC, "chunk_common.h"), os.path.join(CSRC, "gdr_internal.h")]
+    if w.in_dtype == "bf16" and w.gate != "channel":
+        return "chunk_fwd_ws_kernel", [os.path.join(CSRC, "chunk_fwd_ws.hip")] + common
+    return "chunk_fwd_kernel", [os.path.join(CSRC, "chunk_fwd.hip")] + common
 
 
 # ----------------------------------------------------------------------------
@@ -86,20 +96,24 @@ def step_bytes(w: synth.Workload, out_dtype="f32") -> int:
     return b
 
 
-def _sha(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(srcs) -> str:
+    """First 16 hex digits of the sha256 of the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in srcs:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, workload: str, src: str):
+def committed_traffic(kernel: str, workload: str, srcs):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
-    None if there is none or the kernel source changed since it was taken."""
+    None if there is none or the kernel sources changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or not h or h.group(1) != _sha(src):
+    if not m or not h or h.group(1) != source_hash(srcs):
         return None
     return float(m.group(1))
 
@@ -287,7 +301,8 @@ def main():
     nbytes = prefill_bytes(w)
     nflops = prefill_flops(w, w.chunk_size)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-    traffic = committed_traffic("chunk_fwd", w.name, KERNEL_SRC)
+    kname, ksrcs = prefill_kernel(w)
+    traffic = committed_traffic(kname, w.name, ksrcs)
     result = {
         "metric": "prefill tokens/s/layer + decode steps/s; % MFMA peak / % HBM BW",
         "value": tokens_per_s,
@@ -308,7 +323,7 @@ def main():
                    "in_dtype": w.in_dtype, "out_dtype": "f32", "state_dtype": w.state_dtype},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel", "kernel_ms_mean": kernel_ms,
+                     "kernel": kname, "kernel_ms_mean": kernel_ms,
                      "kernel_ms_median": kernel_med, "algorithmic_bytes": nbytes,
                      "algorithmic_flops": nflops,
                      "mfma_tflops": nflops / (kernel_ms * 1e-3) / 1e12,
@@ -324,7 +339,7 @@ def main():
             "algorithmic_bytes_per_step": db,
             "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
             "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": committed_traffic("recurrent_step", dw.name, STEP_SRC)}
+            "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
