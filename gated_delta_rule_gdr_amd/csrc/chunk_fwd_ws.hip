@@ -41,7 +41,58 @@ namespace {
 
 using namespace chunk;
 
-constexpr int NPW = 4;            // prep waves
+constexpr int NSTG = 4;           // prep waves that stage keys and queries (64 * NSTG threads)
+
+// Prep waves per workgroup: six beside two state waves (then every SIMD runs
+// two waves), four beside four state waves (the registers allow no more).
+template <int NSW> constexpr int prep_waves() { return NSW == 2 ? 6 : 4; }
+
+// What prep wave w (of np) does per chunk. Gram tiles come in segments:
+// row block `row` of R (kind 1) or A (kind 2), tile columns j0 .. j1; R
+// segments come first. The wave may invert one diagonal block of R (whose
+// tile it forms), solve one block column of T, and stage keys and queries
+// (stager index 0..3). With six prep waves the four on the SIMDs without a
+// state wave stage, form and invert one diagonal block each and later solve
+// one column of T (the latency-bound chain; the two long columns on
+// different SIMDs); the two that share a SIMD with a state wave form the six
+// off-diagonal tiles of R and then all of A, which is needed only after the
+// end-of-chunk barrier.
+struct SegWS {
+  int kind, row, j0, j1;
+};
+struct RoleWS {
+  SegWS seg[4];
+  int inv, tcol, stager;
+};
+constexpr SegWS NOSEG = {0, 0, 0, 0};
+constexpr RoleWS role_ws(bool delta, int np, int w) {
+  if (!delta) {
+    if (np == 4) return {{{2, 3 - w, 0, 3 - w}, NOSEG, NOSEG, NOSEG}, -1, -1, w};
+    switch (w) {
+      case 0: return {{{2, 3, 0, 3}, NOSEG, NOSEG, NOSEG}, -1, -1, 0};
+      case 1: return {{{2, 2, 0, 2}, NOSEG, NOSEG, NOSEG}, -1, -1, 1};
+      case 4: return {{{2, 1, 0, 1}, NOSEG, NOSEG, NOSEG}, -1, -1, 2};
+      case 5: return {{{2, 0, 0, 0}, NOSEG, NOSEG, NOSEG}, -1, -1, 3};
+      default: return {{NOSEG, NOSEG, NOSEG, NOSEG}, -1, -1, -1};
+    }
+  }
+  if (np == 4) return {{{1, 3 - w, 0, 3 - w}, {2, w ^ 2, 0, w ^ 2}, NOSEG, NOSEG}, 3 - w, w, w};
+  switch (w) {
+    case 0: return {{{1, 0, 0, 0}, NOSEG, NOSEG, NOSEG}, 0, 3, 0};
+    case 1: return {{{1, 1, 1, 1}, NOSEG, NOSEG, NOSEG}, 1, 2, 1};
+    case 2: return {{{1, 1, 0, 0}, {1, 2, 0, 1}, {2, 3, 0, 3}, {2, 0, 0, 0}}, -1, -1, -1};
+    case 3: return {{{1, 3, 0, 2}, {2, 2, 0, 2}, {2, 1, 0, 1}, NOSEG}, -1, -1, -1};
+    case 4: return {{{1, 2, 2, 2}, NOSEG, NOSEG, NOSEG}, 2, 1, 2};
+    default: return {{{1, 3, 3, 3}, NOSEG, NOSEG, NOSEG}, 3, 0, 3};
+  }
+}
+// Prep waves that count in on the R counter (those with an R segment).
+constexpr int r_waves(bool delta, int np) {
+  int n = 0;
+  for (int w = 0; w < np; ++w) n += delta && role_ws(delta, np, w).seg[0].kind == 1;
+  return n;
+}
+
 constexpr int SPIN = 1 << 20;     // bound of every LDS-counter wait
 
 template <int D, int NSW>
@@ -55,14 +106,15 @@ struct SmemWS {
     uint16_t kk[C][PK];
     uint16_t qq[C][PK];
     float G[C], eG[C], eGl[C], beta[C];
+    float eB[C];   // e^{G_b - G_j} with G_b the gate sum at the last token of j's 16-token block (<= 1)
     float eGlast, pad_[3];
   };
   // The fixed-address arrays come first and stay within the 64 KiB that an
   // LDS instruction's immediate offset reaches, so their many access sites
   // share a few base registers; the sets are addressed from a per-chunk base.
-  int kcount;    // prep waves: key/query stores done (4 per chunk)
-  int scount;    // prep waves: R and the diagonal inverses done (4 per chunk)
-  int tacount;   // prep waves: T and A stored (4 per chunk)
+  int kcount;    // stagers: key/query stores done (4 per chunk)
+  int scount;    // R waves: R and the diagonal inverses done (4 per chunk)
+  int tacount;   // prep waves: T and A stored (one per prep wave and chunk)
   int pad2_;
   uint16_t th[C][PT], tl[C][PT];   // T of the chunk the state waves are on (split bf16)
   uint16_t ah[C][PT], al[C][PT];   // A of that chunk
@@ -75,18 +127,18 @@ struct SmemWS {
 // Prep-wave registers for one chunk's keys, queries and gates.
 template <int D>
 struct PrefWS {
-  static constexpr int KU = C * D / 8 / (64 * NPW);   // 16-byte units per prep thread
+  static constexpr int KU = C * D / 8 / (64 * NSTG);   // 16-byte units per staging thread
   typename U32Vec<4 * KU>::type k, q;
   float g, beta;
 };
 
 // Registers a prep wave carries across the end-of-chunk barrier: its block
-// column of T (the diagonal block in row layout, the blocks below it in
-// accumulator layout) and its tiles of A (row layout).
+// column of T and its tiles of A, all in row layout (lane (r, g) holds row
+// r of a 16x16 block, columns 4g .. 4g+3).
 struct HoldWS {
-  f32x4 tdiag;      // T_JJ[r][4g .. 4g+3]
-  f32x4 toff[4];    // T_IJ[4g + i][r] for I > J
-  f32x4 a[4];       // A tile (I, J) of this wave's A row block I: [16I + r][16J + 4g .. +3]
+  f32x4 tdiag;      // T_JJ
+  f32x4 trow[4];    // T_IJ for I > J
+  f32x4 a[2][4];    // tile J of the wave's A segment `slot`
 };
 
 __device__ __forceinline__ void spin_until(const int *ctr, int target) {
@@ -137,7 +189,7 @@ template <int GATE, bool DELTA, int D>
 __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, int64_t t0, int L,
                                           int h, int hk, int ptid) {
   constexpr int KU = PrefWS<D>::KU;
-  const int krow = ptid / (D / 8), krs = 64 * NPW / (D / 8), kc = (ptid % (D / 8)) * 16;
+  const int krow = ptid / (D / 8), krs = 64 * NSTG / (D / 8), kc = (ptid % (D / 8)) * 16;
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * 2;
   const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * 2;
   const uint32_t ks = (uint32_t)(p.k_stride * 2), qs = (uint32_t)(p.q_stride * 2);
@@ -155,117 +207,114 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
   }
 }
 
-// Row blocks of R and A that prep wave W forms. The first two prep waves
-// have a SIMD without a state wave when there are two state waves, so they
-// take the longer rows: delta rule, R rows 3, 2, 1, 0 and A rows 2, 3, 0, 1
-// (7, 7, 3, 3 tiles); linear rule, A rows 3, 2, 1, 0.
-template <int W> struct RowsWS {
-  static constexpr int R = 3 - W;
-  static constexpr int A_DELTA = W ^ 2;
-  static constexpr int A_LINEAR = 3 - W;
-};
-
-// Gram tiles of one chunk (rows RowsWS<W>). Tile (I, J) is computed
-// transposed (keys of block J as the M operand), so a lane ends with row
-// ii = 16I + r, columns 16J + 4g .. +3. R's off-diagonal tiles go to the R
-// planes and its diagonal block, in fp32, to rd, where this wave then
-// replaces it by its inverse (row r of the block read back by lane (r, g)
-// from the rows its own wave wrote). A's tiles stay in registers (h.a).
-template <int W, int GATE, bool DELTA, int D, class SM>
-__device__ __forceinline__ void grams_ws(SM &sm, const typename SM::Set &S, float scale, int r, int g,
+// One segment of Gram tiles: row block I of R (KIND 1) or A (KIND 2), tile
+// columns J0 .. J1. Tile (I, J) is computed transposed (keys of block J as
+// the M operand), so a lane ends with row ii = 16I + r, columns
+// 16J + 4g .. +3. R's off-diagonal tiles go to the R planes, its diagonal
+// tile in fp32 to rd; A's tiles stay in registers (h.a[SLOT]).
+template <int KIND, int I, int J0, int J1, int SLOT, int GATE, int D, class SM>
+__device__ __forceinline__ void gram_seg(SM &sm, const typename SM::Set &S, float scale, int r, int g,
                                          HoldWS &h) {
   constexpr int NS = D / 32;
-  constexpr int PK = SM::PK, PR = SM::PR;
-  // row block rb = 0: R (delta) or A (linear) rows IA; rb = 1: A rows IB
-  constexpr int IA = DELTA ? RowsWS<W>::R : RowsWS<W>::A_LINEAR;
-  constexpr int NRB = DELTA ? 2 : 1;
-  constexpr int IB = DELTA ? RowsWS<W>::A_DELTA : IA;
-  constexpr int JMAX = IB > IA ? IB : IA;
-
-  Frag fn[NRB][NS];
+  constexpr int PK = SM::PK;
+  constexpr bool ISA = KIND == 2;
+  Frag fn[NS], fm[2][NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    ldfrag(DELTA ? &S.kk[0][0] : &S.qq[0][0], PK, 16 * IA + r, 32 * s, g, fn[0][s]);
-    if constexpr (DELTA) ldfrag(&S.qq[0][0], PK, 16 * IB + r, 32 * s, g, fn[1][s]);
+    ldfrag(ISA ? &S.qq[0][0] : &S.kk[0][0], PK, 16 * I + r, 32 * s, g, fn[s]);
+    ldfrag(&S.kk[0][0], PK, 16 * J0 + r, 32 * s, g, fm[0][s]);
   }
-  f32x4 acc[NRB][4];
-  Frag fm[2][NS];
+  f32x4 acc[J1 + 1];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, r, 32 * s, g, fm[0][s]);
+  for (int J = J0; J <= J1; ++J) {
+    if (J < J1) {
 #pragma unroll
-  for (int J = 0; J <= JMAX; ++J) {
-    if (J < JMAX) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, 16 * (J + 1) + r, 32 * s, g, fm[(J + 1) & 1][s]);
+      for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, 16 * (J + 1) + r, 32 * s, g, fm[(J + 1 - J0) & 1][s]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    acc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int I = rb ? IB : IA;
-      if (J <= I) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc[rb][J] = mm<false, false>(fm[J & 1][s], fn[rb][s], acc[rb][J]);
-      }
-    }
+    for (int s = 0; s < NS; ++s) acc[J] = mm<false, false>(fm[(J - J0) & 1][s], fn[s], acc[J]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  const int ii = 16 * I + r;
+  const float Gi = S.G[ii], coef = ISA ? scale : S.beta[ii];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int I = rb ? IB : IA;
-    const bool ISQ = !DELTA || rb == 1;
-    const int ii = 16 * I + r;
-    const float Gi = S.G[ii], bi = S.beta[ii];
-#pragma unroll
-    for (int J = 0; J <= I; ++J) {
-      const float4 Gj4 = *reinterpret_cast<const float4 *>(&S.G[16 * J + 4 * g]);
-      const float Gj[4] = {Gj4.x, Gj4.y, Gj4.z, Gj4.w};
-      f32x4 val;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jj = 16 * J + 4 * g + i;
-        float gam = 1.f;
-        if constexpr (GATE == GDR_GATE_SCALAR) gam = __expf(Gi - Gj[i]);
-        if (ISQ) val[i] = (jj <= ii) ? scale * acc[rb][J][i] * gam : 0.f;
-        else val[i] = (jj < ii) ? bi * acc[rb][J][i] * gam : 0.f;
-      }
-      if (ISQ) {
-        h.a[J] = val;
-      } else if (J == I) {
-        *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
+  for (int J = J0; J <= J1; ++J) {
+    // decay e^{G_i - G_j}: on a diagonal tile directly (and the causal
+    // mask); below it, as e^{G_i - G_b} e^{G_b - G_j} with G_b the gate sum
+    // at block J's last token, both factors <= 1 (G never increases)
+    f32x4 gam = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (GATE == GDR_GATE_SCALAR) {
+      if (J == I) {
+        const float4 Gj4 = *reinterpret_cast<const float4 *>(&S.G[16 * J + 4 * g]);
+        gam = f32x4{__expf(Gi - Gj4.x), __expf(Gi - Gj4.y), __expf(Gi - Gj4.z), __expf(Gi - Gj4.w)};
       } else {
-        uint2 lo;
-        const uint2 hi = pack_hi(val, lo);
-        st8(&sm.rh[ii][16 * J + 4 * g], hi);
-        st8(&sm.rl[ii][16 * J + 4 * g], lo);
+        const float a = __expf(Gi - S.G[16 * J + 15]);
+        const float4 b4 = *reinterpret_cast<const float4 *>(&S.eB[16 * J + 4 * g]);
+        gam = f32x4{a * b4.x, a * b4.y, a * b4.z, a * b4.w};
       }
     }
-  }
-  if constexpr (DELTA) {
-    // T_II = (I + R_II)^{-1} for this wave's R row block I: lane (r, g)
-    // reads row r of R_II (written by lanes (r, 0..3) of this wave), inverts
-    // in registers, writes back its four entries of row r of T_II
-    {
-      constexpr int I = IA;
-      float nrow16[16], t[4];
+    f32x4 val;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * i4]);
-        nrow16[4 * i4] = v4.x; nrow16[4 * i4 + 1] = v4.y; nrow16[4 * i4 + 2] = v4.z; nrow16[4 * i4 + 3] = v4.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[i] = (r == 4 * g + i) ? 1.f : 0.f;
-      unit_lower_inverse16<0>(t, nrow16);
-      *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(t[0], t[1], t[2], t[3]);
+    for (int i = 0; i < 4; ++i) {
+      const int jj = 16 * J + 4 * g + i;
+      val[i] = coef * acc[J][i] * gam[i];
+      if (J == I) val[i] = (ISA ? jj <= ii : jj < ii) ? val[i] : 0.f;
+    }
+    if constexpr (ISA) {
+      h.a[SLOT][J] = val;
+    } else if (J == I) {
+      *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
+    } else {
+      uint2 lo;
+      const uint2 hi = pack_hi(val, lo);
+      st8(&sm.rh[ii][16 * J + 4 * g], hi);
+      st8(&sm.rl[ii][16 * J + 4 * g], lo);
     }
   }
+}
+
+// T_II = (I + R_II)^{-1} in place in rd[I]: lane (r, g) reads row r of R_II
+// (written by lanes (r, 0..3) of this wave), inverts in registers, writes
+// back its four entries of row r of T_II.
+template <int I, class SM>
+__device__ __forceinline__ void invert_diag(SM &sm, int r, int g) {
+  float nrow16[16], t[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * i4]);
+    nrow16[4 * i4] = v4.x; nrow16[4 * i4 + 1] = v4.y; nrow16[4 * i4 + 2] = v4.z; nrow16[4 * i4 + 3] = v4.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = (r == 4 * g + i) ? 1.f : 0.f;
+  unit_lower_inverse16<0>(t, nrow16);
+  *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(t[0], t[1], t[2], t[3]);
+}
+
+// All segments of prep wave W's role of kind KIND, in order (A segments take
+// hold slots 0, 1 in order).
+template <int KIND, int W, int NP, int GATE, bool DELTA, int D, class SM>
+__device__ __forceinline__ void gram_role(SM &sm, const typename SM::Set &S, float scale, int r, int g,
+                                          HoldWS &h) {
+  constexpr RoleWS RL = role_ws(DELTA, NP, W);
+  constexpr SegWS S0 = RL.seg[0], S1 = RL.seg[1], S2 = RL.seg[2], S3 = RL.seg[3];
+  constexpr int SL1 = S0.kind == 2 ? 1 : 0;
+  constexpr int SL2 = SL1 + (S1.kind == 2 ? 1 : 0);
+  constexpr int SL3 = SL2 + (S2.kind == 2 ? 1 : 0);
+  if constexpr (S0.kind == KIND) gram_seg<KIND, S0.row, S0.j0, S0.j1, 0, GATE, D>(sm, S, scale, r, g, h);
+  if constexpr (S1.kind == KIND) gram_seg<KIND, S1.row, S1.j0, S1.j1, SL1, GATE, D>(sm, S, scale, r, g, h);
+  if constexpr (S2.kind == KIND) gram_seg<KIND, S2.row, S2.j0, S2.j1, SL2, GATE, D>(sm, S, scale, r, g, h);
+  if constexpr (S3.kind == KIND) gram_seg<KIND, S3.row, S3.j0, S3.j1, SL3, GATE, D>(sm, S, scale, r, g, h);
 }
 
 // Block column J of T = (I + R)^{-1} by forward substitution over 16-row
 // blocks: T_JJ from rd, then for I > J
 //     T_IJ = -T_II (sum_{K=J}^{I-1} R_IK T_KJ)
 // (16x16x16 products; R_IK and T_II in row layout as A operands, T_KJ in
-// accumulator layout, which is the B operand layout).
+// accumulator layout, which is the B operand layout). Each T_IJ is also
+// formed transposed, (T_II acc)^T = acc^T T_II^T, with the same registers
+// as swapped operands: that product comes out in row layout, for the store.
 template <int J, class SM>
 __device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h) {
   constexpr int PR = SM::PR;
@@ -293,50 +342,40 @@ __device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h)
     const float4 d = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * g]);
     split4(f32x4{d.x, d.y, d.z, d.w}, ft);
     split4(acc, fy);
-    const f32x4 t = -mm16(ft, fy, f32x4{0.f, 0.f, 0.f, 0.f});
-    h.toff[I] = t;
-    if (I < 3) split4(t, tcol[I]);
+    h.trow[I] = -mm16(fy, ft, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (I < 3) split4(-mm16(ft, fy, f32x4{0.f, 0.f, 0.f, 0.f}), tcol[I]);
   }
 }
 
 // Store a prep wave's T block column and A tiles (held across the barrier)
 // into the single-buffered planes: row-major, token columns of each 32-block
 // permuted (perm32) so that a state wave's A fragment is one 16-byte read.
-template <int W, bool DELTA, class SM>
+template <int W, int NP, bool DELTA, class SM>
 __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g) {
   constexpr int PT = SM::PT;
-  if constexpr (DELTA) {
-    constexpr int J = W;
-    {
-      uint2 lo;
-      const uint2 hi = pack_hi(h.tdiag, lo);
-      const int o = (16 * J + r) * PT + perm32(16 * J + 4 * g);
-      st8(&sm.th[0][0] + o, hi);
-      st8(&sm.tl[0][0] + o, lo);
-    }
+  constexpr RoleWS RL = role_ws(DELTA, NP, W);
+  auto put = [&](uint16_t *hp, uint16_t *lp, int row, int col, const f32x4 &x) {
+    uint2 lo;
+    const uint2 hi = pack_hi(x, lo);
+    const int o = row * PT + perm32(col);
+    st8(hp + o, hi);
+    st8(lp + o, lo);
+  };
+  if constexpr (DELTA && RL.tcol >= 0) {
+    constexpr int J = RL.tcol;
+    put(&sm.th[0][0], &sm.tl[0][0], 16 * J + r, 16 * J + 4 * g, h.tdiag);
 #pragma unroll
-    for (int I = J + 1; I < 4; ++I) {
-      const int c = perm32(16 * J + r);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = h.toff[I][i];
-        const __bf16 hh = static_cast<__bf16>(x);
-        const int o = (16 * I + 4 * g + i) * PT + c;
-        sm.th[0][o] = __builtin_bit_cast(uint16_t, hh);
-        sm.tl[0][o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x - static_cast<float>(hh)));
-      }
-    }
+    for (int I = J + 1; I < 4; ++I) put(&sm.th[0][0], &sm.tl[0][0], 16 * I + r, 16 * J + 4 * g, h.trow[I]);
   }
-  {
-    constexpr int I = DELTA ? RowsWS<W>::A_DELTA : RowsWS<W>::A_LINEAR;   // this wave's row block of A
+  int slot = 0;
 #pragma unroll
-    for (int J = 0; J <= I; ++J) {
-      uint2 lo;
-      const uint2 hi = pack_hi(h.a[J], lo);
-      const int o = (16 * I + r) * PT + perm32(16 * J + 4 * g);
-      st8(&sm.ah[0][0] + o, hi);
-      st8(&sm.al[0][0] + o, lo);
-    }
+  for (int k = 0; k < 4; ++k) {
+    const SegWS sg = RL.seg[k];
+    if (sg.kind != 2) continue;
+#pragma unroll
+    for (int J = 0; J <= 3; ++J)
+      if (J >= sg.j0 && J <= sg.j1) put(&sm.ah[0][0], &sm.al[0][0], 16 * sg.row + r, 16 * J + 4 * g, h.a[slot][J]);
+    ++slot;
   }
 }
 
@@ -359,30 +398,34 @@ __device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, 
   f.hi = __builtin_bit_cast(bf16x8, ab);
 }
 
-// Prep role of prep wave PW (the whole loop is instantiated per wave, so
-// every register it carries across the barrier has a fixed place): stages
+// Prep role of prep wave PW of NP (the whole loop is instantiated per wave,
+// so every register it carries across the barrier has a fixed place): stages
 // chunk c+1 while the state waves run chunk c. Per chunk: store the held T
-// and A of chunk c, stage the keys and queries of chunk c+1 (and issue the
-// loads of chunk c+2), then count both in with one wait, so the store
-// latency overlaps the staging; then R and A, the diagonal inverse, and one
-// block column of T of chunk c+1.
-template <int PW, int GATE, bool DELTA, int D, int NSW>
-__device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int ptid,
-                                                int lane, int r, int g, int h, int hk, int64_t bos,
+// and A of chunk c; the stagers stage the keys and queries of chunk c+1 (and
+// issue the loads of chunk c+2); one wait covers all of these stores, so
+// their latency overlaps the staging; then R and A, the diagonal inverses and
+// the block columns of T of chunk c+1 (role_ws).
+template <int PW, int NP, int GATE, bool DELTA, int D, int NSW>
+__device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int lane,
+                                                int r, int g, int h, int hk, int64_t bos,
                                                 int64_t eos, int nc) {
   using PF = PrefWS<D>;
+  constexpr RoleWS RL = role_ws(DELTA, NP, PW);
+  constexpr bool STAGER = RL.stager >= 0;
+  constexpr bool RWAVE = DELTA && RL.seg[0].kind == 1;   // forms R tiles
+  const int ptid = 64 * RL.stager + lane;
   PF pf;
   pf.g = pf.beta = 0.f;
   HoldWS hold;
 
   // keys and queries of chunk ci into set ci % 2 (from pf), its gate
-  // factors (first prep wave), and the loads of chunk ci + 1 into pf
+  // factors (first stager), and the loads of chunk ci + 1 into pf
   auto stage = [&](int ci) {
     auto &S = sm.set[ci & 1];
     const int64_t t0 = bos + (int64_t)ci * C;
     const int L = (int)min<int64_t>(C, eos - t0);
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const int krow = ptid / (D / 8), krs = 64 * NPW / (D / 8), c8 = 8 * (ptid % (D / 8));
+    const int krow = ptid / (D / 8), krs = 64 * NSTG / (D / 8), c8 = 8 * (ptid % (D / 8));
 #pragma unroll
     for (int u = 0; u < PF::KU; ++u) {
       const int row = krow + u * krs;
@@ -394,7 +437,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
       st8(&S.qq[row][perm32(c8)], make_uint2(qx.x, qx.y));
       st8(&S.qq[row][perm32(c8 + 4)], make_uint2(qx.z, qx.w));
     }
-    if constexpr (PW == 0) {
+    if constexpr (RL.stager == 0) {
       const bool ok = lane < L;
       float gl = 0.f;
       if constexpr (GATE == GDR_GATE_SCALAR) gl = ok ? pf.g : 0.f;
@@ -403,6 +446,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
       S.G[lane] = Gi;
       S.eG[lane] = __expf(Gi);
       S.eGl[lane] = __expf(Gl - Gi);
+      S.eB[lane] = __expf(row_bcast16<15>(Gi) - Gi);
       if (lane == 0) S.eGlast = __expf(Gl);
       S.beta[lane] = ok ? pf.beta : 0.f;
     }
@@ -412,38 +456,44 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
     }
   };
 
-  // R, A, the diagonal inverse and T's block column PW of chunk ci, once
-  // every prep wave's key/query stores of that chunk have landed
+  // Gram tiles, the diagonal inverse and a block column of T of chunk ci
+  // (role_ws), once the stagers' key/query stores of that chunk have landed
   auto compute = [&](int ci) {
     const auto &S = sm.set[ci & 1];
-    spin_until(&sm.kcount, NPW * (ci + 1));
-    grams_ws<PW, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
+    if constexpr (RL.seg[0].kind != 0) spin_until(&sm.kcount, NSTG * (ci + 1));
     if constexpr (DELTA) {
-      // R's off-diagonal blocks and the diagonal inverses are complete once
-      // every prep wave has counted in; then this wave solves block column
-      // PW of T (the longest, column 0, goes to the first prep wave, which
-      // with two state waves has a SIMD of its own)
-      count_in(&sm.scount, lane);
-      spin_until(&sm.scount, NPW * (ci + 1));
-      solve_col<PW>(sm, r, g, hold);
+      gram_role<1, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
+      if constexpr (RL.inv >= 0) invert_diag<RL.inv>(sm, r, g);
+      // R's off-diagonal tiles and the diagonal inverses are complete once
+      // every R wave has counted in; then the T waves solve their columns
+      if constexpr (RWAVE) count_in(&sm.scount, lane);
+    }
+    gram_role<2, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
+    if constexpr (DELTA && RL.tcol >= 0) {
+      spin_until(&sm.scount, r_waves(DELTA, NP) * (ci + 1));
+      solve_col<RL.tcol>(sm, r, g, hold);
     }
   };
 
   if (nc == 0) return;
-  prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
-  stage(0);
-  count_in(&sm.kcount, lane);
+  if constexpr (STAGER) {
+    prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
+    stage(0);
+    count_in(&sm.kcount, lane);
+  }
   compute(0);
   __syncthreads();   // chunk 0 staged
   for (int c = 0; c < nc; ++c) {
     // T and A of chunk c: the state waves finished chunk c-1 at the barrier
-    store_hold<PW, DELTA>(sm, hold, r, g);
+    store_hold<PW, NP, DELTA>(sm, hold, r, g);
     const bool more = c + 1 < nc;
-    if (more) stage(c + 1);
+    if constexpr (STAGER) {
+      if (more) stage(c + 1);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (lane == 0) {
       atomicAdd(&sm.tacount, 1);
-      if (more) atomicAdd(&sm.kcount, 1);
+      if (STAGER && more) atomicAdd(&sm.kcount, 1);
     }
     if (more) compute(c + 1);
     __syncthreads();   // set c % 2, T and A are free again once the state waves are done with them
@@ -451,7 +501,9 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
 }
 
 template <int GATE, bool DELTA, int D, int NSW>
-__global__ __launch_bounds__(64 * (NSW + NPW)) void chunk_fwd_ws_kernel(ChunkParams p) {
+__global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_kernel(ChunkParams p) {
+  constexpr int NP = prep_waves<NSW>();
+  constexpr int NTH = 64 * (NSW + NP);
   using SM = SmemWS<D, NSW>;
   constexpr int BVW = 16 * NSW;
   constexpr int NB = D / BVW;
@@ -485,20 +537,23 @@ __global__ __launch_bounds__(64 * (NSW + NPW)) void chunk_fwd_ws_kernel(ChunkPar
     // fragments still read (block rows 0 and 2, next block column) stay zero
     uint4 *tz = reinterpret_cast<uint4 *>(&sm.th[0][0]);
     constexpr int NZ = 4 * C * PT * 2 / 16;   // th, tl, ah, al are contiguous
-    for (int i = tid; i < NZ; i += 64 * (NSW + NPW)) tz[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < NZ; i += NTH) tz[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();   // counters and planes initialised
 
   // Both roles pass the same barriers: one after the prologue and one at the
   // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
   if (w >= NSW) {
-    const int ptid = tid - 64 * NSW;
+#define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW>(p, sm, lane, r, g, h, hk, bos, eos, nc)
     switch (w - NSW) {
-      case 0: chunk_prep_role<0, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
-      case 1: chunk_prep_role<1, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
-      case 2: chunk_prep_role<2, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
-      default: chunk_prep_role<3, GATE, DELTA, D, NSW>(p, sm, ptid, lane, r, g, h, hk, bos, eos, nc); break;
+      case 0: GDR_PREP(0); break;
+      case 1: GDR_PREP(1); break;
+      case 2: GDR_PREP(2); break;
+      case 3: GDR_PREP(3); break;
+      case 4: if constexpr (NP > 4) GDR_PREP(4); break;
+      default: if constexpr (NP > 5) GDR_PREP(5); break;
     }
+#undef GDR_PREP
     return;
   }
 
@@ -610,7 +665,7 @@ __global__ __launch_bounds__(64 * (NSW + NPW)) void chunk_fwd_ws_kernel(ChunkPar
       }
 
       // T and A of this chunk are in LDS once every prep wave has stored them
-      spin_until(&sm.tacount, NPW * (c + 1));
+      spin_until(&sm.tacount, NP * (c + 1));
 
       // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule)
       f32x4 vbar[4];
@@ -798,7 +853,8 @@ template <int GATE, bool DELTA, int D, int NSW>
 hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
   const int grp = p.ratio * (D / (16 * NSW));
   const int blocks = ((p.N * p.HK + 7) / 8) * 8 * grp;
-  hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW>), dim3(blocks), dim3(64 * (NSW + NPW)), 0,
+  hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW>), dim3(blocks),
+                     dim3(64 * (NSW + prep_waves<NSW>())), 0,
                      stream, p);
   return hipGetLastError();
 }
