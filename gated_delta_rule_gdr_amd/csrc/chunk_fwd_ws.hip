@@ -102,7 +102,7 @@ struct SmemWS {
   static constexpr int PK = D + 16;
   static constexpr int PT = C + 16;   // bf16 rows of T and A (permuted 32-token blocks)
   static constexpr int PR = C + 8;    // bf16 rows of R (8-byte fragment reads)
-  struct Set {
+  struct alignas(16) Set {
     uint16_t kk[C][PK];
     uint16_t qq[C][PK];
     float G[C], eG[C], eGl[C], beta[C];
@@ -140,6 +140,24 @@ struct HoldWS {
   f32x4 trow[4];    // T_IJ for I > J
   f32x4 a[2][4];    // tile J of the wave's A segment `slot`
 };
+
+// 16-byte LDS read of four floats at an address known to be that aligned.
+__device__ __forceinline__ float4 ld4(const float *p) {
+  return *static_cast<const float4 *>(__builtin_assume_aligned(p, 16));
+}
+
+// Scheduling hint for the block that follows the code it is placed after:
+// N times, one MFMA followed by up to V VALU and R LDS-read instructions, so
+// that independent vector work and loads issue while the products run.
+template <int N, int V, int R>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
 
 __device__ __forceinline__ void spin_until(const int *ctr, int target) {
   // an LDS-typed pointer: a generic one compiles to a flat load, which would
@@ -401,10 +419,10 @@ __device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, 
 // Prep role of prep wave PW of NP (the whole loop is instantiated per wave,
 // so every register it carries across the barrier has a fixed place): stages
 // chunk c+1 while the state waves run chunk c. Per chunk: store the held T
-// and A of chunk c; the stagers stage the keys and queries of chunk c+1 (and
-// issue the loads of chunk c+2); one wait covers all of these stores, so
-// their latency overlaps the staging; then R and A, the diagonal inverses and
-// the block columns of T of chunk c+1 (role_ws).
+// and A of chunk c and count them in (the state waves wait for that count
+// only); the stagers stage the keys and queries of chunk c+1 (and issue the
+// loads of chunk c+2) and count those in; then R and A, the diagonal
+// inverses and the block columns of T of chunk c+1 (role_ws).
 template <int PW, int NP, int GATE, bool DELTA, int D, int NSW>
 __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int lane,
                                                 int r, int g, int h, int hk, int64_t bos,
@@ -487,13 +505,14 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
     // T and A of chunk c: the state waves finished chunk c-1 at the barrier
     store_hold<PW, NP, DELTA>(sm, hold, r, g);
     const bool more = c + 1 < nc;
+    // T and A are published before the staging, which the state waves do
+    // not wait for
+    count_in(&sm.tacount, lane);
     if constexpr (STAGER) {
-      if (more) stage(c + 1);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) {
-      atomicAdd(&sm.tacount, 1);
-      if (STAGER && more) atomicAdd(&sm.kcount, 1);
+      if (more) {
+        stage(c + 1);
+        count_in(&sm.kcount, lane);
+      }
     }
     if (more) compute(c + 1);
     __syncthreads();   // set c % 2, T and A are free again once the state waves are done with them
@@ -605,100 +624,133 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
       const int64_t t0 = bos + (int64_t)c * C;
       const int L = (int)min<int64_t>(C, eos - t0);
 
-      // this chunk's values, then the next chunk's loads go in flight
-      // Token-major values go through this wave's LDS tile (16-byte halves
+      // This chunk's values go to this wave's LDS tile (16-byte halves
       // swapped on rows with bit 3 set, so the row writes do not collide) and
-      // come back in the accumulator layout: lane (r, g), slot i of block I
-      // holds V[16I + 4g + i][r]. Tokens past the sequence end are zero.
-      f32x4 vt[4];
+      // come back in the accumulator layout through transposing reads; the
+      // next chunk's loads go in flight.
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      uint16_t *vx = &sm.vx[w][0][0];
       {
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        uint16_t *vx = &sm.vx[w][0][0];
         const uint4 z = make_uint4(0, 0, 0, 0);
         const bool okv = lane < L;
         const int sw = (lane >> 3) & 1;
         st16(vx + lane * 16 + 8 * sw, okv ? get4(vreg, 0) : z);
         st16(vx + lane * 16 + 8 * (sw ^ 1), okv ? get4(vreg, 1) : z);
         if (c + 1 < nc) load_v(c + 1);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const int row = 16 * I + 4 * g + (r >> 2);
-          const int half = ((r & 3) >> 1) ^ ((row >> 3) & 1);
-          const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(vx + row * 16 + 8 * half + 4 * (r & 1)));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vt[I][i] = bf16_to_f32((uint16_t)t[i]);
-        }
       }
 
-      // X = K S^T (delta rule) and Q S^T over the NS key steps; the key and
-      // query fragments of step s+1 load while step s multiplies
+      // The state split once per key step (B operand of X and of Q S^T), and
+      // X = K S^T (delta rule): the split and the key fragments of step s+1
+      // are formed while step s multiplies.
+      Frag sf[NS];
       f32x4 xa[4], qa[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) xa[I] = qa[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        Frag fq[2][4], fk[2][4];
+      if constexpr (DELTA) {
+        Frag fk[2][4];
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          ldfrag(&S.qq[0][0], PK, 16 * I + r, 0, g, fq[0][I]);
-          if constexpr (DELTA) ldfrag(&S.kk[0][0], PK, 16 * I + r, 0, g, fk[0][I]);
-        }
+        for (int I = 0; I < 4; ++I) ldfrag(&S.kk[0][0], PK, 16 * I + r, 0, g, fk[0][I]);
+        chainfrag(st[0], st[1], sf[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           if (s + 1 < NS) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-              ldfrag(&S.qq[0][0], PK, 16 * I + r, 32 * (s + 1), g, fq[(s + 1) & 1][I]);
-              if constexpr (DELTA) ldfrag(&S.kk[0][0], PK, 16 * I + r, 32 * (s + 1), g, fk[(s + 1) & 1][I]);
-            }
+            for (int I = 0; I < 4; ++I) ldfrag(&S.kk[0][0], PK, 16 * I + r, 32 * (s + 1), g, fk[(s + 1) & 1][I]);
           }
-          __builtin_amdgcn_sched_barrier(0);
-          Frag sf;
-          chainfrag(st[2 * s], st[2 * s + 1], sf);
 #pragma unroll
-          for (int I = 0; I < 4; ++I) {
-            qa[I] = mm<false, true>(fq[s & 1][I], sf, qa[I]);
-            if constexpr (DELTA) xa[I] = mm<false, true>(fk[s & 1][I], sf, xa[I]);
-          }
+          for (int I = 0; I < 4; ++I) xa[I] = mm<false, true>(fk[s & 1][I], sf[s], xa[I]);
+          if (s + 1 < NS) chainfrag(st[2 * s + 2], st[2 * s + 3], sf[s + 1]);
+          interleave<8, 3, 1>();
           __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) chainfrag(st[2 * s], st[2 * s + 1], sf[s]);
       }
 
-      // T and A of this chunk are in LDS once every prep wave has stored them
-      spin_until(&sm.tacount, NP * (c + 1));
-
-      // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule)
-      f32x4 vbar[4];
-      Frag af[4][2];
-      if constexpr (DELTA) {
-        Frag tf[4][2];
+      // Q S^T. Its first query fragments and the values' transposing reads
+      // issue before the wait for T and A of this chunk (in LDS once every
+      // prep wave has stored them); T's fragments load, and the values and
+      // (delta rule) the split right-hand side beta (V - e^{G} X) of the
+      // solve are formed, under its products.
+      Frag fq[2][4];
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+      for (int I = 0; I < 4; ++I) ldfrag(&S.qq[0][0], PK, 16 * I + r, 0, g, fq[0][I]);
+      s16x4 vtr[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int row = 16 * I + 4 * g + (r >> 2);
+        const int half = ((r & 3) >> 1) ^ ((row >> 3) & 1);
+        vtr[I] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vx + row * 16 + 8 * half + 4 * (r & 1)));
+      }
+      spin_until(&sm.tacount, NP * (c + 1));
+      Frag tf[4][2];
+      float4 Bi[4], Ei[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        Ei[I] = ld4(&S.eG[16 * I + 4 * g]);
+        if constexpr (DELTA) {
+          Bi[I] = ld4(&S.beta[16 * I + 4 * g]);
 #pragma unroll
           for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.th[0][0], &sm.tl[0][0], PT, 16 * I + r, s, g, tf[I][s]);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 rv[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const float4 Bi = *reinterpret_cast<const float4 *>(&S.beta[16 * I + 4 * g]);
-          const float4 Ei = *reinterpret_cast<const float4 *>(&S.eG[16 * I + 4 * g]);
-          const float bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w}, ei[4] = {Ei.x, Ei.y, Ei.z, Ei.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = xa[I][i];
-            if constexpr (GATE == GDR_GATE_SCALAR) x *= ei[i];
-            rv[I][i] = bi[i] * (vt[I][i] - x);
-          }
         }
-        Frag rb[2];
-        chainfrag(rv[0], rv[1], rb[0]);
-        chainfrag(rv[2], rv[3], rb[1]);
-        // A's fragments load while Vb multiplies
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 vt[4], rv[4];
+      Frag rb[2];
+      // vector work under step s: the values (item 0), beta (V - e^{G} X)
+      // for blocks 0-1 and 2-3 (items 1, 2), its two splits (items 3, 4)
+      auto item = [&](int k) {
+        if (k == 0) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+          for (int I = 0; I < 4; ++I)
 #pragma unroll
-          for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
+            for (int i = 0; i < 4; ++i) vt[I][i] = bf16_to_f32((uint16_t)vtr[I][i]);
+        } else if (k <= 2) {
+#pragma unroll
+          for (int I = 2 * k - 2; I < 2 * k; ++I) {
+            const float bi[4] = {Bi[I].x, Bi[I].y, Bi[I].z, Bi[I].w};
+            const float ei[4] = {Ei[I].x, Ei[I].y, Ei[I].z, Ei[I].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = xa[I][i];
+              if constexpr (GATE == GDR_GATE_SCALAR) x *= ei[i];
+              rv[I][i] = bi[i] * (vt[I][i] - x);
+            }
+          }
+        } else {
+          chainfrag(rv[2 * k - 6], rv[2 * k - 5], rb[k - 3]);
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I) ldfrag(&S.qq[0][0], PK, 16 * I + r, 32 * (s + 1), g, fq[(s + 1) & 1][I]);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) qa[I] = mm<false, true>(fq[s & 1][I], sf[s], qa[I]);
+        // items by step: 0 | 1 | 2 3 | 4 over four steps, 0 1 2 | 3 4 over two
+#pragma unroll
+        for (int k = 0; k < (DELTA ? 5 : 1); ++k) {
+          const int at = NS == 4 ? (k < 2 ? k : k < 4 ? 2 : 3) : (k < 3 ? 0 : 1);
+          if (at == s) item(k);
+        }
+        interleave<8, 6, 1>();
         __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule); A's
+      // fragments load and the query part of O and the state decay are
+      // scaled meanwhile
+      f32x4 vbar[4];
+      Frag af[4][2];
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
+      if constexpr (DELTA) {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -706,42 +758,73 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
           for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, true>(tf[I][s], rb[s], acc);
           vbar[I] = acc;
         }
-        __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          vbar[I] = vt[I];
+        for (int I = 0; I < 4; ++I) vbar[I] = vt[I];
+      }
 #pragma unroll
-          for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
+      for (int I = 0; I < 4; ++I) {
+        const float ei[4] = {Ei[I].x, Ei[I].y, Ei[I].z, Ei[I].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sc = p.scale;
+          if constexpr (GATE == GDR_GATE_SCALAR) sc *= ei[i];
+          qa[I][i] *= sc;
         }
       }
+      if constexpr (GATE == GDR_GATE_SCALAR) {
+        const float a = S.eGlast;
+#pragma unroll
+        for (int m = 0; m < NT; ++m) st[m] *= a;
+      }
+      if constexpr (DELTA) interleave<18, 3, 1>();
+      __builtin_amdgcn_sched_barrier(0);
 
-      // O = s e^{G} (.) Q S^T + A Vb; the key fragments of the state update
-      // load while it multiplies
+      // O = s e^{G} (.) Q S^T + A Vb. Under it: the key fragments of the state
+      // update (transposing reads) and its values e^{G_last - G} Vb, split.
       Frag vbf[2];
       chainfrag(vbar[0], vbar[1], vbf[0]);
       chainfrag(vbar[2], vbar[3], vbf[1]);
+      f32x4 oa[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 acc = qa[I];
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, DELTA>(af[I][s], vbf[s], acc);
+        oa[I] = acc;
+      }
       Frag kt[NT][2];
 #pragma unroll
       for (int m = 0; m < NT; ++m)
 #pragma unroll
         for (int s = 0; s < 2; ++s) ldfrag_kt(&S.kk[0][0], PK, m, s, r, g, kt[m][s]);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 oa[4];
+      Frag uf[2];
+      {
+        f32x4 vs[4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = qa[I];
-        const float4 Ei = *reinterpret_cast<const float4 *>(&S.eG[16 * I + 4 * g]);
-        const float ei[4] = {Ei.x, Ei.y, Ei.z, Ei.w};
+        for (int I = 0; I < 4; ++I) {
+          const float4 El = ld4(&S.eGl[16 * I + 4 * g]);
+          const float el[4] = {El.x, El.y, El.z, El.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sc = p.scale;
-          if constexpr (GATE == GDR_GATE_SCALAR) sc *= ei[i];
-          acc[i] *= sc;
+          for (int i = 0; i < 4; ++i) {
+            float x = vbar[I][i];
+            if constexpr (GATE == GDR_GATE_SCALAR) x *= el[i];
+            vs[I][i] = x;
+          }
         }
+        chainfrag(vs[0], vs[1], uf[0]);
+        chainfrag(vs[2], vs[3], uf[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j), then this
+      // chunk's outputs
+      {
+        constexpr bool USPLIT = DELTA || GATE == GDR_GATE_SCALAR;
 #pragma unroll
-        for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, DELTA>(af[I][s], vbf[s], acc);
-        oa[I] = acc;
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) st[m] = mm<false, USPLIT>(kt[m][s], uf[s], st[m]);
       }
       {
         // Buffer stores against a descriptor over this chunk's 64 output
@@ -782,36 +865,6 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
                 __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), ors, olane,
                                                       (16 * I + i) * (int)orow, 0);
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-
-      // S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j)
-      {
-        f32x4 vs[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const float4 El = *reinterpret_cast<const float4 *>(&S.eGl[16 * I + 4 * g]);
-          const float el[4] = {El.x, El.y, El.z, El.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = vbar[I][i];
-            if constexpr (GATE == GDR_GATE_SCALAR) x *= el[i];
-            vs[I][i] = x;
-          }
-        }
-        Frag uf[2];
-        chainfrag(vs[0], vs[1], uf[0]);
-        chainfrag(vs[2], vs[3], uf[1]);
-        if constexpr (GATE == GDR_GATE_SCALAR) {
-          const float a = S.eGlast;
-#pragma unroll
-          for (int m = 0; m < NT; ++m) st[m] *= a;
-        }
-        constexpr bool USPLIT = DELTA || GATE == GDR_GATE_SCALAR;
-#pragma unroll
-        for (int m = 0; m < NT; ++m)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) st[m] = mm<false, USPLIT>(kt[m][s], uf[s], st[m]);
       }
     }
     __syncthreads();   // set c % 2, T and A are refilled by the prep waves next
