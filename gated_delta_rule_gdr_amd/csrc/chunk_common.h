@@ -175,29 +175,39 @@ __device__ __forceinline__ float wave_scan_dpp(float x) {
   return x;
 }
 
-// Lane J of every row of 16 lanes, broadcast to that row (DPP row_newbcast).
+// Lane J of every row of 16 lanes, broadcast to that row (DPP row_newbcast;
+// every lane is written, so no old value is needed).
 template <int J>
 __device__ __forceinline__ float row_bcast16(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, false));
 }
 
 // Right-looking substitution for the inverse of a unit lower triangular
 // 16x16 matrix I + N (N strictly lower, exact zeros on and above the
-// diagonal). Lane (r, g) holds row r of N in n[] and row r, columns
+// diagonal). Lane (r, g) holds row r of -N in nn[] and row r, columns
 // 4g .. 4g+3 of the inverse in t[] (start: row r of I). At step J row J of
-// the inverse is final; every row below subtracts N[r][J] times it.
-template <int J>
-__device__ __forceinline__ void unit_lower_inverse16(float (&t)[4], const float (&n)[16]) {
-  if constexpr (J < 16) {
-    float tj[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tj[i] = row_bcast16<J>(t[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = fmaf(-n[J], tj[i], t[i]);
-    unit_lower_inverse16<J + 1>(t, n);
-  }
+// the inverse is final; every row r adds -N[r][J] times it. One instruction
+// per step and column: v_fmac_f32 with its first source broadcast from lane J
+// of each row of 16 by DPP. Three instructions separate a write of t[i] from
+// the next step's DPP read of it (two wait states are required), and the
+// leading s_nop covers the values written before the sequence.
+#define GDR_INV_STEP(J)                                                                            \
+  "v_fmac_f32_dpp %0, %0, %[n" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n"          \
+  "v_fmac_f32_dpp %1, %1, %[n" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n"          \
+  "v_fmac_f32_dpp %2, %2, %[n" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n"          \
+  "v_fmac_f32_dpp %3, %3, %[n" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n"
+__device__ __forceinline__ void unit_lower_inverse16(float (&t)[4], const float (&nn)[16]) {
+  asm volatile("s_nop 1\n" GDR_INV_STEP(0) GDR_INV_STEP(1) GDR_INV_STEP(2) GDR_INV_STEP(3)
+               GDR_INV_STEP(4) GDR_INV_STEP(5) GDR_INV_STEP(6) GDR_INV_STEP(7) GDR_INV_STEP(8)
+               GDR_INV_STEP(9) GDR_INV_STEP(10) GDR_INV_STEP(11) GDR_INV_STEP(12) GDR_INV_STEP(13)
+               GDR_INV_STEP(14) GDR_INV_STEP(15)
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
+               : [n0] "v"(nn[0]), [n1] "v"(nn[1]), [n2] "v"(nn[2]), [n3] "v"(nn[3]),
+                 [n4] "v"(nn[4]), [n5] "v"(nn[5]), [n6] "v"(nn[6]), [n7] "v"(nn[7]),
+                 [n8] "v"(nn[8]), [n9] "v"(nn[9]), [n10] "v"(nn[10]), [n11] "v"(nn[11]),
+                 [n12] "v"(nn[12]), [n13] "v"(nn[13]), [n14] "v"(nn[14]), [n15] "v"(nn[15]));
 }
+#undef GDR_INV_STEP
 
 __device__ __forceinline__ float lane_value(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));

@@ -119,7 +119,7 @@ struct SmemWS {
   uint16_t th[C][PT], tl[C][PT];   // T of the chunk the state waves are on (split bf16)
   uint16_t ah[C][PT], al[C][PT];   // A of that chunk
   uint16_t rh[C][PR], rl[C][PR];   // R's off-diagonal blocks (prep waves only)
-  float rd[4][16][20];             // R's diagonal blocks, then their inverses (prep waves only)
+  float rd[4][16][20];             // R's diagonal blocks negated, then their inverses (prep waves only)
   uint16_t vx[NSW][C][16];         // per state wave: its value columns, token-major (swizzled halves)
   Set set[2];
 };
@@ -229,7 +229,7 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
 // columns J0 .. J1. Tile (I, J) is computed transposed (keys of block J as
 // the M operand), so a lane ends with row ii = 16I + r, columns
 // 16J + 4g .. +3. R's off-diagonal tiles go to the R planes, its diagonal
-// tile in fp32 to rd; A's tiles stay in registers (h.a[SLOT]).
+// tile negated in fp32 to rd; A's tiles stay in registers (h.a[SLOT]).
 template <int KIND, int I, int J0, int J1, int SLOT, int GATE, int D, class SM>
 __device__ __forceinline__ void gram_seg(SM &sm, const typename SM::Set &S, float scale, int r, int g,
                                          HoldWS &h) {
@@ -283,7 +283,8 @@ __device__ __forceinline__ void gram_seg(SM &sm, const typename SM::Set &S, floa
     if constexpr (ISA) {
       h.a[SLOT][J] = val;
     } else if (J == I) {
-      *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(val[0], val[1], val[2], val[3]);
+      // stored negated, the form the in-register inverse takes
+      *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(-val[0], -val[1], -val[2], -val[3]);
     } else {
       uint2 lo;
       const uint2 hi = pack_hi(val, lo);
@@ -293,12 +294,12 @@ __device__ __forceinline__ void gram_seg(SM &sm, const typename SM::Set &S, floa
   }
 }
 
-// T_II = (I + R_II)^{-1} in place in rd[I]: lane (r, g) reads row r of R_II
-// (written by lanes (r, 0..3) of this wave), inverts in registers, writes
-// back its four entries of row r of T_II.
+// T_II = (I + R_II)^{-1} in place in rd[I]: lane (r, g) reads row r of
+// -R_II (written by lanes (r, 0..3) of this wave), inverts in registers,
+// writes back its four entries of row r of T_II.
 template <int I, class SM>
 __device__ __forceinline__ void invert_diag(SM &sm, int r, int g) {
-  float nrow16[16], t[4];
+  float nrow16[16], t[4];   // row r of -R_II; row r, columns 4g .. 4g+3 of T_II
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const float4 v4 = *reinterpret_cast<const float4 *>(&sm.rd[I][r][4 * i4]);
@@ -306,7 +307,7 @@ __device__ __forceinline__ void invert_diag(SM &sm, int r, int g) {
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) t[i] = (r == 4 * g + i) ? 1.f : 0.f;
-  unit_lower_inverse16<0>(t, nrow16);
+  unit_lower_inverse16(t, nrow16);
   *reinterpret_cast<float4 *>(&sm.rd[I][r][4 * g]) = make_float4(t[0], t[1], t[2], t[3]);
 }
 
