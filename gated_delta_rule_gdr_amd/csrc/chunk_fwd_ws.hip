@@ -34,6 +34,8 @@
 //
 // The state update reads K^T fragments straight from the token-major key
 // array with the transposing LDS read of gfx950 (ds_read_b64_tr_b16).
+#include <type_traits>
+
 #include "chunk_common.h"
 
 namespace gdr {
@@ -52,11 +54,13 @@ template <int NSW> constexpr int prep_waves() { return NSW == 2 ? 6 : 4; }
 // segments come first. The wave may invert one diagonal block of R (whose
 // tile it forms), solve one block column of T, and stage keys and queries
 // (stager index 0..3). With six prep waves the four on the SIMDs without a
-// state wave stage, form and invert one diagonal block each and later solve
-// one column of T (the latency-bound chain; the two long columns on
-// different SIMDs); the two that share a SIMD with a state wave form the six
-// off-diagonal tiles of R and then all of A, which is needed only after the
-// end-of-chunk barrier.
+// state wave stage, form and invert one diagonal block each and solve one
+// column of T (the two long columns on different SIMDs); the two that share a
+// SIMD with a state wave form the six off-diagonal tiles of R, row 1 first.
+// The solves follow R row by row (a counter per row), so they overlap the
+// long rows. A, which is needed only after the end-of-chunk barrier, goes to
+// the waves with the shortest chains: the two with short T columns (before
+// their solve) and the two R waves (after R).
 struct SegWS {
   int kind, row, j0, j1;
 };
@@ -78,18 +82,29 @@ constexpr RoleWS role_ws(bool delta, int np, int w) {
   }
   if (np == 4) return {{{1, 3 - w, 0, 3 - w}, {2, w ^ 2, 0, w ^ 2}, NOSEG, NOSEG}, 3 - w, w, w};
   switch (w) {
-    case 0: return {{{1, 0, 0, 0}, NOSEG, NOSEG, NOSEG}, 0, 3, 0};
-    case 1: return {{{1, 1, 1, 1}, NOSEG, NOSEG, NOSEG}, 1, 2, 1};
-    case 2: return {{{1, 1, 0, 0}, {1, 2, 0, 1}, {2, 3, 0, 3}, {2, 0, 0, 0}}, -1, -1, -1};
-    case 3: return {{{1, 3, 0, 2}, {2, 2, 0, 2}, {2, 1, 0, 1}, NOSEG}, -1, -1, -1};
+    case 0: return {{{1, 0, 0, 0}, {2, 0, 0, 0}, {2, 1, 0, 1}, NOSEG}, 0, 3, 0};
+    case 1: return {{{1, 1, 1, 1}, {2, 2, 0, 2}, NOSEG, NOSEG}, 1, 2, 1};
+    case 2: return {{{1, 1, 0, 0}, {1, 2, 0, 1}, {2, 3, 0, 1}, NOSEG}, -1, -1, -1};
+    case 3: return {{{1, 3, 0, 2}, {2, 3, 2, 3}, NOSEG, NOSEG}, -1, -1, -1};
     case 4: return {{{1, 2, 2, 2}, NOSEG, NOSEG, NOSEG}, 2, 1, 2};
     default: return {{{1, 3, 3, 3}, NOSEG, NOSEG, NOSEG}, 3, 0, 3};
   }
 }
-// Prep waves that count in on the R counter (those with an R segment).
-constexpr int r_waves(bool delta, int np) {
+// Whether an R segment counts in on its row's counter on its own: it holds
+// tiles left of the diagonal and its wave does not invert that row's
+// diagonal block (a wave that does counts in once, after the inverse).
+constexpr bool counts_row(const RoleWS &rl, const SegWS &s) {
+  return s.kind == 1 && s.j0 < s.row && rl.inv != s.row;
+}
+// Waves that count in on row I's counter per chunk: row I of R (left of the
+// diagonal) and T_II are complete once all of them have.
+constexpr int row_producers(bool delta, int np, int I) {
   int n = 0;
-  for (int w = 0; w < np; ++w) n += delta && role_ws(delta, np, w).seg[0].kind == 1;
+  for (int w = 0; w < np; ++w) {
+    const RoleWS rl = role_ws(delta, np, w);
+    if (rl.inv == I) ++n;
+    for (int k = 0; k < 4; ++k) n += rl.seg[k].row == I && counts_row(rl, rl.seg[k]);
+  }
   return n;
 }
 
@@ -112,16 +127,17 @@ struct SmemWS {
   // The fixed-address arrays come first and stay within the 64 KiB that an
   // LDS instruction's immediate offset reaches, so their many access sites
   // share a few base registers; the sets are addressed from a per-chunk base.
-  int kcount;    // stagers: key/query stores done (4 per chunk)
-  int scount;    // R waves: R and the diagonal inverses done (4 per chunk)
-  int tacount;   // prep waves: T and A stored (one per prep wave and chunk)
-  int pad2_;
+  int kcount;   // stagers: keys and gate factors stored (4 per chunk)
+  int qcount;   // stagers: queries stored (4 per chunk)
+  int tcount;   // prep waves: T stored (one per prep wave and chunk)
+  int acount;   // prep waves: A stored (one per prep wave and chunk)
   uint16_t th[C][PT], tl[C][PT];   // T of the chunk the state waves are on (split bf16)
   uint16_t ah[C][PT], al[C][PT];   // A of that chunk
   uint16_t rh[C][PR], rl[C][PR];   // R's off-diagonal blocks (prep waves only)
   float rd[4][16][20];             // R's diagonal blocks negated, then their inverses (prep waves only)
   uint16_t vx[NSW][C][16];         // per state wave: its value columns, token-major (swizzled halves)
   Set set[2];
+  alignas(16) int rcount[4];   // row I of R and T_II done (row_producers per chunk)
 };
 
 // Prep-wave registers for one chunk's keys, queries and gates.
@@ -175,6 +191,13 @@ __device__ __forceinline__ void spin_until(const int *ctr, int target) {
 __device__ __forceinline__ void count_in(int *ctr, int lane) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (lane == 0) atomicAdd(ctr, 1);
+}
+__device__ __forceinline__ void count_in(int *ctr0, int *ctr1, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) {
+    atomicAdd(ctr0, 1);
+    atomicAdd(ctr1, 1);
+  }
 }
 
 // LDS stores of 8 and 16 bytes at addresses known to be that aligned (so
@@ -315,16 +338,28 @@ __device__ __forceinline__ void invert_diag(SM &sm, int r, int g) {
 // hold slots 0, 1 in order).
 template <int KIND, int W, int NP, int GATE, bool DELTA, int D, class SM>
 __device__ __forceinline__ void gram_role(SM &sm, const typename SM::Set &S, float scale, int r, int g,
-                                          HoldWS &h) {
+                                          int lane, HoldWS &h) {
   constexpr RoleWS RL = role_ws(DELTA, NP, W);
   constexpr SegWS S0 = RL.seg[0], S1 = RL.seg[1], S2 = RL.seg[2], S3 = RL.seg[3];
   constexpr int SL1 = S0.kind == 2 ? 1 : 0;
   constexpr int SL2 = SL1 + (S1.kind == 2 ? 1 : 0);
   constexpr int SL3 = SL2 + (S2.kind == 2 ? 1 : 0);
-  if constexpr (S0.kind == KIND) gram_seg<KIND, S0.row, S0.j0, S0.j1, 0, GATE, D>(sm, S, scale, r, g, h);
-  if constexpr (S1.kind == KIND) gram_seg<KIND, S1.row, S1.j0, S1.j1, SL1, GATE, D>(sm, S, scale, r, g, h);
-  if constexpr (S2.kind == KIND) gram_seg<KIND, S2.row, S2.j0, S2.j1, SL2, GATE, D>(sm, S, scale, r, g, h);
-  if constexpr (S3.kind == KIND) gram_seg<KIND, S3.row, S3.j0, S3.j1, SL3, GATE, D>(sm, S, scale, r, g, h);
+  if constexpr (S0.kind == KIND) {
+    gram_seg<KIND, S0.row, S0.j0, S0.j1, 0, GATE, D>(sm, S, scale, r, g, h);
+    if constexpr (counts_row(RL, S0)) count_in(&sm.rcount[S0.row], lane);
+  }
+  if constexpr (S1.kind == KIND) {
+    gram_seg<KIND, S1.row, S1.j0, S1.j1, SL1, GATE, D>(sm, S, scale, r, g, h);
+    if constexpr (counts_row(RL, S1)) count_in(&sm.rcount[S1.row], lane);
+  }
+  if constexpr (S2.kind == KIND) {
+    gram_seg<KIND, S2.row, S2.j0, S2.j1, SL2, GATE, D>(sm, S, scale, r, g, h);
+    if constexpr (counts_row(RL, S2)) count_in(&sm.rcount[S2.row], lane);
+  }
+  if constexpr (S3.kind == KIND) {
+    gram_seg<KIND, S3.row, S3.j0, S3.j1, SL3, GATE, D>(sm, S, scale, r, g, h);
+    if constexpr (counts_row(RL, S3)) count_in(&sm.rcount[S3.row], lane);
+  }
 }
 
 // Block column J of T = (I + R)^{-1} by forward substitution over 16-row
@@ -334,9 +369,32 @@ __device__ __forceinline__ void gram_role(SM &sm, const typename SM::Set &S, flo
 // accumulator layout, which is the B operand layout). Each T_IJ is also
 // formed transposed, (T_II acc)^T = acc^T T_II^T, with the same registers
 // as swapped operands: that product comes out in row layout, for the store.
-template <int J, class SM>
-__device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h) {
+// With six prep waves, block row I starts once its counter says row I of R
+// and T_II are done, so the solve overlaps the forming of the rows below
+// (the long rows are formed by other waves); with four, each wave forms a
+// whole row and all rows are waited for up front, which keeps the loads of
+// the solve free to run ahead.
+template <int J, int NP, class SM>
+__device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h, int ci) {
   constexpr int PR = SM::PR;
+  constexpr bool PER_ROW = NP > 4;
+  if constexpr (PER_ROW) {
+    spin_until(&sm.rcount[J], row_producers(true, NP, J) * (ci + 1));
+  } else {
+    // all four row counters in one 16-byte read per poll
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) volatile i32x4 lds_vi32x4;
+    const lds_vi32x4 *q = (const lds_vi32x4 *)&sm.rcount[0];
+    for (int spin = 0; spin < SPIN; ++spin) {
+      const i32x4 v = *q;
+      const int n = ci + 1;
+      if ((J > 0 || v[0] >= row_producers(true, NP, 0) * n) && (J > 1 || v[1] >= row_producers(true, NP, 1) * n) &&
+          (J > 2 || v[2] >= row_producers(true, NP, 2) * n) && v[3] >= row_producers(true, NP, 3) * n)
+        break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  }
   {
     const float4 d = *reinterpret_cast<const float4 *>(&sm.rd[J][r][4 * g]);
     h.tdiag = f32x4{d.x, d.y, d.z, d.w};
@@ -350,6 +408,8 @@ __device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h)
   }
 #pragma unroll
   for (int I = J + 1; I < 4; ++I) {
+    // row I of R and T_II of this chunk are complete
+    if constexpr (PER_ROW) spin_until(&sm.rcount[I], row_producers(true, NP, I) * (ci + 1));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int K = J; K < I; ++K) {
@@ -366,10 +426,11 @@ __device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h)
   }
 }
 
-// Store a prep wave's T block column and A tiles (held across the barrier)
-// into the single-buffered planes: row-major, token columns of each 32-block
-// permuted (perm32) so that a state wave's A fragment is one 16-byte read.
-template <int W, int NP, bool DELTA, class SM>
+// Store a prep wave's T block column (STORE_T) or its A tiles (held across
+// the barrier) into the single-buffered planes: row-major, token columns of
+// each 32-block permuted (perm32) so that a state wave's fragment is one
+// 16-byte read.
+template <int W, int NP, bool DELTA, bool STORE_T, class SM>
 __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g) {
   constexpr int PT = SM::PT;
   constexpr RoleWS RL = role_ws(DELTA, NP, W);
@@ -380,11 +441,14 @@ __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g
     st8(hp + o, hi);
     st8(lp + o, lo);
   };
-  if constexpr (DELTA && RL.tcol >= 0) {
-    constexpr int J = RL.tcol;
-    put(&sm.th[0][0], &sm.tl[0][0], 16 * J + r, 16 * J + 4 * g, h.tdiag);
+  if constexpr (STORE_T) {
+    if constexpr (DELTA && RL.tcol >= 0) {
+      constexpr int J = RL.tcol;
+      put(&sm.th[0][0], &sm.tl[0][0], 16 * J + r, 16 * J + 4 * g, h.tdiag);
 #pragma unroll
-    for (int I = J + 1; I < 4; ++I) put(&sm.th[0][0], &sm.tl[0][0], 16 * I + r, 16 * J + 4 * g, h.trow[I]);
+      for (int I = J + 1; I < 4; ++I) put(&sm.th[0][0], &sm.tl[0][0], 16 * I + r, 16 * J + 4 * g, h.trow[I]);
+    }
+    return;
   }
   int slot = 0;
 #pragma unroll
@@ -431,15 +495,20 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
   using PF = PrefWS<D>;
   constexpr RoleWS RL = role_ws(DELTA, NP, PW);
   constexpr bool STAGER = RL.stager >= 0;
-  constexpr bool RWAVE = DELTA && RL.seg[0].kind == 1;   // forms R tiles
+  // With six prep waves (delta rule) the keys are published before the
+  // queries and T before A; with four, or for the linear rule, every
+  // wave's part of them is published at once.
+  constexpr bool SPLIT = DELTA && NP > 4;
   const int ptid = 64 * RL.stager + lane;
   PF pf;
   pf.g = pf.beta = 0.f;
   HoldWS hold;
 
-  // keys and queries of chunk ci into set ci % 2 (from pf), its gate
-  // factors (first stager), and the loads of chunk ci + 1 into pf
-  auto stage = [&](int ci) {
+  // Keys (KEYS) or queries of chunk ci into set ci % 2 (from pf); with the
+  // keys its gate factors (first stager), with the queries the loads of
+  // chunk ci + 1 into pf.
+  auto stage = [&](int ci, auto keys) {
+    constexpr bool KEYS = decltype(keys)::value;
     auto &S = sm.set[ci & 1];
     const int64_t t0 = bos + (int64_t)ci * C;
     const int L = (int)min<int64_t>(C, eos - t0);
@@ -449,12 +518,18 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
     for (int u = 0; u < PF::KU; ++u) {
       const int row = krow + u * krs;
       const bool ok = row < L;
-      const uint4 kx = ok ? get4(pf.k, u) : z, qx = ok ? get4(pf.q, u) : z;
+      const uint4 x = ok ? get4(KEYS ? pf.k : pf.q, u) : z;
+      uint16_t *dst = KEYS ? &S.kk[row][0] : &S.qq[row][0];
       // (8-byte aligned: rows are 16-byte multiples and perm32 keeps groups of 4)
-      st8(&S.kk[row][perm32(c8)], make_uint2(kx.x, kx.y));
-      st8(&S.kk[row][perm32(c8 + 4)], make_uint2(kx.z, kx.w));
-      st8(&S.qq[row][perm32(c8)], make_uint2(qx.x, qx.y));
-      st8(&S.qq[row][perm32(c8 + 4)], make_uint2(qx.z, qx.w));
+      st8(dst + perm32(c8), make_uint2(x.x, x.y));
+      st8(dst + perm32(c8 + 4), make_uint2(x.z, x.w));
+    }
+    if constexpr (!KEYS) {
+      if (ci + 1 < nc) {
+        const int64_t tn = t0 + C;
+        prep_load<GATE, DELTA, D>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
+      }
+      return;
     }
     if constexpr (RL.stager == 0) {
       const bool ok = lane < L;
@@ -469,50 +544,68 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
       if (lane == 0) S.eGlast = __expf(Gl);
       S.beta[lane] = ok ? pf.beta : 0.f;
     }
-    if (ci + 1 < nc) {
-      const int64_t tn = t0 + C;
-      prep_load<GATE, DELTA, D>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
-    }
   };
+  using KeysT = std::true_type;
+  using QueriesT = std::false_type;
 
   // Gram tiles, the diagonal inverse and a block column of T of chunk ci
   // (role_ws), once the stagers' key/query stores of that chunk have landed
   auto compute = [&](int ci) {
     const auto &S = sm.set[ci & 1];
-    if constexpr (RL.seg[0].kind != 0) spin_until(&sm.kcount, NSTG * (ci + 1));
+    constexpr bool HAS_A = RL.seg[0].kind == 2 || RL.seg[1].kind == 2 || RL.seg[2].kind == 2 || RL.seg[3].kind == 2;
+    if constexpr (DELTA && RL.seg[0].kind == 1) spin_until(&sm.kcount, NSTG * (ci + 1));
     if constexpr (DELTA) {
-      gram_role<1, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
-      if constexpr (RL.inv >= 0) invert_diag<RL.inv>(sm, r, g);
-      // R's off-diagonal tiles and the diagonal inverses are complete once
-      // every R wave has counted in; then the T waves solve their columns
-      if constexpr (RWAVE) count_in(&sm.scount, lane);
+      gram_role<1, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, lane, hold);
+      if constexpr (RL.inv >= 0) {
+        invert_diag<RL.inv>(sm, r, g);
+        count_in(&sm.rcount[RL.inv], lane);
+      }
     }
-    gram_role<2, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, hold);
-    if constexpr (DELTA && RL.tcol >= 0) {
-      spin_until(&sm.scount, r_waves(DELTA, NP) * (ci + 1));
-      solve_col<RL.tcol>(sm, r, g, hold);
-    }
+    // (the queries are counted in after the keys, so this covers both)
+    if constexpr (HAS_A) spin_until(&sm.qcount, NSTG * (ci + 1));
+    gram_role<2, PW, NP, GATE, DELTA, D>(sm, S, p.scale, r, g, lane, hold);
+    if constexpr (DELTA && RL.tcol >= 0) solve_col<RL.tcol, NP>(sm, r, g, hold, ci);
   };
 
   if (nc == 0) return;
   if constexpr (STAGER) {
     prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
-    stage(0);
-    count_in(&sm.kcount, lane);
+    stage(0, KeysT{});
+    stage(0, QueriesT{});
+    count_in(&sm.kcount, &sm.qcount, lane);
   }
   compute(0);
   __syncthreads();   // chunk 0 staged
   for (int c = 0; c < nc; ++c) {
-    // T and A of chunk c: the state waves finished chunk c-1 at the barrier
-    store_hold<PW, NP, DELTA>(sm, hold, r, g);
     const bool more = c + 1 < nc;
-    // T and A are published before the staging, which the state waves do
-    // not wait for
-    count_in(&sm.tacount, lane);
-    if constexpr (STAGER) {
-      if (more) {
-        stage(c + 1);
-        count_in(&sm.kcount, lane);
+    if constexpr (SPLIT) {
+      // After the barrier (the state waves finished chunk c-1), in the order
+      // the waiting waves need them, each counted in on its own: T of chunk
+      // c (state waves), the keys and gate factors of chunk c+1 (R tiles),
+      // its queries (A tiles), A of chunk c (state waves, later in the chunk).
+      store_hold<PW, NP, DELTA, true>(sm, hold, r, g);
+      count_in(&sm.tcount, lane);
+      if constexpr (STAGER) {
+        if (more) {
+          stage(c + 1, KeysT{});
+          count_in(&sm.kcount, lane);
+          stage(c + 1, QueriesT{});
+          count_in(&sm.qcount, lane);
+        }
+      }
+      store_hold<PW, NP, DELTA, false>(sm, hold, r, g);
+      count_in(&sm.acount, lane);
+    } else {
+      // T and A of chunk c, then chunk c+1 staged, two counts each
+      store_hold<PW, NP, DELTA, true>(sm, hold, r, g);
+      store_hold<PW, NP, DELTA, false>(sm, hold, r, g);
+      count_in(&sm.tcount, &sm.acount, lane);
+      if constexpr (STAGER) {
+        if (more) {
+          stage(c + 1, KeysT{});
+          stage(c + 1, QueriesT{});
+          count_in(&sm.kcount, &sm.qcount, lane);
+        }
       }
     }
     if (more) compute(c + 1);
@@ -551,7 +644,8 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
   const int nc = (int)((eos - bos + C - 1) / C);
   const int64_t HVD = (int64_t)p.HV * D;
-  if (tid == 0) sm.kcount = sm.scount = sm.tacount = 0;
+  if (tid == 0)
+    sm.kcount = sm.qcount = sm.tcount = sm.acount = sm.rcount[0] = sm.rcount[1] = sm.rcount[2] = sm.rcount[3] = 0;
   {
     // T and A are lower triangular: the blocks above the diagonal that their
     // fragments still read (block rows 0 and 2, next block column) stay zero
@@ -685,7 +779,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         const int half = ((r & 3) >> 1) ^ ((row >> 3) & 1);
         vtr[I] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vx + row * 16 + 8 * half + 4 * (r & 1)));
       }
-      spin_until(&sm.tacount, NP * (c + 1));
+      spin_until(&sm.tcount, NP * (c + 1));
       Frag tf[4][2];
       float4 Bi[4], Ei[4];
 #pragma unroll
@@ -747,6 +841,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
       // scaled meanwhile
       f32x4 vbar[4];
       Frag af[4][2];
+      spin_until(&sm.acount, NP * (c + 1));
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
