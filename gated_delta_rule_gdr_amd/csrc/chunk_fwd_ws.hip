@@ -836,11 +836,12 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule); A's
-      // fragments load and the query part of O and the state decay are
+      // Vb = T (beta (V - e^{G} X)) (delta rule) or V (linear rule): blocks
+      // 0-1 first, whose split for O is formed while blocks 2-3 multiply;
+      // A's fragments load and the query part of O and the state decay are
       // scaled meanwhile
       f32x4 vbar[4];
-      Frag af[4][2];
+      Frag af[4][2], vbf[2];
       spin_until(&sm.acount, NP * (c + 1));
 #pragma unroll
       for (int I = 0; I < 4; ++I)
@@ -858,6 +859,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
 #pragma unroll
         for (int I = 0; I < 4; ++I) vbar[I] = vt[I];
       }
+      chainfrag(vbar[0], vbar[1], vbf[0]);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const float ei[4] = {Ei[I].x, Ei[I].y, Ei[I].z, Ei[I].w};
@@ -873,27 +875,22 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
 #pragma unroll
         for (int m = 0; m < NT; ++m) st[m] *= a;
       }
-      if constexpr (DELTA) interleave<18, 3, 1>();
+      if constexpr (DELTA) interleave<18, 5, 0>();
       __builtin_amdgcn_sched_barrier(0);
 
-      // O = s e^{G} (.) Q S^T + A Vb. Under it: the key fragments of the state
-      // update (transposing reads) and its values e^{G_last - G} Vb, split.
-      Frag vbf[2];
-      chainfrag(vbar[0], vbar[1], vbf[0]);
-      chainfrag(vbar[2], vbar[3], vbf[1]);
-      f32x4 oa[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = qa[I];
-#pragma unroll
-        for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, DELTA>(af[I][s], vbf[s], acc);
-        oa[I] = acc;
-      }
+      // O = s e^{G} (.) Q S^T + A Vb: the products with Vb blocks 0-1 first,
+      // while the split of blocks 2-3, the values of the state update
+      // e^{G_last - G} Vb (split) and its key fragments (transposing reads)
+      // are formed and loaded.
       Frag kt[NT][2];
 #pragma unroll
       for (int m = 0; m < NT; ++m)
 #pragma unroll
         for (int s = 0; s < 2; ++s) ldfrag_kt(&S.kk[0][0], PK, m, s, r, g, kt[m][s]);
+      f32x4 oa[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) oa[I] = mm<true, DELTA>(af[I][0], vbf[0], qa[I]);
+      chainfrag(vbar[2], vbar[3], vbf[1]);
       Frag uf[2];
       {
         f32x4 vs[4];
@@ -911,6 +908,9 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         chainfrag(vs[0], vs[1], uf[0]);
         chainfrag(vs[2], vs[3], uf[1]);
       }
+#pragma unroll
+      for (int I = 2; I < 4; ++I) oa[I] = mm<true, DELTA>(af[I][1], vbf[1], oa[I]);
+      interleave<DELTA ? 18 : 12, 6, 0>();
       __builtin_amdgcn_sched_barrier(0);
 
       // S^T <- e^{G_last} S^T + K^T (e^{G_last - G_j} Vb_j), then this
