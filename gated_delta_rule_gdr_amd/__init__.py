@@ -23,7 +23,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "recurrent_step", "lib", "lib_path", "GdrError",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -190,15 +190,41 @@ def _stream(t):
 
 def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk_size=64,
               rule="delta", gate=None, out_dtype=None, zero_init=False, o=None,
-              debug_checks=False):
-    """Chunkwise prefill; returns o [T, HV, DV]; updates pool slots in place."""
+              debug_checks=False, workspace=None):
+    """Chunkwise prefill; returns o [T, HV, DV]; updates pool slots in place.
+
+    ``workspace`` is an optional uint8 device tensor for the calls that need
+    one (gdr_chunk_fwd_workspace_bytes > 0: the channel gate with bf16 inputs);
+    by default one of the preferred size is allocated from torch's allocator.
+    """
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
                     zero_init, debug_checks, chunk_size, out_dtype)
     L = load()
-    _check(L.gdr_chunk_fwd(ctypes.byref(a), None, 0, _stream(q)))
+    if workspace is None:
+        nbytes = L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+            raise TypeError(f"workspace must be a contiguous uint8 tensor on {q.device}")
+        wptr, wbytes = workspace.data_ptr(), workspace.numel()
+    else:
+        wptr, wbytes = None, 0
+    _check(L.gdr_chunk_fwd(ctypes.byref(a), wptr, wbytes, _stream(q)))
     return o
+
+
+def chunk_fwd_workspace_bytes(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None,
+                              chunk_size=64, rule="delta", gate=None, out_dtype=None,
+                              zero_init=False):
+    """Preferred workspace size in bytes of the matching chunk_fwd call (0: none needed)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, _ = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, None, scale, rule, gate,
+                    zero_init, False, chunk_size, out_dtype)
+    return int(load().gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)))
 
 
 def recurrent_step(q, k, v, g, beta, pool, slot_idx, *, scale=None, rule="delta", gate=None,

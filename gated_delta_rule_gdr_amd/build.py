@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr_api.hip", "recurrent_step.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip"]
+SOURCES = ["gdr_api.hip", "recurrent_step.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip", "chunk_fwd_kda.hip"]
 ARCH = "gfx950"
 
 

@@ -240,6 +240,76 @@ __device__ __forceinline__ uint4 get4(const Vec &v, int u) {
 }
 
 
+// Scheduling hint for the block that follows the code it is placed after:
+// N times, one MFMA followed by up to V VALU and R LDS-read instructions, so
+// that independent vector work and loads issue while the products run.
+template <int N, int V, int R>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
+
+// Bound of every wait on an LDS counter (a wait that runs out goes on with
+// whatever the counter's producers have stored by then, so it cannot hang).
+constexpr int SPIN = 1 << 20;
+
+__device__ __forceinline__ void spin_until(const int *ctr, int target) {
+  // an LDS-typed pointer: a generic one compiles to a flat load, which would
+  // also wait for global loads in flight
+  typedef __attribute__((address_space(3))) volatile int lds_vint;
+  const lds_vint *p = (const lds_vint *)ctr;
+  for (int spin = 0; spin < SPIN; ++spin) {
+    if (*p >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// This wave's LDS stores land, then one lane counts the wave in.
+__device__ __forceinline__ void count_in(int *ctr, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) atomicAdd(ctr, 1);
+}
+__device__ __forceinline__ void count_in(int *ctr0, int *ctr1, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) {
+    atomicAdd(ctr0, 1);
+    atomicAdd(ctr1, 1);
+  }
+}
+
+// Fragment of a transposed operand read from a token-major bf16 array with
+// two transposing reads (ds_read_b64_tr_b16): M rows are 16 columns of the
+// array, K the tokens of k step s in slot order K(g). Within each 16-lane
+// group the read hands lane i, slot j element (i mod 4) of the 4 elements
+// addressed by lane 4j + i/4; lane a therefore addresses token
+// 32s + 4g + a/4 (+16 for the second half) at the four consecutive array
+// columns that start at physical column `col4` (the group of logical columns
+// 16m + 4 (a mod 4) .. +3 of the tile).
+__device__ __forceinline__ void ldfrag_tr(const uint16_t *kk, int pitch, int col4, int s, int r, int g,
+                                          Frag &f) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const uint16_t *p0 = kk + (32 * s + 4 * g + (r >> 2)) * pitch + col4;
+  const uint16_t *p1 = p0 + 16 * pitch;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  f.hi = __builtin_bit_cast(bf16x8, ab);
+}
+
+// K^T fragment for the state update: key rows 16m .. 16m+15 (M), tokens of
+// k step s (K), from the token-major key array whose columns are permuted
+// (perm32).
+__device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, int s, int r, int g,
+                                          Frag &f) {
+  ldfrag_tr(kk, pitch, perm32(16 * m + 4 * (r & 3)), s, r, g, f);
+}
+
 }  // namespace chunk
 
 hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream);

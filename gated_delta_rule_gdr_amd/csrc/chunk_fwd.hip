@@ -761,15 +761,19 @@ hipError_t by_gate(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
-  // bf16 inputs without a channel gate take the warp-specialised kernel;
-  // GDR_PREFILL_KERNEL=generic selects this file's kernel for every case
-  // (used to compare the two).
-  static const bool force_generic = [] {
+bool prefill_force_generic() {
+  static const bool force = [] {
     const char *e = getenv("GDR_PREFILL_KERNEL");
     return e && strcmp(e, "generic") == 0;
   }();
-  if (!force_generic && a.in_dtype == GDR_BF16 && a.gate != GDR_GATE_CHANNEL)
+  return force;
+}
+
+hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
+  // bf16 inputs without a channel gate take the warp-specialised kernel;
+  // GDR_PREFILL_KERNEL=generic selects this file's kernel for every case
+  // (used to compare them).
+  if (!prefill_force_generic() && a.in_dtype == GDR_BF16 && a.gate != GDR_GATE_CHANNEL)
     return launch_chunk_fwd_ws(a, stream);
   ChunkParams p;
   p.q = a.q; p.k = a.k; p.v = a.v;

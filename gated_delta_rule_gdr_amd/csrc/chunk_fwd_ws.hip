@@ -108,7 +108,6 @@ constexpr int row_producers(bool delta, int np, int I) {
   return n;
 }
 
-constexpr int SPIN = 1 << 20;     // bound of every LDS-counter wait
 
 template <int D, int NSW>
 struct SmemWS {
@@ -160,44 +159,6 @@ struct HoldWS {
 // 16-byte LDS read of four floats at an address known to be that aligned.
 __device__ __forceinline__ float4 ld4(const float *p) {
   return *static_cast<const float4 *>(__builtin_assume_aligned(p, 16));
-}
-
-// Scheduling hint for the block that follows the code it is placed after:
-// N times, one MFMA followed by up to V VALU and R LDS-read instructions, so
-// that independent vector work and loads issue while the products run.
-template <int N, int V, int R>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-  }
-}
-
-__device__ __forceinline__ void spin_until(const int *ctr, int target) {
-  // an LDS-typed pointer: a generic one compiles to a flat load, which would
-  // also wait for global loads in flight
-  typedef __attribute__((address_space(3))) volatile int lds_vint;
-  const lds_vint *p = (const lds_vint *)ctr;
-  for (int spin = 0; spin < SPIN; ++spin) {
-    if (*p >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-
-// This wave's LDS stores land, then one lane counts the wave in.
-__device__ __forceinline__ void count_in(int *ctr, int lane) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane == 0) atomicAdd(ctr, 1);
-}
-__device__ __forceinline__ void count_in(int *ctr0, int *ctr1, int lane) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane == 0) {
-    atomicAdd(ctr0, 1);
-    atomicAdd(ctr1, 1);
-  }
 }
 
 // LDS stores of 8 and 16 bytes at addresses known to be that aligned (so
@@ -462,24 +423,6 @@ __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g
   }
 }
 
-// K^T fragment for the state update: key rows 16m .. 16m+15 (M), tokens of
-// k step s in slot order K(g) (K), read from the token-major key array with
-// two transposing reads. Within each 16-lane group the read hands lane i,
-// slot j element (i mod 4) of the 4 elements addressed by lane 4j + i/4;
-// lane a therefore addresses token 32s + 4g + a/4 (+16 for the second half),
-// key columns 16m + 4 (a mod 4) .. +3.
-__device__ __forceinline__ void ldfrag_kt(const uint16_t *kk, int pitch, int m, int s, int r, int g,
-                                          Frag &f) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const int col = perm32(16 * m + 4 * (r & 3));
-  const uint16_t *p0 = kk + (32 * s + 4 * g + (r >> 2)) * pitch + col;
-  const uint16_t *p1 = p0 + 16 * pitch;
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  f.hi = __builtin_bit_cast(bf16x8, ab);
-}
 
 // Prep role of prep wave PW of NP (the whole loop is instantiated per wave,
 // so every register it carries across the barrier has a fixed place): stages
@@ -985,18 +928,6 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   }
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
 
 template <int GATE, bool DELTA, int D, int NSW>
 hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
@@ -1030,6 +961,19 @@ hipError_t ws_by_rule(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {
   ChunkParams p;

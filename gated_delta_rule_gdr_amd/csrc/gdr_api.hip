@@ -92,6 +92,14 @@ gdr_status validate(const gdr_args *a, bool prefill) {
     };
     for (const Range &r : ins)
       if (overlap(ro, r)) return fail(GDR_E_INVALID, "o overlaps an input or the state pool");
+    // the kernels move q, k, v, g and o rows in 16-byte units
+    const void *ptrs[] = {a->q, a->k, a->v, a->g, a->o};
+    for (const void *ptr : ptrs)
+      if (reinterpret_cast<uintptr_t>(ptr) % 16)
+        return fail(GDR_E_INVALID, "q, k, v, g and o must be 16-byte aligned");
+    if ((a->q_stride_t * (int64_t)ie) % 16 || (a->k_stride_t * (int64_t)ie) % 16 ||
+        (a->v_stride_t * (int64_t)ie) % 16)
+      return fail(GDR_E_INVALID, "token strides of q, k, v must be multiples of 16 bytes");
   }
   return GDR_OK;
 }
@@ -152,23 +160,40 @@ using namespace gdr;
 
 GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
 
+namespace {
+// The channel-gate prefill for bf16 inputs and the delta rule runs as two
+// kernels that pass per-chunk records through the workspace; every other
+// prefill is one fused kernel and needs none.
+bool uses_workspace(const gdr_args *a) {
+  return a->N > 0 && a->T_total > 0 && chunk_fwd_kda_applies(*a) && !prefill_force_generic();
+}
+}  // namespace
+
 GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a) {
-  (void)a;
-  return 0;  // the fused chunk schedule keeps every intermediate on chip
+  if (validate(a, true) != GDR_OK || !uses_workspace(a)) return 0;
+  return chunk_fwd_kda_workspace(*a);
 }
 
 GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
                                     hipStream_t stream) {
-  (void)workspace;
   gdr_status s = validate(a, true);
   if (s != GDR_OK) return s;
-  if (ws_bytes < gdr_chunk_fwd_workspace_bytes(a)) return fail(GDR_E_WORKSPACE, "workspace too small");
+  const bool ws_path = uses_workspace(a);
+  if (ws_path) {
+    const size_t need = chunk_fwd_kda_min_workspace(*a);
+    if (!workspace || ws_bytes < need)
+      return fail(GDR_E_WORKSPACE, "workspace of %zu bytes at %p: this call needs at least %zu "
+                  "(gdr_chunk_fwd_workspace_bytes gives the preferred size)", ws_bytes, workspace, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GDR_E_INVALID, "workspace is not 256-byte aligned");
+  }
   if (a->N == 0) return GDR_OK;
   if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
     s = run_debug_checks(a, true, stream);
     if (s != GDR_OK) return s;
   }
-  hipError_t e = launch_chunk_fwd(*a, stream);
+  hipError_t e = ws_path ? launch_chunk_fwd_kda(*a, workspace, ws_bytes, stream)
+                         : launch_chunk_fwd(*a, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }

@@ -37,6 +37,18 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
 
 hipError_t launch_recurrent_step(const gdr_args &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
+// True when GDR_PREFILL_KERNEL=generic asks for the general prefill kernel in
+// every case (used to compare kernels).
+bool prefill_force_generic();
+// Compute units of the current device (cached per device).
+int cu_count();
+
+// Channel-gate prefill (bf16 inputs, delta rule): two kernels per slice of
+// chunks, sharing per-chunk records through the caller's workspace.
+bool chunk_fwd_kda_applies(const gdr_args &a);
+size_t chunk_fwd_kda_workspace(const gdr_args &a);       // preferred bytes
+size_t chunk_fwd_kda_min_workspace(const gdr_args &a);   // fewest bytes that work
+hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hipStream_t stream);
 // Writes 0 to *flag_dev when cu_seqlens (prefill) and slot_idx are valid,
 // else a nonzero code; flag_dev is a device int.
 hipError_t launch_index_checks(const gdr_args &a, bool prefill, int *flag_dev,

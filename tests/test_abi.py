@@ -95,6 +95,9 @@ CASES = [
     ("negative N", dict(N=-1), 1),
     ("o aliases q", dict(o=0x1000 + 64), 1),
     ("o aliases pool", dict(o=0x4000000 + 4096), 1),
+    ("misaligned q", dict(q=0x1008), 1),
+    ("misaligned g", dict(g=0x2004), 1),
+    ("stride not 16 bytes", dict(k_stride_t=2 * 128 + 4), 1),
 ]
 
 
@@ -126,6 +129,27 @@ def test_empty_batch_is_a_no_op():
     a.q = a.k = a.v = a.o = a.state_pool = a.slot_idx = a.cu_seqlens = None
     assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 0
     assert L.gdr_recurrent_step(ctypes.byref(a), None) == 0
+    assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_channel_gate_workspace_on_host():
+    """bf16 inputs with the channel gate and the delta rule pass per-chunk
+    records through the workspace: the preferred size is the fp32 carry of
+    every (sequence, head) plus whole rows of (chunk, head) records, and a
+    missing, short or misaligned workspace is rejected before any launch."""
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0   # scalar gate: fused
+    a.gate = 2
+    carry = a.N * a.HV * 128 * 128 * 4
+    record = 3 * 16 * 2048 + 2 * 6 * 2048 + 4 * 128   # W, Q, K_r^T; T', A; gamma
+    flat = (a.T_total + 63) // 64 + a.N
+    want = carry + flat * a.HV * record
+    assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == want
+    assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 3
+    assert L.gdr_chunk_fwd(ctypes.byref(a), 0x10000000, carry + a.HV * record - 1, None) == 3
+    assert L.gdr_chunk_fwd(ctypes.byref(a), 0x10000010, want, None) == 1
+    a.rule = 1   # the linear rule stays fused
     assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
 
 

@@ -136,6 +136,59 @@ def test_chunk_equals_repeated_steps(gate):
         check_state(host(pool_chunk, "f32")[s], host(d["pool"], "f32")[s], "bf16", "f32")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rows", [1, 3])
+def test_channel_gate_slices(D, rows):
+    """The channel-gate prefill (bf16 inputs) passes per-chunk records through
+    the workspace in slices of `rows` flat chunks; the state crosses slice
+    boundaries through the workspace's fp32 carry. The result of a workspace
+    that holds 1 or 3 rows of records equals the oracle's, and equals the
+    result with the preferred workspace bit for bit."""
+    gdr = _gdr()
+    w = small_workload(D, "bf16", "channel", "delta", "f32", zero_init=False,
+                       seqlens=(130, 0, 64, 1, 200), seed=23)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    pool_pref = d["pool"].clone()
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    # record of one (chunk, head): W, Q^ and K_r^T fragments, T' and A^, gamma
+    row = w.HV * ((3 * 4 * (D // 32) + 2 * 6) * 2048 + 4 * D)
+    carry = w.N * w.HV * D * D * 4
+    ws = torch.empty(carry + rows * row, dtype=torch.uint8, device="cuda")
+    print(f"channel-gate slices D={D} rows={rows}", flush=True)
+    o = gdr.chunk_fwd(*args, d["pool"], d["slot_idx"], d["cu_seqlens"], workspace=ws)
+    o_pref = gdr.chunk_fwd(*args, pool_pref, d["slot_idx"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_pref)
+    assert torch.equal(d["pool"], pool_pref)
+    o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], D ** -0.5)
+    check_out(host(o, "bf16"), o_ref, "bf16")
+    for sl in x["slot_idx"]:
+        check_state(host(d["pool"], "f32")[sl], pool_ref[sl], "bf16", "f32")
+
+
+@pytest.mark.parametrize("N", [10, 17, 40])
+def test_channel_gate_workgroup_rounds(N):
+    """The channel-gate state kernel gives every workgroup 16 value columns
+    (d = 128: 8 workgroups per (sequence, head)); 40, 68 and 160 heads need
+    more workgroups than the device's 256 compute units hold at once, so they
+    run in several rounds. Every batch matches the oracle."""
+    gdr = _gdr()
+    lens = tuple(int(x) for x in np.random.default_rng(N).integers(0, 140, size=N))
+    w = small_workload(128, "bf16", "channel", "delta", "f32", zero_init=False, seqlens=lens,
+                       HK=2, HV=4, slots=N + 3, seed=31 + N)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    print(f"channel-gate widths N={N} lens={lens}", flush=True)
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      d["cu_seqlens"])
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], 128 ** -0.5)
+    check_out(host(o, "bf16"), o_ref, "bf16")
+    for sl in x["slot_idx"]:
+        check_state(host(d["pool"], "f32")[sl], pool_ref[sl], "bf16", "f32")
+
+
 def test_fused_qkv_strides():
     """q, k, v may be views into one fused [T, 2 HK DK + HV DV] buffer (the
     channel layout of the Mojo gated_delta module)."""
