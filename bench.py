@@ -43,12 +43,17 @@ STEP_SRC = [os.path.join(CSRC, "recurrent_step.hip"), os.path.join(CSRC, "gdr_in
 
 
 def prefill_kernel(w: synth.Workload):
-    """(kernel name, its source files) of the prefill kernel the library runs
-    for this workload: the warp-specialised kernel for bf16 inputs without a
-    channel gate, the general one otherwise (the dispatch in chunk_fwd.hip)."""
+    """(kernel name, its source files) of the prefill kernel(s) the library
+    runs for this workload: the warp-specialised kernel for bf16 inputs
+    without a channel gate; for bf16 inputs with the channel gate and the
+    delta rule the prep and state kernel pair (timed together, as one call);
+    the general kernel otherwise (the dispatch in gdr_api.hip and
+    chunk_fwd.hip)."""
     common = [os.path.join(CSRC, "chunk_common.h"), os.path.join(CSRC, "gdr_internal.h")]
     if w.in_dtype == "bf16" and w.gate != "channel":
         return "chunk_fwd_ws_kernel", [os.path.join(CSRC, "chunk_fwd_ws.hip")] + common
+    if w.in_dtype == "bf16" and w.rule == "delta":
+        return "kda_prep_kernel+kda_state_kernel", [os.path.join(CSRC, "chunk_fwd_kda.hip")] + common
     return "chunk_fwd_kernel", [os.path.join(CSRC, "chunk_fwd.hip")] + common
 
 

@@ -174,16 +174,18 @@ __device__ __forceinline__ void t_block(PrepSmem<D> &sm, const f32x4 (&rv)[4], i
   *reinterpret_cast<float4 *>(&sm.t.tt[16 * I + r][16 * J + 4 * g]) = make_float4(t[0], t[1], t[2], t[3]);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
-  using RC = KdaRec<D>;
-  using SM = PrepSmem<D>;
-  constexpr int NS = RC::NS, NT = RC::NT, PK = SM::PK;
-  __shared__ SM sm;
+// One (chunk, value head) item of the prep kernel: where its record goes and
+// which tokens it covers (valid is false for a flat index that names no chunk).
+struct PrepItem {
+  int64_t t0;
+  int L, h;
+  bool valid;
+};
 
-  const int HV = p.HV;
-  const int jb = blockIdx.x / HV;
-  const int h = blockIdx.x - jb * HV;
+__device__ __forceinline__ PrepItem prep_item(const KdaParams &p, int64_t item) {
+  PrepItem it;
+  const int64_t jb = item / p.HV;
+  it.h = (int)(item - jb * p.HV);
   const int64_t F = p.F0 + jb;
   // the sequence owning flat chunk F: the last n with base(n) <= F
   int lo = 0, hi = p.N - 1;
@@ -192,45 +194,100 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
     if (flat_base(p.cu_seqlens, mid) <= F) lo = mid;
     else hi = mid - 1;
   }
-  const int n = lo;
-  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
-  const int64_t t0 = bos + 64 * (F - flat_base(p.cu_seqlens, n));
-  if (t0 >= eos) return;   // a flat index that names no chunk
-  const int L = (int)min<int64_t>(C, eos - t0);
-  char *rec = p.rec + ((int64_t)jb * HV + h) * RC::BYTES;
+  const int64_t bos = p.cu_seqlens[lo], eos = p.cu_seqlens[lo + 1];
+  it.t0 = bos + 64 * (F - flat_base(p.cu_seqlens, lo));
+  it.valid = it.t0 < eos;
+  it.L = it.valid ? (int)min<int64_t>(C, eos - it.t0) : 1;
+  if (!it.valid) it.t0 = 0;   // (loads of such an item read token 0 and are not used)
+  return it;
+}
 
+// A lane's raw inputs of one item: token 16w + r, channels 32s + slot_k(g, j)
+// (gate fp32, keys and queries bf16 pairs), and beta; held in registers from
+// one item to the next so that their loads overlap the previous item's work.
+template <int D>
+struct PrepIn {
+  static constexpr int NS = D / 32;
+  typename U32Vec<8 * NS>::type g;
+  typename U32Vec<4 * NS>::type k, q;
+  float beta;
+};
+
+template <int D>
+__device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, const PrepItem &it, int w,
+                                          int r, int g) {
+  constexpr int NS = D / 32;
+  const int i = 16 * w + r;
+  const int64_t t = it.t0 + min(i, it.L - 1);
+  const int hk = it.h / p.ratio;
+  const float *gp = p.g + (t * p.HV + it.h) * (int64_t)D;
+  const uint16_t *kp = static_cast<const uint16_t *>(p.k) + t * p.k_stride + (int64_t)hk * D;
+  const uint16_t *qp = static_cast<const uint16_t *>(p.q) + t * p.q_stride + (int64_t)hk * D;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int col = 32 * s + 16 * hf + 4 * g;
+      const float4 g4 = *reinterpret_cast<const float4 *>(gp + col);
+      const uint2 k2 = *reinterpret_cast<const uint2 *>(kp + col);
+      const uint2 q2 = *reinterpret_cast<const uint2 *>(qp + col);
+      const int u = 2 * s + hf;
+      in.g[4 * u] = __float_as_uint(g4.x);
+      in.g[4 * u + 1] = __float_as_uint(g4.y);
+      in.g[4 * u + 2] = __float_as_uint(g4.z);
+      in.g[4 * u + 3] = __float_as_uint(g4.w);
+      in.k[2 * u] = k2.x;
+      in.k[2 * u + 1] = k2.y;
+      in.q[2 * u] = q2.x;
+      in.q[2 * u + 1] = q2.y;
+    }
+  in.beta = p.beta[t * p.HV + it.h];
+}
+
+// Persistent: each workgroup takes items blockIdx.x, blockIdx.x + gridDim.x, ...
+// and loads the next item's inputs while it works on the current one.
+template <int D>
+__global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
+  using RC = KdaRec<D>;
+  using SM = PrepSmem<D>;
+  constexpr int NS = RC::NS, NT = RC::NT, PK = SM::PK;
+  __shared__ SM sm;
+
+  const int HV = p.HV;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const int hk = h / p.ratio;
   const int i = 16 * w + r;   // this lane's token
-  const bool ok = i < L;
-  const int64_t t = t0 + (ok ? i : L - 1);
-
-  // ---- loads: token i, channels 32s + slot_k(g, j) ----
-  float gv[NS][8], kv[NS][8], qv[NS][8];
-  {
-    const float *gp = p.g + (t * HV + h) * (int64_t)D;
-    const uint16_t *kp = static_cast<const uint16_t *>(p.k) + t * p.k_stride + (int64_t)hk * D;
-    const uint16_t *qp = static_cast<const uint16_t *>(p.q) + t * p.q_stride + (int64_t)hk * D;
+  const int64_t items = (p.F1 - p.F0) * HV;
+  int64_t item = blockIdx.x;
+  PrepItem nx = prep_item(p, item);
+  PrepIn<D> in;
+  prep_load<D>(in, p, nx, w, r, g);
+  for (; item < items; item += gridDim.x) {
+    const PrepItem it = nx;
+    const bool ok = i < it.L;
+    float gv[NS][8], kv[NS][8], qv[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int col = 32 * s + 16 * hf + 4 * g;
-        const float4 g4 = *reinterpret_cast<const float4 *>(gp + col);
-        const uint2 k2 = *reinterpret_cast<const uint2 *>(kp + col);
-        const uint2 q2 = *reinterpret_cast<const uint2 *>(qp + col);
-        const float ga[4] = {g4.x, g4.y, g4.z, g4.w};
-        const float ka[4] = {bf_lo(k2.x), bf_hi(k2.x), bf_lo(k2.y), bf_hi(k2.y)};
-        const float qa[4] = {bf_lo(q2.x), bf_hi(q2.x), bf_lo(q2.y), bf_hi(q2.y)};
+        const int u = 2 * s + hf;
+        const uint32_t kw[2] = {in.k[2 * u], in.k[2 * u + 1]}, qw[2] = {in.q[2 * u], in.q[2 * u + 1]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          gv[s][4 * hf + j] = ok ? ga[j] : 0.f;
-          kv[s][4 * hf + j] = ok ? ka[j] : 0.f;
-          qv[s][4 * hf + j] = ok ? qa[j] : 0.f;
+          gv[s][4 * hf + j] = ok ? __uint_as_float(in.g[4 * u + j]) : 0.f;
+          kv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1])) : 0.f;
+          qv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1])) : 0.f;
         }
       }
-    if (g == 0) sm.beta[i] = ok ? p.beta[t * HV + h] : 0.f;
-  }
+    if (g == 0) sm.beta[i] = ok ? in.beta : 0.f;
+    if (item + gridDim.x < items) {
+      nx = prep_item(p, item + gridDim.x);
+      prep_load<D>(in, p, nx, w, r, g);
+    }
+    if (it.valid) {
+      const int h = it.h;
+      const int L = it.L;
+      char *rec = p.rec + item * (int64_t)RC::BYTES;
+      (void)L;
 
   // ---- gate prefix sums: within the 16-token block (DPP row scan over r),
   //      then the totals of the earlier blocks ----
@@ -438,6 +495,9 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
       split8(x, f);
       st_frag(rec, RC::R1 + RC::wq(I, w), lane, f);
     }
+  }
+    }
+    __syncthreads();   // the next item reuses the LDS
   }
 }
 
@@ -956,13 +1016,15 @@ constexpr size_t kSliceRecordBytes = (size_t)192 << 20;
 
 template <int D, int NSW>
 hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStream_t stream) {
+  const int cus = cu_count();
   const int grp = D / (16 * NSW);
   const int sblocks = ((p0.N * p0.HV + 7) / 8) * 8 * grp;
   for (int64_t F0 = 0; F0 < flat; F0 += per) {
     KdaParams p = p0;
     p.F0 = F0;
     p.F1 = F0 + per < flat ? F0 + per : flat;
-    const int64_t pblocks = (p.F1 - p.F0) * p.HV;
+    const int64_t items = (p.F1 - p.F0) * p.HV;
+    const int64_t pblocks = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;   // two per compute unit
     hipLaunchKernelGGL((kda_prep_kernel<D>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((kda_state_kernel<D, NSW>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0, stream, p);
   }
