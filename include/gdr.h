@@ -38,6 +38,9 @@
  *   cu_seqlens  [N+1] int32, 0 = cu[0] <= cu[1] <= ... <= cu[N] = T_total;
  *               sequence n is tokens cu[n] .. cu[n+1]-1 (prefill only)
  * Value head h reads key head h / (HV / HK) (grouped heads, Mojo page).
+ * q, k, v, g and o must start on 16-byte boundaries and the token strides
+ * of q, k and v must be multiples of 16 bytes (the kernels move rows in
+ * 16-byte units).
  *
  * Errors. Everything checkable on the host is checked before any work is
  * enqueued; on error nothing is launched and no memory is touched. Contents
@@ -66,7 +69,7 @@ typedef enum gdr_status {
   GDR_OK = 0,
   GDR_E_INVALID = 1,      /* malformed arguments (null pointer, bad size, aliasing) */
   GDR_E_UNSUPPORTED = 2,  /* well-formed but not built (head dim, chunk size, dtype) */
-  GDR_E_WORKSPACE = 3,    /* workspace smaller than gdr_chunk_fwd_workspace_bytes */
+  GDR_E_WORKSPACE = 3,    /* workspace missing or below the call's minimum (see below) */
   GDR_E_HIP = 4,          /* the HIP runtime reported an error at launch */
   GDR_E_DEVICE_CHECK = 5  /* GDR_FLAG_DEBUG_CHECKS found a bad cu_seqlens or slot_idx */
 } gdr_status;
@@ -117,14 +120,31 @@ typedef struct gdr_args {
 /* GDR_ABI_VERSION of the loaded library. */
 int gdr_abi_version(void);
 
-/* Bytes of device workspace gdr_chunk_fwd needs for these arguments (0 when
- * the fused schedule needs none). Returns 0 for arguments it cannot size. */
+/* Preferred bytes of device workspace for gdr_chunk_fwd with these arguments;
+ * 0 when the call runs one fused kernel and needs none. Returns 0 for
+ * arguments that fail validation.
+ *
+ * Only the channel gate with bf16 inputs and the delta rule uses a workspace:
+ * it runs as a parallel per-chunk kernel that writes one record per (chunk,
+ * value head) (the decayed keys and queries, the inverse of the chunk's unit
+ * lower triangular system and the products the state recurrence needs; the
+ * chunk regrouping of section 6 of the KDA page) and a state kernel that
+ * reads them in chunk order. The workspace holds an fp32 state carry of
+ * N * HV * DK * DV values plus records for a slice of flat chunks; the call
+ * runs as many slices as it needs, so any size from the carry plus one
+ * chunk's records for every value head (HV * 123392 bytes at DK = 128,
+ * HV * 73984 at DK = 64) up works, a larger one with fewer launches. The
+ * preferred size keeps a slice's records within the 256 MB last-level cache. */
 size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a);
 
 /* Chunkwise prefill over the ragged batch described by cu_seqlens: writes o
  * for every token and the final state of each sequence into its pool slot.
  * Zero-length sequences write their (initial) state back unchanged. N == 0 is
- * a no-op. `workspace` may be NULL when ws_bytes == 0. */
+ * a no-op. `workspace` (device memory, 256-byte aligned, contents need not be
+ * initialised and are garbage afterwards) may be NULL when the call needs
+ * none; a call that needs one and gets less than its minimum returns
+ * GDR_E_WORKSPACE before enqueuing anything. Calls that share a workspace
+ * must not overlap in time. */
 gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
                          hipStream_t stream);
 
