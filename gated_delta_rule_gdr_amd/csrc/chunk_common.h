@@ -70,6 +70,18 @@ __device__ __forceinline__ f32x4 mm(const Frag &a, const Frag &b, f32x4 c) {
   return mfma(a.hi, b.hi, c);
 }
 
+// Pass P of acc += a * b as mm<A_SPLIT, B_SPLIT> issues them (lo terms first,
+// then hi x hi; a pass the operands do not need leaves acc as it is). Blocks
+// of independent products issue pass by pass across their accumulators, so
+// that no MFMA waits on the one just before it; each accumulator still sees
+// mm's sequence of products, so results are unchanged.
+template <int P, bool A_SPLIT, bool B_SPLIT>
+__device__ __forceinline__ f32x4 mm_pass(const Frag &a, const Frag &b, f32x4 c) {
+  if constexpr (P == 0) return A_SPLIT ? mfma(a.lo, b.hi, c) : c;
+  else if constexpr (P == 1) return B_SPLIT ? mfma(a.hi, b.lo, c) : c;
+  else return mfma(a.hi, b.hi, c);
+}
+
 // Operand arrays in LDS store each 32-wide block of their contraction axis
 // permuted so that a lane's slot set K(g) = {4g..4g+3, 16+4g..16+4g+3} is the
 // contiguous physical range 8g .. 8g+7: logical index c sits at perm32(c).

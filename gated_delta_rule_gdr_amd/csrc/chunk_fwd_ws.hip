@@ -234,9 +234,12 @@ __device__ __forceinline__ void gram_seg(SM &sm, const typename SM::Set &S, floa
       for (int s = 0; s < NS; ++s) ldfrag(&S.kk[0][0], PK, 16 * (J + 1) + r, 32 * s, g, fm[(J + 1 - J0) & 1][s]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    acc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // even and odd k steps in two accumulators, so consecutive MFMAs are
+    // independent
+    f32x4 a2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[J] = mm<false, false>(fm[(J - J0) & 1][s], fn[s], acc[J]);
+    for (int s = 0; s < NS; ++s) a2[s & 1] = mfma(fm[(J - J0) & 1][s].hi, fn[s].hi, a2[s & 1]);
+    acc[J] = a2[0] + a2[1];
     __builtin_amdgcn_sched_barrier(0);
   }
   const int ii = 16 * I + r;
@@ -697,7 +700,9 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
             for (int I = 0; I < 4; ++I) ldfrag(&S.kk[0][0], PK, 16 * I + r, 32 * (s + 1), g, fk[(s + 1) & 1][I]);
           }
 #pragma unroll
-          for (int I = 0; I < 4; ++I) xa[I] = mm<false, true>(fk[s & 1][I], sf[s], xa[I]);
+          for (int I = 0; I < 4; ++I) xa[I] = mm_pass<1, false, true>(fk[s & 1][I], sf[s], xa[I]);
+#pragma unroll
+          for (int I = 0; I < 4; ++I) xa[I] = mm_pass<2, false, true>(fk[s & 1][I], sf[s], xa[I]);
           if (s + 1 < NS) chainfrag(st[2 * s + 2], st[2 * s + 3], sf[s + 1]);
           interleave<8, 3, 1>();
           __builtin_amdgcn_sched_barrier(0);
@@ -768,7 +773,9 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
           for (int I = 0; I < 4; ++I) ldfrag(&S.qq[0][0], PK, 16 * I + r, 32 * (s + 1), g, fq[(s + 1) & 1][I]);
         }
 #pragma unroll
-        for (int I = 0; I < 4; ++I) qa[I] = mm<false, true>(fq[s & 1][I], sf[s], qa[I]);
+        for (int I = 0; I < 4; ++I) qa[I] = mm_pass<1, false, true>(fq[s & 1][I], sf[s], qa[I]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) qa[I] = mm_pass<2, false, true>(fq[s & 1][I], sf[s], qa[I]);
         // items by step: 0 | 1 | 2 3 | 4 over four steps, 0 1 2 | 3 4 over two
 #pragma unroll
         for (int k = 0; k < (DELTA ? 5 : 1); ++k) {
@@ -792,11 +799,18 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         for (int s = 0; s <= (I >> 1); ++s) ldfrag2(&sm.ah[0][0], &sm.al[0][0], PT, 16 * I + r, s, g, af[I][s]);
       if constexpr (DELTA) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < 4; ++I) vbar[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // (k step 0 for all four blocks, then step 1 for blocks 2-3)
+        auto vpass = [&](auto P, int s) {
 #pragma unroll
-          for (int s = 0; s <= (I >> 1); ++s) acc = mm<true, true>(tf[I][s], rb[s], acc);
-          vbar[I] = acc;
+          for (int I = 2 * s; I < 4; ++I)
+            vbar[I] = mm_pass<decltype(P)::value, true, true>(tf[I][s], rb[s], vbar[I]);
+        };
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          vpass(std::integral_constant<int, 0>{}, s);
+          vpass(std::integral_constant<int, 1>{}, s);
+          vpass(std::integral_constant<int, 2>{}, s);
         }
       } else {
 #pragma unroll
@@ -832,7 +846,11 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         for (int s = 0; s < 2; ++s) ldfrag_kt(&S.kk[0][0], PK, m, s, r, g, kt[m][s]);
       f32x4 oa[4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) oa[I] = mm<true, DELTA>(af[I][0], vbf[0], qa[I]);
+      for (int I = 0; I < 4; ++I) oa[I] = mm_pass<0, true, DELTA>(af[I][0], vbf[0], qa[I]);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) oa[I] = mm_pass<1, true, DELTA>(af[I][0], vbf[0], oa[I]);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) oa[I] = mm_pass<2, true, DELTA>(af[I][0], vbf[0], oa[I]);
       chainfrag(vbar[2], vbar[3], vbf[1]);
       Frag uf[2];
       {
@@ -852,7 +870,11 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         chainfrag(vs[2], vs[3], uf[1]);
       }
 #pragma unroll
-      for (int I = 2; I < 4; ++I) oa[I] = mm<true, DELTA>(af[I][1], vbf[1], oa[I]);
+      for (int I = 2; I < 4; ++I) oa[I] = mm_pass<0, true, DELTA>(af[I][1], vbf[1], oa[I]);
+#pragma unroll
+      for (int I = 2; I < 4; ++I) oa[I] = mm_pass<1, true, DELTA>(af[I][1], vbf[1], oa[I]);
+#pragma unroll
+      for (int I = 2; I < 4; ++I) oa[I] = mm_pass<2, true, DELTA>(af[I][1], vbf[1], oa[I]);
       interleave<DELTA ? 18 : 12, 6, 0>();
       __builtin_amdgcn_sched_barrier(0);
 
@@ -861,9 +883,12 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
       {
         constexpr bool USPLIT = DELTA || GATE == GDR_GATE_SCALAR;
 #pragma unroll
-        for (int m = 0; m < NT; ++m)
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) st[m] = mm<false, USPLIT>(kt[m][s], uf[s], st[m]);
+          for (int m = 0; m < NT; ++m) st[m] = mm_pass<1, false, USPLIT>(kt[m][s], uf[s], st[m]);
+#pragma unroll
+          for (int m = 0; m < NT; ++m) st[m] = mm_pass<2, false, USPLIT>(kt[m][s], uf[s], st[m]);
+        }
       }
       {
         // Buffer stores against a descriptor over this chunk's 64 output
