@@ -17,12 +17,14 @@ Parity status: every function here is pinned by a CPU test against a property
 the pages or the mathematics fix (tests/test_oracle_*.py). None is "parity
 unpinned".
 """
-from .recurrent import recurrent_fp64, round_to_storage, round_f64_to_bf16
+from .recurrent import (recurrent_fp64, round_to_storage, round_f64_to_bf16,
+                        l2_normalise_fp64, L2_EPS)
 from .chunkwise import chunkwise_fp64, forward_substitution_unit_lower
 from .bruteforce import (linear_parallel_fp64, delta_parallel_fp64,
                          four_token_chunk_fractions)
 
 __all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16",
+           "l2_normalise_fp64", "L2_EPS",
            "chunkwise_fp64", "forward_substitution_unit_lower",
            "linear_parallel_fp64", "delta_parallel_fp64",
            "four_token_chunk_fractions"]

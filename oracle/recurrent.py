@@ -33,7 +33,11 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16"]
+__all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16", "l2_normalise_fp64",
+           "L2_EPS"]
+
+# Guard of the L2 normalisation (see l2_normalise_fp64).
+L2_EPS = 1e-6
 
 
 def round_f64_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -142,3 +146,19 @@ def recurrent_fp64(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale,
     for n in range(N):
         pool_out[slot_idx[n]] = round_to_storage(np.swapaxes(S[n], -1, -2), state_dtype)
     return o, pool_out
+
+
+def l2_normalise_fp64(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
+    """x / sqrt(sum_k x_k^2 + eps) over the last axis, in fp64.
+
+    The "gated_delta" Mojo page (its kernel steps 2, 4 and 5) reads the state
+    with L2-normalised keys and queries, and "From Attention to Learned
+    Memory" (the paragraph after the causal read) notes that models apply SiLU
+    and then L2 normalisation to q and k ahead of the recurrence, leaving the
+    state algebra unchanged. The pages give no guard for a zero vector; the
+    reading taken here adds eps = 1e-6 to the squared norm, so a zero vector
+    stays zero and any other vector comes out with norm
+    sqrt(|x|^2 / (|x|^2 + eps)).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)

@@ -460,3 +460,52 @@ def test_pool_write_rounds_to_bf16():
                             state_dtype="bf16")
     np.testing.assert_array_equal(pbf[0], round_f64_to_bf16(p64[0]))
     np.testing.assert_array_equal(pbf[1], pool[1])
+
+
+# ---------------------------------------------------------------------------
+# L2 normalisation of q and k ("gated_delta" Mojo page, kernel steps 2, 4, 5)
+# ---------------------------------------------------------------------------
+
+def test_l2_normalise_closed_forms():
+    """A 3-4-5 vector, a one-hot vector, the zero vector and the guard's
+    effect, each against its value worked out by hand."""
+    from oracle import l2_normalise_fp64, L2_EPS
+    assert L2_EPS == 1e-6
+    np.testing.assert_array_equal(l2_normalise_fp64(np.array([3.0, 4.0]), eps=0.0), [0.6, 0.8])
+    np.testing.assert_array_equal(l2_normalise_fp64(np.array([0.0, -2.0, 0.0]), eps=0.0),
+                                  [0.0, -1.0, 0.0])
+    np.testing.assert_array_equal(l2_normalise_fp64(np.zeros(4)), np.zeros(4))
+    # with the guard: 3 / sqrt(25 + 1e-6) = 0.6 / sqrt(1 + 4e-8)
+    y = l2_normalise_fp64(np.array([3.0, 4.0]))
+    np.testing.assert_allclose(y, np.array([0.6, 0.8]) / np.sqrt(1.0 + 4e-8), rtol=2e-16, atol=0)
+
+
+def test_l2_normalise_norm_and_scale_invariance():
+    """|x^|^2 = |x|^2 / (|x|^2 + eps) row by row (rows over the last axis of
+    a [T, H, D] array), and with eps = 0 the result ignores positive scales."""
+    from oracle import l2_normalise_fp64
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 3, 16)) * rng.uniform(0.01, 5.0, size=(6, 3, 1))
+    y = l2_normalise_fp64(x, eps=1e-6)
+    n2 = np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(np.sum(y * y, axis=-1), n2 / (n2 + 1e-6), rtol=1e-14)
+    np.testing.assert_allclose(l2_normalise_fp64(7.5 * x, eps=0.0), l2_normalise_fp64(x, eps=0.0),
+                               rtol=1e-15, atol=1e-16)
+
+
+def test_normalised_key_writes_exactly():
+    """With beta = 1 and no decay, a raw key k writes v along k / |k| exactly:
+    S (k / |k|) = v after the step (the delta write of the KDA page section 2
+    with the Mojo page's normalised key)."""
+    from oracle import l2_normalise_fp64
+    rng = np.random.default_rng(6)
+    DK, DV = 5, 3
+    k = 3.0 * rng.standard_normal((1, 1, DK))
+    q = rng.standard_normal((1, 1, DK))
+    v = rng.standard_normal((1, 1, DV))
+    pool = rng.standard_normal((1, 1, DK, DV))
+    kn = l2_normalise_fp64(k, eps=0.0)
+    _, p = oracle.recurrent_fp64(l2_normalise_fp64(q, eps=0.0), kn, v, np.zeros((1, 1)),
+                                 np.ones((1, 1)), pool, [0], [0, 1], scale=1.0, state_dtype="f64")
+    S = p[0, 0].T
+    np.testing.assert_allclose(S @ kn[0, 0], v[0, 0], rtol=1e-13, atol=1e-13)
