@@ -6,6 +6,7 @@ supplies device memory and the current HIP stream. There is no CPU fallback:
 if the library is missing, importing the binding works but every call raises.
 
     o = chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens)
+    o = recurrent_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, qk_l2norm=False)
     o = recurrent_step(q, k, v, g, beta, pool, slot_idx)
 
 Layouts (torch tensors on the GPU):
@@ -23,7 +24,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "lib", "lib_path", "GdrError",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +36,7 @@ _RULE = {"delta": 0, "linear": 1}
 _GATE = {"none": 0, "scalar": 1, "channel": 2}
 FLAG_ZERO_INIT = 1
 FLAG_DEBUG_CHECKS = 2
+FLAG_QK_L2NORM = 4
 
 
 class GdrError(RuntimeError):
@@ -85,6 +87,8 @@ def load() -> ctypes.CDLL:
                                 ctypes.c_void_p]
     L.gdr_recurrent_step.restype = ctypes.c_int
     L.gdr_recurrent_step.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
+    L.gdr_recurrent_fwd.restype = ctypes.c_int
+    L.gdr_recurrent_fwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
     L.gdr_status_string.restype = ctypes.c_char_p
     L.gdr_status_string.argtypes = [ctypes.c_int]
     L.gdr_last_error.restype = ctypes.c_char_p
@@ -236,4 +240,21 @@ def recurrent_step(q, k, v, g, beta, pool, slot_idx, *, scale=None, rule="delta"
                     zero_init, debug_checks, 64, out_dtype)
     L = load()
     _check(L.gdr_recurrent_step(ctypes.byref(a), _stream(q)))
+    return o
+
+
+def recurrent_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, rule="delta",
+                  gate=None, out_dtype=None, zero_init=False, o=None, debug_checks=False,
+                  qk_l2norm=False):
+    """Tokenwise recurrence over a ragged batch (the state on chip across each
+    sequence); same results as chunk_fwd. qk_l2norm normalises q and k per
+    token and key head inside the kernel. Returns o [T, HV, DV]."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
+                    zero_init, debug_checks, 64, out_dtype)
+    if qk_l2norm:
+        a.flags |= FLAG_QK_L2NORM
+    L = load()
+    _check(L.gdr_recurrent_fwd(ctypes.byref(a), _stream(q)))
     return o

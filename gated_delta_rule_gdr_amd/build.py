@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr_api.hip", "recurrent_step.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip", "chunk_fwd_kda.hip"]
+SOURCES = ["gdr_api.hip", "recurrent_step.hip", "recurrent_fwd.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip",
+           "chunk_fwd_kda.hip"]
 ARCH = "gfx950"
 
 

@@ -41,8 +41,13 @@ Range span(const void *p, int64_t rows, int64_t row_stride, int64_t row_len, siz
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-// Checks shared by both entry points. `prefill` selects the chunk rules.
-gdr_status validate(const gdr_args *a, bool prefill) {
+// Which entry point is validating: the chunk prefill, the one-token step or
+// the tokenwise recurrence over a ragged batch.
+enum class Call { Chunk, Step, Recur };
+
+// Checks shared by the entry points.
+gdr_status validate(const gdr_args *a, Call call) {
+  const bool prefill = call != Call::Step;   // a ragged batch described by cu_seqlens
   g_last_error[0] = '\0';
   if (!a) return fail(GDR_E_INVALID, "args is NULL");
   if (a->N < 0) return fail(GDR_E_INVALID, "N = %d < 0", a->N);
@@ -54,15 +59,17 @@ gdr_status validate(const gdr_args *a, bool prefill) {
   if (a->rule != GDR_RULE_DELTA && a->rule != GDR_RULE_LINEAR) return fail(GDR_E_INVALID, "unknown rule %d", (int)a->rule);
   if (a->gate != GDR_GATE_NONE && a->gate != GDR_GATE_SCALAR && a->gate != GDR_GATE_CHANNEL)
     return fail(GDR_E_INVALID, "unknown gate %d", (int)a->gate);
-  if (a->flags & ~(uint32_t)(GDR_FLAG_ZERO_INIT | GDR_FLAG_DEBUG_CHECKS))
+  if (a->flags & ~(uint32_t)(GDR_FLAG_ZERO_INIT | GDR_FLAG_DEBUG_CHECKS | GDR_FLAG_QK_L2NORM))
     return fail(GDR_E_INVALID, "unknown flag bits 0x%x", a->flags);
+  if ((a->flags & GDR_FLAG_QK_L2NORM) && call != Call::Recur)
+    return fail(GDR_E_UNSUPPORTED, "GDR_FLAG_QK_L2NORM is taken by gdr_recurrent_fwd only");
   if (!std::isfinite(a->scale)) return fail(GDR_E_INVALID, "scale is not finite");
   if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK))
     return fail(GDR_E_UNSUPPORTED, "head dims DK = %d, DV = %d: built for DK = DV in {64, 128}", a->DK, a->DV);
   if (!prefill && a->T_total != a->N)
     return fail(GDR_E_INVALID, "recurrent step needs one token per sequence (T_total = %lld, N = %d)",
                 (long long)a->T_total, a->N);
-  if (prefill && a->chunk_size != 64)
+  if (call == Call::Chunk && a->chunk_size != 64)
     return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: built for 64", a->chunk_size);
   if (a->N == 0) return GDR_OK;  // nothing to do; pointers may be NULL
 
@@ -93,10 +100,10 @@ gdr_status validate(const gdr_args *a, bool prefill) {
     for (const Range &r : ins)
       if (overlap(ro, r)) return fail(GDR_E_INVALID, "o overlaps an input or the state pool");
     // the kernels move q, k, v, g and o rows in 16-byte units
-    const void *ptrs[] = {a->q, a->k, a->v, a->g, a->o};
+    const void *ptrs[] = {a->q, a->k, a->v, a->g, a->o, a->state_pool};
     for (const void *ptr : ptrs)
       if (reinterpret_cast<uintptr_t>(ptr) % 16)
-        return fail(GDR_E_INVALID, "q, k, v, g and o must be 16-byte aligned");
+        return fail(GDR_E_INVALID, "q, k, v, g, o and state_pool must be 16-byte aligned");
     if ((a->q_stride_t * (int64_t)ie) % 16 || (a->k_stride_t * (int64_t)ie) % 16 ||
         (a->v_stride_t * (int64_t)ie) % 16)
       return fail(GDR_E_INVALID, "token strides of q, k, v must be multiples of 16 bytes");
@@ -170,13 +177,13 @@ bool uses_workspace(const gdr_args *a) {
 }  // namespace
 
 GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a) {
-  if (validate(a, true) != GDR_OK || !uses_workspace(a)) return 0;
+  if (validate(a, Call::Chunk) != GDR_OK || !uses_workspace(a)) return 0;
   return chunk_fwd_kda_workspace(*a);
 }
 
 GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
                                     hipStream_t stream) {
-  gdr_status s = validate(a, true);
+  gdr_status s = validate(a, Call::Chunk);
   if (s != GDR_OK) return s;
   const bool ws_path = uses_workspace(a);
   if (ws_path) {
@@ -199,7 +206,7 @@ GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t w
 }
 
 GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) {
-  gdr_status s = validate(a, false);
+  gdr_status s = validate(a, Call::Step);
   if (s != GDR_OK) return s;
   if (a->N == 0) return GDR_OK;
   if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
@@ -208,6 +215,19 @@ GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) 
   }
   hipError_t e = launch_recurrent_step(*a, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent_step launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+GDR_EXPORT gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream) {
+  gdr_status s = validate(a, Call::Recur);
+  if (s != GDR_OK) return s;
+  if (a->N == 0) return GDR_OK;
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_recurrent_fwd(*a, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent_fwd launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

@@ -36,6 +36,7 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
 // ---------------------------------------------------------------------------
 
 hipError_t launch_recurrent_step(const gdr_args &a, hipStream_t stream);
+hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
 // True when GDR_PREFILL_KERNEL=generic asks for the general prefill kernel in
 // every case (used to compare kernels).

@@ -1,0 +1,438 @@
+// Tokenwise recurrence over a ragged batch: the decode step's schedule walked
+// over every token of each sequence, with the state held in registers from
+// the first token to the last (the "gated_delta" Mojo page, its thread
+// mapping: one block per (sequence, value head), the state column of a value
+// element in registers across the whole sequence). Per token, in the order
+// of that page's five steps and of the boxed KDA update:
+//
+//   S~ = S alpha_t | S Diag(alpha_t);  vhat = S~ k_t;  e = beta (v_t - vhat);
+//   S = S~ + e k_t^T;  o_t = S (scale q_t)          (linear rule: S = S~ + v k^T)
+//
+// optionally with k_t and q_t L2-normalised first (x / sqrt(|x|^2 + 1e-6)),
+// folded in as scalars on the reductions as the Mojo page describes, so no
+// normalised array is formed.
+//
+// Layout on gfx950: one workgroup of 256 threads per (sequence, value head,
+// 32 value columns). Lane (w, l) owns value column 8w + l / 8 of the block
+// and key group l % 8 (D / 8 consecutive keys), so the state S^T[keys,
+// column] sits in D / 8 registers per lane. A reduction over the keys is the
+// sum over the 8 lanes of a column: three DPP steps inside an 8-lane group
+// (quad swaps, then the half-row mirror), with no LDS and no barrier.
+//
+// Inputs arrive in blocks of 64 tokens: the workgroup copies a block's keys,
+// queries, value columns, gates and beta into LDS with coalesced 16-byte
+// loads, and while the 64 tokens run from LDS the next block's loads are in
+// flight in registers, so the serial per-token chain never waits on HBM.
+// Outputs collect in LDS and leave as whole rows after each block; the state
+// tile enters and leaves through LDS as coalesced rows as well.
+#include <cstdint>
+#include <type_traits>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr int VB = 32;   // value columns per workgroup
+constexpr int KG = 8;    // lanes (key groups) per value column
+constexpr float L2_EPS = 1e-6f;
+
+// (Vector types, not arrays: a block's loads stay in registers.)
+template <int N>
+struct U32VecR {
+  typedef unsigned int type __attribute__((ext_vector_type(N)));
+};
+template <class Vec>
+__device__ __forceinline__ void putv(Vec &v, int u, const uint4 x) {
+  v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
+}
+template <class Vec>
+__device__ __forceinline__ uint4 getv(const Vec &v, int u) {
+  return make_uint4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+}
+
+struct RecParams {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  const float *g, *beta;
+  void *o;
+  void *pool;
+  const int32_t *slot_idx, *cu_seqlens;
+  int32_t N, HV, ratio;
+  float scale;
+  int zero_init, st_bf16, out_bf16;
+};
+
+// Sum over the 8 lanes of a key-group set: every lane of the group gets it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_perm<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_perm<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_perm<0x141>(x);   // row_half_mirror: the other quad of the 8
+  return x;
+}
+
+constexpr int TB = 64;   // tokens staged per block
+
+// LDS of one workgroup: a block of TB tokens' inputs (keys, queries, this
+// workgroup's value columns, gates, beta) and its outputs; the state tile
+// passes through the key array at the sequence's start and end.
+template <bool IN_F32, int GATE, int D>
+struct RecSmem {
+  using In = std::conditional_t<IN_F32, float, uint16_t>;
+  static constexpr int KP = D + 16 / (int)sizeof(In) * 2;   // row pitch (elements)
+  static constexpr int VP = VB + 16 / (int)sizeof(In);
+  static constexpr int GP = GATE == GDR_GATE_CHANNEL ? D + 4 : 4;
+  union {
+    struct {
+      alignas(16) In kk[TB][KP];
+      alignas(16) In qq[TB][KP];
+    } tk;
+    alignas(16) float st[D][VB + 4];   // state tile S^T[keys][block columns]
+  };
+  alignas(16) In vv[TB][VP];
+  alignas(16) float gg[TB][GP];
+  alignas(16) float oo[TB][VB + 4];
+  float bb[TB];
+};
+
+// A block's inputs in flight, per thread: 16-byte units of keys and queries
+// (KU each), of values (VU), of channel gates (GU), and one float of the
+// scalar gate and of beta (threads below TB).
+template <bool IN_F32, int GATE, int D>
+struct RecPre {
+  static constexpr int ES = IN_F32 ? 4 : 2;
+  static constexpr int KU = TB * D * ES / 16 / 256;
+  static constexpr int VU = (TB * VB * ES / 16 + 255) / 256;
+  static constexpr int GU = GATE == GDR_GATE_CHANNEL ? TB * D * 4 / 16 / 256 : 0;
+  typename U32VecR<4 * KU>::type k, q;
+  typename U32VecR<4 * VU>::type v;
+  typename U32VecR<4 * (GU > 0 ? GU : 1)>::type g;
+  float gs, beta;
+};
+
+template <bool IN_F32, int GATE, bool DELTA, int D>
+__device__ __forceinline__ void block_load(RecPre<IN_F32, GATE, D> &pf, const RecParams &p, int64_t t0,
+                                           int L, int h, int hk, int vb, int tid) {
+  using PF = RecPre<IN_F32, GATE, D>;
+  constexpr int ES = PF::ES;
+  constexpr int KRU = D * ES / 16;       // units per key row
+  const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * ES;
+  const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * ES;
+#pragma unroll
+  for (int u = 0; u < PF::KU; ++u) {
+    const int e = tid + 256 * u, row = min(e / KRU, L - 1), c = e % KRU;
+    putv(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (int64_t)row * p.k_stride * ES + 16 * c));
+    putv(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (int64_t)row * p.q_stride * ES + 16 * c));
+  }
+  constexpr int VRU = VB * ES / 16;      // units per value row
+  const char *vbp = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * VB) * ES;
+#pragma unroll
+  for (int u = 0; u < PF::VU; ++u) {
+    const int e = tid + 256 * u, row = min(e / VRU, L - 1), c = e % VRU;
+    if (e < TB * VRU) putv(pf.v, u, *reinterpret_cast<const uint4 *>(vbp + (int64_t)row * p.v_stride * ES + 16 * c));
+  }
+  if constexpr (GATE == GDR_GATE_CHANNEL) {
+    constexpr int GRU = D * 4 / 16;
+    const float *gb = p.g + (t0 * p.HV + h) * (int64_t)D;
+#pragma unroll
+    for (int u = 0; u < PF::GU; ++u) {
+      const int e = tid + 256 * u, row = min(e / GRU, L - 1), c = e % GRU;
+      putv(pf.g, u, *reinterpret_cast<const uint4 *>(gb + (int64_t)row * p.HV * D + 4 * c));
+    }
+  }
+  if (tid < TB) {
+    const int64_t t = t0 + min(tid, L - 1);
+    pf.gs = GATE == GDR_GATE_SCALAR ? p.g[t * p.HV + h] : 0.f;
+    pf.beta = DELTA ? p.beta[t * p.HV + h] : 0.f;
+  }
+}
+
+template <bool IN_F32, int GATE, bool DELTA, int D>
+__device__ __forceinline__ void block_store(const RecPre<IN_F32, GATE, D> &pf, RecSmem<IN_F32, GATE, D> &sm,
+                                            int tid) {
+  using PF = RecPre<IN_F32, GATE, D>;
+  constexpr int ES = PF::ES;
+  constexpr int KRU = D * ES / 16;
+#pragma unroll
+  for (int u = 0; u < PF::KU; ++u) {
+    const int e = tid + 256 * u, row = e / KRU, c = e % KRU;
+    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.tk.kk[row][0]) + 16 * c) = getv(pf.k, u);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.tk.qq[row][0]) + 16 * c) = getv(pf.q, u);
+  }
+  constexpr int VRU = VB * ES / 16;
+#pragma unroll
+  for (int u = 0; u < PF::VU; ++u) {
+    const int e = tid + 256 * u, row = e / VRU, c = e % VRU;
+    if (e < TB * VRU) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.vv[row][0]) + 16 * c) = getv(pf.v, u);
+  }
+  if constexpr (GATE == GDR_GATE_CHANNEL) {
+    constexpr int GRU = D * 4 / 16;
+#pragma unroll
+    for (int u = 0; u < PF::GU; ++u) {
+      const int e = tid + 256 * u, row = e / GRU, c = e % GRU;
+      *reinterpret_cast<uint4 *>(&sm.gg[row][4 * c]) = getv(pf.g, u);
+    }
+  }
+  if (tid < TB) {
+    if constexpr (GATE == GDR_GATE_SCALAR) sm.gg[tid][0] = pf.gs;
+    if constexpr (DELTA) sm.bb[tid] = pf.beta;
+  }
+}
+
+template <bool IN_F32, int GATE, bool DELTA, bool L2, int D>
+__global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
+  using SM = RecSmem<IN_F32, GATE, D>;
+  using PF = RecPre<IN_F32, GATE, D>;
+  using In = typename SM::In;
+  constexpr int NK = D / KG;             // keys per lane
+  constexpr int NVB = D / VB;
+  constexpr int ES = PF::ES;
+  __shared__ SM sm;
+  const int b = blockIdx.x;
+  const int vb = b % NVB;
+  const int nh = b / NVB;
+  const int n = nh / p.HV;
+  const int h = nh - n * p.HV;
+  const int hk = h / p.ratio;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int kg = lane & (KG - 1);
+  const int vl = 8 * w + (lane >> 3);    // value column within the block
+  const int col = vb * VB + vl;
+  const int k0 = kg * NK;                // first key of this lane
+
+  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  // the workgroup's state tile: row k of S^T, columns vb*VB .. +VB-1
+  const int64_t tbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + vb * VB;
+  const int sw = p.st_bf16 ? 2 : 4;
+  const int RU = VB * sw / 16;           // 16-byte units per tile row
+  char *pool = static_cast<char *>(p.pool);
+
+  if (bos == eos) {
+    // a zero-length sequence under ZERO_INIT writes its zero state back
+    if (p.zero_init)
+      for (int e = tid; e < D * RU; e += 256)
+        *reinterpret_cast<uint4 *>(pool + (tbase + (int64_t)(e / RU) * D) * sw + 16 * (e % RU)) =
+            make_uint4(0, 0, 0, 0);
+    return;
+  }
+
+  // state in, coalesced through LDS: s[j] = S^T[k0 + j][col]
+  float s[NK];
+  if (p.zero_init) {
+#pragma unroll
+    for (int j = 0; j < NK; ++j) s[j] = 0.f;
+  } else {
+    for (int e = tid; e < D * RU; e += 256) {
+      const uint4 x = *reinterpret_cast<const uint4 *>(pool + (tbase + (int64_t)(e / RU) * D) * sw + 16 * (e % RU));
+      const int row = e / RU, c0 = (e % RU) * (16 / sw);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+      if (p.st_bf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          sm.st[row][c0 + i] = __uint_as_float((i & 1) ? (xw[i >> 1] & 0xffff0000u) : (xw[i >> 1] << 16));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.st[row][c0 + i] = __uint_as_float(xw[i]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NK; ++j) s[j] = sm.st[k0 + j][vl];
+  }
+
+  const int64_t HVD = (int64_t)p.HV * D;
+  const int64_t len = eos - bos;
+  const int nblk = (int)((len + TB - 1) / TB);
+  PF pf;
+  block_load<IN_F32, GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(TB, len), h, hk, vb, tid);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int64_t t0 = bos + (int64_t)blk * TB;
+    const int L = (int)min<int64_t>(TB, eos - t0);
+    __syncthreads();   // the previous block (or the state tile) is consumed
+    block_store<IN_F32, GATE, DELTA, D>(pf, sm, tid);
+    __syncthreads();
+    if (blk + 1 < nblk)
+      block_load<IN_F32, GATE, DELTA, D>(pf, p, t0 + TB, (int)min<int64_t>(TB, eos - t0 - TB), h, hk, vb, tid);
+
+    for (int i = 0; i < L; ++i) {
+      float kx[NK], qx[NK];
+      if constexpr (IN_F32) {
+#pragma unroll
+        for (int j = 0; j < NK; j += 4) {
+          const float4 a = *reinterpret_cast<const float4 *>(&sm.tk.kk[i][k0 + j]);
+          const float4 c = *reinterpret_cast<const float4 *>(&sm.tk.qq[i][k0 + j]);
+          kx[j] = a.x; kx[j + 1] = a.y; kx[j + 2] = a.z; kx[j + 3] = a.w;
+          qx[j] = c.x; qx[j + 1] = c.y; qx[j + 2] = c.z; qx[j + 3] = c.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NK; j += 8) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(&sm.tk.kk[i][k0 + j]);
+          const uint4 c = *reinterpret_cast<const uint4 *>(&sm.tk.qq[i][k0 + j]);
+          const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            kx[j + 2 * m] = __uint_as_float(aw[m] << 16);
+            kx[j + 2 * m + 1] = __uint_as_float(aw[m] & 0xffff0000u);
+            qx[j + 2 * m] = __uint_as_float(cw[m] << 16);
+            qx[j + 2 * m + 1] = __uint_as_float(cw[m] & 0xffff0000u);
+          }
+        }
+      }
+      const In vraw = sm.vv[i][vl];
+      float vval;
+      if constexpr (IN_F32) vval = vraw;
+      else vval = bf16_to_f32(vraw);
+      // L2 norms of k and q (as scalars on the reductions)
+      float rk = 1.f, rq = 1.f;
+      if constexpr (L2) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+          a = fmaf(kx[j], kx[j], a);
+          c = fmaf(qx[j], qx[j], c);
+        }
+        rk = rsqrtf(sum8(a) + L2_EPS);
+        rq = rsqrtf(sum8(c) + L2_EPS);
+      }
+      // 1. decay
+      if constexpr (GATE == GDR_GATE_SCALAR) {
+        const float al = __expf(sm.gg[i][0]);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) s[j] *= al;
+      } else if constexpr (GATE == GDR_GATE_CHANNEL) {
+#pragma unroll
+        for (int j = 0; j < NK; j += 4) {
+          const float4 gv = *reinterpret_cast<const float4 *>(&sm.gg[i][k0 + j]);
+          s[j] *= __expf(gv.x);
+          s[j + 1] *= __expf(gv.y);
+          s[j + 2] *= __expf(gv.z);
+          s[j + 3] *= __expf(gv.w);
+        }
+      }
+      if constexpr (DELTA) {
+        // 2-4. prediction from the decayed state, error, rank-one write
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NK; j += 2) {
+          a0 = fmaf(s[j], kx[j], a0);
+          a1 = fmaf(s[j + 1], kx[j + 1], a1);
+        }
+        const float vhat = sum8(a0 + a1) * rk;
+        const float e = sm.bb[i] * (vval - vhat) * rk;
+#pragma unroll
+        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j]);
+      } else {
+        const float e = vval * rk;
+#pragma unroll
+        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j]);
+      }
+      // 5. read after the write
+      float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NK; j += 2) {
+        b0 = fmaf(s[j], qx[j], b0);
+        b1 = fmaf(s[j + 1], qx[j + 1], b1);
+      }
+      const float o = sum8(b0 + b1) * (p.scale * rq);
+      if (kg == 0) sm.oo[i][vl] = o;
+    }
+    __syncthreads();
+    // the block's outputs, coalesced: row i, this workgroup's VB columns
+    const int ow = p.out_bf16 ? 2 : 4;
+    const int ORU = VB * ow / 16;
+    char *ob = static_cast<char *>(p.o) + (t0 * HVD + (int64_t)h * D + vb * VB) * ow;
+    for (int e = tid; e < L * ORU; e += 256) {
+      const int row = e / ORU, c0 = (e % ORU) * (16 / ow);
+      uint4 x;
+      if (p.out_bf16) {
+        uint32_t xw[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          xw[m] = (uint32_t)f32_to_bf16(sm.oo[row][c0 + 2 * m]) | ((uint32_t)f32_to_bf16(sm.oo[row][c0 + 2 * m + 1]) << 16);
+        x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+      } else {
+        x = make_uint4(__float_as_uint(sm.oo[row][c0]), __float_as_uint(sm.oo[row][c0 + 1]),
+                       __float_as_uint(sm.oo[row][c0 + 2]), __float_as_uint(sm.oo[row][c0 + 3]));
+      }
+      *reinterpret_cast<uint4 *>(ob + (int64_t)row * HVD * ow + 16 * (e % ORU)) = x;
+    }
+  }
+
+  // state out, coalesced through LDS (RNE to a bf16 pool)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NK; ++j) sm.st[k0 + j][vl] = s[j];
+  __syncthreads();
+  for (int e = tid; e < D * RU; e += 256) {
+    const int row = e / RU, c0 = (e % RU) * (16 / sw);
+    uint4 x;
+    if (p.st_bf16) {
+      uint32_t xw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        xw[m] = (uint32_t)f32_to_bf16(sm.st[row][c0 + 2 * m]) | ((uint32_t)f32_to_bf16(sm.st[row][c0 + 2 * m + 1]) << 16);
+      x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+    } else {
+      x = make_uint4(__float_as_uint(sm.st[row][c0]), __float_as_uint(sm.st[row][c0 + 1]),
+                     __float_as_uint(sm.st[row][c0 + 2]), __float_as_uint(sm.st[row][c0 + 3]));
+    }
+    *reinterpret_cast<uint4 *>(pool + (tbase + (int64_t)row * D) * sw + 16 * (e % RU)) = x;
+  }
+}
+
+template <bool IN_F32, int GATE, bool DELTA, bool L2>
+hipError_t by_dim(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  if (a.DK == 128) {
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 128>), dim3(a.N * a.HV * (128 / VB)),
+                       dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 64>), dim3(a.N * a.HV * (64 / VB)),
+                       dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+template <bool IN_F32, int GATE, bool DELTA>
+hipError_t by_norm(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  if (a.flags & GDR_FLAG_QK_L2NORM) return by_dim<IN_F32, GATE, DELTA, true>(a, p, st);
+  return by_dim<IN_F32, GATE, DELTA, false>(a, p, st);
+}
+
+template <bool IN_F32, int GATE>
+hipError_t by_rule(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  if (a.rule == GDR_RULE_DELTA) return by_norm<IN_F32, GATE, true>(a, p, st);
+  return by_norm<IN_F32, GATE, false>(a, p, st);
+}
+
+template <bool IN_F32>
+hipError_t by_gate(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  switch (a.gate) {
+    case GDR_GATE_SCALAR: return by_rule<IN_F32, GDR_GATE_SCALAR>(a, p, st);
+    case GDR_GATE_CHANNEL: return by_rule<IN_F32, GDR_GATE_CHANNEL>(a, p, st);
+    default: return by_rule<IN_F32, GDR_GATE_NONE>(a, p, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream) {
+  RecParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v;
+  p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
+  p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;
+  p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
+  p.N = a.N; p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.scale = a.scale;
+  p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
+  p.st_bf16 = a.state_dtype == GDR_BF16;
+  p.out_bf16 = a.out_dtype == GDR_BF16;
+  if (a.in_dtype == GDR_BF16) return by_gate<false>(a, p, stream);
+  return by_gate<true>(a, p, stream);
+}
+
+}  // namespace gdr

@@ -17,7 +17,10 @@
  *   gdr_chunk_fwd       chunkwise prefill over a ragged batch (the chunk
  *                       regrouping of section 6 of the KDA page and section 4
  *                       of "From Attention to Learned Memory");
- *   gdr_recurrent_step  one token per sequence (the tokenwise recurrence).
+ *   gdr_recurrent_step  one token per sequence (the tokenwise recurrence);
+ *   gdr_recurrent_fwd   the tokenwise recurrence over a ragged batch, the
+ *                       state in registers across each sequence (the
+ *                       "gated_delta" Mojo page's kernel).
  *
  * Memory. Every pointer is device memory owned by the caller; the library
  * neither allocates, frees nor keeps any of them after the call returns.
@@ -38,9 +41,9 @@
  *   cu_seqlens  [N+1] int32, 0 = cu[0] <= cu[1] <= ... <= cu[N] = T_total;
  *               sequence n is tokens cu[n] .. cu[n+1]-1 (prefill only)
  * Value head h reads key head h / (HV / HK) (grouped heads, Mojo page).
- * q, k, v, g and o must start on 16-byte boundaries and the token strides
- * of q, k and v must be multiples of 16 bytes (the kernels move rows in
- * 16-byte units).
+ * q, k, v, g, o and state_pool must start on 16-byte boundaries and the
+ * token strides of q, k and v must be multiples of 16 bytes (the kernels move
+ * rows in 16-byte units).
  *
  * Errors. Everything checkable on the host is checked before any work is
  * enqueued; on error nothing is launched and no memory is touched. Contents
@@ -63,7 +66,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -86,7 +89,9 @@ typedef enum gdr_gate { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL
 
 enum {
   GDR_FLAG_ZERO_INIT = 1u,     /* start every sequence from S = 0 instead of its pool slot */
-  GDR_FLAG_DEBUG_CHECKS = 2u   /* verify cu_seqlens / slot_idx on the device first */
+  GDR_FLAG_DEBUG_CHECKS = 2u,  /* verify cu_seqlens / slot_idx on the device first */
+  GDR_FLAG_QK_L2NORM = 4u      /* gdr_recurrent_fwd only: use q / |q| and k / |k| per token and
+                                  key head, |x| = sqrt(sum x^2 + 1e-6) */
 };
 
 typedef struct gdr_args {
@@ -151,6 +156,17 @@ gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
 /* One recurrent step: token n of q/k/v/g/beta belongs to sequence n
  * (T_total == N); reads and writes pool slot slot_idx[n] in place. */
 gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
+
+/* Tokenwise recurrence over the ragged batch described by cu_seqlens (same
+ * arguments, layouts and results as gdr_chunk_fwd; chunk_size is ignored):
+ * each (sequence, value head) walks its tokens in order with the state held
+ * on chip, the schedule of the "gated_delta" Mojo page, suited to short
+ * sequences and to serving that feeds a few tokens per sequence at a time.
+ * With GDR_FLAG_QK_L2NORM, q and k are L2-normalised per token and key head
+ * inside the kernel (that page's steps 2, 4 and 5), so q, k may be raw (for
+ * example views into a fused qkv buffer through the token strides). Needs no
+ * workspace. */
+gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdr_status_string(gdr_status s);

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_chunk_fwd_workspace_bytes", "gdr_chunk_fwd",
-                            "gdr_recurrent_step", "gdr_status_string", "gdr_last_error"])
+                            "gdr_recurrent_step", "gdr_recurrent_fwd", "gdr_status_string",
+                            "gdr_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == 1
+    assert L.gdr_abi_version() == 2
 
 
 def test_args_struct_matches_header_field_order():
@@ -97,6 +98,7 @@ CASES = [
     ("o aliases pool", dict(o=0x4000000 + 4096), 1),
     ("misaligned q", dict(q=0x1008), 1),
     ("misaligned g", dict(g=0x2004), 1),
+    ("misaligned pool", dict(state_pool=0x4000008), 1),
     ("stride not 16 bytes", dict(k_stride_t=2 * 128 + 4), 1),
 ]
 
@@ -110,6 +112,23 @@ def test_chunk_fwd_rejects_on_host(name, change, status):
     s = L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None)
     assert s == status, (name, L.gdr_last_error())
     assert L.gdr_last_error().decode()
+
+
+def test_l2norm_flag_only_for_the_ragged_recurrence():
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    a.flags = gdr.FLAG_QK_L2NORM
+    assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 2
+    b = _valid_args(gdr)
+    b.T_total = 2
+    b.flags = gdr.FLAG_QK_L2NORM
+    assert L.gdr_recurrent_step(ctypes.byref(b), None) == 2
+    c = _valid_args(gdr)
+    c.flags = 0x80
+    assert L.gdr_recurrent_fwd(ctypes.byref(c), None) == 1   # unknown bit
+    d = _valid_args(gdr)
+    d.cu_seqlens = None
+    assert L.gdr_recurrent_fwd(ctypes.byref(d), None) == 1   # ragged batch needs offsets
 
 
 def test_recurrent_step_rejects_on_host():
@@ -129,6 +148,7 @@ def test_empty_batch_is_a_no_op():
     a.q = a.k = a.v = a.o = a.state_pool = a.slot_idx = a.cu_seqlens = None
     assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 0
     assert L.gdr_recurrent_step(ctypes.byref(a), None) == 0
+    assert L.gdr_recurrent_fwd(ctypes.byref(a), None) == 0
     assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
 
 
