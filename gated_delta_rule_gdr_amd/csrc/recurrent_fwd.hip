@@ -75,25 +75,24 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-constexpr int TB = 64;   // tokens staged per block
+constexpr int TB = 32;   // tokens staged per block
 
-// LDS of one workgroup: a block of TB tokens' inputs (keys, queries, this
-// workgroup's value columns, gates, beta) and its outputs; the state tile
-// passes through the key array at the sequence's start and end.
-template <bool IN_F32, int GATE, int D>
+// LDS of one workgroup: a block of TB tokens' inputs, widened to fp32 once
+// on the way in (keys, queries, this workgroup's value columns, gates, beta),
+// and the block's outputs. The state tile passes through the key and query
+// arrays at the sequence's start and end.
+template <int GATE, int D>
 struct RecSmem {
-  using In = std::conditional_t<IN_F32, float, uint16_t>;
-  static constexpr int KP = D + 16 / (int)sizeof(In) * 2;   // row pitch (elements)
-  static constexpr int VP = VB + 16 / (int)sizeof(In);
+  static constexpr int KP = D + 4;   // row pitch: the 8 key groups of a row are contiguous
   static constexpr int GP = GATE == GDR_GATE_CHANNEL ? D + 4 : 4;
   union {
     struct {
-      alignas(16) In kk[TB][KP];
-      alignas(16) In qq[TB][KP];
+      alignas(16) float kk[TB][KP];
+      alignas(16) float qq[TB][KP];
     } tk;
     alignas(16) float st[D][VB + 4];   // state tile S^T[keys][block columns]
   };
-  alignas(16) In vv[TB][VP];
+  alignas(16) float vv[TB][VB + 4];
   alignas(16) float gg[TB][GP];
   alignas(16) float oo[TB][VB + 4];
   float bb[TB];
@@ -151,23 +150,37 @@ __device__ __forceinline__ void block_load(RecPre<IN_F32, GATE, D> &pf, const Re
   }
 }
 
+// A 16-byte unit of inputs into LDS as fp32: 8 bf16 values (two float4) or
+// 4 fp32 values.
+template <bool IN_F32>
+__device__ __forceinline__ void put_unit(float *dst, const uint4 x) {
+  if constexpr (IN_F32) {
+    *reinterpret_cast<uint4 *>(dst) = x;
+  } else {
+    *reinterpret_cast<float4 *>(dst) = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                                                   __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    *reinterpret_cast<float4 *>(dst + 4) = make_float4(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xffff0000u),
+                                                       __uint_as_float(x.w << 16), __uint_as_float(x.w & 0xffff0000u));
+  }
+}
+
 template <bool IN_F32, int GATE, bool DELTA, int D>
-__device__ __forceinline__ void block_store(const RecPre<IN_F32, GATE, D> &pf, RecSmem<IN_F32, GATE, D> &sm,
-                                            int tid) {
+__device__ __forceinline__ void block_store(const RecPre<IN_F32, GATE, D> &pf, RecSmem<GATE, D> &sm, int tid) {
   using PF = RecPre<IN_F32, GATE, D>;
   constexpr int ES = PF::ES;
-  constexpr int KRU = D * ES / 16;
+  constexpr int UE = 16 / ES;            // elements per unit
+  constexpr int KRU = D / UE;
 #pragma unroll
   for (int u = 0; u < PF::KU; ++u) {
     const int e = tid + 256 * u, row = e / KRU, c = e % KRU;
-    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.tk.kk[row][0]) + 16 * c) = getv(pf.k, u);
-    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.tk.qq[row][0]) + 16 * c) = getv(pf.q, u);
+    put_unit<IN_F32>(&sm.tk.kk[row][UE * c], getv(pf.k, u));
+    put_unit<IN_F32>(&sm.tk.qq[row][UE * c], getv(pf.q, u));
   }
-  constexpr int VRU = VB * ES / 16;
+  constexpr int VRU = VB / UE;
 #pragma unroll
   for (int u = 0; u < PF::VU; ++u) {
     const int e = tid + 256 * u, row = e / VRU, c = e % VRU;
-    if (e < TB * VRU) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&sm.vv[row][0]) + 16 * c) = getv(pf.v, u);
+    if (e < TB * VRU) put_unit<IN_F32>(&sm.vv[row][UE * c], getv(pf.v, u));
   }
   if constexpr (GATE == GDR_GATE_CHANNEL) {
     constexpr int GRU = D * 4 / 16;
@@ -183,14 +196,22 @@ __device__ __forceinline__ void block_store(const RecPre<IN_F32, GATE, D> &pf, R
   }
 }
 
+// One token's operands for one lane, read from LDS: its NK keys and queries,
+// its value, its gate (NK channel gates, or the scalar) and beta.
+template <int GATE, int NK>
+struct TokOps {
+  float k[NK], q[NK];
+  float g[GATE == GDR_GATE_CHANNEL ? NK : 1];
+  float v, beta;
+};
+
 template <bool IN_F32, int GATE, bool DELTA, bool L2, int D>
 __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
-  using SM = RecSmem<IN_F32, GATE, D>;
+  using SM = RecSmem<GATE, D>;
   using PF = RecPre<IN_F32, GATE, D>;
-  using In = typename SM::In;
+  using Ops = TokOps<GATE, D / KG>;
   constexpr int NK = D / KG;             // keys per lane
   constexpr int NVB = D / VB;
-  constexpr int ES = PF::ES;
   __shared__ SM sm;
   const int b = blockIdx.x;
   const int vb = b % NVB;
@@ -258,88 +279,87 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
     if (blk + 1 < nblk)
       block_load<IN_F32, GATE, DELTA, D>(pf, p, t0 + TB, (int)min<int64_t>(TB, eos - t0 - TB), h, hk, vb, tid);
 
-    for (int i = 0; i < L; ++i) {
-      float kx[NK], qx[NK];
-      if constexpr (IN_F32) {
+    // token i's operands from LDS (rows past L hold copies of row L - 1)
+    auto read = [&](int i, Ops &t) {
+#pragma unroll
+      for (int j = 0; j < NK; j += 4) {
+        const float4 a = *reinterpret_cast<const float4 *>(&sm.tk.kk[i][k0 + j]);
+        const float4 c = *reinterpret_cast<const float4 *>(&sm.tk.qq[i][k0 + j]);
+        t.k[j] = a.x; t.k[j + 1] = a.y; t.k[j + 2] = a.z; t.k[j + 3] = a.w;
+        t.q[j] = c.x; t.q[j + 1] = c.y; t.q[j + 2] = c.z; t.q[j + 3] = c.w;
+      }
+      if constexpr (GATE == GDR_GATE_CHANNEL) {
 #pragma unroll
         for (int j = 0; j < NK; j += 4) {
-          const float4 a = *reinterpret_cast<const float4 *>(&sm.tk.kk[i][k0 + j]);
-          const float4 c = *reinterpret_cast<const float4 *>(&sm.tk.qq[i][k0 + j]);
-          kx[j] = a.x; kx[j + 1] = a.y; kx[j + 2] = a.z; kx[j + 3] = a.w;
-          qx[j] = c.x; qx[j + 1] = c.y; qx[j + 2] = c.z; qx[j + 3] = c.w;
+          const float4 gv = *reinterpret_cast<const float4 *>(&sm.gg[i][k0 + j]);
+          t.g[j] = gv.x; t.g[j + 1] = gv.y; t.g[j + 2] = gv.z; t.g[j + 3] = gv.w;
         }
       } else {
-#pragma unroll
-        for (int j = 0; j < NK; j += 8) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(&sm.tk.kk[i][k0 + j]);
-          const uint4 c = *reinterpret_cast<const uint4 *>(&sm.tk.qq[i][k0 + j]);
-          const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            kx[j + 2 * m] = __uint_as_float(aw[m] << 16);
-            kx[j + 2 * m + 1] = __uint_as_float(aw[m] & 0xffff0000u);
-            qx[j + 2 * m] = __uint_as_float(cw[m] << 16);
-            qx[j + 2 * m + 1] = __uint_as_float(cw[m] & 0xffff0000u);
-          }
-        }
+        t.g[0] = sm.gg[i][0];
       }
-      const In vraw = sm.vv[i][vl];
-      float vval;
-      if constexpr (IN_F32) vval = vraw;
-      else vval = bf16_to_f32(vraw);
+      t.v = sm.vv[i][vl];
+      t.beta = DELTA ? sm.bb[i] : 0.f;
+    };
+    // one token of the recurrence on the lane's NK state entries
+    auto step = [&](int i, const Ops &t) {
       // L2 norms of k and q (as scalars on the reductions)
       float rk = 1.f, rq = 1.f;
       if constexpr (L2) {
         float a = 0.f, c = 0.f;
 #pragma unroll
         for (int j = 0; j < NK; ++j) {
-          a = fmaf(kx[j], kx[j], a);
-          c = fmaf(qx[j], qx[j], c);
+          a = fmaf(t.k[j], t.k[j], a);
+          c = fmaf(t.q[j], t.q[j], c);
         }
         rk = rsqrtf(sum8(a) + L2_EPS);
         rq = rsqrtf(sum8(c) + L2_EPS);
       }
       // 1. decay
       if constexpr (GATE == GDR_GATE_SCALAR) {
-        const float al = __expf(sm.gg[i][0]);
+        const float al = __expf(t.g[0]);
 #pragma unroll
         for (int j = 0; j < NK; ++j) s[j] *= al;
       } else if constexpr (GATE == GDR_GATE_CHANNEL) {
 #pragma unroll
-        for (int j = 0; j < NK; j += 4) {
-          const float4 gv = *reinterpret_cast<const float4 *>(&sm.gg[i][k0 + j]);
-          s[j] *= __expf(gv.x);
-          s[j + 1] *= __expf(gv.y);
-          s[j + 2] *= __expf(gv.z);
-          s[j + 3] *= __expf(gv.w);
-        }
+        for (int j = 0; j < NK; ++j) s[j] *= __expf(t.g[j]);
       }
       if constexpr (DELTA) {
         // 2-4. prediction from the decayed state, error, rank-one write
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int j = 0; j < NK; j += 2) {
-          a0 = fmaf(s[j], kx[j], a0);
-          a1 = fmaf(s[j + 1], kx[j + 1], a1);
+          a0 = fmaf(s[j], t.k[j], a0);
+          a1 = fmaf(s[j + 1], t.k[j + 1], a1);
         }
         const float vhat = sum8(a0 + a1) * rk;
-        const float e = sm.bb[i] * (vval - vhat) * rk;
+        const float e = t.beta * (t.v - vhat) * rk;
 #pragma unroll
-        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j]);
+        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, t.k[j], s[j]);
       } else {
-        const float e = vval * rk;
+        const float e = t.v * rk;
 #pragma unroll
-        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j]);
+        for (int j = 0; j < NK; ++j) s[j] = fmaf(e, t.k[j], s[j]);
       }
       // 5. read after the write
       float b0 = 0.f, b1 = 0.f;
 #pragma unroll
       for (int j = 0; j < NK; j += 2) {
-        b0 = fmaf(s[j], qx[j], b0);
-        b1 = fmaf(s[j + 1], qx[j + 1], b1);
+        b0 = fmaf(s[j], t.q[j], b0);
+        b1 = fmaf(s[j + 1], t.q[j + 1], b1);
       }
       const float o = sum8(b0 + b1) * (p.scale * rq);
       if (kg == 0) sm.oo[i][vl] = o;
+    };
+    // two operand sets in turn: token i + 1's LDS reads are in flight while
+    // token i computes
+    Ops ta, tb;
+    read(0, ta);
+    for (int i = 0; i < L; i += 2) {
+      read(min(i + 1, TB - 1), tb);
+      step(i, ta);
+      if (i + 1 == L) break;
+      read(min(i + 2, TB - 1), ta);
+      step(i + 1, tb);
     }
     __syncthreads();
     // the block's outputs, coalesced: row i, this workgroup's VB columns
