@@ -10,13 +10,15 @@ HBM. Three copies of the inputs/outputs are used in rotation so that no step
 reads what the previous one left in the 256 MB last-level cache. The decode
 path is timed alongside: 1000 consecutive gdr_recurrent_step launches over
 the 256-sequence decode workload, each step with a new token per sequence
-(64 distinct token sets in rotation; the state pool carries over).
+(64 distinct token sets in rotation; the state pool carries over). The
+ragged tokenwise recurrence (gdr_recurrent_fwd) is timed on 256 sequences of
+16 tokens over the same fp32 pool, with gdr_chunk_fwd on that batch beside it.
 
 Prints one JSON line. `value` is prefill tokens per second for one layer (all
 heads); `roofline` describes the prefill kernel against HBM bandwidth (its
 binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
 fraction alongside; `decode` gives steps/s and HBM fraction of the step
-kernel; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+kernel; `recurrent_fwd` the same for the tokenwise recurrence; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc")
 STEP_SRC = [os.path.join(CSRC, "recurrent_step.hip"), os.path.join(CSRC, "gdr_internal.h")]
+RECUR_SRC = [os.path.join(CSRC, "recurrent_fwd.hip"), os.path.join(CSRC, "gdr_internal.h")]
 
 
 def prefill_kernel(w: synth.Workload):
@@ -218,6 +221,38 @@ def bench_decode(w: synth.Workload, steps: int, warmup: int = 10):
     return wall / steps, e0.elapsed_time(e1) / steps
 
 
+def bench_recurrent_fwd(w: synth.Workload, steps: int, warmup: int = 5):
+    """Mean kernel time (ms) of gdr_recurrent_fwd and of gdr_chunk_fwd on the
+    same ragged batch, each call updating the pool in place."""
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    x = synth.generate(w)
+    a = dict(q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
+             v=_dev(x["v"], w.in_dtype, dev), g=_dev(x["g"], "f32", dev),
+             beta=_dev(x["beta"], "f32", dev), pool=_dev(x["pool"], w.state_dtype, dev),
+             slot_idx=_dev(x["slot_idx"], "i32", dev), cu_seqlens=_dev(x["cu_seqlens"], "i32", dev))
+    o = torch.empty((w.T_total, w.HV, w.DV), dtype=torch.float32, device=dev)
+    del x
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, fn in (("recurrent_fwd", gdr.recurrent_fwd), ("chunk_fwd", gdr.chunk_fwd)):
+        def run():
+            fn(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["slot_idx"],
+               a["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init, o=o)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / steps
+    return out
+
+
 # ----------------------------------------------------------------------------
 # CPU leg: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -271,6 +306,8 @@ def main():
     ap.add_argument("--workload", default=synth.HEADLINE)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--recurrent-steps", type=int, default=50)
+    ap.add_argument("--no-recurrent", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of a known size (scales the HBM "
@@ -345,6 +382,19 @@ def main():
             "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
             "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC)}
+    if not args.no_recurrent:
+        rw = synth.workload("short_prefill_n256_t16_hk16_hv32_d128")
+        t = bench_recurrent_fwd(rw, args.recurrent_steps)
+        rb = prefill_bytes(rw)
+        result["recurrent_fwd"] = {
+            "workload": rw.name, "steps": args.recurrent_steps,
+            "kernel_us": t["recurrent_fwd"] * 1e3,
+            "tokens_per_s": rw.T_total / (t["recurrent_fwd"] * 1e-3),
+            "algorithmic_bytes": rb,
+            "hbm_gbs": rb / (t["recurrent_fwd"] * 1e-3) / 1e9,
+            "hbm_frac": rb / (t["recurrent_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": committed_traffic("recurrent_fwd_kernel", rw.name, RECUR_SRC),
+            "chunk_fwd_kernel_us_same_batch": t["chunk_fwd"] * 1e3}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)

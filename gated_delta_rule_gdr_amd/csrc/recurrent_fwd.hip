@@ -13,7 +13,8 @@
 // normalised array is formed.
 //
 // Layout on gfx950: one workgroup of 256 threads per (sequence, value head,
-// 32 value columns). Lane (w, l) owns value column 8w + l / 8 of the block
+// 32 value columns), numbered so that all workgroups reading one key head of
+// one sequence share an XCD. Lane (w, l) owns value column 8w + l / 8 of the block
 // and key group l % 8 (D / 8 consecutive keys), so the state S^T[keys,
 // column] sits in D / 8 registers per lane. A reduction over the keys is the
 // sum over the 8 lanes of a column: three DPP steps inside an 8-lane group
@@ -213,12 +214,19 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
   constexpr int NK = D / KG;             // keys per lane
   constexpr int NVB = D / VB;
   __shared__ SM sm;
+  // Workgroups go round-robin over the 8 XCDs (each with its own L2). The
+  // ratio * NVB workgroups that read one key head of one sequence get ids
+  // equal modulo 8, so they run on one XCD and share those reads.
+  const int HK = p.HV / p.ratio;
+  const int GRP = p.ratio * NVB;                 // workgroups per (sequence, key head)
   const int b = blockIdx.x;
-  const int vb = b % NVB;
-  const int nh = b / NVB;
-  const int n = nh / p.HV;
-  const int h = nh - n * p.HV;
-  const int hk = h / p.ratio;
+  const int gi = (b / (8 * GRP)) * 8 + (b & 7);  // (sequence, key head) group
+  if (gi >= p.N * HK) return;                    // padding of the last XCD round
+  const int jg = (b >> 3) % GRP;
+  const int n = gi / HK;
+  const int hk = gi - n * HK;
+  const int h = hk * p.ratio + jg / NVB;
+  const int vb = jg % NVB;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int kg = lane & (KG - 1);
   const int vl = 8 * w + (lane >> 3);    // value column within the block
@@ -407,12 +415,12 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
 
 template <bool IN_F32, int GATE, bool DELTA, bool L2>
 hipError_t by_dim(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  // one XCD round covers 8 (sequence, key head) groups
+  const int blocks = ((a.N * a.HK + 7) / 8) * 8 * (a.HV / a.HK) * (a.DK / VB);
   if (a.DK == 128) {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 128>), dim3(a.N * a.HV * (128 / VB)),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 128>), dim3(blocks), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 64>), dim3(a.N * a.HV * (64 / VB)),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 64>), dim3(blocks), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -121,6 +121,13 @@ _reg(Workload(
     state_dtype="f32", num_slots=1, zero_init=True, seed=5,
     description="KDA long-context prefill, T=131072, H=32, d=128, per-key-channel gate"))
 
+_reg(Workload(
+    name="short_prefill_n256_t16_hk16_hv32_d128", seqlens=(16,) * 256, HK=16, HV=32, DK=128,
+    DV=128, in_dtype="bf16", gate="scalar", rule="delta", gate_shift=2.0,
+    state_dtype="f32", num_slots=256, zero_init=False, seed=6,
+    description="short ragged prefill over the decode pool: 256 sequences x 16 tokens, fp32 "
+                "pool [256,32,128,128] (the tokenwise schedule's case: state I/O dominates)"))
+
 # The prefill workload the throughput figure is quoted on.
 HEADLINE = "gdn_prefill_b4_t4096_h16_d128"
 

@@ -134,3 +134,26 @@ def test_kda_prefill_t131072_h32():
     o = run_prefill(gdr, w, d)
     assert torch.isfinite(o).all()
     check_sampled(w, x, o, d["pool"], [5])
+
+
+def test_short_prefill_n256_t16_recurrent_fwd():
+    """The tokenwise schedule on the benchmark's short-prefill batch (256
+    sequences of 16 tokens over the fp32 decode pool): two whole head groups
+    recomputed by the oracle for every sequence; the chunkwise prefill on the
+    same batch agrees with it."""
+    gdr = _gdr()
+    w = synth.workload("short_prefill_n256_t16_hk16_hv32_d128")
+    x = synth.generate(w)
+    d = to_device(w, x)
+    pool2 = d["pool"].clone()
+    print(f"launch {w.name} recurrent_fwd", flush=True)
+    o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                          d["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    check_sampled(w, x, o, d["pool"], [0, 1, 30, 31])
+    print(f"launch {w.name} chunk_fwd", flush=True)
+    o2 = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], pool2, d["slot_idx"],
+                       d["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init)
+    torch.cuda.synchronize()
+    check_out(host(o, "f32"), host(o2, "f32"), w.in_dtype)
