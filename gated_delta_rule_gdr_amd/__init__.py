@@ -39,6 +39,10 @@ FLAG_DEBUG_CHECKS = 2
 FLAG_QK_L2NORM = 4
 
 
+# GDR_ABI_VERSION of include/gdr.h that Args mirrors.
+ABI_VERSION = 3
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"gdr status {status}: {msg}")
@@ -64,6 +68,7 @@ class Args(ctypes.Structure):
         ("chunk_size", ctypes.c_int32),
         ("rule", ctypes.c_int), ("gate", ctypes.c_int),
         ("flags", ctypes.c_uint32),
+        ("products", ctypes.c_int32),
     ]
 
 
@@ -80,6 +85,9 @@ def load() -> ctypes.CDLL:
             f"{lib_path} is missing: build it with `python -m gated_delta_rule_gdr_amd.build`")
     L = ctypes.CDLL(lib_path)
     L.gdr_abi_version.restype = ctypes.c_int
+    if L.gdr_abi_version() != ABI_VERSION:
+        raise ImportError(f"{lib_path} has ABI {L.gdr_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}: rebuild it")
     L.gdr_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
     L.gdr_chunk_fwd.restype = ctypes.c_int
@@ -135,10 +143,13 @@ def _ptr(t) -> Optional[int]:
 
 
 def _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
-             zero_init, debug_checks, chunk_size, out_dtype):
+             zero_init, debug_checks, chunk_size, out_dtype, products=1):
     import torch
     T, HK, DK = q.shape
     HV, DV = v.shape[1], v.shape[2]
+    P = max(int(products), 1)
+    if k.shape[0] != T * P or v.shape[0] != T * P or (beta is not None and beta.shape[0] != T * P):
+        raise ValueError(f"k, v and beta need T * products = {T * P} rows (q has {T} tokens)")
     if gate is None:
         gate = "none" if g is None else ("channel" if g.dim() == 3 else "scalar")
     if scale is None:
@@ -182,6 +193,7 @@ def _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
     a.rule = _RULE[rule]
     a.gate = _GATE[gate]
     a.flags = (FLAG_ZERO_INIT if zero_init else 0) | (FLAG_DEBUG_CHECKS if debug_checks else 0)
+    a.products = P
     if tuple(pool.shape[1:]) != (HV, DK, DV):
         raise ValueError(f"pool must be [slots, {HV}, {DK}, {DV}], got {tuple(pool.shape)}")
     return a, o
@@ -194,7 +206,7 @@ def _stream(t):
 
 def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk_size=64,
               rule="delta", gate=None, out_dtype=None, zero_init=False, o=None,
-              debug_checks=False, workspace=None):
+              debug_checks=False, workspace=None, products=1):
     """Chunkwise prefill; returns o [T, HV, DV]; updates pool slots in place.
 
     ``workspace`` is an optional uint8 device tensor for the calls that need
@@ -204,7 +216,7 @@ def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
-                    zero_init, debug_checks, chunk_size, out_dtype)
+                    zero_init, debug_checks, chunk_size, out_dtype, products)
     L = load()
     if workspace is None:
         nbytes = L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a))
@@ -222,22 +234,23 @@ def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk
 
 def chunk_fwd_workspace_bytes(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None,
                               chunk_size=64, rule="delta", gate=None, out_dtype=None,
-                              zero_init=False):
+                              zero_init=False, products=1):
     """Preferred workspace size in bytes of the matching chunk_fwd call (0: none needed)."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     a, _ = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, None, scale, rule, gate,
-                    zero_init, False, chunk_size, out_dtype)
+                    zero_init, False, chunk_size, out_dtype, products)
     return int(load().gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)))
 
 
 def recurrent_step(q, k, v, g, beta, pool, slot_idx, *, scale=None, rule="delta", gate=None,
-                   out_dtype=None, zero_init=False, o=None, debug_checks=False):
-    """One token per sequence (q: [N, HK, DK]); returns o [N, HV, DV]."""
+                   out_dtype=None, zero_init=False, o=None, debug_checks=False, products=1):
+    """One token per sequence (q: [N, HK, DK]; k, v, beta: N * products rows);
+    returns o [N, HV, DV]."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     a, o = _prepare(q, k, v, g, beta, pool, slot_idx, None, o, scale, rule, gate,
-                    zero_init, debug_checks, 64, out_dtype)
+                    zero_init, debug_checks, 64, out_dtype, products)
     L = load()
     _check(L.gdr_recurrent_step(ctypes.byref(a), _stream(q)))
     return o
@@ -245,14 +258,14 @@ def recurrent_step(q, k, v, g, beta, pool, slot_idx, *, scale=None, rule="delta"
 
 def recurrent_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, rule="delta",
                   gate=None, out_dtype=None, zero_init=False, o=None, debug_checks=False,
-                  qk_l2norm=False):
+                  qk_l2norm=False, products=1):
     """Tokenwise recurrence over a ragged batch (the state on chip across each
     sequence); same results as chunk_fwd. qk_l2norm normalises q and k per
     token and key head inside the kernel. Returns o [T, HV, DV]."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
-                    zero_init, debug_checks, 64, out_dtype)
+                    zero_init, debug_checks, 64, out_dtype, products)
     if qk_l2norm:
         a.flags |= FLAG_QK_L2NORM
     L = load()

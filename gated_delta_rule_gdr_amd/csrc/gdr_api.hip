@@ -64,6 +64,8 @@ gdr_status validate(const gdr_args *a, Call call) {
   if ((a->flags & GDR_FLAG_QK_L2NORM) && call != Call::Recur)
     return fail(GDR_E_UNSUPPORTED, "GDR_FLAG_QK_L2NORM is taken by gdr_recurrent_fwd only");
   if (!std::isfinite(a->scale)) return fail(GDR_E_INVALID, "scale is not finite");
+  if (a->products < 0 || a->products > kMaxProducts)
+    return fail(GDR_E_INVALID, "products = %d: 0 .. %d transitions per token", a->products, kMaxProducts);
   if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK))
     return fail(GDR_E_UNSUPPORTED, "head dims DK = %d, DV = %d: built for DK = DV in {64, 128}", a->DK, a->DV);
   if (!prefill && a->T_total != a->N)
@@ -71,6 +73,9 @@ gdr_status validate(const gdr_args *a, Call call) {
                 (long long)a->T_total, a->N);
   if (call == Call::Chunk && a->chunk_size != 64)
     return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: built for 64", a->chunk_size);
+  if (call == Call::Chunk && products_of(*a) > 1)
+    return fail(GDR_E_UNSUPPORTED, "products = %d: the chunkwise prefill takes one transition per token "
+                "(gdr_recurrent_fwd takes more)", a->products);
   if (a->N == 0) return GDR_OK;  // nothing to do; pointers may be NULL
 
   if (!a->state_pool || !a->slot_idx) return fail(GDR_E_INVALID, "state_pool / slot_idx is NULL");
@@ -87,14 +92,15 @@ gdr_status validate(const gdr_args *a, Call call) {
                   (long long)a->q_stride_t, (long long)a->k_stride_t, (long long)a->v_stride_t,
                   (long long)kd, (long long)vd);
     const size_t ie = dtype_bytes(a->in_dtype);
+    const int64_t TP = a->T_total * products_of(*a);   // key / value / beta rows
     const Range ro = span(a->o, a->T_total, vd, vd, dtype_bytes(a->out_dtype));
     const Range ins[] = {
         span(a->q, a->T_total, a->q_stride_t, kd, ie),
-        span(a->k, a->T_total, a->k_stride_t, kd, ie),
-        span(a->v, a->T_total, a->v_stride_t, vd, ie),
+        span(a->k, TP, a->k_stride_t, kd, ie),
+        span(a->v, TP, a->v_stride_t, vd, ie),
         span(a->g, a->gate == GDR_GATE_NONE ? 0 : a->T_total, 1, 1,
              4 * (size_t)a->HV * (a->gate == GDR_GATE_CHANNEL ? a->DK : 1)),
-        span(a->beta, a->rule == GDR_RULE_DELTA ? a->T_total : 0, 1, 1, 4 * (size_t)a->HV),
+        span(a->beta, a->rule == GDR_RULE_DELTA ? TP : 0, 1, 1, 4 * (size_t)a->HV),
         span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV, dtype_bytes(a->state_dtype)),
     };
     for (const Range &r : ins)

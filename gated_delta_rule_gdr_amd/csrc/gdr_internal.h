@@ -31,6 +31,10 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// Transitions per token (Gated DeltaProduct's n_h; 0 in the arguments means 1).
+constexpr int kMaxProducts = 8;
+inline int products_of(const gdr_args &a) { return a.products > 1 ? a.products : 1; }
+
 // ---------------------------------------------------------------------------
 // launchers (defined next to their kernels)
 // ---------------------------------------------------------------------------

@@ -10,7 +10,10 @@
 //
 // optionally with k_t and q_t L2-normalised first (x / sqrt(|x|^2 + 1e-6)),
 // folded in as scalars on the reductions as the Mojo page describes, so no
-// normalised array is formed.
+// normalised array is formed. With n_h > 1 transitions per token (Gated
+// DeltaProduct, "Linear attention visualized") the kernel walks the substeps
+// (rows of k, v, beta) in order: a token's decay comes with its first
+// substep and its output after its last.
 //
 // Layout on gfx950: one workgroup of 256 threads per (sequence, value head,
 // 32 value columns), numbered so that all workgroups reading one key head of
@@ -62,6 +65,7 @@ struct RecParams {
   int32_t N, HV, ratio;
   float scale;
   int zero_init, st_bf16, out_bf16;
+  int32_t P;   // transitions per token: key, value and beta rows per q, g, o row
 };
 
 // Sum over the 8 lanes of a key-group set: every lane of the group gets it.
@@ -114,40 +118,42 @@ struct RecPre {
   float gs, beta;
 };
 
+// Rows m0 .. m0 + Lv - 1 of k, v and beta (substeps; tokens when P = 1) and
+// rows r0 .. r0 + Lq - 1 of q and g (tokens), each clamped to its last row.
 template <bool IN_F32, int GATE, bool DELTA, int D>
-__device__ __forceinline__ void block_load(RecPre<IN_F32, GATE, D> &pf, const RecParams &p, int64_t t0,
-                                           int L, int h, int hk, int vb, int tid) {
+__device__ __forceinline__ void block_load(RecPre<IN_F32, GATE, D> &pf, const RecParams &p, int64_t m0,
+                                           int Lv, int64_t r0, int Lq, int h, int hk, int vb, int tid) {
   using PF = RecPre<IN_F32, GATE, D>;
   constexpr int ES = PF::ES;
   constexpr int KRU = D * ES / 16;       // units per key row
-  const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * ES;
-  const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * ES;
+  const char *kb = static_cast<const char *>(p.k) + (m0 * p.k_stride + (int64_t)hk * D) * ES;
+  const char *qb = static_cast<const char *>(p.q) + (r0 * p.q_stride + (int64_t)hk * D) * ES;
 #pragma unroll
   for (int u = 0; u < PF::KU; ++u) {
-    const int e = tid + 256 * u, row = min(e / KRU, L - 1), c = e % KRU;
-    putv(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (int64_t)row * p.k_stride * ES + 16 * c));
-    putv(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (int64_t)row * p.q_stride * ES + 16 * c));
+    const int e = tid + 256 * u, c = e % KRU;
+    const int kr = min(e / KRU, Lv - 1), qr = min(e / KRU, Lq - 1);
+    putv(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (int64_t)kr * p.k_stride * ES + 16 * c));
+    putv(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (int64_t)qr * p.q_stride * ES + 16 * c));
   }
   constexpr int VRU = VB * ES / 16;      // units per value row
-  const char *vbp = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * VB) * ES;
+  const char *vbp = static_cast<const char *>(p.v) + (m0 * p.v_stride + (int64_t)h * D + vb * VB) * ES;
 #pragma unroll
   for (int u = 0; u < PF::VU; ++u) {
-    const int e = tid + 256 * u, row = min(e / VRU, L - 1), c = e % VRU;
+    const int e = tid + 256 * u, row = min(e / VRU, Lv - 1), c = e % VRU;
     if (e < TB * VRU) putv(pf.v, u, *reinterpret_cast<const uint4 *>(vbp + (int64_t)row * p.v_stride * ES + 16 * c));
   }
   if constexpr (GATE == GDR_GATE_CHANNEL) {
     constexpr int GRU = D * 4 / 16;
-    const float *gb = p.g + (t0 * p.HV + h) * (int64_t)D;
+    const float *gb = p.g + (r0 * p.HV + h) * (int64_t)D;
 #pragma unroll
     for (int u = 0; u < PF::GU; ++u) {
-      const int e = tid + 256 * u, row = min(e / GRU, L - 1), c = e % GRU;
+      const int e = tid + 256 * u, row = min(e / GRU, Lq - 1), c = e % GRU;
       putv(pf.g, u, *reinterpret_cast<const uint4 *>(gb + (int64_t)row * p.HV * D + 4 * c));
     }
   }
   if (tid < TB) {
-    const int64_t t = t0 + min(tid, L - 1);
-    pf.gs = GATE == GDR_GATE_SCALAR ? p.g[t * p.HV + h] : 0.f;
-    pf.beta = DELTA ? p.beta[t * p.HV + h] : 0.f;
+    pf.gs = GATE == GDR_GATE_SCALAR ? p.g[(r0 + min(tid, Lq - 1)) * p.HV + h] : 0.f;
+    pf.beta = DELTA ? p.beta[(m0 + min(tid, Lv - 1)) * p.HV + h] : 0.f;
   }
 }
 
@@ -206,7 +212,9 @@ struct TokOps {
   float v, beta;
 };
 
-template <bool IN_F32, int GATE, bool DELTA, bool L2, int D>
+// PROD: more than one transition per token (P > 1); without it every
+// substep is a token and the substep bookkeeping compiles away.
+template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD, int D>
 __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
   using SM = RecSmem<GATE, D>;
   using PF = RecPre<IN_F32, GATE, D>;
@@ -273,43 +281,53 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
     for (int j = 0; j < NK; ++j) s[j] = sm.st[k0 + j][vl];
   }
 
+  // Blocks run over substeps: sequence n's token t has substeps t*P .. t*P+P-1
+  // (rows of k, v, beta); q, g and o have one row per token.
+  const int P = PROD ? p.P : 1;
   const int64_t HVD = (int64_t)p.HV * D;
-  const int64_t len = eos - bos;
-  const int nblk = (int)((len + TB - 1) / TB);
+  const int64_t bosv = bos * P, eosv = eos * P;
+  const int nblk = (int)((eosv - bosv + TB - 1) / TB);
   PF pf;
-  block_load<IN_F32, GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(TB, len), h, hk, vb, tid);
+  auto load_block = [&](int64_t m0) {
+    const int64_t r0 = m0 / P;
+    block_load<IN_F32, GATE, DELTA, D>(pf, p, m0, (int)min<int64_t>(TB, eosv - m0), r0,
+                                       (int)min<int64_t>(TB, eos - r0), h, hk, vb, tid);
+  };
+  load_block(bosv);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int64_t t0 = bos + (int64_t)blk * TB;
-    const int L = (int)min<int64_t>(TB, eos - t0);
+    const int64_t m0 = bosv + (int64_t)blk * TB;   // first substep of the block
+    const int64_t r0 = m0 / P;                      // its token: row 0 of q, g, o
+    const int L = (int)min<int64_t>(TB, eosv - m0);
     __syncthreads();   // the previous block (or the state tile) is consumed
     block_store<IN_F32, GATE, DELTA, D>(pf, sm, tid);
     __syncthreads();
-    if (blk + 1 < nblk)
-      block_load<IN_F32, GATE, DELTA, D>(pf, p, t0 + TB, (int)min<int64_t>(TB, eos - t0 - TB), h, hk, vb, tid);
+    if (blk + 1 < nblk) load_block(m0 + TB);
 
-    // token i's operands from LDS (rows past L hold copies of row L - 1)
-    auto read = [&](int i, Ops &t) {
+    // operands of substep i (k, v, beta row i) of token row r (q, g row r);
+    // rows past the block's end hold copies of its last row
+    auto read = [&](int i, int r, Ops &t) {
 #pragma unroll
       for (int j = 0; j < NK; j += 4) {
         const float4 a = *reinterpret_cast<const float4 *>(&sm.tk.kk[i][k0 + j]);
-        const float4 c = *reinterpret_cast<const float4 *>(&sm.tk.qq[i][k0 + j]);
+        const float4 c = *reinterpret_cast<const float4 *>(&sm.tk.qq[r][k0 + j]);
         t.k[j] = a.x; t.k[j + 1] = a.y; t.k[j + 2] = a.z; t.k[j + 3] = a.w;
         t.q[j] = c.x; t.q[j + 1] = c.y; t.q[j + 2] = c.z; t.q[j + 3] = c.w;
       }
       if constexpr (GATE == GDR_GATE_CHANNEL) {
 #pragma unroll
         for (int j = 0; j < NK; j += 4) {
-          const float4 gv = *reinterpret_cast<const float4 *>(&sm.gg[i][k0 + j]);
+          const float4 gv = *reinterpret_cast<const float4 *>(&sm.gg[r][k0 + j]);
           t.g[j] = gv.x; t.g[j + 1] = gv.y; t.g[j + 2] = gv.z; t.g[j + 3] = gv.w;
         }
       } else {
-        t.g[0] = sm.gg[i][0];
+        t.g[0] = sm.gg[r][0];
       }
       t.v = sm.vv[i][vl];
       t.beta = DELTA ? sm.bb[i] : 0.f;
     };
-    // one token of the recurrence on the lane's NK state entries
-    auto step = [&](int i, const Ops &t) {
+    // one substep of the recurrence on the lane's NK state entries: the
+    // token's decay on its first substep (js == 0), its output on its last
+    auto step = [&](int js, int r, const Ops &t) {
       // L2 norms of k and q (as scalars on the reductions)
       float rk = 1.f, rq = 1.f;
       if constexpr (L2) {
@@ -323,13 +341,15 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
         rq = rsqrtf(sum8(c) + L2_EPS);
       }
       // 1. decay
-      if constexpr (GATE == GDR_GATE_SCALAR) {
-        const float al = __expf(t.g[0]);
+      if (!PROD || js == 0) {
+        if constexpr (GATE == GDR_GATE_SCALAR) {
+          const float al = __expf(t.g[0]);
 #pragma unroll
-        for (int j = 0; j < NK; ++j) s[j] *= al;
-      } else if constexpr (GATE == GDR_GATE_CHANNEL) {
+          for (int j = 0; j < NK; ++j) s[j] *= al;
+        } else if constexpr (GATE == GDR_GATE_CHANNEL) {
 #pragma unroll
-        for (int j = 0; j < NK; ++j) s[j] *= __expf(t.g[j]);
+          for (int j = 0; j < NK; ++j) s[j] *= __expf(t.g[j]);
+        }
       }
       if constexpr (DELTA) {
         // 2-4. prediction from the decayed state, error, rank-one write
@@ -348,33 +368,52 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
 #pragma unroll
         for (int j = 0; j < NK; ++j) s[j] = fmaf(e, t.k[j], s[j]);
       }
-      // 5. read after the write
-      float b0 = 0.f, b1 = 0.f;
+      // 5. read after the write (after the token's last substep)
+      if (!PROD || js == P - 1) {
+        float b0 = 0.f, b1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < NK; j += 2) {
-        b0 = fmaf(s[j], t.q[j], b0);
-        b1 = fmaf(s[j + 1], t.q[j + 1], b1);
+        for (int j = 0; j < NK; j += 2) {
+          b0 = fmaf(s[j], t.q[j], b0);
+          b1 = fmaf(s[j + 1], t.q[j + 1], b1);
+        }
+        const float o = sum8(b0 + b1) * (p.scale * rq);
+        if (kg == 0) sm.oo[r][vl] = o;
       }
-      const float o = sum8(b0 + b1) * (p.scale * rq);
-      if (kg == 0) sm.oo[i][vl] = o;
     };
-    // two operand sets in turn: token i + 1's LDS reads are in flight while
-    // token i computes
+    // two operand sets in turn: substep i + 1's LDS reads are in flight while
+    // substep i computes. (js, r): substep within its token, token row.
+    auto next = [&](int &js, int &r) {
+      if (!PROD) {
+        ++r;
+      } else if (++js == P) {
+        js = 0;
+        ++r;
+      }
+    };
+    int js = (int)(m0 - r0 * P), r = 0;
     Ops ta, tb;
-    read(0, ta);
+    read(0, 0, ta);
     for (int i = 0; i < L; i += 2) {
-      read(min(i + 1, TB - 1), tb);
-      step(i, ta);
+      int js1 = js, r1 = r;
+      next(js1, r1);
+      read(min(i + 1, TB - 1), min(r1, TB - 1), tb);
+      step(js, r, ta);
       if (i + 1 == L) break;
-      read(min(i + 2, TB - 1), ta);
-      step(i + 1, tb);
+      int js2 = js1, r2 = r1;
+      next(js2, r2);
+      read(min(i + 2, TB - 1), min(r2, TB - 1), ta);
+      step(js1, r1, tb);
+      js = js2;
+      r = r2;
     }
     __syncthreads();
-    // the block's outputs, coalesced: row i, this workgroup's VB columns
+    // the block's outputs, coalesced: the tokens whose last substep is in
+    // this block, rows r0 .. (m0 + L) / P - 1, this workgroup's VB columns
     const int ow = p.out_bf16 ? 2 : 4;
     const int ORU = VB * ow / 16;
-    char *ob = static_cast<char *>(p.o) + (t0 * HVD + (int64_t)h * D + vb * VB) * ow;
-    for (int e = tid; e < L * ORU; e += 256) {
+    const int Lo = (int)((m0 + L) / P - r0);
+    char *ob = static_cast<char *>(p.o) + (r0 * HVD + (int64_t)h * D + vb * VB) * ow;
+    for (int e = tid; e < Lo * ORU; e += 256) {
       const int row = e / ORU, c0 = (e % ORU) * (16 / ow);
       uint4 x;
       if (p.out_bf16) {
@@ -413,22 +452,28 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
   }
 }
 
-template <bool IN_F32, int GATE, bool DELTA, bool L2>
+template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD>
 hipError_t by_dim(const gdr_args &a, const RecParams &p, hipStream_t st) {
   // one XCD round covers 8 (sequence, key head) groups
   const int blocks = ((a.N * a.HK + 7) / 8) * 8 * (a.HV / a.HK) * (a.DK / VB);
   if (a.DK == 128) {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 128>), dim3(blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, 128>), dim3(blocks), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, 64>), dim3(blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, 64>), dim3(blocks), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }
 
+template <bool IN_F32, int GATE, bool DELTA, bool L2>
+hipError_t by_prod(const gdr_args &a, const RecParams &p, hipStream_t st) {
+  if (p.P > 1) return by_dim<IN_F32, GATE, DELTA, L2, true>(a, p, st);
+  return by_dim<IN_F32, GATE, DELTA, L2, false>(a, p, st);
+}
+
 template <bool IN_F32, int GATE, bool DELTA>
 hipError_t by_norm(const gdr_args &a, const RecParams &p, hipStream_t st) {
-  if (a.flags & GDR_FLAG_QK_L2NORM) return by_dim<IN_F32, GATE, DELTA, true>(a, p, st);
-  return by_dim<IN_F32, GATE, DELTA, false>(a, p, st);
+  if (a.flags & GDR_FLAG_QK_L2NORM) return by_prod<IN_F32, GATE, DELTA, true>(a, p, st);
+  return by_prod<IN_F32, GATE, DELTA, false>(a, p, st);
 }
 
 template <bool IN_F32, int GATE>
@@ -455,6 +500,7 @@ hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream) {
   p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;
   p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
   p.N = a.N; p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.P = products_of(a);
   p.scale = a.scale;
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   p.st_bf16 = a.state_dtype == GDR_BF16;

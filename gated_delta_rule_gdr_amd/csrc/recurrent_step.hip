@@ -6,7 +6,10 @@
 // "gated_delta" Mojo page lists them, the KDA page boxes them in sections 3
 // and 4) and writes the state back in place. The step is a pure HBM
 // read-modify-write of the state: 2 * DK * DV * sizeof(state) bytes per
-// (sequence, head) against ~6 DK DV flops.
+// (sequence, head) against ~6 DK DV flops. With n_h > 1 transitions per token
+// (Gated DeltaProduct, "Linear attention visualized") the decay is applied
+// once and steps 2-4 repeat for each substep's key, value and beta before the
+// read.
 //
 // Thread layout (TPB threads): thread t owns value elements 4*jq .. 4*jq+3
 // (jq = t % (DV/4)) for key rows kg*KP .. kg*KP+KP-1 (kg = t / (DV/4)). A
@@ -30,6 +33,7 @@ struct StepParams {
   int32_t HV, ratio;  // ratio = HV / HK
   float scale;
   int zero_init;
+  int32_t products;   // transitions per token (rows of k, v, beta per token)
 };
 
 template <bool BF16>
@@ -82,14 +86,19 @@ __device__ __forceinline__ void reduce_over_k(float (&x)[4], float *buf) {
   x[0] = s.x; x[1] = s.y; x[2] = s.z; x[3] = s.w;
 }
 
-template <bool IN_BF16, bool ST_BF16, bool OUT_BF16, int GATE, int RULE, int DK, int DV, int TPB>
+// PROD: more than one transition per token (Gated DeltaProduct's substeps).
+template <bool IN_BF16, bool ST_BF16, bool OUT_BF16, int GATE, int RULE, bool PROD, int DK, int DV, int TPB>
 __global__ __launch_bounds__(TPB) void recurrent_step_kernel(StepParams p) {
   constexpr int QUADS = DV / 4;       // lanes across one key row
   constexpr int KG = TPB / QUADS;     // key-row groups
   constexpr int KP = DK / KG;         // key rows per thread
   constexpr int NW = TPB / 64;        // waves
   static_assert(KP >= 1 && DK % KG == 0 && QUADS <= 64, "head dims");
-  __shared__ float4 red[2][NW * QUADS];
+  // reductions of the substeps' predictions alternate between red[0] and
+  // red[1] (a buffer is rewritten only after every thread has passed the
+  // barrier that follows its last read); the last buffer takes the output's
+  constexpr int NRED = PROD ? 3 : 2;
+  __shared__ float4 red[NRED][NW * QUADS];
 
   const int n = blockIdx.x / p.HV;
   const int h = blockIdx.x - n * p.HV;
@@ -126,20 +135,22 @@ __global__ __launch_bounds__(TPB) void recurrent_step_kernel(StepParams p) {
     }
   }
 
-  // ---- token inputs ----
+  // ---- token inputs (substep 0's key, value and beta) ----
+  const int P = PROD ? p.products : 1;
   float kv[KP], qv[KP];
   const int64_t qoff = n * p.q_stride + (int64_t)hk * DK + k0;
-  const int64_t koff = n * p.k_stride + (int64_t)hk * DK + k0;
+  const int64_t koff = (int64_t)n * P * p.k_stride + (int64_t)hk * DK + k0;
 #pragma unroll
   for (int r = 0; r < KP; ++r) {
     kv[r] = ld_in<IN_BF16>(p.k, koff + r);
     qv[r] = ld_in<IN_BF16>(p.q, qoff + r);
   }
   float vv[4];
-  const int64_t voff = n * p.v_stride + (int64_t)h * DV + 4 * jq;
+  const int64_t voff = (int64_t)n * P * p.v_stride + (int64_t)h * DV + 4 * jq;
 #pragma unroll
   for (int j = 0; j < 4; ++j) vv[j] = ld_in<IN_BF16>(p.v, voff + j);
   const int64_t th = (int64_t)n * p.HV + h;
+  float bv = RULE == GDR_RULE_DELTA ? p.beta[(int64_t)n * P * p.HV + h] : 0.f;
 
   // ---- 1. decay ----
   if constexpr (GATE == GDR_GATE_SCALAR) {
@@ -158,27 +169,37 @@ __global__ __launch_bounds__(TPB) void recurrent_step_kernel(StepParams p) {
     }
   }
 
-  // ---- 2-4. predict, correct, write ----
-  if constexpr (RULE == GDR_RULE_DELTA) {
-    float vh[4] = {0.f, 0.f, 0.f, 0.f};
+  // ---- 2-4. predict, correct, write: once per substep, in order (with
+  // more than one, Gated DeltaProduct's transitions of one token) ----
+  for (int sub = 0;;) {
+    if constexpr (RULE == GDR_RULE_DELTA) {
+      float vh[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < KP; ++r)
+      for (int r = 0; r < KP; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vh[j] += s[r][j] * kv[r];
-    reduce_over_k<QUADS, NW>(vh, reinterpret_cast<float *>(red[0]));
-    const float b = p.beta[th];
-    float e[4];
+        for (int j = 0; j < 4; ++j) vh[j] += s[r][j] * kv[r];
+      reduce_over_k<QUADS, NW>(vh, reinterpret_cast<float *>(red[sub & 1]));
+      float e[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) e[j] = b * (vv[j] - vh[j]);
+      for (int j = 0; j < 4; ++j) e[j] = bv * (vv[j] - vh[j]);
 #pragma unroll
-    for (int r = 0; r < KP; ++r)
+      for (int r = 0; r < KP; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[r][j] += kv[r] * e[j];
-  } else {
+        for (int j = 0; j < 4; ++j) s[r][j] += kv[r] * e[j];
+    } else {
 #pragma unroll
-    for (int r = 0; r < KP; ++r)
+      for (int r = 0; r < KP; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[r][j] += kv[r] * vv[j];
+        for (int j = 0; j < 4; ++j) s[r][j] += kv[r] * vv[j];
+    }
+    if (!PROD || ++sub == P) break;
+    // the next substep's key, value and beta (row n * P + sub)
+    const int64_t m = (int64_t)n * P + sub;
+#pragma unroll
+    for (int r = 0; r < KP; ++r) kv[r] = ld_in<IN_BF16>(p.k, m * p.k_stride + (int64_t)hk * DK + k0 + r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = ld_in<IN_BF16>(p.v, m * p.v_stride + (int64_t)h * DV + 4 * jq + j);
+    if constexpr (RULE == GDR_RULE_DELTA) bv = p.beta[m * p.HV + h];
   }
 
   // ---- write the state back (in place) ----
@@ -204,7 +225,7 @@ __global__ __launch_bounds__(TPB) void recurrent_step_kernel(StepParams p) {
   for (int r = 0; r < KP; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ov[j] += s[r][j] * qv[r];
-  reduce_over_k<QUADS, NW>(ov, reinterpret_cast<float *>(red[1]));
+  reduce_over_k<QUADS, NW>(ov, reinterpret_cast<float *>(red[NRED - 1]));
   if (kg == 0) {
     const int64_t ooff = th * DV + 4 * jq;
     if constexpr (OUT_BF16) {
@@ -225,8 +246,12 @@ constexpr int STEP_TPB = 1024;
 
 template <bool IN_BF16, bool ST_BF16, bool OUT_BF16, int GATE, int RULE, int D>
 hipError_t launch_t(const StepParams &p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((recurrent_step_kernel<IN_BF16, ST_BF16, OUT_BF16, GATE, RULE, D, D, STEP_TPB>),
-                     dim3(blocks), dim3(STEP_TPB), 0, stream, p);
+  if (p.products > 1)
+    hipLaunchKernelGGL((recurrent_step_kernel<IN_BF16, ST_BF16, OUT_BF16, GATE, RULE, true, D, D, STEP_TPB>),
+                       dim3(blocks), dim3(STEP_TPB), 0, stream, p);
+  else
+    hipLaunchKernelGGL((recurrent_step_kernel<IN_BF16, ST_BF16, OUT_BF16, GATE, RULE, false, D, D, STEP_TPB>),
+                       dim3(blocks), dim3(STEP_TPB), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -272,6 +297,7 @@ hipError_t launch_recurrent_step(const gdr_args &a, hipStream_t stream) {
   p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;
   p.slot_idx = a.slot_idx;
   p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.products = products_of(a);
   p.scale = a.scale;
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   const int blocks = a.N * a.HV;

@@ -27,12 +27,14 @@
  * Work is enqueued on `stream` and runs asynchronously: outputs and the state
  * pool are ready once the stream has reached that point.
  *
- * Layouts (elements, row-major):
- *   q, k        [T_total, HK, DK]   token t starts at t * {q,k}_stride_t; the
+ * Layouts (elements, row-major; P = products, 1 unless Gated DeltaProduct):
+ *   q           [T_total, HK, DK]   token t starts at t * q_stride_t; the
  *                                   HK*DK values of one token are contiguous
- *   v           [T_total, HV, DV]   token t starts at t * v_stride_t
+ *   k           [T_total*P, HK, DK] row t*P + j (substep j of token t) starts
+ *                                   at (t*P + j) * k_stride_t
+ *   v           [T_total*P, HV, DV] row t*P + j starts at (t*P + j) * v_stride_t
  *   g           [T_total, HV] (SCALAR) or [T_total, HV, DK] (CHANNEL), fp32
- *   beta        [T_total, HV] fp32, in (0, 1]
+ *   beta        [T_total*P, HV] fp32, in (0, 1]
  *   o           [T_total, HV, DV]   contiguous, written (never read)
  *   state_pool  [num_slots, HV, DK, DV]: S^T per slot and value head, updated
  *               in place for the slots named by slot_idx; other slots are
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -120,6 +122,12 @@ typedef struct gdr_args {
   gdr_rule rule;
   gdr_gate gate;
   uint32_t flags;               /* GDR_FLAG_*                                              */
+  int32_t products;             /* Gated DeltaProduct: n_h transitions per token, 1..8;    */
+                                /* 0 means 1. Token t decays once, then applies the delta  */
+                                /* (or linear) write of each substep j = 0..P-1 in order   */
+                                /* with key, value and beta row t*P + j, then q_t reads    */
+                                /* the state ("Linear attention visualized", section       */
+                                /* "Gated Delta Product (GDP)")                            */
 } gdr_args;
 
 /* GDR_ABI_VERSION of the loaded library. */

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == 2
+    assert L.gdr_abi_version() == gdr.ABI_VERSION == 3
 
 
 def test_args_struct_matches_header_field_order():
@@ -99,6 +99,8 @@ CASES = [
     ("misaligned q", dict(q=0x1008), 1),
     ("misaligned g", dict(g=0x2004), 1),
     ("misaligned pool", dict(state_pool=0x4000008), 1),
+    ("negative products", dict(products=-1), 1),
+    ("too many products", dict(products=9), 1),
     ("stride not 16 bytes", dict(k_stride_t=2 * 128 + 4), 1),
 ]
 
@@ -186,3 +188,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(gdr, "_lib", None)
     with pytest.raises(ImportError):
         gdr.load()
+
+
+def test_binding_checks_product_rows():
+    """k, v and beta must carry T * products rows (checked before any call)."""
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    T, P = 4, 2
+    q = torch.zeros(T, 1, 64)
+    k = torch.zeros(T, 1, 64)
+    v = torch.zeros(T * P, 1, 64)
+    beta = torch.zeros(T * P, 1)
+    pool = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError, match="T \\* products"):
+        gdr.recurrent_fwd(q, k, v, None, beta, pool, torch.zeros(1, dtype=torch.int32),
+                          torch.tensor([0, T], dtype=torch.int32), gate="none", products=P)

@@ -1,0 +1,154 @@
+"""GPU parity of Gated DeltaProduct ("Linear attention visualized", section
+"Gated Delta Product (GDP)": n_h transitions per token, the decay once before
+the first, the query after the last) in the tokenwise kernels, against the
+fp64 oracle's delta_product_fp64."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import check_out, check_state, dev, host, widened
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+RAGGED = (0, 1, 11, 40, 7)
+
+
+def _gdr():
+    import gated_delta_rule_gdr_amd as gdr
+    gdr.load()
+    return gdr
+
+
+def product_inputs(w, P):
+    """Seeded inputs: q, g, pool, slots, cu_seqlens per real token from w;
+    k, v, beta with P rows per token from the same recipe at P times the
+    lengths (another seed)."""
+    xr = synth.generate(w)
+    xv = synth.generate(w.replace(seqlens=tuple(P * n for n in w.seqlens), seed=w.seed + 1000))
+    x = dict(xr)
+    x["k"], x["v"], x["beta"] = xv["k"], xv["v"], xv["beta"]
+    return x
+
+
+def to_dev(w, x):
+    return {
+        "q": dev(x["q"], w.in_dtype), "k": dev(x["k"], w.in_dtype), "v": dev(x["v"], w.in_dtype),
+        "g": dev(x["g"], "f32"), "beta": dev(x["beta"], "f32"),
+        "pool": dev(x["pool"], w.state_dtype), "slot_idx": dev(x["slot_idx"], "i32"),
+        "cu_seqlens": dev(x["cu_seqlens"], "i32"),
+    }
+
+
+def reference(w, x, P, scale, l2=False):
+    xw = widened(w, x)
+    if l2:
+        xw["q"] = oracle.l2_normalise_fp64(xw["q"])
+        xw["k"] = oracle.l2_normalise_fp64(xw["k"])
+    return oracle.delta_product_fp64(
+        xw["q"], xw["k"], xw["v"], xw["g"], xw["beta"], xw["pool"], x["slot_idx"],
+        x["cu_seqlens"], products=P, scale=scale, rule=w.rule, gate=w.gate,
+        zero_init=w.zero_init, state_dtype=w.state_dtype)
+
+
+def small(D, in_dtype, gate, rule, state_dtype="f32", seqlens=RAGGED, seed=61):
+    return synth.Workload(
+        name="small", seqlens=tuple(seqlens), HK=2, HV=4, DK=D, DV=D, in_dtype=in_dtype,
+        gate=gate, rule=rule, gate_shift=2.0 if gate != "channel" else 3.0,
+        state_dtype=state_dtype, num_slots=7, zero_init=False, seed=seed)
+
+
+COMBOS = [(P, D, i, g, r) for P, D, i, g, r in itertools.product(
+    [2, 3], [64, 128], ["bf16", "f32"], ["none", "scalar", "channel"], ["delta", "linear"])
+    if not (r == "linear" and g == "none" and P == 3)]
+
+
+@pytest.mark.parametrize("P,D,in_dtype,gate,rule", COMBOS,
+                         ids=[f"p{P}-d{D}-{i}-{g}-{r}" for P, D, i, g, r in COMBOS])
+def test_recurrent_fwd_products_match_oracle(P, D, in_dtype, gate, rule):
+    gdr = _gdr()
+    state_dtype = "bf16" if (D == 128 and gate == "scalar") else "f32"
+    w = small(D, in_dtype, gate, rule, state_dtype)
+    x = product_inputs(w, P)
+    d = to_dev(w, x)
+    before = d["pool"].clone()
+    print(f"recurrent_fwd products={P} D={D} in={in_dtype} gate={gate} rule={rule}", flush=True)
+    o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"] if rule == "delta" else None,
+                          d["pool"], d["slot_idx"], d["cu_seqlens"], scale=D ** -0.5, rule=rule,
+                          gate=gate, products=P)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = reference(w, x, P, D ** -0.5)
+    check_out(host(o, in_dtype), o_ref, in_dtype)
+    pool = host(d["pool"], state_dtype)
+    for s in x["slot_idx"]:
+        check_state(pool[s], pool_ref[s], in_dtype, state_dtype)
+    untouched = np.setdiff1d(np.arange(w.num_slots), x["slot_idx"])
+    assert torch.equal(d["pool"][untouched], before[untouched])
+
+
+@pytest.mark.parametrize("P", [2, 4])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_recurrent_step_products_match_oracle(P, gate):
+    """Six chained decode steps, each token with P transitions."""
+    gdr = _gdr()
+    steps = 6
+    w = synth.Workload(name="dec", seqlens=(1,) * 5, HK=2, HV=4, DK=128, DV=128, in_dtype="bf16",
+                       gate=gate, rule="delta", gate_shift=2.0, state_dtype="f32", num_slots=8,
+                       zero_init=False, steps=steps, seed=71)
+    x = product_inputs(w, P)
+    d = to_dev(w, x)
+    xw = widened(w, x)
+    N = w.N
+    pool_ref = xw["pool"]
+    print(f"recurrent_step products={P} gate={gate}", flush=True)
+    for s in range(steps):
+        sq, sk = slice(s * N, (s + 1) * N), slice(s * N * P, (s + 1) * N * P)
+        o = gdr.recurrent_step(d["q"][sq], d["k"][sk], d["v"][sk], d["g"][sq], d["beta"][sk],
+                               d["pool"], d["slot_idx"], products=P)
+        torch.cuda.synchronize()
+        o_ref, pool_ref = oracle.delta_product_fp64(
+            xw["q"][sq], xw["k"][sk], xw["v"][sk], xw["g"][sq], xw["beta"][sk], pool_ref,
+            x["slot_idx"], np.arange(N + 1), products=P, scale=128 ** -0.5, gate=gate,
+            state_dtype="f64")
+        check_out(host(o, "f32"), o_ref, "bf16")
+    pool = host(d["pool"], "f32")
+    for sl in x["slot_idx"]:
+        check_state(pool[sl], pool_ref[sl], "bf16", "f32")
+
+
+def test_recurrent_fwd_products_with_l2norm():
+    gdr = _gdr()
+    P = 2
+    w = small(128, "bf16", "scalar", "delta", seqlens=(9, 33, 0), seed=63)
+    x = product_inputs(w, P)
+    rng = np.random.default_rng(5)
+    for name in ("q", "k"):
+        raw = synth.widen(x[name], "bf16") * rng.uniform(0.3, 4.0, size=x[name].shape[:2] + (1,))
+        x[name] = synth.f64_to_bf16_bits(raw)
+    d = to_dev(w, x)
+    o = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                          d["cu_seqlens"], products=P, qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = reference(w, x, P, 128 ** -0.5, l2=True)
+    check_out(host(o, "bf16"), o_ref, "bf16")
+    for s in x["slot_idx"]:
+        check_state(host(d["pool"], "f32")[s], pool_ref[s], "bf16", "f32")
+
+
+def test_one_product_is_the_plain_recurrence():
+    """products=1 is bit-identical to the call without it."""
+    gdr = _gdr()
+    w = small(128, "bf16", "scalar", "delta", seqlens=(50, 3))
+    x = synth.generate(w)
+    d = to_dev(w, x)
+    p2 = d["pool"].clone()
+    o1 = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                           d["cu_seqlens"])
+    o2 = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], p2, d["slot_idx"],
+                           d["cu_seqlens"], products=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(d["pool"], p2)
