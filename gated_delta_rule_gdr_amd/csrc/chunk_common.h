@@ -26,6 +26,7 @@ struct ChunkParams {
   int32_t N, HK, HV, ratio;
   float scale;
   int zero_init, st_bf16, out_bf16;
+  int32_t P;   // transitions per token (Gated DeltaProduct substeps); 1 otherwise
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {

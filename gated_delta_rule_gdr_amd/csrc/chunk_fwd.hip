@@ -157,6 +157,7 @@ struct Prefetch {
   typename U32Vec<4 * KU>::type k, q;
   typename U32Vec<4 * VU>::type v;
   float g, beta;                                 // wave 0: token `lane`
+  bool gfirst;                                   // wave 0: row `lane` is a token's first substep
 };
 
 // Where each lane's prefetch units sit inside a chunk: unit u of the keys is
@@ -192,8 +193,12 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
                                            int hk, int vb) {
   using PF = Prefetch<IN_F32, D>;
   constexpr int es = IN_F32 ? 4 : 2;
+  // rows are substeps when P > 1: keys, values and beta by substep, the
+  // query and gate of the substep's token (the gate on its first substep)
+  const int P = p.P;
+  const int64_t r0 = t0 / P;
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * es;
-  const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * es;
+  const char *qb = static_cast<const char *>(p.q) + (r0 * p.q_stride + (int64_t)hk * D) * es;
   const char *vb_ = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BV) * es;
   const uint32_t ks = (uint32_t)(p.k_stride * es), qs = (uint32_t)(p.q_stride * es),
                  vs = (uint32_t)(p.v_stride * es);
@@ -201,8 +206,9 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
 #pragma unroll
   for (int u = 0; u < PF::KU; ++u) {
     const uint32_t row = (uint32_t)min(lo.krow + u * lo.krs, last);
+    const uint32_t qr = (uint32_t)((t0 + row) / P - r0);
     put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + lo.kc)));
-    put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (row * qs + lo.kc)));
+    put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (qr * qs + lo.kc)));
   }
 #pragma unroll
   for (int u = 0; u < PF::VU; ++u) {
@@ -211,9 +217,10 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
   }
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const int64_t th = (t0 + min(tid, last)) * p.HV + h;
-    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
-    if constexpr (DELTA) pf.beta = p.beta[th];
+    const int64_t m = t0 + min(tid, last);
+    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(m / P) * p.HV + h];
+    pf.gfirst = m % P == 0;
+    if constexpr (DELTA) pf.beta = p.beta[m * p.HV + h];
   }
 }
 
@@ -342,7 +349,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int col = vb * BV + 16 * w + r;   // value column this lane owns in C tiles
 
-  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  // bos and eos count substeps: token t is rows t*P .. t*P+P-1 (P = 1 but
+  // for Gated DeltaProduct, run as GDN over its virtual sequence)
+  const int64_t bos = (int64_t)p.cu_seqlens[n] * p.P, eos = (int64_t)p.cu_seqlens[n + 1] * p.P;
   const int64_t slot = p.slot_idx[n];
 
   // ---- initial state: st[m][i] = S^T[16m + 4g + i][col] ----
@@ -375,6 +384,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 
   PF pf;
   pf.g = pf.beta = 0.f;
+  pf.gfirst = true;
   const LaneOffsets lo = lane_offsets<IN_F32, D>();
   if constexpr (GATE != GDR_GATE_CHANNEL) {
     if (bos < eos)
@@ -411,7 +421,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       if (w == 0) {
         const bool ok = lane < L;
         float gl = 0.f;
-        if constexpr (GATE == GDR_GATE_SCALAR) gl = ok ? pf.g : 0.f;
+        if constexpr (GATE == GDR_GATE_SCALAR) gl = ok && pf.gfirst ? pf.g : 0.f;
         const float Gi = wave_scan(gl);
         const float Gl = __shfl(Gi, 63, 64);
         sm.G[lane] = Gi;
@@ -456,8 +466,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       for (int it = tid; it < C * (D / 4); it += 256) {
         const int row = it / (D / 4), c4 = 4 * (it % (D / 4));
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < L)
-          x = *reinterpret_cast<const float4 *>(p.g + ((t0 + row) * p.HV + h) * (int64_t)D + c4);
+        if (row < L && (t0 + row) % p.P == 0)
+          x = *reinterpret_cast<const float4 *>(p.g + ((t0 + row) / p.P * p.HV + h) * (int64_t)D + c4);
         *reinterpret_cast<float4 *>(&sm.gstage[row][c4]) = x;
       }
       if (w == 0) {
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         const bool ok = row < L;
         float kx[8], qx[8];
         load8<IN_F32>(p.k, (t0 + row) * p.k_stride + (int64_t)hk * D + c8, ok, kx);
-        load8<IN_F32>(p.q, (t0 + row) * p.q_stride + (int64_t)hk * D + c8, ok, qx);
+        load8<IN_F32>(p.q, (t0 + row) / p.P * p.q_stride + (int64_t)hk * D + c8, ok, qx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float Gv = sm.gstage[row][c8 + j];
@@ -646,7 +656,22 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       // row (16I + 4g + i) of this chunk, column col: 32-bit offsets from the
       // chunk's first output row
       const uint32_t HVDu = (uint32_t)HVD;
-      if (p.out_bf16) {
+      if (p.P > 1) {
+        // substeps: a token's output is its last substep's, at o row
+        // (t0 + ii) / P; the other rows are dropped
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ii = 16 * I + 4 * g + i;
+            const int64_t m = t0 + ii;
+            if (ii < L && m % p.P == p.P - 1) {
+              const int64_t off = (m / p.P) * HVD + (int64_t)h * D + col;
+              if (p.out_bf16) static_cast<uint16_t *>(p.o)[off] = f32_to_bf16(oa[I][i]);
+              else static_cast<float *>(p.o)[off] = oa[I][i];
+            }
+          }
+      } else if (p.out_bf16) {
         uint16_t *ob = static_cast<uint16_t *>(p.o) + t0 * HVD + (int64_t)h * D + col;
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -785,6 +810,7 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   p.st_bf16 = a.state_dtype == GDR_BF16;
   p.out_bf16 = a.out_dtype == GDR_BF16;
+  p.P = products_of(a);
   if (a.in_dtype == GDR_BF16) return by_gate<false>(a, p, stream);
   return by_gate<true>(a, p, stream);
 }

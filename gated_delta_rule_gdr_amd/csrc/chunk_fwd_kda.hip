@@ -1034,7 +1034,8 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
 }  // namespace
 
 bool chunk_fwd_kda_applies(const gdr_args &a) {
-  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && a.rule == GDR_RULE_DELTA;
+  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && a.rule == GDR_RULE_DELTA &&
+         products_of(a) == 1;
 }
 
 size_t chunk_fwd_kda_min_workspace(const gdr_args &a) {

@@ -145,6 +145,7 @@ struct PrefWS {
   static constexpr int KU = C * D / 8 / (64 * NSTG);   // 16-byte units per staging thread
   typename U32Vec<4 * KU>::type k, q;
   float g, beta;
+  bool gfirst;   // (more than one transition per token) the row is a token's first substep
 };
 
 // Registers a prep wave carries across the end-of-chunk barrier: its block
@@ -187,25 +188,48 @@ __device__ __forceinline__ void ldfrag2(const uint16_t *hi, const uint16_t *lo, 
   f.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(lo + o));
 }
 
-template <int GATE, bool DELTA, int D>
+// Rows t0 .. t0 + L - 1 of a chunk (clamped to the last). With PROD (P > 1
+// transitions per token) the rows are substeps: keys and beta by substep,
+// the query of the substep's token (only a token's last substep keeps its
+// output, and an output row depends on no other row's query), and the
+// token's gate on its first substep only (gfirst; the others decay by 1).
+template <int GATE, bool DELTA, int D, bool PROD>
 __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, int64_t t0, int L,
                                           int h, int hk, int ptid) {
   constexpr int KU = PrefWS<D>::KU;
   const int krow = ptid / (D / 8), krs = 64 * NSTG / (D / 8), kc = (ptid % (D / 8)) * 16;
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * 2;
-  const char *qb = static_cast<const char *>(p.q) + (t0 * p.q_stride + (int64_t)hk * D) * 2;
+  const char *qb = static_cast<const char *>(p.q) + ((PROD ? t0 / p.P : t0) * p.q_stride + (int64_t)hk * D) * 2;
   const uint32_t ks = (uint32_t)(p.k_stride * 2), qs = (uint32_t)(p.q_stride * 2);
   const int last = L - 1;
+  if constexpr (!PROD) {
 #pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const uint32_t row = (uint32_t)min(krow + u * krs, last);
-    put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + kc)));
-    put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (row * qs + kc)));
-  }
-  if (ptid < 64) {
-    const int64_t th = (t0 + min(ptid, last)) * p.HV + h;
-    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
-    if constexpr (DELTA) pf.beta = p.beta[th];
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t row = (uint32_t)min(krow + u * krs, last);
+      put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + kc)));
+      put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (row * qs + kc)));
+    }
+    if (ptid < 64) {
+      const int64_t th = (t0 + min(ptid, last)) * p.HV + h;
+      if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
+      if constexpr (DELTA) pf.beta = p.beta[th];
+    }
+  } else {
+    const int P = p.P;
+    const int64_t r0 = t0 / P;   // qb's row
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t row = (uint32_t)min(krow + u * krs, last);
+      const uint32_t qr = (uint32_t)((t0 + row) / P - r0);
+      put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + kc)));
+      put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (qr * qs + kc)));
+    }
+    if (ptid < 64) {
+      const int64_t m = t0 + min(ptid, last);
+      if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(m / P) * p.HV + h];
+      pf.gfirst = m % P == 0;
+      if constexpr (DELTA) pf.beta = p.beta[m * p.HV + h];
+    }
   }
 }
 
@@ -434,7 +458,7 @@ __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g
 // only); the stagers stage the keys and queries of chunk c+1 (and issue the
 // loads of chunk c+2) and count those in; then R and A, the diagonal
 // inverses and the block columns of T of chunk c+1 (role_ws).
-template <int PW, int NP, int GATE, bool DELTA, int D, int NSW>
+template <int PW, int NP, int GATE, bool DELTA, int D, int NSW, bool PROD>
 __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int lane,
                                                 int r, int g, int h, int hk, int64_t bos,
                                                 int64_t eos, int nc) {
@@ -448,6 +472,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
   const int ptid = 64 * RL.stager + lane;
   PF pf;
   pf.g = pf.beta = 0.f;
+  pf.gfirst = true;
   HoldWS hold;
 
   // Keys (KEYS) or queries of chunk ci into set ci % 2 (from pf); with the
@@ -473,14 +498,14 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
     if constexpr (!KEYS) {
       if (ci + 1 < nc) {
         const int64_t tn = t0 + C;
-        prep_load<GATE, DELTA, D>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
+        prep_load<GATE, DELTA, D, PROD>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
       }
       return;
     }
     if constexpr (RL.stager == 0) {
       const bool ok = lane < L;
       float gl = 0.f;
-      if constexpr (GATE == GDR_GATE_SCALAR) gl = ok ? pf.g : 0.f;
+      if constexpr (GATE == GDR_GATE_SCALAR) gl = ok && (!PROD || pf.gfirst) ? pf.g : 0.f;
       const float Gi = wave_scan_dpp(gl);
       const float Gl = lane_value(Gi, 63);
       S.G[lane] = Gi;
@@ -515,7 +540,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
 
   if (nc == 0) return;
   if constexpr (STAGER) {
-    prep_load<GATE, DELTA, D>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
+    prep_load<GATE, DELTA, D, PROD>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
     stage(0, KeysT{});
     stage(0, QueriesT{});
     count_in(&sm.kcount, &sm.qcount, lane);
@@ -559,7 +584,10 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
   }
 }
 
-template <int GATE, bool DELTA, int D, int NSW>
+// PROD: more than one transition per token (Gated DeltaProduct): the kernel
+// runs the virtual sequence of substeps ("Linear attention visualized",
+// GDP as GDN over a virtual sequence) and keeps each token's last output.
+template <int GATE, bool DELTA, int D, int NSW, bool PROD>
 __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_kernel(ChunkParams p) {
   constexpr int NP = prep_waves<NSW>();
   constexpr int NTH = 64 * (NSW + NP);
@@ -587,7 +615,9 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   // the wave index through readfirstlane is provably uniform, so the role
   // branch below is a scalar branch and each role runs its own loop
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  // (with PROD, bos and eos count substeps: token t is rows t*P .. t*P+P-1)
+  const int64_t bos = (int64_t)p.cu_seqlens[n] * (PROD ? p.P : 1);
+  const int64_t eos = (int64_t)p.cu_seqlens[n + 1] * (PROD ? p.P : 1);
   const int nc = (int)((eos - bos + C - 1) / C);
   const int64_t HVD = (int64_t)p.HV * D;
   if (tid == 0)
@@ -604,7 +634,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   // Both roles pass the same barriers: one after the prologue and one at the
   // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
   if (w >= NSW) {
-#define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW>(p, sm, lane, r, g, h, hk, bos, eos, nc)
+#define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW, PROD>(p, sm, lane, r, g, h, hk, bos, eos, nc)
     switch (w - NSW) {
       case 0: GDR_PREP(0); break;
       case 1: GDR_PREP(1); break;
@@ -903,7 +933,24 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         const uint32_t olane = ((uint32_t)(4 * g) * HVDu + (uint32_t)col) * osz;
         // (uniform branches: a full chunk stores unmasked; rows past a
         // partial chunk's end are skipped)
-        if (!p.out_bf16) {
+        if constexpr (PROD) {
+          // a token's output is its last substep's: row t0 + ii goes to o
+          // row (t0 + ii) / P when it is one, and is dropped otherwise
+          const int P = p.P;
+          char *ocol = static_cast<char *>(p.o) + ((int64_t)h * D + col) * osz;
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ii = 16 * I + 4 * g + i;
+              const int64_t m = t0 + ii;
+              if (ii < L && m % P == P - 1) {
+                char *dst = ocol + (m / P) * HVD * osz;
+                if (p.out_bf16) *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(oa[I][i]);
+                else *reinterpret_cast<float *>(dst) = oa[I][i];
+              }
+            }
+        } else if (!p.out_bf16) {
           if (L == C) {
 #pragma unroll
             for (int I = 0; I < 4; ++I)
@@ -958,9 +1005,12 @@ template <int GATE, bool DELTA, int D, int NSW>
 hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
   const int grp = p.ratio * (D / (16 * NSW));
   const int blocks = ((p.N * p.HK + 7) / 8) * 8 * grp;
-  hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW>), dim3(blocks),
-                     dim3(64 * (NSW + prep_waves<NSW>())), 0,
-                     stream, p);
+  if (p.P > 1)
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, true>), dim3(blocks),
+                       dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, false>), dim3(blocks),
+                       dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1011,6 +1061,7 @@ hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   p.st_bf16 = a.state_dtype == GDR_BF16;
   p.out_bf16 = a.out_dtype == GDR_BF16;
+  p.P = products_of(a);
   if (a.gate == GDR_GATE_SCALAR) return ws_by_rule<GDR_GATE_SCALAR>(a, p, stream);
   return ws_by_rule<GDR_GATE_NONE>(a, p, stream);
 }

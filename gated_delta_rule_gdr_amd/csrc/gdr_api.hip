@@ -73,9 +73,6 @@ gdr_status validate(const gdr_args *a, Call call) {
                 (long long)a->T_total, a->N);
   if (call == Call::Chunk && a->chunk_size != 64)
     return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: built for 64", a->chunk_size);
-  if (call == Call::Chunk && products_of(*a) > 1)
-    return fail(GDR_E_UNSUPPORTED, "products = %d: the chunkwise prefill takes one transition per token "
-                "(gdr_recurrent_fwd takes more)", a->products);
   if (a->N == 0) return GDR_OK;  // nothing to do; pointers may be NULL
 
   if (!a->state_pool || !a->slot_idx) return fail(GDR_E_INVALID, "state_pool / slot_idx is NULL");

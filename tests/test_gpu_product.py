@@ -152,3 +152,65 @@ def test_one_product_is_the_plain_recurrence():
                            d["cu_seqlens"], products=1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(d["pool"], p2)
+
+
+CHUNK_COMBOS = [
+    # (P, D, in_dtype, gate, rule): the warp-specialised kernel (bf16, no or
+    # scalar gate) and the general kernel (fp32 inputs, the channel gate)
+    (2, 128, "bf16", "scalar", "delta"), (3, 128, "bf16", "scalar", "delta"),
+    (3, 64, "bf16", "none", "delta"), (2, 128, "bf16", "scalar", "linear"),
+    (3, 128, "bf16", "channel", "delta"), (2, 64, "bf16", "channel", "linear"),
+    (3, 64, "f32", "scalar", "delta"), (2, 128, "f32", "channel", "delta"),
+    (4, 128, "f32", "none", "linear"),
+]
+
+
+@pytest.mark.parametrize("P,D,in_dtype,gate,rule", CHUNK_COMBOS,
+                         ids=[f"p{P}-d{D}-{i}-{g}-{r}" for P, D, i, g, r in CHUNK_COMBOS])
+def test_chunk_fwd_products_match_oracle(P, D, in_dtype, gate, rule):
+    """GDP as GDN over the virtual sequence of substeps, chunk by chunk (the
+    page's construction), with tokens whose substeps straddle chunk ends."""
+    gdr = _gdr()
+    state_dtype = "bf16" if gate == "none" else "f32"
+    w = small(D, in_dtype, gate, rule, state_dtype, seqlens=(0, 1, 40, 70, 129), seed=67)
+    x = product_inputs(w, P)
+    d = to_dev(w, x)
+    before = d["pool"].clone()
+    print(f"chunk_fwd products={P} D={D} in={in_dtype} gate={gate} rule={rule}", flush=True)
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"] if rule == "delta" else None,
+                      d["pool"], d["slot_idx"], d["cu_seqlens"], scale=D ** -0.5, rule=rule,
+                      gate=gate, products=P)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = reference(w, x, P, D ** -0.5)
+    check_out(host(o, "f32"), o_ref, in_dtype)
+    pool = host(d["pool"], state_dtype)
+    for s in x["slot_idx"]:
+        check_state(pool[s], pool_ref[s], in_dtype, state_dtype)
+    untouched = np.setdiff1d(np.arange(w.num_slots), x["slot_idx"])
+    assert torch.equal(d["pool"][untouched], before[untouched])
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_chunk_fwd_products_equal_recurrent_fwd(out_dtype):
+    gdr = _gdr()
+    P = 2
+    w = small(128, "bf16", "scalar", "delta", seqlens=(100, 33, 64), seed=69)
+    x = product_inputs(w, P)
+    d = to_dev(w, x)
+    p2 = d["pool"].clone()
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o1 = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                       d["cu_seqlens"], products=P, out_dtype=od)
+    o2 = gdr.recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], p2, d["slot_idx"],
+                           d["cu_seqlens"], products=P, out_dtype=od)
+    torch.cuda.synchronize()
+    a, b = host(o1, "f32"), host(o2, "f32")
+    if out_dtype == "f32":
+        check_out(a, b, "bf16")
+    else:
+        # each side rounds its fp32 result to bf16: two values that straddle
+        # a rounding midpoint land one bf16 step (2^-7 of the value) apart
+        r = np.sqrt(np.mean(b * b))
+        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 3e-3 * r)
+    for s in x["slot_idx"]:
+        check_state(host(d["pool"], "f32")[s], host(p2, "f32")[s], "bf16", "f32")
