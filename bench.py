@@ -18,7 +18,9 @@ Prints one JSON line. `value` is prefill tokens per second for one layer (all
 heads); `roofline` describes the prefill kernel against HBM bandwidth (its
 binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
 fraction alongside; `decode` gives steps/s and HBM fraction of the step
-kernel; `recurrent_fwd` the same for the tokenwise recurrence; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+kernel; `recurrent_fwd` the same for the tokenwise recurrence; `delta_product`
+the chunkwise prefill of Gated DeltaProduct (2 transitions per token) on the
+headline shapes; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -253,6 +255,52 @@ def bench_recurrent_fwd(w: synth.Workload, steps: int, warmup: int = 5):
     return out
 
 
+def product_bytes(w: synth.Workload, P: int, out_dtype="f32") -> int:
+    """Gated DeltaProduct over w's batch with P transitions per token: q and
+    g once per token, k, v and beta once per substep, o per token, the state
+    read (unless zero-initialised) and written."""
+    T, ie = w.T_total, _isz(w.in_dtype)
+    b = T * w.HK * w.DK * ie + P * T * w.HK * w.DK * ie + P * T * w.HV * w.DV * ie
+    b += T * w.HV * 4 if w.gate == "scalar" else 0
+    b += P * T * w.HV * 4 if w.rule == "delta" else 0
+    b += T * w.HV * w.DV * _isz(out_dtype)
+    st = w.N * w.HV * w.DK * w.DV * _isz(w.state_dtype)
+    return b + (st if w.zero_init else 2 * st)
+
+
+def bench_product(w: synth.Workload, P: int, steps: int, warmup: int = 3):
+    """Mean kernel time (ms) of gdr_chunk_fwd with P transitions per token on
+    w's batch: q, g from w; k, v, beta from the same recipe at P times the
+    lengths (another seed)."""
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    xr = synth.generate(w)
+    xv = synth.generate(w.replace(seqlens=tuple(P * n for n in w.seqlens), seed=w.seed + 1000))
+    a = dict(q=_dev(xr["q"], w.in_dtype, dev), k=_dev(xv["k"], w.in_dtype, dev),
+             v=_dev(xv["v"], w.in_dtype, dev), g=_dev(xr["g"], "f32", dev),
+             beta=_dev(xv["beta"], "f32", dev), pool=_dev(xr["pool"], w.state_dtype, dev),
+             slot_idx=_dev(xr["slot_idx"], "i32", dev), cu_seqlens=_dev(xr["cu_seqlens"], "i32", dev))
+    o = torch.empty((w.T_total, w.HV, w.DV), dtype=torch.float32, device=dev)
+    del xr, xv
+
+    def run():
+        gdr.chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["slot_idx"],
+                      a["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init, o=o,
+                      products=P)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 # ----------------------------------------------------------------------------
 # CPU leg: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -308,6 +356,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--recurrent-steps", type=int, default=50)
     ap.add_argument("--no-recurrent", action="store_true")
+    ap.add_argument("--product-steps", type=int, default=20)
+    ap.add_argument("--no-product", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of a known size (scales the HBM "
@@ -395,6 +445,19 @@ def main():
             "hbm_frac": rb / (t["recurrent_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": committed_traffic("recurrent_fwd_kernel", rw.name, RECUR_SRC),
             "chunk_fwd_kernel_us_same_batch": t["chunk_fwd"] * 1e3}
+    if not args.no_product:
+        pw, P = synth.workload(synth.HEADLINE), 2
+        pt = bench_product(pw, P, args.product_steps)
+        pb = product_bytes(pw, P)
+        result["delta_product"] = {
+            "workload": pw.name, "products": P, "steps": args.product_steps,
+            "kernel_ms": pt, "tokens_per_s": pw.T_total / (pt * 1e-3),
+            "algorithmic_bytes": pb, "hbm_gbs": pb / (pt * 1e-3) / 1e9,
+            "hbm_frac": pb / (pt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": prefill_flops(pw.replace(seqlens=tuple(P * n for n in pw.seqlens)),
+                                         pw.chunk_size) / (pt * 1e-3) / 1e12,
+            "traffic": committed_traffic("chunk_fwd_ws_kernel", "gdp_nh2_prefill_b4_t4096_h16_d128",
+                                         prefill_kernel(pw)[1])}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
