@@ -16,6 +16,24 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int C = 64;    // tokens per chunk
 constexpr int BV = 64;   // value columns per workgroup (16 per wave)
 
+// Substep bookkeeping for P transitions per token (Gated DeltaProduct run
+// as a virtual sequence): row i of a run of rows that starts at substep t0
+// belongs to token r0 + tok(i) and is its substep j0 + i - tok(i) * P.
+// tok() divides by P with a 16-bit reciprocal, exact while j0 + i < 4096
+// (the rounding error stays below 1/16, and a quotient's fraction is at
+// most (P - 1) / P <= 7/8 for P <= 8).
+struct SubMap {
+  int64_t r0;
+  int j0, P, M;
+  __device__ __forceinline__ SubMap(int64_t t0, int P_) : P(P_) {
+    r0 = t0 / P_;
+    j0 = (int)(t0 - r0 * P_);
+    M = (65536 + P_ - 1) / P_;
+  }
+  __device__ __forceinline__ int tok(int i) const { return ((j0 + i) * M) >> 16; }
+  __device__ __forceinline__ int sub(int i) const { return j0 + i - tok(i) * P; }
+};
+
 struct ChunkParams {
   const void *q, *k, *v;
   int64_t q_stride, k_stride, v_stride;

@@ -195,10 +195,9 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
   constexpr int es = IN_F32 ? 4 : 2;
   // rows are substeps when P > 1: keys, values and beta by substep, the
   // query and gate of the substep's token (the gate on its first substep)
-  const int P = p.P;
-  const int64_t r0 = t0 / P;
+  const SubMap map(t0, p.P);
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * es;
-  const char *qb = static_cast<const char *>(p.q) + (r0 * p.q_stride + (int64_t)hk * D) * es;
+  const char *qb = static_cast<const char *>(p.q) + (map.r0 * p.q_stride + (int64_t)hk * D) * es;
   const char *vb_ = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BV) * es;
   const uint32_t ks = (uint32_t)(p.k_stride * es), qs = (uint32_t)(p.q_stride * es),
                  vs = (uint32_t)(p.v_stride * es);
@@ -206,7 +205,7 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
 #pragma unroll
   for (int u = 0; u < PF::KU; ++u) {
     const uint32_t row = (uint32_t)min(lo.krow + u * lo.krs, last);
-    const uint32_t qr = (uint32_t)((t0 + row) / P - r0);
+    const uint32_t qr = (uint32_t)map.tok((int)row);
     put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + lo.kc)));
     put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (qr * qs + lo.kc)));
   }
@@ -217,10 +216,10 @@ __device__ __forceinline__ void load_chunk(Prefetch<IN_F32, D> &pf, const ChunkP
   }
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const int64_t m = t0 + min(tid, last);
-    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(m / P) * p.HV + h];
-    pf.gfirst = m % P == 0;
-    if constexpr (DELTA) pf.beta = p.beta[m * p.HV + h];
+    const int row = min(tid, last);
+    if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(map.r0 + map.tok(row)) * p.HV + h];
+    pf.gfirst = map.sub(row) == 0;
+    if constexpr (DELTA) pf.beta = p.beta[(t0 + row) * p.HV + h];
   }
 }
 
@@ -463,11 +462,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         copy8<IN_F32>(p.v, (t0 + row) * p.v_stride + (int64_t)h * D + vb * BV + c8, row < L,
                       &sm.vv[row][c8]);
       }
+      const SubMap map(t0, p.P);   // substeps: the gate on a token's first
       for (int it = tid; it < C * (D / 4); it += 256) {
         const int row = it / (D / 4), c4 = 4 * (it % (D / 4));
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < L && (t0 + row) % p.P == 0)
-          x = *reinterpret_cast<const float4 *>(p.g + ((t0 + row) / p.P * p.HV + h) * (int64_t)D + c4);
+        if (row < L && map.sub(row) == 0)
+          x = *reinterpret_cast<const float4 *>(p.g + ((map.r0 + map.tok(row)) * p.HV + h) * (int64_t)D + c4);
         *reinterpret_cast<float4 *>(&sm.gstage[row][c4]) = x;
       }
       if (w == 0) {
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         const bool ok = row < L;
         float kx[8], qx[8];
         load8<IN_F32>(p.k, (t0 + row) * p.k_stride + (int64_t)hk * D + c8, ok, kx);
-        load8<IN_F32>(p.q, (t0 + row) / p.P * p.q_stride + (int64_t)hk * D + c8, ok, qx);
+        load8<IN_F32>(p.q, (map.r0 + map.tok(row)) * p.q_stride + (int64_t)hk * D + c8, ok, qx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float Gv = sm.gstage[row][c8 + j];
@@ -659,14 +659,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       if (p.P > 1) {
         // substeps: a token's output is its last substep's, at o row
         // (t0 + ii) / P; the other rows are dropped
+        const SubMap map(t0, p.P);
 #pragma unroll
         for (int I = 0; I < 4; ++I)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ii = 16 * I + 4 * g + i;
-            const int64_t m = t0 + ii;
-            if (ii < L && m % p.P == p.P - 1) {
-              const int64_t off = (m / p.P) * HVD + (int64_t)h * D + col;
+            if (ii < L && map.sub(ii) == map.P - 1) {
+              const int64_t off = (map.r0 + map.tok(ii)) * HVD + (int64_t)h * D + col;
               if (p.out_bf16) static_cast<uint16_t *>(p.o)[off] = f32_to_bf16(oa[I][i]);
               else static_cast<float *>(p.o)[off] = oa[I][i];
             }

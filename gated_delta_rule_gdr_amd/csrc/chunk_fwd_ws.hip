@@ -215,20 +215,19 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
       if constexpr (DELTA) pf.beta = p.beta[th];
     }
   } else {
-    const int P = p.P;
-    const int64_t r0 = t0 / P;   // qb's row
+    const SubMap sm_(t0, p.P);   // qb starts at its token r0
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const uint32_t row = (uint32_t)min(krow + u * krs, last);
-      const uint32_t qr = (uint32_t)((t0 + row) / P - r0);
+      const uint32_t qr = (uint32_t)sm_.tok((int)row);
       put4(pf.k, u, *reinterpret_cast<const uint4 *>(kb + (row * ks + kc)));
       put4(pf.q, u, *reinterpret_cast<const uint4 *>(qb + (qr * qs + kc)));
     }
     if (ptid < 64) {
-      const int64_t m = t0 + min(ptid, last);
-      if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(m / P) * p.HV + h];
-      pf.gfirst = m % P == 0;
-      if constexpr (DELTA) pf.beta = p.beta[m * p.HV + h];
+      const int row = min(ptid, last);
+      if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[(sm_.r0 + sm_.tok(row)) * p.HV + h];
+      pf.gfirst = sm_.sub(row) == 0;
+      if constexpr (DELTA) pf.beta = p.beta[(t0 + row) * p.HV + h];
     }
   }
 }
@@ -936,16 +935,15 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         if constexpr (PROD) {
           // a token's output is its last substep's: row t0 + ii goes to o
           // row (t0 + ii) / P when it is one, and is dropped otherwise
-          const int P = p.P;
-          char *ocol = static_cast<char *>(p.o) + ((int64_t)h * D + col) * osz;
+          const SubMap map(t0, p.P);
+          char *ocol = static_cast<char *>(p.o) + ((map.r0 * HVD + (int64_t)h * D + col) * osz);
 #pragma unroll
           for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int ii = 16 * I + 4 * g + i;
-              const int64_t m = t0 + ii;
-              if (ii < L && m % P == P - 1) {
-                char *dst = ocol + (m / P) * HVD * osz;
+              if (ii < L && map.sub(ii) == map.P - 1) {
+                char *dst = ocol + (int64_t)map.tok(ii) * HVD * osz;
                 if (p.out_bf16) *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(oa[I][i]);
                 else *reinterpret_cast<float *>(dst) = oa[I][i];
               }
