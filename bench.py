@@ -18,7 +18,8 @@ Prints one JSON line. `value` is prefill tokens per second for one layer (all
 heads); `roofline` describes the prefill kernel against HBM bandwidth (its
 binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
 fraction alongside; `decode` gives steps/s and HBM fraction of the step
-kernel; `recurrent_fwd` the same for the tokenwise recurrence; `delta_product`
+kernel; `linear_mode` the same shapes with alpha = 1 and no delta (linear
+attention); `recurrent_fwd` the same for the tokenwise recurrence; `delta_product`
 the chunkwise prefill of Gated DeltaProduct (2 transitions per token) on the
 headline shapes; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
@@ -50,14 +51,15 @@ RECUR_SRC = [os.path.join(CSRC, "recurrent_fwd.hip"), os.path.join(CSRC, "gdr_in
 def prefill_kernel(w: synth.Workload):
     """(kernel name, its source files) of the prefill kernel(s) the library
     runs for this workload: the warp-specialised kernel for bf16 inputs
-    without a channel gate; for bf16 inputs with the channel gate and the
-    delta rule the prep and state kernel pair (timed together, as one call);
+    without a channel gate; for bf16 inputs with the channel gate (KDA's
+    delta rule, GLA's linear rule) the prep and state kernel pair (timed
+    together, as one call);
     the general kernel otherwise (the dispatch in gdr_api.hip and
     chunk_fwd.hip)."""
     common = [os.path.join(CSRC, "chunk_common.h"), os.path.join(CSRC, "gdr_internal.h")]
     if w.in_dtype == "bf16" and w.gate != "channel":
         return "chunk_fwd_ws_kernel", [os.path.join(CSRC, "chunk_fwd_ws.hip")] + common
-    if w.in_dtype == "bf16" and w.rule == "delta":
+    if w.in_dtype == "bf16":
         return "kda_prep_kernel+kda_state_kernel", [os.path.join(CSRC, "chunk_fwd_kda.hip")] + common
     return "chunk_fwd_kernel", [os.path.join(CSRC, "chunk_fwd.hip")] + common
 
@@ -357,6 +359,7 @@ def main():
     ap.add_argument("--recurrent-steps", type=int, default=50)
     ap.add_argument("--no-recurrent", action="store_true")
     ap.add_argument("--product-steps", type=int, default=20)
+    ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--no-product", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -445,6 +448,20 @@ def main():
             "hbm_frac": rb / (t["recurrent_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": committed_traffic("recurrent_fwd_kernel", rw.name, RECUR_SRC),
             "chunk_fwd_kernel_us_same_batch": t["chunk_fwd"] * 1e3}
+    if not args.no_linear and w.name == synth.HEADLINE:
+        # the same shapes in linear-attention mode (alpha = 1, no delta)
+        lw = synth.workload("la_prefill_b4_t4096_h16_d128")
+        l_step, l_ms, l_med = bench_prefill(lw, args.steps, args.warmup)
+        lb = prefill_bytes(lw)
+        lf = prefill_flops(lw, lw.chunk_size)
+        lk, lsrc = prefill_kernel(lw)
+        result["linear_mode"] = {
+            "workload": lw.name, "tokens_per_s": lw.T_total / l_step, "kernel": lk,
+            "kernel_ms_mean": l_ms, "kernel_ms_median": l_med, "algorithmic_bytes": lb,
+            "hbm_gbs": lb / (l_ms * 1e-3) / 1e9, "hbm_frac": lb / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": lf / (l_ms * 1e-3) / 1e12,
+            "mfma_frac": lf / (l_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": committed_traffic(lk, lw.name, lsrc)}
     if not args.no_product:
         pw, P = synth.workload(synth.HEADLINE), 2
         pt = bench_product(pw, P, args.product_steps)

@@ -1,4 +1,5 @@
-// Chunkwise prefill with a per-key-channel gate (KDA), bf16 q/k/v, delta rule.
+// Chunkwise prefill with a per-key-channel gate, bf16 q/k/v: KDA (the delta
+// rule) and, with T' = I and W = 0 in its records, GLA (the linear rule).
 //
 // Math (section 6 of "You Could Have Come Up With Kimi Delta Attention",
 // section 4 of "From Attention to Learned Memory"): per chunk of C = 64
@@ -91,6 +92,7 @@ struct KdaParams {
   int32_t N, HK, HV, ratio;
   float scale;
   int zero_init, st_bf16, out_bf16;
+  int delta;         // the delta rule (else the linear rule: T' = I, W = 0)
   char *rec;         // records of this slice: [(F - F0) * HV + h]
   float *carry;      // [N, HV, D, D] fp32 S^T between slices
   int64_t F0, F1;    // flat chunk range of this slice
@@ -213,7 +215,7 @@ struct PrepIn {
   float beta;
 };
 
-template <int D>
+template <int D, bool DELTA>
 __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, const PrepItem &it, int w,
                                           int r, int g) {
   constexpr int NS = D / 32;
@@ -241,12 +243,15 @@ __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, con
       in.q[2 * u] = q2.x;
       in.q[2 * u + 1] = q2.y;
     }
-  in.beta = p.beta[t * p.HV + it.h];
+  in.beta = DELTA ? p.beta[t * p.HV + it.h] : 1.f;
 }
 
 // Persistent: each workgroup takes items blockIdx.x, blockIdx.x + gridDim.x, ...
 // and loads the next item's inputs while it works on the current one.
-template <int D>
+// DELTA false (the linear rule, GLA's channel-gated linear attention): no
+// correction, so the records hold T' = I (beta = 1, R = 0) and W = 0, and the
+// state kernel's Vb = T'V - W S^T is V itself.
+template <int D, bool DELTA>
 __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   using RC = KdaRec<D>;
   using SM = PrepSmem<D>;
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   int64_t item = blockIdx.x;
   PrepItem nx = prep_item(p, item);
   PrepIn<D> in;
-  prep_load<D>(in, p, nx, w, r, g);
+  prep_load<D, DELTA>(in, p, nx, w, r, g);
   for (; item < items; item += gridDim.x) {
     const PrepItem it = nx;
     const bool ok = i < it.L;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
     if (g == 0) sm.beta[i] = ok ? in.beta : 0.f;
     if (item + gridDim.x < items) {
       nx = prep_item(p, item + gridDim.x);
-      prep_load<D>(in, p, nx, w, r, g);
+      prep_load<D, DELTA>(in, p, nx, w, r, g);
     }
     if (it.valid) {
       const int h = it.h;
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jj = 4 * g + e;
-      rv[J][e] = (J < w || (J == w && jj < r)) ? bi * ar[e] : 0.f;
+      rv[J][e] = DELTA && (J < w || (J == w && jj < r)) ? bi * ar[e] : 0.f;
       av[J][e] = (J < w || (J == w && jj <= r)) ? aa[e] : 0.f;
     }
   }
@@ -465,9 +470,9 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   // ---- W^T = K_l^T T'^T: wave w < NS forms key tiles m = 2w, 2w + 1, which
   //      are exactly the W fragments (I, s = w); the record holds -W ----
   if (w < NS) {
-    f32x4 acc[2][4];
+    f32x4 acc[2][4] = {};
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2 && DELTA; ++h2) {
       const int m = 2 * w + h2;
       const int pc = perm32(16 * m + r);
       Frag fa[2];
@@ -1025,7 +1030,10 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
     p.F1 = F0 + per < flat ? F0 + per : flat;
     const int64_t items = (p.F1 - p.F0) * p.HV;
     const int64_t pblocks = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;   // two per compute unit
-    hipLaunchKernelGGL((kda_prep_kernel<D>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
+    if (p.delta)
+      hipLaunchKernelGGL((kda_prep_kernel<D, true>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((kda_prep_kernel<D, false>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((kda_state_kernel<D, NSW>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0, stream, p);
   }
   return hipGetLastError();
@@ -1034,8 +1042,7 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
 }  // namespace
 
 bool chunk_fwd_kda_applies(const gdr_args &a) {
-  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && a.rule == GDR_RULE_DELTA &&
-         products_of(a) == 1;
+  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && products_of(a) == 1;
 }
 
 size_t chunk_fwd_kda_min_workspace(const gdr_args &a) {
@@ -1062,6 +1069,7 @@ hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hi
   p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
   p.st_bf16 = a.state_dtype == GDR_BF16;
   p.out_bf16 = a.out_dtype == GDR_BF16;
+  p.delta = a.rule == GDR_RULE_DELTA;
   const size_t cb = carry_bytes(a);
   p.carry = static_cast<float *>(ws);
   p.rec = static_cast<char *>(ws) + cb;

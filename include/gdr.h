@@ -137,7 +137,8 @@ int gdr_abi_version(void);
  * 0 when the call runs one fused kernel and needs none. Returns 0 for
  * arguments that fail validation.
  *
- * Only the channel gate with bf16 inputs and the delta rule uses a workspace:
+ * Only the channel gate with bf16 inputs (KDA's delta rule or GLA's linear
+ * rule, one transition per token) uses a workspace:
  * it runs as a parallel per-chunk kernel that writes one record per (chunk,
  * value head) (the decayed keys and queries, the inverse of the chunk's unit
  * lower triangular system and the products the state recurrence needs; the

@@ -155,8 +155,8 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_channel_gate_workspace_on_host():
-    """bf16 inputs with the channel gate and the delta rule pass per-chunk
-    records through the workspace: the preferred size is the fp32 carry of
+    """bf16 inputs with the channel gate pass per-chunk records through the
+    workspace: the preferred size is the fp32 carry of
     every (sequence, head) plus whole rows of (chunk, head) records, and a
     missing, short or misaligned workspace is rejected before any launch."""
     gdr, L = _lib()
@@ -171,7 +171,9 @@ def test_channel_gate_workspace_on_host():
     assert L.gdr_chunk_fwd(ctypes.byref(a), None, 0, None) == 3
     assert L.gdr_chunk_fwd(ctypes.byref(a), 0x10000000, carry + a.HV * record - 1, None) == 3
     assert L.gdr_chunk_fwd(ctypes.byref(a), 0x10000010, want, None) == 1
-    a.rule = 1   # the linear rule stays fused
+    a.rule = 1   # GLA's linear rule takes the same records (T' = I, W = 0)
+    assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == want
+    a.products = 2   # Gated DeltaProduct runs fused on the general kernel
     assert L.gdr_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
 
 

@@ -138,26 +138,28 @@ def test_chunk_equals_repeated_steps(gate):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("rows", [1, 3])
-def test_channel_gate_slices(D, rows):
+@pytest.mark.parametrize("rule", ["delta", "linear"])
+def test_channel_gate_slices(D, rows, rule):
     """The channel-gate prefill (bf16 inputs) passes per-chunk records through
     the workspace in slices of `rows` flat chunks; the state crosses slice
     boundaries through the workspace's fp32 carry. The result of a workspace
     that holds 1 or 3 rows of records equals the oracle's, and equals the
-    result with the preferred workspace bit for bit."""
+    result with the preferred workspace bit for bit. The linear rule (GLA)
+    takes the same records with T' = I and W = 0."""
     gdr = _gdr()
-    w = small_workload(D, "bf16", "channel", "delta", "f32", zero_init=False,
+    w = small_workload(D, "bf16", "channel", rule, "f32", zero_init=False,
                        seqlens=(130, 0, 64, 1, 200), seed=23)
     x = synth.generate(w)
     d = to_device(w, x)
     pool_pref = d["pool"].clone()
-    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"] if rule == "delta" else None)
     # record of one (chunk, head): W, Q^ and K_r^T fragments, T' and A^, gamma
     row = w.HV * ((3 * 4 * (D // 32) + 2 * 6) * 2048 + 4 * D)
     carry = w.N * w.HV * D * D * 4
     ws = torch.empty(carry + rows * row, dtype=torch.uint8, device="cuda")
-    print(f"channel-gate slices D={D} rows={rows}", flush=True)
-    o = gdr.chunk_fwd(*args, d["pool"], d["slot_idx"], d["cu_seqlens"], workspace=ws)
-    o_pref = gdr.chunk_fwd(*args, pool_pref, d["slot_idx"], d["cu_seqlens"])
+    print(f"channel-gate slices D={D} rows={rows} rule={rule}", flush=True)
+    o = gdr.chunk_fwd(*args, d["pool"], d["slot_idx"], d["cu_seqlens"], workspace=ws, rule=rule)
+    o_pref = gdr.chunk_fwd(*args, pool_pref, d["slot_idx"], d["cu_seqlens"], rule=rule)
     torch.cuda.synchronize()
     assert torch.equal(o, o_pref)
     assert torch.equal(d["pool"], pool_pref)
