@@ -128,6 +128,18 @@ _reg(Workload(
     description="short ragged prefill over the decode pool: 256 sequences x 16 tokens, fp32 "
                 "pool [256,32,128,128] (the tokenwise schedule's case: state I/O dominates)"))
 
+_reg(Workload(
+    name="gla_prefill_t131072_h32_d128", seqlens=(131072,), HK=32, HV=32, DK=128,
+    DV=128, in_dtype="bf16", gate="channel", rule="linear", gate_shift=3.0,
+    state_dtype="f32", num_slots=1, zero_init=True, seed=7,
+    description="GLA (channel-gated linear attention) on the KDA workload's shapes"))
+_reg(Workload(
+    name="mamba2_prefill_b4_t4096_h16_d128", seqlens=(4096,) * 4, HK=16, HV=16, DK=128,
+    DV=128, in_dtype="bf16", gate="scalar", rule="linear", gate_shift=2.0,
+    state_dtype="f32", num_slots=4, zero_init=True, seed=8,
+    description="scalar-gated linear attention (Mamba-2; RetNet with a constant gate) on the "
+                "headline prefill's shapes"))
+
 # The prefill workload the throughput figure is quoted on.
 HEADLINE = "gdn_prefill_b4_t4096_h16_d128"
 

@@ -136,6 +136,21 @@ def test_kda_prefill_t131072_h32():
     check_sampled(w, x, o, d["pool"], [5])
 
 
+@pytest.mark.parametrize("name", ["gla_prefill_t131072_h32_d128", "mamba2_prefill_b4_t4096_h16_d128"])
+def test_gated_linear_prefill(name):
+    """The gated linear variants at the sizes bench.py --workload times: GLA
+    (channel gate, through the KDA kernel pair with T' = I, W = 0) and the
+    scalar-gated linear rule (Mamba-2; RetNet with a constant gate)."""
+    gdr = _gdr()
+    w = synth.workload(name)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    print(f"launch {w.name}", flush=True)
+    o = run_prefill(gdr, w, d)
+    assert torch.isfinite(o).all()
+    check_sampled(w, x, o, d["pool"], [3] if w.N == 1 else [0, 11])
+
+
 def test_short_prefill_n256_t16_recurrent_fwd():
     """The tokenwise schedule on the benchmark's short-prefill batch (256
     sequences of 16 tokens over the fp32 decode pool): two whole head groups
