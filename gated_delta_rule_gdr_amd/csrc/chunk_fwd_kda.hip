@@ -1,5 +1,5 @@
 // Chunkwise prefill with a per-key-channel gate, bf16 q/k/v: KDA (the delta
-// rule) and, with T' = I and W = 0 in its records, GLA (the linear rule).
+// rule) and GLA (the linear rule: no correction, records without region 1).
 //
 // Math (section 6 of "You Could Have Come Up With Kimi Delta Attention",
 // section 4 of "From Attention to Learned Memory"): per chunk of C = 64
@@ -243,14 +243,14 @@ __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, con
       in.q[2 * u] = q2.x;
       in.q[2 * u + 1] = q2.y;
     }
-  in.beta = DELTA ? p.beta[t * p.HV + it.h] : 1.f;
+  in.beta = DELTA ? p.beta[t * p.HV + it.h] : 0.f;
 }
 
 // Persistent: each workgroup takes items blockIdx.x, blockIdx.x + gridDim.x, ...
 // and loads the next item's inputs while it works on the current one.
 // DELTA false (the linear rule, GLA's channel-gated linear attention): no
-// correction, so the records hold T' = I (beta = 1, R = 0) and W = 0, and the
-// state kernel's Vb = T'V - W S^T is V itself.
+// correction (Vb = V), so no R, T or W: the record's region 1 is not
+// written, and the state kernel's linear variant neither reads it.
 template <int D, bool DELTA>
 __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   using RC = KdaRec<D>;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       for (int s = 0; s < NS; ++s) {
         Frag fk;
         ldfrag(&sm.kr[0][0], PK, 16 * J + r, 32 * s, g, fk);
-        ar = mm<true, true>(fk, klf[s], ar);
+        if constexpr (DELTA) ar = mm<true, true>(fk, klf[s], ar);
         aa = mm<true, true>(fk, qf[s], aa);
       }
     }
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jj = 4 * g + e;
-      rv[J][e] = DELTA && (J < w || (J == w && jj < r)) ? bi * ar[e] : 0.f;
+      rv[J][e] = (J < w || (J == w && jj < r)) ? bi * ar[e] : 0.f;
       av[J][e] = (J < w || (J == w && jj <= r)) ? aa[e] : 0.f;
     }
   }
@@ -412,6 +412,8 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   }
   __syncthreads();   // K_r is dead: its storage holds T from here on
 
+  // (the linear rule stops here: its records need no region 1)
+  if constexpr (DELTA) {
   // ---- T = (I + R)^{-1}: diagonal blocks in registers, then the blocks
   //      below the diagonal by block forward substitution (three rounds) ----
   {
@@ -470,9 +472,9 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   // ---- W^T = K_l^T T'^T: wave w < NS forms key tiles m = 2w, 2w + 1, which
   //      are exactly the W fragments (I, s = w); the record holds -W ----
   if (w < NS) {
-    f32x4 acc[2][4] = {};
+    f32x4 acc[2][4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2 && DELTA; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2) {
       const int m = 2 * w + h2;
       const int pc = perm32(16 * m + r);
       Frag fa[2];
@@ -501,6 +503,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       st_frag(rec, RC::R1 + RC::wq(I, w), lane, f);
     }
   }
+  }   // DELTA
     }
     __syncthreads();   // the next item reuses the LDS
   }
@@ -555,13 +558,16 @@ struct LoadR2 {
   typename U32Vec<4 * KdaRec<D>::R1_BLOCKS / NLO>::type r2;
 };
 
-template <int D, int NSW>
+// (the linear rule needs no region 1: its corrected values are the values)
+template <int D, int NSW, bool DELTA>
 __device__ __forceinline__ void issue_r1(LoadR1<D, NSW> &l1, const KdaParams &p, const char *rec,
                                          int64_t t0, int L, int h, int vb, int lw, int lane) {
   const char *base = rec + 16 * lane;
+  if constexpr (DELTA) {
 #pragma unroll
-  for (int u = 0; u < LoadN<D>::N1; ++u)
-    put4(l1.r1, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)));
+    for (int u = 0; u < LoadN<D>::N1; ++u)
+      put4(l1.r1, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)));
+  }
   // values: 64 rows of 2 NSW 16-byte units
   const uint16_t *vb_ = static_cast<const uint16_t *>(p.v) + (int64_t)h * D + 16 * NSW * vb;
 #pragma unroll
@@ -591,12 +597,14 @@ __device__ __forceinline__ void issue_r2(LoadR2<D> &l2, const char *rec, int lw,
     put4(l2.r2, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R2 + 1024 * (lw + NLO * u)));
 }
 
-template <int D, int NSW>
+template <int D, int NSW, bool DELTA>
 __device__ __forceinline__ void store_r1(const LoadR1<D, NSW> &l1, StateSmem<D, NSW> &sm, int lw, int lane) {
   char *base = sm.rec + 16 * lane;
+  if constexpr (DELTA) {
 #pragma unroll
-  for (int u = 0; u < LoadN<D>::N1; ++u)
-    *reinterpret_cast<uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)) = get4(l1.r1, u);
+    for (int u = 0; u < LoadN<D>::N1; ++u)
+      *reinterpret_cast<uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)) = get4(l1.r1, u);
+  }
 #pragma unroll
   for (int u = 0; u < value_units<NSW>(); ++u) {
     const int q = 64 * lw + lane + 64 * NLW * u;
@@ -621,7 +629,8 @@ __device__ __forceinline__ void store_r2(const LoadR2<D> &l2, StateSmem<D, NSW> 
     *reinterpret_cast<uint4 *>(base + KdaRec<D>::R2 + 1024 * (lw + NLO * u)) = get4(l2.r2, u);
 }
 
-template <int D, int NSW>
+// DELTA false: the linear rule (GLA), Vb = V, region 1 neither loaded nor used.
+template <int D, int NSW, bool DELTA>
 __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(KdaParams p) {
   using RC = KdaRec<D>;
   using SM = StateSmem<D, NSW>;
@@ -713,11 +722,11 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
     LoadR3<D> l3;
     auto i1 = [&](LoadR1<D, NSW> &l1, int64_t c) {
       const int64_t t0 = bos + C * c;
-      issue_r1<D, NSW>(l1, p, rec_of(c), t0, (int)min<int64_t>(C, eos - t0), h, vb, lw, lane);
+      issue_r1<D, NSW, DELTA>(l1, p, rec_of(c), t0, (int)min<int64_t>(C, eos - t0), h, vb, lw, lane);
     };
     i1(s0, cb);
     issue_r3<D>(l3, rec_of(cb), lw, lane);
-    store_r1<D, NSW>(s0, sm, lw, lane);
+    store_r1<D, NSW, DELTA>(s0, sm, lw, lane);
     store_r3<D, NSW>(l3, sm, lw, lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (lane == 0) {
@@ -734,7 +743,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
     auto step = [&](LoadR1<D, NSW> &l1, int64_t c) {
       const int k = (int)(c - cb);
       spin_until(&sm.freed[0], NSW * (k + 1));
-      store_r1<D, NSW>(l1, sm, lw, lane);
+      store_r1<D, NSW, DELTA>(l1, sm, lw, lane);
       count_in(&sm.ready[0], lane);
       spin_until(&sm.freed[2], NSW * (k + 1));
       store_r3<D, NSW>(l3, sm, lw, lane);
@@ -884,7 +893,13 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
     // fragments after each MFMA (interleave), so reads and products overlap.
     spin_until(&sm.ready[0], NLW * (k + 1));
     f32x4 acc[4];
-    {
+    if constexpr (!DELTA) {
+      // linear rule: Vb = V, read in the accumulator layout (row 16I + 4g + i)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[I][i] = bf16_to_f32(sm.vv[16 * I + 4 * g + i][16 * pw + r]);
+    } else {
       Frag vf[2], ta[6], wf[2][4];
 #pragma unroll
       for (int s = 0; s < 2; ++s) ldfrag_tr(&sm.vv[0][0], SM::VP, 16 * pw + 4 * (r & 3), s, r, g, vf[s]);
@@ -1034,7 +1049,12 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
       hipLaunchKernelGGL((kda_prep_kernel<D, true>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((kda_prep_kernel<D, false>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((kda_state_kernel<D, NSW>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0, stream, p);
+    if (p.delta)
+      hipLaunchKernelGGL((kda_state_kernel<D, NSW, true>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((kda_state_kernel<D, NSW, false>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0,
+                         stream, p);
   }
   return hipGetLastError();
 }
