@@ -24,7 +24,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "lib", "lib_path", "GdrError",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +40,7 @@ FLAG_QK_L2NORM = 4
 
 
 # GDR_ABI_VERSION of include/gdr.h that Args mirrors.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class GdrError(RuntimeError):
@@ -97,6 +97,11 @@ def load() -> ctypes.CDLL:
     L.gdr_recurrent_step.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
     L.gdr_recurrent_fwd.restype = ctypes.c_int
     L.gdr_recurrent_fwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
+    L.gdr_linear_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.gdr_linear_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
+    L.gdr_linear_chunk_bwd.restype = ctypes.c_int
+    L.gdr_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.gdr_status_string.restype = ctypes.c_char_p
     L.gdr_status_string.argtypes = [ctypes.c_int]
     L.gdr_last_error.restype = ctypes.c_char_p
@@ -271,3 +276,32 @@ def recurrent_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, r
     L = load()
     _check(L.gdr_recurrent_fwd(ctypes.byref(a), _stream(q)))
     return o
+
+
+def linear_chunk_bwd(q, k, v, do, pool, slot_idx, cu_seqlens, *, scale=None, zero_init=False,
+                     out_dtype=None, workspace=None, debug_checks=False):
+    """Gradients (dq, dk, dv) of causal linear attention (no gate, no delta)
+    for the forward call with these arguments and upstream gradient do
+    [T, HV, DV] (contiguous, q's dtype). The pool supplies the initial state
+    (read only) unless zero_init. ``workspace`` is an optional uint8 device
+    tensor of at least the size the library asks for (allocated from torch
+    by default)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    T, HK, DK = q.shape
+    dq = torch.empty((T, HK, DK), dtype=out_dtype, device=q.device)
+    a, _ = _prepare(q, k, v, None, None, pool, slot_idx, cu_seqlens, dq, scale, "linear", "none",
+                    zero_init, debug_checks, 64, out_dtype)
+    if do.dtype != q.dtype or not do.is_contiguous() or tuple(do.shape) != tuple(v.shape) or do.device != q.device:
+        raise ValueError("do must be a contiguous tensor shaped like v, in q's dtype, on q's device")
+    dk = torch.empty_like(dq)
+    dv = torch.empty(tuple(v.shape), dtype=out_dtype, device=q.device)
+    L = load()
+    if workspace is None:
+        nbytes = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise TypeError(f"workspace must be a contiguous uint8 tensor on {q.device}")
+    _check(L.gdr_linear_chunk_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv

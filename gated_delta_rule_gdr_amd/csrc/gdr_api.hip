@@ -171,9 +171,50 @@ using namespace gdr;
 GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
 
 namespace {
-// The channel-gate prefill for bf16 inputs and the delta rule runs as two
-// kernels that pass per-chunk records through the workspace; every other
-// prefill is one fused kernel and needs none.
+// The channel-gate prefill for bf16 inputs runs as two kernels that pass
+// per-chunk records through the workspace; every other prefill is one fused
+// kernel and needs none.
+// What the linear-attention backward covers (the plain linear rule of the
+// page that derives it), on top of the forward's checks of the arguments.
+gdr_status validate_bwd_shape(const gdr_args *a) {
+  if (a->rule != GDR_RULE_LINEAR || a->gate != GDR_GATE_NONE)
+    return fail(GDR_E_UNSUPPORTED, "the backward covers the linear rule without a gate");
+  if (a->HV != a->HK)
+    return fail(GDR_E_UNSUPPORTED, "the backward takes one value head per key head (HV = %d, HK = %d)", a->HV, a->HK);
+  if (products_of(*a) > 1) return fail(GDR_E_UNSUPPORTED, "the backward takes one transition per token");
+  return GDR_OK;
+}
+
+gdr_status validate_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv) {
+  if (!a) return fail(GDR_E_INVALID, "args is NULL");
+  gdr_args b = *a;
+  b.o = dq;   // the forward's checks then cover dq as its output
+  if (a->T_total > 0 && a->N > 0 && !dq) return fail(GDR_E_INVALID, "dq is NULL");
+  gdr_status st = validate(&b, Call::Chunk);
+  if (st != GDR_OK) return st;
+  if ((st = validate_bwd_shape(a)) != GDR_OK) return st;
+  if (a->N == 0 || a->T_total == 0) return GDR_OK;
+  if (!dout || !dk || !dv) return fail(GDR_E_INVALID, "dout / dk / dv is NULL");
+  const void *ptrs[] = {dout, dk, dv};
+  for (const void *ptr : ptrs)
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return fail(GDR_E_INVALID, "dout, dk and dv must be 16-byte aligned");
+  const int64_t row = (int64_t)a->HV * a->DV;
+  const size_t ie = dtype_bytes(a->in_dtype), oe = dtype_bytes(a->out_dtype);
+  const Range outs[] = {span(dq, a->T_total, row, row, oe), span(dk, a->T_total, row, row, oe),
+                        span(dv, a->T_total, row, row, oe)};
+  const Range ins[] = {span(a->q, a->T_total, a->q_stride_t, row, ie), span(a->k, a->T_total, a->k_stride_t, row, ie),
+                       span(a->v, a->T_total, a->v_stride_t, row, ie), span(dout, a->T_total, row, row, ie),
+                       span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV,
+                            dtype_bytes(a->state_dtype))};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range &r : ins)
+      if (overlap(outs[i], r)) return fail(GDR_E_INVALID, "dq / dk / dv overlaps an input or the state pool");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDR_E_INVALID, "dq, dk and dv overlap each other");
+  }
+  return GDR_OK;
+}
+
 bool uses_workspace(const gdr_args *a) {
   return a->N > 0 && a->T_total > 0 && chunk_fwd_kda_applies(*a) && !prefill_force_generic();
 }
@@ -218,6 +259,32 @@ GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) 
   }
   hipError_t e = launch_recurrent_step(*a, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent_step launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+GDR_EXPORT size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a) {
+  if (!a) return 0;
+  g_last_error[0] = '\0';
+  if (validate_bwd_shape(a) != GDR_OK || a->N <= 0 || a->T_total <= 0) return 0;
+  if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK)) return 0;
+  return linear_bwd_workspace(*a);
+}
+
+GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                           void *workspace, size_t ws_bytes, hipStream_t stream) {
+  gdr_status s = validate_bwd(a, dout, dq, dk, dv);
+  if (s != GDR_OK) return s;
+  if (a->N == 0 || a->T_total == 0) return GDR_OK;
+  const size_t need = linear_bwd_workspace(*a);
+  if (!workspace || ws_bytes < need)
+    return fail(GDR_E_WORKSPACE, "workspace of %zu bytes at %p: the backward needs %zu", ws_bytes, workspace, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_E_INVALID, "workspace is not 256-byte aligned");
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_linear_bwd(*a, dout, dq, dk, dv, workspace, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "linear_chunk_bwd launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

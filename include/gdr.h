@@ -13,7 +13,7 @@
  * Gates arrive as g = log(alpha) <= 0 (the KDA page, section 4, notes that
  * implementations store this form and exponentiate it).
  *
- * Two schedules compute the same result:
+ * Three entry points compute the same result:
  *   gdr_chunk_fwd       chunkwise prefill over a ragged batch (the chunk
  *                       regrouping of section 6 of the KDA page and section 4
  *                       of "From Attention to Learned Memory");
@@ -21,6 +21,7 @@
  *   gdr_recurrent_fwd   the tokenwise recurrence over a ragged batch, the
  *                       state in registers across each sequence (the
  *                       "gated_delta" Mojo page's kernel).
+ * gdr_linear_chunk_bwd gives the gradients of the plain linear rule.
  *
  * Memory. Every pointer is device memory owned by the caller; the library
  * neither allocates, frees nor keeps any of them after the call returns.
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -176,6 +177,31 @@ gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
  * example views into a fused qkv buffer through the token strides). Needs no
  * workspace. */
 gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream);
+
+/* Bytes of device workspace gdr_linear_chunk_bwd needs with these arguments
+ * (0 for arguments it does not cover, or when there is no work). For T_total
+ * tokens of H heads of width D it is about 4 reversed input copies and one
+ * output copy of T_total * H * D elements plus an fp32 pool of N * H * D * D. */
+size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
+
+/* Gradients of causal linear attention ("From Attention to Learned Memory",
+ * section "Backward: reverse the boundary scan, then differentiate each
+ * chunk"): for o_t = scale * S_t q_t, S_t = S_0 + sum_{tau <= t} v_tau k_tau^T
+ * and a loss with upstream gradient dout (= dL/do), writes
+ *   dq [T_total, HK, DK], dk [T_total, HK, DK], dv [T_total, HV, DV]
+ * (contiguous, out_dtype). `a` describes the forward call: q, k, v, their
+ * strides and in_dtype, cu_seqlens, the initial state S_0 read from
+ * state_pool[slot_idx[n]] (never written) unless GDR_FLAG_ZERO_INIT, scale,
+ * chunk_size 64; `a->o` is ignored. dout is [T_total, HV, DV], contiguous, in
+ * in_dtype. Covered: the linear rule with gate NONE, HV == HK, one transition
+ * per token (else GDR_E_UNSUPPORTED). The final state's gradient is taken as
+ * zero and the initial state's is not formed. `workspace` (device memory,
+ * 256-byte aligned, at least gdr_linear_chunk_bwd_workspace_bytes) is scratch;
+ * calls sharing one must not overlap. Each gradient runs as one chunkwise
+ * forward pass with the roles of q, k, v and dout exchanged (dk and dv with
+ * every sequence's tokens reversed). */
+gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdr_status_string(gdr_status s);

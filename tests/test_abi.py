@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["gdr_abi_version", "gdr_chunk_fwd_workspace_bytes", "gdr_chunk_fwd",
                             "gdr_recurrent_step", "gdr_recurrent_fwd", "gdr_status_string",
-                            "gdr_last_error"])
+                            "gdr_last_error", "gdr_linear_chunk_bwd_workspace_bytes",
+                            "gdr_linear_chunk_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == gdr.ABI_VERSION == 3
+    assert L.gdr_abi_version() == gdr.ABI_VERSION == 4
 
 
 def test_args_struct_matches_header_field_order():
@@ -205,3 +206,32 @@ def test_binding_checks_product_rows():
     with pytest.raises(ValueError, match="T \\* products"):
         gdr.recurrent_fwd(q, k, v, None, beta, pool, torch.zeros(1, dtype=torch.int32),
                           torch.tensor([0, T], dtype=torch.int32), gate="none", products=P)
+
+
+
+def test_linear_backward_rejects_on_host():
+    """The backward covers the linear rule without a gate and HV == HK; it
+    checks its outputs, their overlaps and the workspace before any launch."""
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    a.rule, a.gate, a.HV, a.beta, a.g = 1, 0, 2, None, None
+    a.v_stride_t = 2 * 128
+    need = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    rows = a.T_total * 2 * 128
+    assert need >= 4 * rows * 2 + rows * 4 + a.N * 2 * 128 * 128 * 4
+    dout, dq, dk, dv, ws = 0x7000000, 0x8000000, 0x8100000, 0x8200000, 0x10000000
+    call = lambda aa, **kw: L.gdr_linear_chunk_bwd(
+        ctypes.byref(aa), kw.get("dout", dout), kw.get("dq", dq), kw.get("dk", dk), kw.get("dv", dv),
+        kw.get("ws", ws), kw.get("wsb", need), None)
+    assert call(a, ws=None) == 3                      # no workspace
+    assert call(a, wsb=need - 1) == 3                 # short workspace
+    assert call(a, ws=ws + 16) == 1                   # misaligned workspace
+    assert call(a, dk=None) == 1
+    assert call(a, dv=dq + 64) == 1                   # outputs overlap
+    assert call(a, dq=0x1000) == 1                    # dq overlaps q
+    assert call(a, dout=dout + 4) == 1                # misaligned dout
+    b = _valid_args(gdr)                              # delta rule, scalar gate
+    assert L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(b)) == 0
+    assert call(b) == 2
+    a.HV, a.v_stride_t = 4, 4 * 128                   # grouped heads
+    assert call(a) == 2
