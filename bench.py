@@ -19,7 +19,8 @@ heads); `roofline` describes the prefill kernel against HBM bandwidth (its
 binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
 fraction alongside; `decode` gives steps/s and HBM fraction of the step
 kernel; `linear_mode` the same shapes with alpha = 1 and no delta (linear
-attention); `recurrent_fwd` the same for the tokenwise recurrence; `delta_product`
+attention) and `linear_backward` its gradients (dq, dk, dv); `recurrent_fwd` the
+same for the tokenwise recurrence; `delta_product`
 the chunkwise prefill of Gated DeltaProduct (2 transitions per token) on the
 headline shapes; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
@@ -303,6 +304,46 @@ def bench_product(w: synth.Workload, P: int, steps: int, warmup: int = 3):
     return e0.elapsed_time(e1) / steps
 
 
+def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
+    """Mean time (ms) of gdr_linear_chunk_bwd on w's batch (all of its
+    kernels: the input reversals, three chunkwise passes, the output
+    reversals), with a workspace allocated once."""
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    x = synth.generate(w)
+    do = synth.generate(w.replace(seed=w.seed + 500))["v"]
+    a = dict(q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
+             v=_dev(x["v"], w.in_dtype, dev), do=_dev(do, w.in_dtype, dev),
+             pool=_dev(x["pool"], w.state_dtype, dev), slot_idx=_dev(x["slot_idx"], "i32", dev),
+             cu_seqlens=_dev(x["cu_seqlens"], "i32", dev))
+    del x, do
+    L = gdr.load()
+    ws = None
+
+    def run():
+        return gdr.linear_chunk_bwd(a["q"], a["k"], a["v"], a["do"], a["pool"], a["slot_idx"],
+                                    a["cu_seqlens"], zero_init=w.zero_init, workspace=ws)
+    run()
+    import ctypes
+    args, _ = gdr._prepare(a["q"], a["k"], a["v"], None, None, a["pool"], a["slot_idx"],
+                           a["cu_seqlens"], None, None, "linear", "none", w.zero_init, False, 64,
+                           torch.float32)
+    ws = torch.empty(L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(args)), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 # ----------------------------------------------------------------------------
 # CPU leg: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -360,6 +401,7 @@ def main():
     ap.add_argument("--no-recurrent", action="store_true")
     ap.add_argument("--product-steps", type=int, default=20)
     ap.add_argument("--no-linear", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-product", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -462,6 +504,18 @@ def main():
             "mfma_tflops": lf / (l_ms * 1e-3) / 1e12,
             "mfma_frac": lf / (l_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "traffic": committed_traffic(lk, lw.name, lsrc)}
+    if not args.no_backward and w.name == synth.HEADLINE:
+        # gradients of the linear-attention mode (dq, dk, dv from dO)
+        bw = synth.workload("la_prefill_b4_t4096_h16_d128")
+        bt = bench_linear_bwd(bw, args.steps)
+        T, HD = bw.T_total, bw.HV * bw.DK
+        bb = 4 * T * HD * _isz(bw.in_dtype) + 3 * T * HD * 4   # q, k, v, dO read; dq, dk, dv fp32
+        bf = 3 * prefill_flops(bw, bw.chunk_size)                # one linear pass per gradient
+        result["linear_backward"] = {
+            "workload": bw.name, "steps": args.steps, "ms": bt, "tokens_per_s": T / (bt * 1e-3),
+            "algorithmic_bytes": bb, "hbm_gbs": bb / (bt * 1e-3) / 1e9,
+            "hbm_frac": bb / (bt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_flops": bf, "mfma_tflops": bf / (bt * 1e-3) / 1e12}
     if not args.no_product:
         pw, P = synth.workload(synth.HEADLINE), 2
         pt = bench_product(pw, P, args.product_steps)
