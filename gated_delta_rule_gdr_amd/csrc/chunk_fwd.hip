@@ -811,6 +811,7 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   p.st_bf16 = a.state_dtype == GDR_BF16;
   p.out_bf16 = a.out_dtype == GDR_BF16;
   p.P = products_of(a);
+  p.rev = 0;   // (the reversed walk is the warp-specialised kernel's)
   if (a.in_dtype == GDR_BF16) return by_gate<false>(a, p, stream);
   return by_gate<true>(a, p, stream);
 }

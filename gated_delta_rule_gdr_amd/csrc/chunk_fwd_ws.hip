@@ -193,16 +193,33 @@ __device__ __forceinline__ void ldfrag2(const uint16_t *hi, const uint16_t *lo, 
 // the query of the substep's token (only a token's last substep keeps its
 // output, and an output row depends on no other row's query), and the
 // token's gate on its first substep only (gfirst; the others decay by 1).
-template <int GATE, bool DELTA, int D, bool PROD>
+// With REV the sequence is walked backwards: its row t is memory row
+// mirror - t (mirror = the sequence's first row + its last row).
+template <int GATE, bool DELTA, int D, bool PROD, bool REV>
 __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, int64_t t0, int L,
-                                          int h, int hk, int ptid) {
+                                          int h, int hk, int ptid, int64_t mirror) {
   constexpr int KU = PrefWS<D>::KU;
   const int krow = ptid / (D / 8), krs = 64 * NSTG / (D / 8), kc = (ptid % (D / 8)) * 16;
   const char *kb = static_cast<const char *>(p.k) + (t0 * p.k_stride + (int64_t)hk * D) * 2;
   const char *qb = static_cast<const char *>(p.q) + ((PROD ? t0 / p.P : t0) * p.q_stride + (int64_t)hk * D) * 2;
   const uint32_t ks = (uint32_t)(p.k_stride * 2), qs = (uint32_t)(p.q_stride * 2);
   const int last = L - 1;
-  if constexpr (!PROD) {
+  if constexpr (REV) {
+    const int64_t top = mirror - t0;   // memory row of row t0; later rows lie below it
+    const char *kt = static_cast<const char *>(p.k) + (top * p.k_stride + (int64_t)hk * D) * 2;
+    const char *qt = static_cast<const char *>(p.q) + (top * p.q_stride + (int64_t)hk * D) * 2;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int64_t row = min(krow + u * krs, last);
+      put4(pf.k, u, *reinterpret_cast<const uint4 *>(kt - row * ks + kc));
+      put4(pf.q, u, *reinterpret_cast<const uint4 *>(qt - row * qs + kc));
+    }
+    if (ptid < 64) {
+      const int64_t th = (top - min(ptid, last)) * p.HV + h;
+      if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
+      if constexpr (DELTA) pf.beta = p.beta[th];
+    }
+  } else if constexpr (!PROD) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const uint32_t row = (uint32_t)min(krow + u * krs, last);
@@ -457,7 +474,7 @@ __device__ __forceinline__ void store_hold(SM &sm, const HoldWS &h, int r, int g
 // only); the stagers stage the keys and queries of chunk c+1 (and issue the
 // loads of chunk c+2) and count those in; then R and A, the diagonal
 // inverses and the block columns of T of chunk c+1 (role_ws).
-template <int PW, int NP, int GATE, bool DELTA, int D, int NSW, bool PROD>
+template <int PW, int NP, int GATE, bool DELTA, int D, int NSW, bool PROD, bool REV>
 __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, NSW> &sm, int lane,
                                                 int r, int g, int h, int hk, int64_t bos,
                                                 int64_t eos, int nc) {
@@ -497,7 +514,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
     if constexpr (!KEYS) {
       if (ci + 1 < nc) {
         const int64_t tn = t0 + C;
-        prep_load<GATE, DELTA, D, PROD>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid);
+        prep_load<GATE, DELTA, D, PROD, REV>(pf, p, tn, (int)min<int64_t>(C, eos - tn), h, hk, ptid, bos + eos - 1);
       }
       return;
     }
@@ -539,7 +556,7 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
 
   if (nc == 0) return;
   if constexpr (STAGER) {
-    prep_load<GATE, DELTA, D, PROD>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid);
+    prep_load<GATE, DELTA, D, PROD, REV>(pf, p, bos, (int)min<int64_t>(C, eos - bos), h, hk, ptid, bos + eos - 1);
     stage(0, KeysT{});
     stage(0, QueriesT{});
     count_in(&sm.kcount, &sm.qcount, lane);
@@ -586,7 +603,9 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
 // PROD: more than one transition per token (Gated DeltaProduct): the kernel
 // runs the virtual sequence of substeps ("Linear attention visualized",
 // GDP as GDN over a virtual sequence) and keeps each token's last output.
-template <int GATE, bool DELTA, int D, int NSW, bool PROD>
+// REV: each sequence's rows walked backwards (its last row first); the
+// gradients of linear attention run the forward pass this way.
+template <int GATE, bool DELTA, int D, int NSW, bool PROD, bool REV>
 __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_kernel(ChunkParams p) {
   constexpr int NP = prep_waves<NSW>();
   constexpr int NTH = 64 * (NSW + NP);
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   // Both roles pass the same barriers: one after the prologue and one at the
   // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
   if (w >= NSW) {
-#define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW, PROD>(p, sm, lane, r, g, h, hk, bos, eos, nc)
+#define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW, PROD, REV>(p, sm, lane, r, g, h, hk, bos, eos, nc)
     switch (w - NSW) {
       case 0: GDR_PREP(0); break;
       case 1: GDR_PREP(1); break;
@@ -676,6 +695,13 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   auto load_v = [&](int ci) {
     const int64_t t0 = bos + (int64_t)ci * C;
     const int last = (int)min<int64_t>(C, eos - t0) - 1;
+    if constexpr (REV) {
+      const int64_t row = bos + eos - 1 - t0 - min(lane, last);
+      const char *vr = static_cast<const char *>(p.v) + (row * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
+      put4(vreg, 0, *reinterpret_cast<const uint4 *>(vr));
+      put4(vreg, 1, *reinterpret_cast<const uint4 *>(vr + 16));
+      return;
+    }
     const char *vbase = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
     const uint32_t off = (uint32_t)min(lane, last) * (uint32_t)(p.v_stride * 2);
     put4(vreg, 0, *reinterpret_cast<const uint4 *>(vbase + off));
@@ -932,7 +958,21 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         const uint32_t olane = ((uint32_t)(4 * g) * HVDu + (uint32_t)col) * osz;
         // (uniform branches: a full chunk stores unmasked; rows past a
         // partial chunk's end are skipped)
-        if constexpr (PROD) {
+        if constexpr (REV) {
+          // row t0 + ii of the walk is memory row bos + eos - 1 - (t0 + ii)
+          char *ocol = static_cast<char *>(p.o) + ((bos + eos - 1 - t0) * HVD + (int64_t)h * D + col) * osz;
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ii = 16 * I + 4 * g + i;
+              if (ii < L) {
+                char *dst = ocol - (int64_t)ii * HVD * osz;
+                if (p.out_bf16) *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(oa[I][i]);
+                else *reinterpret_cast<float *>(dst) = oa[I][i];
+              }
+            }
+        } else if constexpr (PROD) {
           // a token's output is its last substep's: row t0 + ii goes to o
           // row (t0 + ii) / P when it is one, and is dropped otherwise
           const SubMap map(t0, p.P);
@@ -1004,10 +1044,17 @@ hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
   const int grp = p.ratio * (D / (16 * NSW));
   const int blocks = ((p.N * p.HK + 7) / 8) * 8 * grp;
   if (p.P > 1)
-    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, true>), dim3(blocks),
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, true, false>), dim3(blocks),
                        dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
-  else
-    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, false>), dim3(blocks),
+  else if (p.rev) {
+    // (the reversed walk serves the linear-attention gradients only)
+    if constexpr (GATE == GDR_GATE_NONE && !DELTA)
+      hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, false, true>), dim3(blocks),
+                         dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+  } else
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, false, false>), dim3(blocks),
                        dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
   return hipGetLastError();
 }
@@ -1060,6 +1107,7 @@ hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {
   p.st_bf16 = a.state_dtype == GDR_BF16;
   p.out_bf16 = a.out_dtype == GDR_BF16;
   p.P = products_of(a);
+  p.rev = (a.flags & kFlagReverse) ? 1 : 0;
   if (a.gate == GDR_GATE_SCALAR) return ws_by_rule<GDR_GATE_SCALAR>(a, p, stream);
   return ws_by_rule<GDR_GATE_NONE>(a, p, stream);
 }

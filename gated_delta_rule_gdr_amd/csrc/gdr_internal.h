@@ -31,6 +31,12 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// Internal flag (never accepted from callers): the prefill walks each
+// sequence's rows backwards, its last row first, and writes each output row
+// to the row it was read from. Taken by the warp-specialised kernel (bf16
+// inputs, no channel gate, one transition per token) only.
+constexpr uint32_t kFlagReverse = 1u << 31;
+
 // Transitions per token (Gated DeltaProduct's n_h; 0 in the arguments means 1).
 constexpr int kMaxProducts = 8;
 inline int products_of(const gdr_args &a) { return a.products > 1 ? a.products : 1; }

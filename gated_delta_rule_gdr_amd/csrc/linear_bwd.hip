@@ -17,10 +17,12 @@
 // (queries k, keys q, values dO) from a zero state. The state those reversed
 // passes carry from chunk to chunk is the page's boundary-state gradient G,
 // scanned from the last chunk back. So the backward runs on the chunkwise
-// forward kernels, MFMA and all, and this file adds only what they do not do:
-// copies of the inputs with each sequence's rows reversed, the reversal of
-// the two reversed outputs, the transposed initial states, and the slot
-// indices of the scratch pool the passes write their (unused) final states to.
+// forward kernels, MFMA and all. With bf16 inputs the warp-specialised kernel
+// walks the sequences backwards itself (reading and writing the original
+// rows); otherwise this file copies the inputs with each sequence's rows
+// reversed and reverses the two outputs back. It also forms the transposed
+// initial states and the slot indices of the scratch pool the passes write
+// their (unused) final states to.
 //
 // Readings where the page is silent: the final state's gradient is zero (the
 // loss reads the outputs only) and the initial state's gradient is not formed.
@@ -89,9 +91,14 @@ struct BwdLayout {
   size_t rq, rk, rv, rdo, rout, pool, slots, total;
 };
 
+// Whether the passes run on reversed copies (the general kernel) or walk the
+// sequences backwards themselves (the warp-specialised kernel, bf16 inputs).
+bool walks_backwards(const gdr_args &a) { return a.in_dtype == GDR_BF16 && !prefill_force_generic(); }
+
 BwdLayout layout(const gdr_args &a) {
   const size_t ie = a.in_dtype == GDR_BF16 ? 2 : 4, oe = a.out_dtype == GDR_BF16 ? 2 : 4;
-  const size_t rows = (size_t)a.T_total * a.HV * a.DK;   // one [T, H, D] array (HK = HV, DK = DV)
+  // one [T, H, D] array (HK = HV, DK = DV), when copies are needed
+  const size_t rows = walks_backwards(a) ? 0 : (size_t)a.T_total * a.HV * a.DK;
   BwdLayout l;
   l.rq = 0;
   l.rk = l.rq + align256(rows * ie);
@@ -120,6 +127,45 @@ hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void
   const unsigned T = (unsigned)a.T_total;
 
   hipLaunchKernelGGL(iota_kernel, dim3((a.N + 255) / 256), dim3(256), 0, stream, slots, a.N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // one forward pass of the linear rule from the given state (or zero)
+  auto pass = [&](const void *q, int64_t qs, const void *k, int64_t ks, const void *v, int64_t vs, void *o,
+                  bool zero, bool rev) {
+    gdr_args b = a;
+    b.q = q; b.k = k; b.v = v;
+    b.q_stride_t = qs; b.k_stride_t = ks; b.v_stride_t = vs;
+    b.g = nullptr; b.beta = nullptr;
+    b.o = o;
+    b.state_pool = aux; b.state_dtype = GDR_F32; b.num_slots = a.N; b.slot_idx = slots;
+    b.rule = GDR_RULE_LINEAR; b.gate = GDR_GATE_NONE; b.products = 1;
+    b.flags = (zero ? GDR_FLAG_ZERO_INIT : 0u) | (rev ? kFlagReverse : 0u);
+    return launch_chunk_fwd(b, stream);
+  };
+  const bool zero = (a.flags & GDR_FLAG_ZERO_INIT) != 0;
+  auto dq_pass = [&]() {
+    // dq: forward time, queries dO, keys v, values k, from S_0^T
+    if (!zero) {
+      if (a.state_dtype == GDR_BF16)
+        hipLaunchKernelGGL(transpose_state_kernel<true>, dim3(a.N * a.HV), dim3(256), 0, stream, a.state_pool,
+                           a.slot_idx, aux, a.HV, a.DK);
+      else
+        hipLaunchKernelGGL(transpose_state_kernel<false>, dim3(a.N * a.HV), dim3(256), 0, stream, a.state_pool,
+                           a.slot_idx, aux, a.HV, a.DK);
+      const hipError_t te = hipGetLastError();
+      if (te != hipSuccess) return te;
+    }
+    return pass(dout, HD, a.v, a.v_stride_t, a.k, a.k_stride_t, dq, zero, false);
+  };
+
+  if (walks_backwards(a)) {
+    // the warp-specialised kernel walks the sequences backwards itself
+    if ((e = pass(a.k, a.k_stride_t, a.q, a.q_stride_t, dout, HD, dv, true, true)) != hipSuccess) return e;
+    if ((e = pass(a.v, a.v_stride_t, dout, HD, a.q, a.q_stride_t, dk, true, true)) != hipSuccess) return e;
+    return dq_pass();
+  }
+
   // reversed copies of q, k, v (token strides as given) and dO (contiguous)
   auto rev_in = [&](const void *src, int64_t stride_elems, size_t off) {
     hipLaunchKernelGGL(reverse_rows_kernel, dim3(T), dim3(RTPB), 0, stream, static_cast<const char *>(src),
@@ -129,22 +175,7 @@ hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void
   rev_in(a.k, a.k_stride_t, l.rk);
   rev_in(a.v, a.v_stride_t, l.rv);
   rev_in(dout, HD, l.rdo);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  // one forward pass of the linear rule from the given state (or zero)
-  auto pass = [&](const void *q, int64_t qs, const void *k, int64_t ks, const void *v, int64_t vs, void *o,
-                  bool zero) {
-    gdr_args b = a;
-    b.q = q; b.k = k; b.v = v;
-    b.q_stride_t = qs; b.k_stride_t = ks; b.v_stride_t = vs;
-    b.g = nullptr; b.beta = nullptr;
-    b.o = o;
-    b.state_pool = aux; b.state_dtype = GDR_F32; b.num_slots = a.N; b.slot_idx = slots;
-    b.rule = GDR_RULE_LINEAR; b.gate = GDR_GATE_NONE; b.products = 1;
-    b.flags = zero ? GDR_FLAG_ZERO_INIT : 0u;
-    return launch_chunk_fwd(b, stream);
-  };
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   auto rev_out = [&](void *dst) {
     hipLaunchKernelGGL(reverse_rows_kernel, dim3(T), dim3(RTPB), 0, stream, (const char *)(w + l.rout),
                        (int64_t)(HD * oe), static_cast<char *>(dst), (int64_t)(HD * oe), units_out, a.cu_seqlens,
@@ -152,23 +183,12 @@ hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void
     return hipGetLastError();
   };
   // dv: reversed time, queries k, keys q, values dO
-  if ((e = pass(w + l.rk, HD, w + l.rq, HD, w + l.rdo, HD, w + l.rout, true)) != hipSuccess) return e;
+  if ((e = pass(w + l.rk, HD, w + l.rq, HD, w + l.rdo, HD, w + l.rout, true, false)) != hipSuccess) return e;
   if ((e = rev_out(dv)) != hipSuccess) return e;
   // dk: reversed time, queries v, keys dO, values q
-  if ((e = pass(w + l.rv, HD, w + l.rdo, HD, w + l.rq, HD, w + l.rout, true)) != hipSuccess) return e;
+  if ((e = pass(w + l.rv, HD, w + l.rdo, HD, w + l.rq, HD, w + l.rout, true, false)) != hipSuccess) return e;
   if ((e = rev_out(dk)) != hipSuccess) return e;
-  // dq: forward time, queries dO, keys v, values k, from S_0^T
-  const bool zero = (a.flags & GDR_FLAG_ZERO_INIT) != 0;
-  if (!zero) {
-    if (a.state_dtype == GDR_BF16)
-      hipLaunchKernelGGL(transpose_state_kernel<true>, dim3(a.N * a.HV), dim3(256), 0, stream, a.state_pool,
-                         a.slot_idx, aux, a.HV, a.DK);
-    else
-      hipLaunchKernelGGL(transpose_state_kernel<false>, dim3(a.N * a.HV), dim3(256), 0, stream, a.state_pool,
-                         a.slot_idx, aux, a.HV, a.DK);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return pass(dout, HD, a.v, a.v_stride_t, a.k, a.k_stride_t, dq, zero);
+  return dq_pass();
 }
 
 }  // namespace gdr

@@ -179,9 +179,10 @@ gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
 gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream);
 
 /* Bytes of device workspace gdr_linear_chunk_bwd needs with these arguments
- * (0 for arguments it does not cover, or when there is no work). For T_total
- * tokens of H heads of width D it is about 4 reversed input copies and one
- * output copy of T_total * H * D elements plus an fp32 pool of N * H * D * D. */
+ * (0 for arguments it does not cover, or when there is no work): an fp32
+ * scratch pool of N * H * D * D values and N slot indices; with fp32 inputs
+ * also four reversed input copies and one output copy of T_total * H * D
+ * elements. */
 size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
 
 /* Gradients of causal linear attention ("From Attention to Learned Memory",
@@ -198,8 +199,8 @@ size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
  * zero and the initial state's is not formed. `workspace` (device memory,
  * 256-byte aligned, at least gdr_linear_chunk_bwd_workspace_bytes) is scratch;
  * calls sharing one must not overlap. Each gradient runs as one chunkwise
- * forward pass with the roles of q, k, v and dout exchanged (dk and dv with
- * every sequence's tokens reversed). */
+ * forward pass with the roles of q, k, v and dout exchanged (dk and dv walk
+ * every sequence's tokens backwards). */
 gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
 

@@ -218,7 +218,10 @@ def test_linear_backward_rejects_on_host():
     a.v_stride_t = 2 * 128
     need = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
     rows = a.T_total * 2 * 128
-    assert need >= 4 * rows * 2 + rows * 4 + a.N * 2 * 128 * 128 * 4
+    assert need >= a.N * 2 * 128 * 128 * 4 + a.N * 4   # bf16: scratch pool and slots only
+    a.in_dtype = 0                                     # fp32 inputs: reversed copies as well
+    assert L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a)) >= 4 * rows * 4 + rows * 4 + need
+    a.in_dtype = 1
     dout, dq, dk, dv, ws = 0x7000000, 0x8000000, 0x8100000, 0x8200000, 0x10000000
     call = lambda aa, **kw: L.gdr_linear_chunk_bwd(
         ctypes.byref(aa), kw.get("dout", dout), kw.get("dq", dq), kw.get("dk", dk), kw.get("dv", dv),
