@@ -959,18 +959,23 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
         // (uniform branches: a full chunk stores unmasked; rows past a
         // partial chunk's end are skipped)
         if constexpr (REV) {
-          // row t0 + ii of the walk is memory row bos + eos - 1 - (t0 + ii)
-          char *ocol = static_cast<char *>(p.o) + ((bos + eos - 1 - t0) * HVD + (int64_t)h * D + col) * osz;
+          // Row t0 + ii of the walk is memory row bos + eos - 1 - (t0 + ii).
+          // The descriptor starts at the lowest of the chunk's L rows and
+          // spans L rows, so row ii sits (L - 1 - ii) rows up; rows past
+          // the chunk's end (ii >= L) wrap to huge offsets and are dropped
+          // by the descriptor's range check.
+          char *rbase = static_cast<char *>(p.o) + ((bos + eos - 1 - t0 - (L - 1)) * HVD + (int64_t)h * D) * osz;
+          const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(rbase, 0, (int)(L * orow), 0x00020000);
+          const uint32_t rlane = (uint32_t)(L - 1 - 4 * g) * orow + (uint32_t)col * osz;
 #pragma unroll
           for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int ii = 16 * I + 4 * g + i;
-              if (ii < L) {
-                char *dst = ocol - (int64_t)ii * HVD * osz;
-                if (p.out_bf16) *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(oa[I][i]);
-                else *reinterpret_cast<float *>(dst) = oa[I][i];
-              }
+              const uint32_t voff = rlane - (uint32_t)(16 * I + i) * orow;
+              if (p.out_bf16)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), rrs, voff, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][i]), rrs, voff, 0, 0);
             }
         } else if constexpr (PROD) {
           // a token's output is its last substep's: row t0 + ii goes to o
