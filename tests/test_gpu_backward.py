@@ -100,3 +100,22 @@ def test_linear_backward_full_size_headline_shapes():
     hh = torch.as_tensor(heads, device=dq.device)
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_out(host(got[:, hh], "f32"), want, "bf16", what=name)
+
+
+def test_linear_backward_on_fused_qkv_views():
+    """q, k, v as views into one fused [T, 3 H D] buffer (token strides of
+    3 H D): the gradients equal those from separate contiguous tensors."""
+    gdr = _gdr()
+    w = small(128, "bf16", False, seqlens=(90, 0, 33, 130), seed=83)
+    x = inputs(w)
+    d = {n: dev(x[n], w.in_dtype) for n in ("q", "k", "v", "do")}
+    pool = dev(x["pool"], w.state_dtype)
+    slot, cu = dev(x["slot_idx"], "i32"), dev(x["cu_seqlens"], "i32")
+    T, HD = w.T_total, w.HK * w.DK
+    fused = torch.cat([d["q"].reshape(T, HD), d["k"].reshape(T, HD), d["v"].reshape(T, HD)], 1)
+    q, k, v = (fused[:, i * HD:(i + 1) * HD].view(T, w.HK, w.DK) for i in range(3))
+    a = gdr.linear_chunk_bwd(d["q"], d["k"], d["v"], d["do"], pool, slot, cu)
+    b = gdr.linear_chunk_bwd(q, k, v, d["do"], pool, slot, cu)
+    torch.cuda.synchronize()
+    for ga, gb in zip(a, b):
+        assert torch.equal(ga, gb)
