@@ -205,17 +205,19 @@ __device__ __forceinline__ void prep_load(PrefWS<D> &pf, const ChunkParams &p, i
   const uint32_t ks = (uint32_t)(p.k_stride * 2), qs = (uint32_t)(p.q_stride * 2);
   const int last = L - 1;
   if constexpr (REV) {
-    const int64_t top = mirror - t0;   // memory row of row t0; later rows lie below it
-    const char *kt = static_cast<const char *>(p.k) + (top * p.k_stride + (int64_t)hk * D) * 2;
-    const char *qt = static_cast<const char *>(p.q) + (top * p.q_stride + (int64_t)hk * D) * 2;
+    // the chunk's rows t0 .. t0 + last are memory rows bot + last .. bot:
+    // 32-bit offsets up from the lowest, as in the forward walk
+    const int64_t bot = mirror - t0 - last;
+    const char *kl = static_cast<const char *>(p.k) + (bot * p.k_stride + (int64_t)hk * D) * 2;
+    const char *ql = static_cast<const char *>(p.q) + (bot * p.q_stride + (int64_t)hk * D) * 2;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int64_t row = min(krow + u * krs, last);
-      put4(pf.k, u, *reinterpret_cast<const uint4 *>(kt - row * ks + kc));
-      put4(pf.q, u, *reinterpret_cast<const uint4 *>(qt - row * qs + kc));
+      const uint32_t up = (uint32_t)(last - min(krow + u * krs, last));
+      put4(pf.k, u, *reinterpret_cast<const uint4 *>(kl + (up * ks + kc)));
+      put4(pf.q, u, *reinterpret_cast<const uint4 *>(ql + (up * qs + kc)));
     }
     if (ptid < 64) {
-      const int64_t th = (top - min(ptid, last)) * p.HV + h;
+      const int64_t th = (bot + last - min(ptid, last)) * p.HV + h;
       if constexpr (GATE == GDR_GATE_SCALAR) pf.g = p.g[th];
       if constexpr (DELTA) pf.beta = p.beta[th];
     }
@@ -696,10 +698,11 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
     const int64_t t0 = bos + (int64_t)ci * C;
     const int last = (int)min<int64_t>(C, eos - t0) - 1;
     if constexpr (REV) {
-      const int64_t row = bos + eos - 1 - t0 - min(lane, last);
-      const char *vr = static_cast<const char *>(p.v) + (row * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
-      put4(vreg, 0, *reinterpret_cast<const uint4 *>(vr));
-      put4(vreg, 1, *reinterpret_cast<const uint4 *>(vr + 16));
+      const int64_t bot = bos + eos - 1 - t0 - last;   // lowest memory row of the chunk
+      const char *vl = static_cast<const char *>(p.v) + (bot * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
+      const uint32_t up = (uint32_t)(last - min(lane, last)) * (uint32_t)(p.v_stride * 2);
+      put4(vreg, 0, *reinterpret_cast<const uint4 *>(vl + up));
+      put4(vreg, 1, *reinterpret_cast<const uint4 *>(vl + up + 16));
       return;
     }
     const char *vbase = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + vb * BVW + 16 * w) * 2;
