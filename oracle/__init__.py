@@ -11,7 +11,8 @@ Three independent statements of the method:
   * ``bruteforce`` - closed parallel forms on tiny inputs (masked linear
                      attention, decayed scores, the full-sequence delta solve).
 ``product`` states Gated DeltaProduct (n_h transitions per token) the same
-tokenwise way; ``backward`` the gradients of causal linear attention.
+tokenwise way; ``backward`` the gradients of causal linear attention;
+``ring`` the speculative-decode verify ring and its state fold.
 Every function names the passage of the pages it follows. Where the pages are
 silent the reading taken is stated in the function's docstring.
 
@@ -26,10 +27,12 @@ from .bruteforce import (linear_parallel_fp64, delta_parallel_fp64,
                          four_token_chunk_fractions)
 from .product import delta_product_fp64
 from .backward import linear_attention_grads_fp64
+from .ring import ring_record_elements, verify_ring_fp64, state_fold_fp64
 
 __all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16",
            "l2_normalise_fp64", "L2_EPS",
            "chunkwise_fp64", "forward_substitution_unit_lower",
            "linear_parallel_fp64", "delta_parallel_fp64",
            "four_token_chunk_fractions", "delta_product_fp64",
-           "linear_attention_grads_fp64"]
+           "linear_attention_grads_fp64", "ring_record_elements", "verify_ring_fp64",
+           "state_fold_fp64"]
