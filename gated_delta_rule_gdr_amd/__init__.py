@@ -24,7 +24,8 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd", "lib", "lib_path", "GdrError",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd",
+           "verify_ring", "state_fold", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +41,7 @@ FLAG_QK_L2NORM = 4
 
 
 # GDR_ABI_VERSION of include/gdr.h that Args mirrors.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class GdrError(RuntimeError):
@@ -102,6 +103,14 @@ def load() -> ctypes.CDLL:
     L.gdr_linear_chunk_bwd.restype = ctypes.c_int
     L.gdr_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.gdr_ring_record_elements.restype = ctypes.c_int
+    L.gdr_ring_record_elements.argtypes = [ctypes.POINTER(Args)]
+    L.gdr_ring_record_stride.restype = ctypes.c_int
+    L.gdr_ring_record_stride.argtypes = [ctypes.POINTER(Args)]
+    L.gdr_verify_ring.restype = ctypes.c_int
+    L.gdr_verify_ring.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p]
+    L.gdr_state_fold.restype = ctypes.c_int
+    L.gdr_state_fold.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.gdr_status_string.restype = ctypes.c_char_p
     L.gdr_status_string.argtypes = [ctypes.c_int]
     L.gdr_last_error.restype = ctypes.c_char_p
@@ -305,3 +314,42 @@ def linear_chunk_bwd(q, k, v, do, pool, slot_idx, cu_seqlens, *, scale=None, zer
     _check(L.gdr_linear_chunk_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def verify_ring(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, rule="delta", gate=None,
+                out_dtype=None, zero_init=False, o=None, debug_checks=False, qk_l2norm=False):
+    """Verify of a speculative window: the tokenwise recurrence over each
+    sequence's window with the pool left untouched. Returns (o, ring) with
+    ring [T, HV, stride] fp32 records (e, k, log-gate) for state_fold."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
+                    zero_init, debug_checks, 64, out_dtype)
+    if qk_l2norm:
+        a.flags |= FLAG_QK_L2NORM
+    L = load()
+    stride = L.gdr_ring_record_stride(ctypes.byref(a))
+    ring = torch.empty((q.shape[0], v.shape[1], stride), dtype=torch.float32, device=q.device)
+    _check(L.gdr_verify_ring(ctypes.byref(a), ring.data_ptr(), _stream(q)))
+    return o, ring
+
+
+def state_fold(ring, accepted, pool, slot_idx, cu_seqlens, *, HK, gate, debug_checks=False):
+    """Apply each sequence's first accepted[n] records of a verify to its pool
+    slot in place (accepted: [N] int32 on the device)."""
+    import torch
+    T, HV, _ = ring.shape
+    DK = pool.shape[2]
+    if accepted.dtype != torch.int32 or not accepted.is_contiguous():
+        raise TypeError("accepted must be a contiguous int32 tensor")
+    a = Args()
+    a.N, a.HK, a.HV, a.DK, a.DV = slot_idx.shape[0], HK, HV, DK, pool.shape[3]
+    a.T_total = T
+    a.gate = _GATE[gate]
+    a.state_pool, a.state_dtype, a.num_slots = pool.data_ptr(), _dt(pool), pool.shape[0]
+    a.slot_idx, a.cu_seqlens = slot_idx.data_ptr(), cu_seqlens.data_ptr()
+    a.flags = FLAG_DEBUG_CHECKS if debug_checks else 0
+    L = load()
+    if ring.shape[2] != L.gdr_ring_record_stride(ctypes.byref(a)):
+        raise ValueError("ring does not match these shapes and gate")
+    _check(L.gdr_state_fold(ctypes.byref(a), ring.data_ptr(), accepted.data_ptr(), _stream(pool)))

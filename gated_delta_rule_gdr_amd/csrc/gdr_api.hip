@@ -288,6 +288,60 @@ GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, 
   return GDR_OK;
 }
 
+GDR_EXPORT int gdr_ring_record_elements(const gdr_args *a) { return a ? ring_record_elements(*a) : 0; }
+
+GDR_EXPORT int gdr_ring_record_stride(const gdr_args *a) { return a ? ring_record_stride(*a) : 0; }
+
+GDR_EXPORT gdr_status gdr_verify_ring(const gdr_args *a, float *ring, hipStream_t stream) {
+  gdr_status s = validate(a, Call::Recur);
+  if (s != GDR_OK) return s;
+  if (products_of(*a) > 1) return fail(GDR_E_UNSUPPORTED, "the verify takes one transition per token");
+  if (a->N == 0 || a->T_total == 0) return GDR_OK;
+  if (!ring) return fail(GDR_E_INVALID, "ring is NULL");
+  if (reinterpret_cast<uintptr_t>(ring) % 16) return fail(GDR_E_INVALID, "ring must be 16-byte aligned");
+  const Range rr = span(ring, a->T_total * a->HV, ring_record_stride(*a), ring_record_stride(*a), 4);
+  const Range others[] = {span(a->o, a->T_total, (int64_t)a->HV * a->DV, (int64_t)a->HV * a->DV, dtype_bytes(a->out_dtype)),
+                          span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV, dtype_bytes(a->state_dtype)),
+                          span(a->q, a->T_total, a->q_stride_t, (int64_t)a->HK * a->DK, dtype_bytes(a->in_dtype)),
+                          span(a->k, a->T_total, a->k_stride_t, (int64_t)a->HK * a->DK, dtype_bytes(a->in_dtype)),
+                          span(a->v, a->T_total, a->v_stride_t, (int64_t)a->HV * a->DV, dtype_bytes(a->in_dtype))};
+  for (const Range &r : others)
+    if (overlap(rr, r)) return fail(GDR_E_INVALID, "ring overlaps o, an input or the state pool");
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_recurrent_fwd(*a, stream, ring);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "verify_ring launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+GDR_EXPORT gdr_status gdr_state_fold(const gdr_args *a, const float *ring, const int32_t *accepted,
+                                     hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!a) return fail(GDR_E_INVALID, "args is NULL");
+  if (a->N < 0 || a->HK <= 0 || a->HV <= 0 || a->HV % a->HK)
+    return fail(GDR_E_INVALID, "N = %d, HK = %d, HV = %d", a->N, a->HK, a->HV);
+  if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK))
+    return fail(GDR_E_UNSUPPORTED, "head dims DK = %d, DV = %d: built for DK = DV in {64, 128}", a->DK, a->DV);
+  if (!dtype_ok(a->state_dtype)) return fail(GDR_E_INVALID, "unknown state dtype");
+  if (a->gate != GDR_GATE_NONE && a->gate != GDR_GATE_SCALAR && a->gate != GDR_GATE_CHANNEL)
+    return fail(GDR_E_INVALID, "unknown gate %d", (int)a->gate);
+  if (a->N == 0) return GDR_OK;
+  if (!a->state_pool || !a->slot_idx || !a->cu_seqlens || !ring || !accepted)
+    return fail(GDR_E_INVALID, "state_pool / slot_idx / cu_seqlens / ring / accepted is NULL");
+  if (a->num_slots < a->N) return fail(GDR_E_INVALID, "num_slots = %lld < N = %d", (long long)a->num_slots, a->N);
+  if (reinterpret_cast<uintptr_t>(ring) % 16 || reinterpret_cast<uintptr_t>(a->state_pool) % 16)
+    return fail(GDR_E_INVALID, "ring and state_pool must be 16-byte aligned");
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    gdr_status s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_state_fold(*a, ring, accepted, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "state_fold launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
 GDR_EXPORT gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream) {
   gdr_status s = validate(a, Call::Recur);
   if (s != GDR_OK) return s;

@@ -46,7 +46,13 @@ inline int products_of(const gdr_args &a) { return a.products > 1 ? a.products :
 // ---------------------------------------------------------------------------
 
 hipError_t launch_recurrent_step(const gdr_args &a, hipStream_t stream);
-hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream);
+// (ring != nullptr: the verify of a speculative window, recording into ring)
+hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream, float *ring = nullptr);
+// Elements of one verify record: e (DV), k (DK), the gate (1, DK or none);
+// records lie ring_record_stride apart (rounded up to a multiple of 4).
+int ring_record_elements(const gdr_args &a);
+int ring_record_stride(const gdr_args &a);
+hipError_t launch_state_fold(const gdr_args &a, const float *ring, const int32_t *accepted, hipStream_t stream);
 hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
 // Linear-attention backward: three chunkwise forward passes with exchanged
 // roles (linear_bwd.hip); its workspace in bytes.

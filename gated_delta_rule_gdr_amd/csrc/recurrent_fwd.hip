@@ -66,6 +66,8 @@ struct RecParams {
   float scale;
   int zero_init, st_bf16, out_bf16;
   int32_t P;   // transitions per token: key, value and beta rows per q, g, o row
+  float *ring; // (verify) records [T, HV, E]: e (D), k (D), the gate (G), padding
+  int32_t E;   // record stride in floats (a multiple of 4)
 };
 
 // Sum over the 8 lanes of a key-group set: every lane of the group gets it.
@@ -214,7 +216,11 @@ struct TokOps {
 
 // PROD: more than one transition per token (P > 1); without it every
 // substep is a token and the substep bookkeeping compiles away.
-template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD, int D>
+// RING: the verify of a speculative window: the pool is read, never written,
+// and every token's update is recorded as e (per value column), the key it
+// is written along (normalised when L2) and its gate, so that a later fold
+// applies S <- S~ + e k^T for the accepted tokens.
+template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD, bool RING, int D>
 __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
   using SM = RecSmem<GATE, D>;
   using PF = RecPre<IN_F32, GATE, D>;
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
 
   if (bos == eos) {
     // a zero-length sequence under ZERO_INIT writes its zero state back
-    if (p.zero_init)
+    if (!RING && p.zero_init)
       for (int e = tid; e < D * RU; e += 256)
         *reinterpret_cast<uint4 *>(pool + (tbase + (int64_t)(e / RU) * D) * sw + 16 * (e % RU)) =
             make_uint4(0, 0, 0, 0);
@@ -325,6 +331,22 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
       t.v = sm.vv[i][vl];
       t.beta = DELTA ? sm.bb[i] : 0.f;
     };
+    // (verify) token row r's record: e for this lane's column, and from the
+    // first column of the first block the key times rk and the gate
+    auto record = [&](int r, float er, float rk, const Ops &t) {
+      float *rec = p.ring + ((r0 + r) * p.HV + h) * (int64_t)p.E;
+      if (kg == 0) rec[col] = er;
+      if (vb == 0 && vl == 0) {
+#pragma unroll
+        for (int j = 0; j < NK; ++j) rec[D + k0 + j] = t.k[j] * rk;
+        if constexpr (GATE == GDR_GATE_SCALAR) {
+          if (kg == 0) rec[2 * D] = t.g[0];
+        } else if constexpr (GATE == GDR_GATE_CHANNEL) {
+#pragma unroll
+          for (int j = 0; j < NK; ++j) rec[2 * D + k0 + j] = t.g[j];
+        }
+      }
+    };
     // one substep of the recurrence on the lane's NK state entries: the
     // token's decay on its first substep (js == 0), its output on its last
     auto step = [&](int js, int r, const Ops &t) {
@@ -360,13 +382,16 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
           a1 = fmaf(s[j + 1], t.k[j + 1], a1);
         }
         const float vhat = sum8(a0 + a1) * rk;
-        const float e = t.beta * (t.v - vhat) * rk;
+        const float er = t.beta * (t.v - vhat);
+        const float e = er * rk;
 #pragma unroll
         for (int j = 0; j < NK; ++j) s[j] = fmaf(e, t.k[j], s[j]);
+        if constexpr (RING) record(r, er, rk, t);
       } else {
         const float e = t.v * rk;
 #pragma unroll
         for (int j = 0; j < NK; ++j) s[j] = fmaf(e, t.k[j], s[j]);
+        if constexpr (RING) record(r, t.v, rk, t);
       }
       // 5. read after the write (after the token's last substep)
       if (!PROD || js == P - 1) {
@@ -430,7 +455,9 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
     }
   }
 
-  // state out, coalesced through LDS (RNE to a bf16 pool)
+  // state out, coalesced through LDS (RNE to a bf16 pool); a verify leaves
+  // the pool as it was
+  if constexpr (RING) return;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NK; ++j) sm.st[k0 + j][vl] = s[j];
@@ -452,22 +479,25 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecParams p) {
   }
 }
 
-template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD>
+template <bool IN_F32, int GATE, bool DELTA, bool L2, bool PROD, bool RING>
 hipError_t by_dim(const gdr_args &a, const RecParams &p, hipStream_t st) {
   // one XCD round covers 8 (sequence, key head) groups
   const int blocks = ((a.N * a.HK + 7) / 8) * 8 * (a.HV / a.HK) * (a.DK / VB);
   if (a.DK == 128) {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, 128>), dim3(blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, RING, 128>), dim3(blocks), dim3(256), 0,
+                       st, p);
   } else {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, 64>), dim3(blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<IN_F32, GATE, DELTA, L2, PROD, RING, 64>), dim3(blocks), dim3(256), 0,
+                       st, p);
   }
   return hipGetLastError();
 }
 
 template <bool IN_F32, int GATE, bool DELTA, bool L2>
 hipError_t by_prod(const gdr_args &a, const RecParams &p, hipStream_t st) {
-  if (p.P > 1) return by_dim<IN_F32, GATE, DELTA, L2, true>(a, p, st);
-  return by_dim<IN_F32, GATE, DELTA, L2, false>(a, p, st);
+  if (p.ring) return by_dim<IN_F32, GATE, DELTA, L2, false, true>(a, p, st);   // (one transition)
+  if (p.P > 1) return by_dim<IN_F32, GATE, DELTA, L2, true, false>(a, p, st);
+  return by_dim<IN_F32, GATE, DELTA, L2, false, false>(a, p, st);
 }
 
 template <bool IN_F32, int GATE, bool DELTA>
@@ -491,10 +521,128 @@ hipError_t by_gate(const gdr_args &a, const RecParams &p, hipStream_t st) {
   }
 }
 
+// Fold of a verify's accepted records: for sequence n, S <- S~ + e k^T with
+// the records of its first accepted[n] window tokens (clamped to the window),
+// in order, on pool slot slot_idx[n]. One workgroup per (sequence, value
+// head, 32 value columns), the lane layout of the recurrence above; the
+// state tile enters and leaves through LDS as coalesced rows.
+struct FoldParams {
+  const float *ring;
+  const int32_t *accepted;
+  void *pool;
+  const int32_t *slot_idx, *cu_seqlens;
+  int32_t HV, E;
+  int st_bf16;
+};
+
+template <int GATE, int D>
+__global__ __launch_bounds__(256) void state_fold_kernel(FoldParams p) {
+  constexpr int NK = D / KG, NVB = D / VB;
+  __shared__ float st[D][VB + 4];
+  const int b = blockIdx.x;
+  const int vb = b % NVB, nh = b / NVB;
+  const int n = nh / p.HV, h = nh - n * p.HV;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int kg = lane & (KG - 1), vl = 8 * w + (lane >> 3), col = vb * VB + vl, k0 = kg * NK;
+  const int64_t bos = p.cu_seqlens[n];
+  const int64_t len = p.cu_seqlens[n + 1] - bos;
+  const int acc = (int)max<int64_t>(0, min<int64_t>(p.accepted[n], len));
+  if (acc == 0) return;   // (uniform) nothing accepted: the state stays
+
+  const int64_t tbase = ((int64_t)p.slot_idx[n] * p.HV + h) * (int64_t)(D * D) + vb * VB;
+  const int sw = p.st_bf16 ? 2 : 4, RU = VB * sw / 16;
+  char *pool = static_cast<char *>(p.pool);
+  for (int e = tid; e < D * RU; e += 256) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(pool + (tbase + (int64_t)(e / RU) * D) * sw + 16 * (e % RU));
+    const int row = e / RU, c0 = (e % RU) * (16 / sw);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    if (p.st_bf16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        st[row][c0 + i] = __uint_as_float((i & 1) ? (xw[i >> 1] & 0xffff0000u) : (xw[i >> 1] << 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[row][c0 + i] = __uint_as_float(xw[i]);
+    }
+  }
+  __syncthreads();
+  float s[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) s[j] = st[k0 + j][vl];
+
+  for (int t = 0; t < acc; ++t) {
+    const float *rec = p.ring + ((bos + t) * p.HV + h) * (int64_t)p.E;
+    const float e = rec[col];
+    float kx[NK];
+#pragma unroll
+    for (int j = 0; j < NK; j += 4) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(rec + D + k0 + j);
+      kx[j] = k4.x; kx[j + 1] = k4.y; kx[j + 2] = k4.z; kx[j + 3] = k4.w;
+    }
+    if constexpr (GATE == GDR_GATE_SCALAR) {
+      const float al = __expf(rec[2 * D]);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j] * al);
+    } else if constexpr (GATE == GDR_GATE_CHANNEL) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j] * __expf(rec[2 * D + k0 + j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) s[j] = fmaf(e, kx[j], s[j]);
+    }
+  }
+
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NK; ++j) st[k0 + j][vl] = s[j];
+  __syncthreads();
+  for (int e = tid; e < D * RU; e += 256) {
+    const int row = e / RU, c0 = (e % RU) * (16 / sw);
+    uint4 x;
+    if (p.st_bf16) {
+      uint32_t xw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        xw[m] = (uint32_t)f32_to_bf16(st[row][c0 + 2 * m]) | ((uint32_t)f32_to_bf16(st[row][c0 + 2 * m + 1]) << 16);
+      x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+    } else {
+      x = make_uint4(__float_as_uint(st[row][c0]), __float_as_uint(st[row][c0 + 1]),
+                     __float_as_uint(st[row][c0 + 2]), __float_as_uint(st[row][c0 + 3]));
+    }
+    *reinterpret_cast<uint4 *>(pool + (tbase + (int64_t)row * D) * sw + 16 * (e % RU)) = x;
+  }
+}
+
+template <int GATE>
+hipError_t fold_by_dim(const gdr_args &a, const FoldParams &p, hipStream_t st) {
+  const unsigned blocks = (unsigned)(a.N * a.HV * (a.DK / VB));
+  if (a.DK == 128) hipLaunchKernelGGL((state_fold_kernel<GATE, 128>), dim3(blocks), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((state_fold_kernel<GATE, 64>), dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream) {
+int ring_record_elements(const gdr_args &a) {
+  return a.DV + a.DK + (a.gate == GDR_GATE_SCALAR ? 1 : a.gate == GDR_GATE_CHANNEL ? a.DK : 0);
+}
+int ring_record_stride(const gdr_args &a) { return (ring_record_elements(a) + 3) & ~3; }
+
+hipError_t launch_state_fold(const gdr_args &a, const float *ring, const int32_t *accepted, hipStream_t stream) {
+  FoldParams p;
+  p.ring = ring; p.accepted = accepted;
+  p.pool = a.state_pool; p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
+  p.HV = a.HV; p.E = ring_record_stride(a);
+  p.st_bf16 = a.state_dtype == GDR_BF16;
+  if (a.gate == GDR_GATE_SCALAR) return fold_by_dim<GDR_GATE_SCALAR>(a, p, stream);
+  if (a.gate == GDR_GATE_CHANNEL) return fold_by_dim<GDR_GATE_CHANNEL>(a, p, stream);
+  return fold_by_dim<GDR_GATE_NONE>(a, p, stream);
+}
+
+hipError_t launch_recurrent_fwd(const gdr_args &a, hipStream_t stream, float *ring) {
   RecParams p;
+  p.ring = ring;
+  p.E = ring_record_stride(a);
   p.q = a.q; p.k = a.k; p.v = a.v;
   p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
   p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;

@@ -21,7 +21,9 @@
  *   gdr_recurrent_fwd   the tokenwise recurrence over a ragged batch, the
  *                       state in registers across each sequence (the
  *                       "gated_delta" Mojo page's kernel).
- * gdr_linear_chunk_bwd gives the gradients of the plain linear rule.
+ * gdr_linear_chunk_bwd gives the gradients of the plain linear rule;
+ * gdr_verify_ring and gdr_state_fold split a speculative-decode window into a
+ * verify that writes no state and a fold of the accepted tokens.
  *
  * Memory. Every pointer is device memory owned by the caller; the library
  * neither allocates, frees nor keeps any of them after the call returns.
@@ -69,7 +71,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -203,6 +205,32 @@ size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
  * every sequence's tokens backwards). */
 gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Speculative decoding ("gated_delta" Mojo page, its verify-ring, record and
+ * fold functions, which it names without detail; the reading taken here):
+ *
+ * gdr_verify_ring runs gdr_recurrent_fwd over each sequence's window of draft
+ * tokens (same arguments, outputs o, QK_L2NORM allowed, one transition per
+ * token) but leaves state_pool untouched, and records every token's state
+ * update in `ring` [T_total, HV, stride] fp32: the error e = beta (v - S~ k)
+ * (v for the linear rule, DV values), the key it is written along (DK values,
+ * normalised under QK_L2NORM), then the token's log-gate (1 value for SCALAR,
+ * DK for CHANNEL, none for NONE); `stride` = gdr_ring_record_stride(a) (the
+ * gdr_ring_record_elements(a) values rounded up to a multiple of 4). ring is
+ * device memory, 16-byte aligned, not overlapping o, the inputs or the pool.
+ *
+ * gdr_state_fold then applies, for each sequence n, the records of its first
+ * accepted[n] window tokens (accepted: [N] int32 device array, clamped to
+ * [0, window length]) in order to pool slot slot_idx[n]:
+ * S <- S~ + e k^T, with S~ the decayed state. The result equals the state the
+ * recurrence reaches after those tokens. `a` is the verify's arguments (only
+ * N, HK, HV, DK, DV, gate, state_pool, state_dtype, num_slots, slot_idx,
+ * cu_seqlens and T_total are read). */
+int gdr_ring_record_elements(const gdr_args *a);
+int gdr_ring_record_stride(const gdr_args *a);
+gdr_status gdr_verify_ring(const gdr_args *a, float *ring, hipStream_t stream);
+gdr_status gdr_state_fold(const gdr_args *a, const float *ring, const int32_t *accepted,
+                          hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdr_status_string(gdr_status s);

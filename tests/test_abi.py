@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["gdr_abi_version", "gdr_chunk_fwd_workspace_bytes", "gdr_chunk_fwd",
                             "gdr_recurrent_step", "gdr_recurrent_fwd", "gdr_status_string",
                             "gdr_last_error", "gdr_linear_chunk_bwd_workspace_bytes",
-                            "gdr_linear_chunk_bwd"])
+                            "gdr_linear_chunk_bwd", "gdr_ring_record_elements",
+                            "gdr_ring_record_stride", "gdr_verify_ring", "gdr_state_fold"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == gdr.ABI_VERSION == 4
+    assert L.gdr_abi_version() == gdr.ABI_VERSION == 5
 
 
 def test_args_struct_matches_header_field_order():
@@ -238,3 +239,25 @@ def test_linear_backward_rejects_on_host():
     assert call(b) == 2
     a.HV, a.v_stride_t = 4, 4 * 128                   # grouped heads
     assert call(a) == 2
+
+
+
+def test_verify_ring_and_fold_on_host():
+    """Record sizes by gate, and the host checks of the verify and the fold."""
+    gdr, L = _lib()
+    a = _valid_args(gdr)
+    for gate, elems in ((0, 256), (1, 257), (2, 384)):
+        a.gate = gate
+        assert L.gdr_ring_record_elements(ctypes.byref(a)) == elems
+        assert L.gdr_ring_record_stride(ctypes.byref(a)) == (elems + 3) // 4 * 4
+    a.gate = 1
+    assert L.gdr_verify_ring(ctypes.byref(a), None, None) == 1            # no ring
+    assert L.gdr_verify_ring(ctypes.byref(a), 0x20000004, None) == 1      # misaligned
+    assert L.gdr_verify_ring(ctypes.byref(a), 0x1000, None) == 1          # overlaps q
+    a.products = 2
+    assert L.gdr_verify_ring(ctypes.byref(a), 0x20000000, None) == 2
+    a.products = 1
+    assert L.gdr_state_fold(ctypes.byref(a), None, 0x30000000, None) == 1
+    assert L.gdr_state_fold(ctypes.byref(a), 0x20000000, None, None) == 1
+    a.DK = 96
+    assert L.gdr_state_fold(ctypes.byref(a), 0x20000000, 0x30000000, None) == 2
