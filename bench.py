@@ -22,7 +22,8 @@ kernel; `linear_mode` the same shapes with alpha = 1 and no delta (linear
 attention) and `linear_backward` its gradients (dq, dk, dv); `recurrent_fwd` the
 same for the tokenwise recurrence; `delta_product`
 the chunkwise prefill of Gated DeltaProduct (2 transitions per token) on the
-headline shapes; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+headline shapes; `speculative` a 4-token verify window per sequence and the fold
+of its accepted prefix on the decode pool; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -344,6 +345,40 @@ def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
     return e0.elapsed_time(e1) / steps
 
 
+def bench_speculative(w: synth.Workload, window: int, steps: int, warmup: int = 3):
+    """Mean time (ms) of one verify of `window` draft tokens per sequence
+    plus the fold of a seeded accepted prefix, on the decode workload's pool."""
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    ww = w.replace(seqlens=(window,) * w.N, steps=1)
+    x = synth.generate(ww)
+    a = dict(q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
+             v=_dev(x["v"], w.in_dtype, dev), g=_dev(x["g"], "f32", dev),
+             beta=_dev(x["beta"], "f32", dev), pool=_dev(x["pool"], w.state_dtype, dev),
+             slot_idx=_dev(x["slot_idx"], "i32", dev), cu_seqlens=_dev(x["cu_seqlens"], "i32", dev))
+    rng = np.random.default_rng(11)
+    acc = torch.from_numpy(rng.integers(0, window + 1, size=w.N).astype(np.int32)).to(dev)
+    del x
+    o = torch.empty((w.N * window, w.HV, w.DV), dtype=torch.float32, device=dev)
+
+    def run():
+        _, ring = gdr.verify_ring(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["slot_idx"],
+                                  a["cu_seqlens"], o=o)
+        gdr.state_fold(ring, acc, a["pool"], a["slot_idx"], a["cu_seqlens"], HK=w.HK, gate=w.gate)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, float(acc.float().mean())
+
+
 # ----------------------------------------------------------------------------
 # CPU leg: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -402,6 +437,7 @@ def main():
     ap.add_argument("--product-steps", type=int, default=20)
     ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-speculative", action="store_true")
     ap.add_argument("--no-product", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -529,6 +565,15 @@ def main():
                                          pw.chunk_size) / (pt * 1e-3) / 1e12,
             "traffic": committed_traffic("chunk_fwd_ws_kernel", "gdp_nh2_prefill_b4_t4096_h16_d128",
                                          prefill_kernel(pw)[1])}
+    if not args.no_speculative and not args.no_decode:
+        # speculative decoding: verify 4 draft tokens per sequence, fold the
+        # accepted prefix (the decode workload's pool and heads)
+        sw_ = synth.workload("decode_n256_hk16_hv32_d128")
+        sp_ms, mean_acc = bench_speculative(sw_, 4, 50)
+        result["speculative"] = {
+            "workload": sw_.name, "window": 4, "mean_accepted": mean_acc, "ms_per_window": sp_ms,
+            "accepted_tokens_per_s": sw_.N * mean_acc / (sp_ms * 1e-3),
+            "decode_steps_same_tokens_ms": result["decode"]["kernel_us_per_step"] * 1e-3 * mean_acc}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
