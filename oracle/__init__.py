@@ -12,7 +12,8 @@ Three independent statements of the method:
                      attention, decayed scores, the full-sequence delta solve).
 ``product`` states Gated DeltaProduct (n_h transitions per token) the same
 tokenwise way; ``backward`` the gradients of causal linear attention;
-``ring`` the speculative-decode verify ring and its state fold.
+``ring`` the speculative-decode verify ring and its state fold;
+``recurrent_bwd`` the gradients of the gated delta and gated linear rules.
 Every function names the passage of the pages it follows. Where the pages are
 silent the reading taken is stated in the function's docstring.
 
@@ -28,6 +29,7 @@ from .bruteforce import (linear_parallel_fp64, delta_parallel_fp64,
 from .product import delta_product_fp64
 from .backward import linear_attention_grads_fp64
 from .ring import ring_record_elements, verify_ring_fp64, state_fold_fp64
+from .recurrent_bwd import recurrent_grads_fp64
 
 __all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16",
            "l2_normalise_fp64", "L2_EPS",
@@ -35,4 +37,4 @@ __all__ = ["recurrent_fp64", "round_to_storage", "round_f64_to_bf16",
            "linear_parallel_fp64", "delta_parallel_fp64",
            "four_token_chunk_fractions", "delta_product_fp64",
            "linear_attention_grads_fp64", "ring_record_elements", "verify_ring_fp64",
-           "state_fold_fp64"]
+           "state_fold_fp64", "recurrent_grads_fp64"]
