@@ -41,7 +41,7 @@ FLAG_QK_L2NORM = 4
 
 
 # GDR_ABI_VERSION of include/gdr.h that Args mirrors.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class GdrError(RuntimeError):
@@ -103,6 +103,11 @@ def load() -> ctypes.CDLL:
     L.gdr_linear_chunk_bwd.restype = ctypes.c_int
     L.gdr_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.gdr_recurrent_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.gdr_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
+    L.gdr_recurrent_bwd.restype = ctypes.c_int
+    L.gdr_recurrent_bwd.argtypes = [ctypes.POINTER(Args)] + [ctypes.c_void_p] * 8 + [ctypes.c_size_t,
+                                                                                   ctypes.c_void_p]
     L.gdr_ring_record_elements.restype = ctypes.c_int
     L.gdr_ring_record_elements.argtypes = [ctypes.POINTER(Args)]
     L.gdr_ring_record_stride.restype = ctypes.c_int
@@ -314,6 +319,43 @@ def linear_chunk_bwd(q, k, v, do, pool, slot_idx, cu_seqlens, *, scale=None, zer
     _check(L.gdr_linear_chunk_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def recurrent_bwd(q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, *, scale=None, rule="delta",
+                  gate=None, zero_init=False, out_dtype=None, dstate0=True, workspace=None,
+                  debug_checks=False):
+    """Gradients of the tokenwise recurrence (any rule and gate) for the
+    forward call with these arguments and upstream gradient do [T, HV, DV]
+    (contiguous, q's dtype). Returns a dict with dq, dk [T, HK, DK] and dv
+    [T, HV, DV] (out_dtype), dbeta [T, HV] (delta rule), dg shaped like g
+    (gated calls) and dstate0 [N, HV, DK, DV] fp32 (the initial state's
+    gradient, transposed like the pool) unless ``dstate0`` is False; absent
+    entries are None. The pool is read, never written."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    T, HK, DK = q.shape
+    dv = torch.empty(tuple(v.shape), dtype=out_dtype, device=q.device)
+    a, _ = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, dv, scale, rule, gate,
+                    zero_init, debug_checks, 64, out_dtype)
+    if do.dtype != q.dtype or not do.is_contiguous() or tuple(do.shape) != tuple(v.shape) or do.device != q.device:
+        raise ValueError("do must be a contiguous tensor shaped like v, in q's dtype, on q's device")
+    dq = torch.empty((T, HK, DK), dtype=out_dtype, device=q.device)
+    dk = torch.empty_like(dq)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dbeta = torch.empty((T, v.shape[1]), **f32) if rule == "delta" else None
+    dg = torch.empty(tuple(g.shape), **f32) if g is not None and a.gate != 0 else None
+    ds = torch.empty((slot_idx.shape[0], v.shape[1], DK, v.shape[2]), **f32) if dstate0 else None
+    L = load()
+    if workspace is None:
+        nbytes = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(a))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise TypeError(f"workspace must be a contiguous uint8 tensor on {q.device}")
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check(L.gdr_recurrent_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               ptr(dbeta), ptr(dg), ptr(ds), workspace.data_ptr(), workspace.numel(),
+                               _stream(q)))
+    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dstate0=ds)
 
 
 def verify_ring(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, rule="delta", gate=None,

@@ -215,6 +215,56 @@ gdr_status validate_bwd(const gdr_args *a, const void *dout, void *dq, void *dk,
   return GDR_OK;
 }
 
+// What the tokenwise backward takes, on top of the forward's checks (with
+// dv standing in for the output): one transition per token, no in-kernel
+// L2 normalisation, and the gradients' buffers.
+gdr_status validate_rbwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
+                         float *dg, float *dstate0) {
+  if (!a) return fail(GDR_E_INVALID, "args is NULL");
+  gdr_args b = *a;
+  b.o = dv;   // dv [T_total, HV, DV] in out_dtype has the output's layout
+  if (a->T_total > 0 && a->N > 0 && !dv) return fail(GDR_E_INVALID, "dv is NULL");
+  gdr_status st = validate(&b, Call::Recur);
+  if (st != GDR_OK) return st;
+  if (a->flags & GDR_FLAG_QK_L2NORM)
+    return fail(GDR_E_UNSUPPORTED, "the backward does not differentiate the in-kernel L2 normalisation");
+  if (products_of(*a) > 1) return fail(GDR_E_UNSUPPORTED, "the backward takes one transition per token");
+  if (a->N == 0) return GDR_OK;
+  if (a->T_total > 0) {
+    if (!dout || !dq || !dk) return fail(GDR_E_INVALID, "dout / dq / dk is NULL");
+    if (a->rule == GDR_RULE_DELTA && !dbeta) return fail(GDR_E_INVALID, "dbeta is NULL for the delta rule");
+    if (a->gate != GDR_GATE_NONE && !dg) return fail(GDR_E_INVALID, "dg is NULL for a gated call");
+  }
+  const void *al[] = {dout, dq, dk};
+  for (const void *ptr : al)
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return fail(GDR_E_INVALID, "dout, dq and dk must be 16-byte aligned");
+  const void *al4[] = {dbeta, dg, dstate0};
+  for (const void *ptr : al4)
+    if (reinterpret_cast<uintptr_t>(ptr) % 4) return fail(GDR_E_INVALID, "dbeta, dg and dstate0 must be 4-byte aligned");
+  const int64_t kd = (int64_t)a->HK * a->DK, vd = (int64_t)a->HV * a->DV, T = a->T_total;
+  const size_t ie = dtype_bytes(a->in_dtype), oe = dtype_bytes(a->out_dtype);
+  const int64_t gw = a->gate == GDR_GATE_CHANNEL ? (int64_t)a->HV * a->DK : a->HV;
+  const Range outs[] = {span(dv, T, vd, vd, oe),
+                        span(dq, T, kd, kd, oe),
+                        span(dk, T, kd, kd, oe),
+                        span(dbeta, a->rule == GDR_RULE_DELTA ? T : 0, a->HV, a->HV, 4),
+                        span(dg, a->gate != GDR_GATE_NONE ? T : 0, gw, gw, 4),
+                        span(dstate0, 1, 0, (int64_t)a->N * a->HV * a->DK * a->DV, 4)};
+  const Range ins[] = {span(a->q, T, a->q_stride_t, kd, ie), span(a->k, T, a->k_stride_t, kd, ie),
+                       span(a->v, T, a->v_stride_t, vd, ie), span(dout, T, vd, vd, ie),
+                       span(a->g, a->gate == GDR_GATE_NONE ? 0 : T, gw, gw, 4),
+                       span(a->beta, a->rule == GDR_RULE_DELTA ? T : 0, a->HV, a->HV, 4),
+                       span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV,
+                            dtype_bytes(a->state_dtype))};
+  for (int i = 0; i < 6; ++i) {
+    for (const Range &r : ins)
+      if (overlap(outs[i], r)) return fail(GDR_E_INVALID, "a gradient buffer overlaps an input or the state pool");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDR_E_INVALID, "gradient buffers overlap each other");
+  }
+  return GDR_OK;
+}
+
 bool uses_workspace(const gdr_args *a) {
   return a->N > 0 && a->T_total > 0 && chunk_fwd_kda_applies(*a) && !prefill_force_generic();
 }
@@ -368,3 +418,28 @@ GDR_EXPORT const char *gdr_status_string(gdr_status s) {
 }
 
 GDR_EXPORT const char *gdr_last_error(void) { return g_last_error; }
+
+GDR_EXPORT size_t gdr_recurrent_bwd_workspace_bytes(const gdr_args *a) {
+  if (validate(a, Call::Recur) != GDR_OK || a->N == 0) return 0;
+  return recurrent_bwd_workspace(*a);
+}
+
+GDR_EXPORT gdr_status gdr_recurrent_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                        float *dbeta, float *dg, float *dstate0, void *workspace, size_t ws_bytes,
+                                        hipStream_t stream) {
+  gdr_status s = validate_rbwd(a, dout, dq, dk, dv, dbeta, dg, dstate0);
+  if (s != GDR_OK) return s;
+  if (a->N == 0) return GDR_OK;
+  const size_t need = recurrent_bwd_workspace(*a);
+  if (!workspace || ws_bytes < need)
+    return fail(GDR_E_WORKSPACE, "workspace of %zu bytes at %p: this call needs %zu "
+                "(gdr_recurrent_bwd_workspace_bytes)", ws_bytes, workspace, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_E_INVALID, "workspace is not 256-byte aligned");
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_recurrent_bwd(*a, dout, dq, dk, dv, dbeta, dg, dstate0, workspace, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent_bwd launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}

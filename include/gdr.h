@@ -22,6 +22,8 @@
  *                       state in registers across each sequence (the
  *                       "gated_delta" Mojo page's kernel).
  * gdr_linear_chunk_bwd gives the gradients of the plain linear rule;
+ * gdr_recurrent_bwd gives the gradients of the gated delta and gated linear
+ * rules, tokenwise;
  * gdr_verify_ring and gdr_state_fold split a speculative-decode window into a
  * verify that writes no state and a fold of the accepted tokens.
  *
@@ -71,7 +73,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -205,6 +207,39 @@ size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
  * every sequence's tokens backwards). */
 gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gdr_recurrent_bwd needs with these arguments
+ * (0 when N == 0 or the arguments are invalid): fp32 checkpoints of the state
+ * every 8 tokens ((T_total / 8 + N + 1) * HV * DK * DV values) and per-token
+ * partial sums (T_total * HV * (DV / 32) * (2 or 3) * DK values, plus two
+ * T_total * HV * (DV / 32) arrays). */
+size_t gdr_recurrent_bwd_workspace_bytes(const gdr_args *a);
+
+/* Gradients of the tokenwise recurrence of gdr_recurrent_fwd (the forward of
+ * "You Could Have Come Up With Kimi Delta Attention", recurrent form, with the
+ * gated variants of "Linear attention visualized"; the pages give no backward
+ * for the delta rule, so this is that recurrence differentiated in reverse
+ * mode) for a loss with upstream gradient dout = dL/do. `a` describes the
+ * forward call: q, k, v, their strides and in_dtype, g, beta, rule, gate,
+ * scale, cu_seqlens and the initial state from state_pool[slot_idx[n]] (read,
+ * never written) unless GDR_FLAG_ZERO_INIT; `a->o` is ignored. Any rule and
+ * gate, grouped heads, DK = DV in {64, 128}; one transition per token and no
+ * GDR_FLAG_QK_L2NORM (else GDR_E_UNSUPPORTED). Writes
+ *   dq, dk   [T_total, HK, DK] out_dtype (summed over the value heads of a
+ *            key head), contiguous, 16-byte aligned
+ *   dv       [T_total, HV, DV] out_dtype, contiguous, 16-byte aligned
+ *   dbeta    [T_total, HV] fp32 (delta rule; ignored for the linear rule)
+ *   dg       shaped like g, fp32 (gated calls; ignored for GATE_NONE)
+ *   dstate0  [N, HV, DK, DV] fp32 or NULL: dL/dS_0 per sequence, transposed
+ *            like the pool (also under ZERO_INIT: the gradient at the zero
+ *            state); zeros for an empty sequence
+ * dout is [T_total, HV, DV], contiguous, in in_dtype, 16-byte aligned. No
+ * gradient buffer may overlap another, an input or the pool. The final
+ * state's gradient is taken as zero (the loss reads the outputs only).
+ * `workspace` (device, 256-byte aligned, at least
+ * gdr_recurrent_bwd_workspace_bytes) is scratch. */
+gdr_status gdr_recurrent_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
+                             float *dg, float *dstate0, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Speculative decoding ("gated_delta" Mojo page, its verify-ring, record and
  * fold functions, which it names without detail; the reading taken here):

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
                             "gdr_recurrent_step", "gdr_recurrent_fwd", "gdr_status_string",
                             "gdr_last_error", "gdr_linear_chunk_bwd_workspace_bytes",
                             "gdr_linear_chunk_bwd", "gdr_ring_record_elements",
-                            "gdr_ring_record_stride", "gdr_verify_ring", "gdr_state_fold"])
+                            "gdr_ring_record_stride", "gdr_verify_ring", "gdr_state_fold",
+                            "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == gdr.ABI_VERSION == 5
+    assert L.gdr_abi_version() == gdr.ABI_VERSION == 6
 
 
 def test_args_struct_matches_header_field_order():
@@ -240,6 +241,46 @@ def test_linear_backward_rejects_on_host():
     a.HV, a.v_stride_t = 4, 4 * 128                   # grouped heads
     assert call(a) == 2
 
+
+
+def test_recurrent_backward_rejects_on_host():
+    """The tokenwise backward takes any rule and gate; it checks the gradients'
+    buffers, their overlaps, the workspace, L2 norm and products before any
+    launch."""
+    gdr, L = _lib()
+    a = _valid_args(gdr)                              # delta rule, scalar gate, HK 2, HV 4
+    need = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(a))
+    slots = a.T_total // 8 + a.N + 1
+    assert need >= slots * 4 * 128 * 128 * 4 + a.T_total * 4 * 4 * 2 * 128 * 4
+    bufs = dict(dout=0x7000000, dq=0x8000000, dk=0x8100000, dv=0x8200000, dbeta=0x8300000,
+                dg=0x8400000, ds=0x8500000, ws=0x10000000)
+    call = lambda aa, **kw: L.gdr_recurrent_bwd(
+        ctypes.byref(aa), *[kw.get(n, bufs[n]) for n in ("dout", "dq", "dk", "dv", "dbeta", "dg", "ds", "ws")],
+        kw.get("wsb", need), None)
+    assert call(a, ws=None) == 3                      # no workspace
+    assert call(a, wsb=need - 1) == 3                 # short workspace
+    assert call(a, ws=bufs["ws"] + 16) == 1           # misaligned workspace
+    assert call(a, dbeta=None) == 1                   # delta rule needs dbeta
+    assert call(a, dg=None) == 1                      # gated call needs dg
+    assert call(a, dq=None) == 1
+    assert call(a, dk=bufs["dq"] + 64) == 1           # gradients overlap
+    assert call(a, dg=0x2000) == 1                    # dg overlaps g
+    assert call(a, ds=0x4000000) == 1                 # dstate0 overlaps the pool
+    assert call(a, dout=bufs["dout"] + 4) == 1        # misaligned dout
+    b = _valid_args(gdr)
+    b.flags = gdr.FLAG_QK_L2NORM
+    assert call(b) == 2
+    b = _valid_args(gdr)
+    b.products = 2
+    assert call(b) == 2
+    b = _valid_args(gdr)                              # the linear rule ignores dbeta
+    b.rule, b.gate, b.beta, b.g = 1, 0, None, None
+    nb = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(b))
+    assert nb == need                                 # two partial-sum vectors per token either way
+    b.gate, b.g = 2, 0x2000
+    assert L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(b)) > nb   # a third (dg per column)
+    b.N = 0
+    assert L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(b)) == 0
 
 
 def test_verify_ring_and_fold_on_host():
