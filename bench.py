@@ -48,6 +48,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc")
 STEP_SRC = [os.path.join(CSRC, "recurrent_step.hip"), os.path.join(CSRC, "gdr_internal.h")]
 RECUR_SRC = [os.path.join(CSRC, "recurrent_fwd.hip"), os.path.join(CSRC, "gdr_internal.h")]
+RBWD_SRC = [os.path.join(CSRC, "recurrent_bwd.hip"), os.path.join(CSRC, "recurrent_bwd.h"),
+            os.path.join(CSRC, "gdr_internal.h")]
 
 
 def prefill_kernel(w: synth.Workload):
@@ -345,6 +347,47 @@ def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
     return e0.elapsed_time(e1) / steps
 
 
+def bench_recurrent_bwd(w: synth.Workload, steps: int, warmup: int = 2):
+    """Mean time (ms) of gdr_recurrent_bwd on w's batch (the checkpointing
+    walk and the reduction of the partial sums), with a workspace allocated
+    once; also its workspace bytes."""
+    import ctypes
+    import torch
+    import gated_delta_rule_gdr_amd as gdr
+    dev = torch.device("cuda", 0)
+    x = synth.generate(w)
+    do = synth.generate(w.replace(seed=w.seed + 500))["v"]
+    a = dict(q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
+             v=_dev(x["v"], w.in_dtype, dev), do=_dev(do, w.in_dtype, dev),
+             g=_dev(x["g"], "f32", dev) if w.gate != "none" else None,
+             beta=_dev(x["beta"], "f32", dev) if w.rule == "delta" else None,
+             pool=_dev(x["pool"], w.state_dtype, dev), slot_idx=_dev(x["slot_idx"], "i32", dev),
+             cu_seqlens=_dev(x["cu_seqlens"], "i32", dev))
+    del x, do
+    L = gdr.load()
+    args, _ = gdr._prepare(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["slot_idx"],
+                           a["cu_seqlens"], None, None, w.rule, w.gate, w.zero_init, False, 64,
+                           torch.float32)
+    nbytes = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(args))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def run():
+        return gdr.recurrent_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"], a["pool"], a["slot_idx"],
+                                 a["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init,
+                                 workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, nbytes
+
+
 def bench_speculative(w: synth.Workload, window: int, steps: int, warmup: int = 3):
     """Mean time (ms) of one verify of `window` draft tokens per sequence
     plus the fold of a seeded accepted prefix, on the decode workload's pool."""
@@ -437,6 +480,7 @@ def main():
     ap.add_argument("--product-steps", type=int, default=20)
     ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--no-speculative", action="store_true")
     ap.add_argument("--no-product", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -552,6 +596,21 @@ def main():
             "algorithmic_bytes": bb, "hbm_gbs": bb / (bt * 1e-3) / 1e9,
             "hbm_frac": bb / (bt * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_flops": bf, "mfma_tflops": bf / (bt * 1e-3) / 1e12}
+    if not args.no_backward and w.name == synth.HEADLINE:
+        # gradients of the gated delta rule on the headline batch (tokenwise)
+        gw = synth.workload(synth.HEADLINE)
+        gt, gws = bench_recurrent_bwd(gw, args.backward_steps)
+        T, HD, HVT = gw.T_total, gw.HV * gw.DK, gw.T_total * gw.HV
+        # q, k, v, dO, g, beta and the initial states read; dq, dk, dv, dbeta,
+        # dg and the initial state's gradient written (fp32)
+        sb = gw.N * gw.HV * gw.DK * gw.DV
+        gb = (4 * T * HD * _isz(gw.in_dtype) + 2 * HVT * 4 + sb * _isz(gw.state_dtype)
+              + 3 * T * HD * 4 + 2 * HVT * 4 + sb * 4)
+        result["gdn_backward"] = {
+            "workload": gw.name, "steps": args.backward_steps, "ms": gt, "tokens_per_s": T / (gt * 1e-3),
+            "algorithmic_bytes": gb, "hbm_gbs": gb / (gt * 1e-3) / 1e9,
+            "hbm_frac": gb / (gt * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": gws,
+            "traffic": committed_traffic("recurrent_bwd_kernel+recurrent_bwd_reduce_kernel", gw.name, RBWD_SRC)}
     if not args.no_product:
         pw, P = synth.workload(synth.HEADLINE), 2
         pt = bench_product(pw, P, args.product_steps)

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "gdr_internal.h"
+#include "recurrent_bwd.h"
 
 #define GDR_EXPORT extern "C" __attribute__((visibility("default")))
 

@@ -59,11 +59,6 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
 size_t linear_bwd_workspace(const gdr_args &a);
 hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, void *ws,
                              hipStream_t stream);
-// Tokenwise backward of the gated delta / gated linear rules
-// (recurrent_bwd.hip): checkpoints and partial sums in the workspace.
-size_t recurrent_bwd_workspace(const gdr_args &a);
-hipError_t launch_recurrent_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
-                                float *dg, float *dstate0, void *ws, hipStream_t stream);
 // True when GDR_PREFILL_KERNEL=generic asks for the general prefill kernel in
 // every case (used to compare kernels).
 bool prefill_force_generic();

@@ -23,7 +23,7 @@
 // After the first token D is the gradient of the initial state.
 //
 // Schedule. Each row j of S and of D evolves on its own in both directions,
-// so one workgroup takes 32 value rows of one (sequence, value head) and
+// so one workgroup takes RW = 32 value rows of one (sequence, value head) and
 // walks the whole sequence without talking to other workgroups. Only dq, dk,
 // dg and dbeta sum over rows: each workgroup writes its partial sums to the
 // workspace and a second kernel adds them up, over the row groups and over
@@ -33,19 +33,19 @@
 //   Phase 2 takes the blocks last to first: it reloads the block's
 //   checkpoint, reruns the block's forward steps keeping St~, u and e of each
 //   token in registers, then walks the block's tokens backwards.
-// A thread holds 2 rows x DK/16 columns of S (and of D); the 16 lanes of a
-// DPP row share 2 rows, so the dots over k (u, de) are 16-lane DPP sums, and
+// A thread holds RW/16 rows x DK/16 columns of S (and of D); the 16 lanes of
+// a DPP row share those rows, so the dots over k (u, de) are 16-lane DPP sums,
+// and
 // the sums over rows are lane shuffles across the four 16-lane groups of a
 // wave, then a sum over the four waves through LDS at the end of the block.
 #include <cstdint>
 
-#include "gdr_internal.h"
+#include "recurrent_bwd.h"
 
 namespace gdr {
 namespace {
 
 constexpr int BB = 8;     // tokens per block (checkpoint spacing)
-constexpr int RW = 32;    // value rows per workgroup
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -96,7 +96,7 @@ struct BwdParams {
 template <int GATE>
 constexpr int nvec() { return GATE == GDR_GATE_CHANNEL ? 3 : 2; }
 
-template <int GATE, int D>
+template <int GATE, int D, int RW>
 struct BwdSmem {
   static constexpr int GP = GATE == GDR_GATE_CHANNEL ? D : 1;
   alignas(16) float kk[BB][D];
@@ -110,8 +110,8 @@ struct BwdSmem {
 
 // Stage tokens t0 .. t0 + len - 1 of the block: keys (and queries, upstream
 // gradients with `back`), this workgroup's value rows, beta and exp(g).
-template <bool IN_F32, int GATE, bool DELTA, int D>
-__device__ __forceinline__ void stage(BwdSmem<GATE, D> &sm, const BwdParams &p, int64_t t0, int len, int h,
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
+__device__ __forceinline__ void stage(BwdSmem<GATE, D, RW> &sm, const BwdParams &p, int64_t t0, int len, int h,
                                       int hk, int r0, bool back, int tid) {
   for (int e = tid; e < BB * D; e += 256) {
     const int i = e / D, c = e % D;
@@ -137,17 +137,18 @@ __device__ __forceinline__ void stage(BwdSmem<GATE, D> &sm, const BwdParams &p, 
   }
 }
 
-template <bool IN_F32, int GATE, bool DELTA, int D>
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
 __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
   constexpr int C = D / 16;          // key columns per thread
   constexpr int NS = D / RW;         // row groups per head
   constexpr int NV = nvec<GATE>();
-  __shared__ BwdSmem<GATE, D> sm;
+  constexpr int R = RW / 16;         // rows per thread
+  __shared__ BwdSmem<GATE, D, RW> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int rg = lane >> 4, cg = lane & 15;
   const int kc = cg * C;                 // first key column
-  const int lr = w * 8 + rg * 2;         // first of the thread's two local rows
+  const int lr = w * (RW / 4) + rg * R;  // first of the thread's local rows
   const int split = blockIdx.x % NS;
   const int nh = blockIdx.x / NS;
   const int n = nh / p.HV, h = nh - n * p.HV, hk = h / p.ratio;
@@ -157,16 +158,16 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
   const int64_t slot0 = bos / BB + n;    // this sequence's first checkpoint
   const int64_t HD2 = (int64_t)D * D;
 
-  float s[2][C];
+  float s[R][C];
   if (p.zero_init) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int x = 0; x < C; ++x) s[r][x] = 0.f;
   } else {
     const int64_t base = ((int64_t)p.slot_idx[n] * p.HV + h) * HD2;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int x = 0; x < C; ++x) {
         const int64_t e = base + (int64_t)(kc + x) * D + r0 + lr + r;
@@ -181,12 +182,12 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
 
   // One forward step of token i of the staged block: s becomes S_t; returns
   // u and e of the two rows (st, if given, receives St~).
-  auto fwd = [&](int i, float (&u)[2], float (&e)[2], float (*st)[C]) {
+  auto fwd = [&](int i, float (&u)[R], float (&e)[R], float (*st)[C]) {
     float k[C];
 #pragma unroll
     for (int x = 0; x < C; ++x) k[x] = sm.kk[i][kc + x];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) {
       float a = 0.f;
 #pragma unroll
       for (int x = 0; x < C; ++x) {
@@ -210,22 +211,22 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
     stage<IN_F32, GATE, DELTA, D>(sm, p, t0, len, h, hk, r0, false, tid);
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) {
       float4 *dst = reinterpret_cast<float4 *>(ck(b, r));
 #pragma unroll
       for (int x = 0; x < C; x += 4) dst[x / 4] = make_float4(s[r][x], s[r][x + 1], s[r][x + 2], s[r][x + 3]);
     }
     for (int i = 0; i < len; ++i) {
-      float u[2], e[2];
+      float u[R], e[R];
       fwd(i, u, e, nullptr);
     }
     __syncthreads();
   }
 
   // phase 2: blocks last to first
-  float D_[2][C];
+  float D_[R][C];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int x = 0; x < C; ++x) D_[r][x] = 0.f;
 
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
     __syncthreads();
     // the block's checkpoint (written by this same thread in phase 1)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) {
       const float4 *src = reinterpret_cast<const float4 *>(ck(b, r));
 #pragma unroll
       for (int x = 0; x < C; x += 4) {
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
         s[r][x] = f.x; s[r][x + 1] = f.y; s[r][x + 2] = f.z; s[r][x + 3] = f.w;
       }
     }
-    float sts[BB][2][C], us[BB][2], es[BB][2];
+    float sts[BB][R][C], us[BB][R], es[BB][R];
 #pragma unroll
     for (int i = 0; i < BB; ++i)
       if (i < len) fwd(i, us[i], es[i], sts[i]);
@@ -252,18 +253,18 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = BB - 1; i >= 0; --i) {
       if (i >= len) continue;
-      float k[C], q[C], dov[2];
+      float k[C], q[C], dov[R];
 #pragma unroll
       for (int x = 0; x < C; ++x) {
         k[x] = sm.kk[i][kc + x];
         q[x] = sm.qq[i][kc + x];
       }
-      dov[0] = sm.dd[i][lr];
-      dov[1] = sm.dd[i][lr + 1];
-      float pq[C], pk[C], pg[C];
-      float de[2];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < R; ++r) dov[r] = sm.dd[i][lr + r];
+      float pq[C], pk[C], pg[C];
+      float de[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
         const float sd = p.scale * dov[r];
         float a = 0.f;
 #pragma unroll
@@ -276,49 +277,53 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int x = 0; x < C; ++x) {
         // S_t = St~ + e k^T for dq; D^T e for dk
-        const float s0 = fmaf(es[i][0], k[x], sts[i][0][x]);
-        const float s1 = fmaf(es[i][1], k[x], sts[i][1][x]);
-        pq[x] = fmaf(s1, dov[1], s0 * dov[0]);
-        pk[x] = fmaf(D_[1][x], es[i][1], D_[0][x] * es[i][0]);
+        pq[x] = 0.f;
+        pk[x] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          pq[x] = fmaf(fmaf(es[i][r], k[x], sts[i][r][x]), dov[r], pq[x]);
+          pk[x] = fmaf(D_[r][x], es[i][r], pk[x]);
+        }
       }
-      float db = 0.f, dvr[2];
+      float db = 0.f, dvr[R];
       if constexpr (DELTA) {
         const float beta = sm.bb[i];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < R; ++r) {
           dvr[r] = beta * de[r];
           db = fmaf(de[r], sm.vv[i][lr + r] - us[i][r], db);
-        }
-        const float du0 = -beta * de[0], du1 = -beta * de[1];
+          const float du = -beta * de[r];
 #pragma unroll
-        for (int x = 0; x < C; ++x) {
-          pk[x] = fmaf(sts[i][0][x], du0, pk[x]);
-          pk[x] = fmaf(sts[i][1][x], du1, pk[x]);
-          D_[0][x] = fmaf(du0, k[x], D_[0][x]);
-          D_[1][x] = fmaf(du1, k[x], D_[1][x]);
+          for (int x = 0; x < C; ++x) {
+            pk[x] = fmaf(sts[i][r][x], du, pk[x]);
+            D_[r][x] = fmaf(du, k[x], D_[r][x]);
+          }
         }
       } else {
-        dvr[0] = de[0];
-        dvr[1] = de[1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) dvr[r] = de[r];
       }
       float gs = 0.f;
       if constexpr (GATE == GDR_GATE_SCALAR) {
         const float a = sm.ga[i][0];
 #pragma unroll
-        for (int x = 0; x < C; ++x) {
-          gs = fmaf(D_[0][x], sts[i][0][x], gs);
-          gs = fmaf(D_[1][x], sts[i][1][x], gs);
-          D_[0][x] *= a;
-          D_[1][x] *= a;
-        }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int x = 0; x < C; ++x) {
+            gs = fmaf(D_[r][x], sts[i][r][x], gs);
+            D_[r][x] *= a;
+          }
         gs = sum_groups(sum16(gs));
       } else if constexpr (GATE == GDR_GATE_CHANNEL) {
 #pragma unroll
         for (int x = 0; x < C; ++x) {
-          pg[x] = fmaf(D_[1][x], sts[i][1][x], D_[0][x] * sts[i][0][x]);
           const float a = sm.ga[i][kc + x];
-          D_[0][x] *= a;
-          D_[1][x] *= a;
+          pg[x] = 0.f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            pg[x] = fmaf(D_[r][x], sts[i][r][x], pg[x]);
+            D_[r][x] *= a;
+          }
         }
       }
 #pragma unroll
@@ -343,8 +348,8 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
         sm.redg[i][w] = gs;
       }
       if (cg == 0) {
-        sm.dvs[i][lr] = dvr[0];
-        sm.dvs[i][lr + 1] = dvr[1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) sm.dvs[i][lr + r] = dvr[r];
       }
     }
     __syncthreads();
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
   if (p.dstate0) {
     const int64_t base = ((int64_t)n * p.HV + h) * HD2;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int x = 0; x < C; ++x) p.dstate0[base + (int64_t)(kc + x) * D + r0 + lr + r] = D_[r][x];
   }
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
 
 // dq, dk (summed over row groups and over the value heads of a key head), dg
 // and dbeta (summed over row groups). One workgroup per token.
-template <int GATE, bool DELTA, int D>
+template <int GATE, bool DELTA, int D, int RW>
 __global__ __launch_bounds__(256) void recurrent_bwd_reduce_kernel(const float *part, const float *partb,
                                                                    const float *partg, void *dq, void *dk,
                                                                    float *dbeta, float *dg, int HK, int HV,
@@ -423,8 +428,13 @@ struct RbLayout {
   size_t ckpt, part, partb, partg, total;
 };
 
+// Value rows per workgroup. 32 rows (one workgroup per compute unit on the
+// headline shapes) ran faster than 16 rows (two per compute unit, twice the
+// partial sums): 8.6 against 9.3 ms.
+constexpr int kRows = 32;
+
 RbLayout rb_layout(const gdr_args &a) {
-  const int D = a.DK, NS = D / RW, NV = a.gate == GDR_GATE_CHANNEL ? 3 : 2;
+  const int D = a.DK, NS = D / kRows, NV = a.gate == GDR_GATE_CHANNEL ? 3 : 2;
   const size_t T = (size_t)a.T_total;
   const size_t slots = T / BB + (size_t)a.N + 1;   // bounds bos/B + n + blocks over every sequence
   RbLayout l;
@@ -436,17 +446,22 @@ RbLayout rb_layout(const gdr_args &a) {
   return l;
 }
 
-template <bool IN_F32, int GATE, bool DELTA, int D>
-hipError_t launch_typed(const gdr_args &a, const BwdParams &p, void *dq, void *dk, float *dbeta, float *dg,
-                        hipStream_t stream) {
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
+hipError_t launch_rw(const gdr_args &a, const BwdParams &p, void *dq, void *dk, float *dbeta, float *dg,
+                     hipStream_t stream) {
   constexpr int NS = D / RW;
-  hipLaunchKernelGGL((recurrent_bwd_kernel<IN_F32, GATE, DELTA, D>), dim3((unsigned)(a.N * a.HV * NS)), dim3(256),
+  hipLaunchKernelGGL((recurrent_bwd_kernel<IN_F32, GATE, DELTA, D, RW>), dim3((unsigned)(a.N * a.HV * NS)), dim3(256),
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T_total == 0) return e;
-  hipLaunchKernelGGL((recurrent_bwd_reduce_kernel<GATE, DELTA, D>), dim3((unsigned)a.T_total), dim3(256), 0, stream,
+  hipLaunchKernelGGL((recurrent_bwd_reduce_kernel<GATE, DELTA, D, RW>), dim3((unsigned)a.T_total), dim3(256), 0, stream,
                      p.part, p.partb, p.partg, dq, dk, dbeta, dg, a.HK, a.HV, a.scale, p.out_bf16);
   return hipGetLastError();
+}
+template <bool IN_F32, int GATE, bool DELTA, int D>
+hipError_t launch_typed(const gdr_args &a, const BwdParams &p, void *dq, void *dk, float *dbeta, float *dg,
+                        hipStream_t stream) {
+  return launch_rw<IN_F32, GATE, DELTA, D, kRows>(a, p, dq, dk, dbeta, dg, stream);
 }
 
 template <bool IN_F32, int GATE, bool DELTA>
