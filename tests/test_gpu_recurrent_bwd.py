@@ -201,3 +201,32 @@ def test_recurrent_bwd_headline_shapes_sampled():
         check(got["dbeta"][rows][:, h], ref["dbeta"][:, i], w.in_dtype, "dbeta")
         check(got["dg"][rows][:, h], ref["dg"][:, i], w.in_dtype, "dg")
         check(got["dstate0"][seqs][:, h], ref["dstate0"][:, i], w.in_dtype, "dstate0")
+
+
+def test_recurrent_bwd_debug_checks_reject_bad_indices():
+    """GDR_FLAG_DEBUG_CHECKS verifies cu_seqlens and slot_idx on the device
+    before the walk is launched; valid indices pass and compute."""
+    gdr = _gdr()
+    w = small(64, "bf16", "delta", "scalar", seqlens=(5, 6))
+    x = inputs(w)
+    print("recurrent_bwd debug checks", flush=True)
+    d = {n: dev(x[n], "bf16") for n in ("q", "k", "v", "do")}
+    g, beta, pool = dev(x["g"], "f32"), dev(x["beta"], "f32"), dev(x["pool"], w.state_dtype)
+    slots, cu = dev(x["slot_idx"], "i32"), dev(x["cu_seqlens"], "i32")
+    call = lambda s, c: gdr.recurrent_bwd(d["q"], d["k"], d["v"], g, beta, d["do"], pool, s, c,
+                                          debug_checks=True)
+    bad = slots.clone()
+    bad[1] = bad[0]
+    with pytest.raises(gdr.GdrError) as e:
+        call(bad, cu)
+    assert e.value.status == 5
+    badcu = cu.clone()
+    badcu[1] = 9
+    badcu[2] = 8
+    with pytest.raises(gdr.GdrError) as e:
+        call(slots, badcu)
+    assert e.value.status == 5
+    got = call(slots, cu)
+    torch.cuda.synchronize()
+    ref = reference(w, x)
+    check(host(got["dk"], "f32"), ref["dk"], "bf16", "dk")
