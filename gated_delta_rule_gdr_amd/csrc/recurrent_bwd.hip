@@ -33,11 +33,12 @@
 //   Phase 2 takes the blocks last to first: it reloads the block's
 //   checkpoint, reruns the block's forward steps keeping St~, u and e of each
 //   token in registers, then walks the block's tokens backwards.
-// A thread holds RW/16 rows x DK/16 columns of S (and of D); the 16 lanes of
+// A thread holds RW/(4 NW) rows x DK/16 columns of S (and of D), NW waves per
+// workgroup (8: one row per thread, two waves per SIMD); the 16 lanes of
 // a DPP row share those rows, so the dots over k (u, de) are 16-lane DPP sums,
 // and
-// the sums over rows are lane shuffles across the four 16-lane groups of a
-// wave, then a sum over the four waves through LDS at the end of the block.
+// the sums over rows are lane swaps across the four 16-lane groups of a
+// wave, then a sum over the waves through LDS at the end of the block.
 #include <cstdint>
 
 #include "recurrent_bwd.h"
@@ -59,11 +60,17 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0x140>(x);   // row_mirror: the other 8 of the 16
   return x;
 }
-// Sum over the four 16-lane groups of the wave (the same lane of each).
+// Sum over the four 16-lane groups of the wave (the same lane of each), with
+// gfx950's lane swaps: permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second, permlane32_swap the upper
+// half of the first with the lower half of the second. With x in both, every
+// lane ends up holding x in one result and its partner's x in the other, so
+// their sum adds the partner lane (lane ^ 16, then lane ^ 32) in the VALU.
 __device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <bool F32>
@@ -96,24 +103,24 @@ struct BwdParams {
 template <int GATE>
 constexpr int nvec() { return GATE == GDR_GATE_CHANNEL ? 3 : 2; }
 
-template <int GATE, int D, int RW>
+template <int GATE, int D, int RW, int NW>
 struct BwdSmem {
   static constexpr int GP = GATE == GDR_GATE_CHANNEL ? D : 1;
   alignas(16) float kk[BB][D];
   alignas(16) float qq[BB][D];
   alignas(16) float ga[BB][GP];   // exp(g)
   float vv[BB][RW], dd[BB][RW], bb[BB];
-  alignas(16) float red[BB][4][nvec<GATE>() * D];   // per wave: the block's column sums
-  float redb[BB][4], redg[BB][4];
+  alignas(16) float red[BB][NW][nvec<GATE>() * D];   // per wave: the block's column sums
+  float redb[BB][NW], redg[BB][NW];
   float dvs[BB][RW];
 };
 
 // Stage tokens t0 .. t0 + len - 1 of the block: keys (and queries, upstream
 // gradients with `back`), this workgroup's value rows, beta and exp(g).
-template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
-__device__ __forceinline__ void stage(BwdSmem<GATE, D, RW> &sm, const BwdParams &p, int64_t t0, int len, int h,
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW, int NW>
+__device__ __forceinline__ void stage(BwdSmem<GATE, D, RW, NW> &sm, const BwdParams &p, int64_t t0, int len, int h,
                                       int hk, int r0, bool back, int tid) {
-  for (int e = tid; e < BB * D; e += 256) {
+  for (int e = tid; e < BB * D; e += 64 * NW) {
     const int i = e / D, c = e % D;
     if (i < len) {
       const int64_t t = t0 + i;
@@ -122,7 +129,7 @@ __device__ __forceinline__ void stage(BwdSmem<GATE, D, RW> &sm, const BwdParams 
       if constexpr (GATE == GDR_GATE_CHANNEL) sm.ga[i][c] = __expf(p.g[(t * p.HV + h) * D + c]);
     }
   }
-  for (int e = tid; e < BB * RW; e += 256) {
+  for (int e = tid; e < BB * RW; e += 64 * NW) {
     const int i = e / RW, r = e % RW;
     if (i < len) {
       const int64_t t = t0 + i;
@@ -137,18 +144,19 @@ __device__ __forceinline__ void stage(BwdSmem<GATE, D, RW> &sm, const BwdParams 
   }
 }
 
-template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
-__global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW, int NW>
+__global__ __launch_bounds__(64 * NW) void recurrent_bwd_kernel(BwdParams p) {
   constexpr int C = D / 16;          // key columns per thread
   constexpr int NS = D / RW;         // row groups per head
   constexpr int NV = nvec<GATE>();
-  constexpr int R = RW / 16;         // rows per thread
-  __shared__ BwdSmem<GATE, D, RW> sm;
+  constexpr int R = RW / (4 * NW);   // rows per thread (each wave: four 16-lane row groups)
+  static_assert(R >= 1 && R * 4 * NW == RW, "rows per workgroup must fill the waves");
+  __shared__ BwdSmem<GATE, D, RW, NW> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int rg = lane >> 4, cg = lane & 15;
   const int kc = cg * C;                 // first key column
-  const int lr = w * (RW / 4) + rg * R;  // first of the thread's local rows
+  const int lr = w * (RW / NW) + rg * R;  // first of the thread's local rows
   const int split = blockIdx.x % NS;
   const int nh = blockIdx.x / NS;
   const int n = nh / p.HV, h = nh - n * p.HV, hk = h / p.ratio;
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
   for (int b = 0; b < nb; ++b) {
     const int64_t t0 = bos + (int64_t)b * BB;
     const int len = (int)min<int64_t>(BB, L - (int64_t)b * BB);
-    stage<IN_F32, GATE, DELTA, D>(sm, p, t0, len, h, hk, r0, false, tid);
+    stage<IN_F32, GATE, DELTA, D, RW, NW>(sm, p, t0, len, h, hk, r0, false, tid);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
   for (int b = nb - 1; b >= 0; --b) {
     const int64_t t0 = bos + (int64_t)b * BB;
     const int len = (int)min<int64_t>(BB, L - (int64_t)b * BB);
-    stage<IN_F32, GATE, DELTA, D>(sm, p, t0, len, h, hk, r0, true, tid);
+    stage<IN_F32, GATE, DELTA, D, RW, NW>(sm, p, t0, len, h, hk, r0, true, tid);
     __syncthreads();
     // the block's checkpoint (written by this same thread in phase 1)
 #pragma unroll
@@ -354,20 +362,27 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdParams p) {
     }
     __syncthreads();
     // the block's partial sums over this workgroup's rows, and dv
-    for (int e = tid; e < len * NV * D; e += 256) {
+    for (int e = tid; e < len * NV * D; e += 64 * NW) {
       const int i = e / (NV * D), c = e - i * (NV * D);
-      const float x = sm.red[i][0][c] + sm.red[i][1][c] + sm.red[i][2][c] + sm.red[i][3][c];
+      float x = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) x += sm.red[i][v][c];
       p.part[(((t0 + i) * p.HV + h) * NS + split) * (NV * D) + c] = x;
     }
-    for (int e = tid; e < len * RW; e += 256) {
+    for (int e = tid; e < len * RW; e += 64 * NW) {
       const int i = e / RW, r = e % RW;
       st_out(p.dv, ((t0 + i) * p.HV + h) * D + r0 + r, sm.dvs[i][r], p.out_bf16);
     }
     if (tid < len) {
       const int64_t o = ((t0 + tid) * p.HV + h) * NS + split;
-      if constexpr (DELTA) p.partb[o] = sm.redb[tid][0] + sm.redb[tid][1] + sm.redb[tid][2] + sm.redb[tid][3];
-      if constexpr (GATE == GDR_GATE_SCALAR)
-        p.partg[o] = sm.redg[tid][0] + sm.redg[tid][1] + sm.redg[tid][2] + sm.redg[tid][3];
+      float sb = 0.f, sg = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        sb += sm.redb[tid][v];
+        sg += sm.redg[tid][v];
+      }
+      if constexpr (DELTA) p.partb[o] = sb;
+      if constexpr (GATE == GDR_GATE_SCALAR) p.partg[o] = sg;
     }
   }
 
@@ -432,6 +447,7 @@ struct RbLayout {
 // headline shapes) ran faster than 16 rows (two per compute unit, twice the
 // partial sums): 8.6 against 9.3 ms.
 constexpr int kRows = 32;
+constexpr int kWaves = 8;   // one row per thread: two waves per SIMD
 
 RbLayout rb_layout(const gdr_args &a) {
   const int D = a.DK, NS = D / kRows, NV = a.gate == GDR_GATE_CHANNEL ? 3 : 2;
@@ -446,11 +462,12 @@ RbLayout rb_layout(const gdr_args &a) {
   return l;
 }
 
-template <bool IN_F32, int GATE, bool DELTA, int D, int RW>
+template <bool IN_F32, int GATE, bool DELTA, int D, int RW, int NW>
 hipError_t launch_rw(const gdr_args &a, const BwdParams &p, void *dq, void *dk, float *dbeta, float *dg,
                      hipStream_t stream) {
   constexpr int NS = D / RW;
-  hipLaunchKernelGGL((recurrent_bwd_kernel<IN_F32, GATE, DELTA, D, RW>), dim3((unsigned)(a.N * a.HV * NS)), dim3(256),
+  hipLaunchKernelGGL((recurrent_bwd_kernel<IN_F32, GATE, DELTA, D, RW, NW>), dim3((unsigned)(a.N * a.HV * NS)),
+                     dim3(64 * NW),
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T_total == 0) return e;
@@ -461,7 +478,7 @@ hipError_t launch_rw(const gdr_args &a, const BwdParams &p, void *dq, void *dk, 
 template <bool IN_F32, int GATE, bool DELTA, int D>
 hipError_t launch_typed(const gdr_args &a, const BwdParams &p, void *dq, void *dk, float *dbeta, float *dg,
                         hipStream_t stream) {
-  return launch_rw<IN_F32, GATE, DELTA, D, kRows>(a, p, dq, dk, dbeta, dg, stream);
+  return launch_rw<IN_F32, GATE, DELTA, D, kRows, kWaves>(a, p, dq, dk, dbeta, dg, stream);
 }
 
 template <bool IN_F32, int GATE, bool DELTA>
