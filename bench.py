@@ -6,8 +6,9 @@
 A step is one gdr_chunk_fwd call (the whole prefill path: loads, gate sums,
 Gram matrices, triangular solve, corrected values, outputs, state scan and
 write-back) over the workload's full batch, with inputs already resident in
-HBM. Three copies of the inputs/outputs are used in rotation so that no step
-reads what the previous one left in the 256 MB last-level cache. The decode
+HBM. For workloads under 1 GB three copies of the inputs/outputs are used in
+rotation so that no step reads what the previous one left in the 256 MB
+last-level cache. The decode
 path is timed alongside: 1000 consecutive gdr_recurrent_step launches over
 the 256-sequence decode workload, each step with a new token per sequence
 (64 distinct token sets in rotation; the state pool carries over). The
@@ -15,15 +16,17 @@ ragged tokenwise recurrence (gdr_recurrent_fwd) is timed on 256 sequences of
 16 tokens over the same fp32 pool, with gdr_chunk_fwd on that batch beside it.
 
 Prints one JSON line. `value` is prefill tokens per second for one layer (all
-heads); `roofline` describes the prefill kernel against HBM bandwidth (its
-binding roofline: ~126 flop/byte against a ridge of ~315), with its MFMA
-fraction alongside; `decode` gives steps/s and HBM fraction of the step
-kernel; `linear_mode` the same shapes with alpha = 1 and no delta (linear
-attention) and `linear_backward` its gradients (dq, dk, dv); `recurrent_fwd` the
-same for the tokenwise recurrence; `delta_product`
-the chunkwise prefill of Gated DeltaProduct (2 transitions per token) on the
-headline shapes; `speculative` a 4-token verify window per sequence and the fold
-of its accepted prefix on the decode pool; `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+heads) on the largest configuration, the KDA long-context prefill (T = 131072,
+32 heads, per-key-channel gate); `roofline` describes its prefill call against
+HBM bandwidth (its binding roofline), with its MFMA fraction alongside;
+`configs` holds the same figures for each of the five configurations (and
+configuration 2's linear-attention run), the decode step's as steps/s and HBM
+fraction; `linear_backward` and `gdn_backward` time the gradients on the
+Gated DeltaNet batch; `recurrent_fwd` the tokenwise recurrence on a short
+batch; `delta_product` the chunkwise prefill of Gated DeltaProduct (2
+transitions per token); `speculative` a 4-token verify window per sequence and
+the fold of its accepted prefix on the decode pool; `cpu_baseline` times the
+fp64 oracle on bounded samples on the host's cores.
 """
 from __future__ import annotations
 
@@ -149,11 +152,15 @@ def _dev(x, dtype, device):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
 
 
-def bench_prefill(w: synth.Workload, steps: int, warmup: int, copies: int = 3):
+def bench_prefill(w: synth.Workload, steps: int, warmup: int, copies: int = 0):
     import torch
     import gated_delta_rule_gdr_amd as gdr
     gdr.load()
     dev = torch.device("cuda", 0)
+    if copies <= 0:
+        # rotate copies only where one call's inputs could stay in the 256 MB
+        # last-level cache between calls
+        copies = 3 if prefill_bytes(w) < (1 << 30) else 1
     x = synth.generate(w)
     sets = []
     for _ in range(copies):
@@ -426,46 +433,138 @@ def bench_speculative(w: synth.Workload, window: int, steps: int, warmup: int = 
 # CPU leg: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w: synth.Workload, budget_s: float = 15.0):
-    """Time the oracle (single BLAS thread) on the first sequence's first
-    tokens for all value heads; report tokens/s/layer for that sample."""
+def _oracle_args(w: synth.Workload, x: dict) -> dict:
+    return dict(q=synth.widen(x["q"], w.in_dtype), k=synth.widen(x["k"], w.in_dtype),
+                v=synth.widen(x["v"], w.in_dtype),
+                g=None if x["g"] is None else x["g"].astype(np.float64),
+                beta=None if x["beta"] is None else x["beta"].astype(np.float64),
+                pool=synth.widen(x["pool"], w.state_dtype))
+
+
+_ORACLE_JOB = {}
+
+
+def _oracle_heads(kh):
+    """Worker: the oracle over key heads kh (and their value heads) of the
+    batch in _ORACLE_JOB (inherited from the parent when the pool forks)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    tok = 64
-    x = None
-    elapsed = 0.0
-    while True:
-        ws = w.replace(seqlens=(tok,))
-        x = synth.generate(ws)
-        args = dict(q=synth.widen(x["q"], w.in_dtype), k=synth.widen(x["k"], w.in_dtype),
-                    v=synth.widen(x["v"], w.in_dtype),
-                    g=None if x["g"] is None else x["g"].astype(np.float64),
-                    beta=None if x["beta"] is None else x["beta"].astype(np.float64),
-                    pool=synth.widen(x["pool"], w.state_dtype))
-        ctx = threadpool_limits(1) if threadpool_limits else None
+    w, x, a = _ORACLE_JOB["w"], _ORACLE_JOB["x"], _ORACLE_JOB["a"]
+    ratio = w.HV // w.HK
+    heads = (kh[:, None] * ratio + np.arange(ratio)[None, :]).ravel()
+    t0 = time.perf_counter()
+    oracle.recurrent_fp64(a["q"][:, kh], a["k"][:, kh], a["v"][:, heads],
+                          None if a["g"] is None else a["g"][:, heads],
+                          None if a["beta"] is None else a["beta"][:, heads],
+                          a["pool"][:, heads], x["slot_idx"], x["cu_seqlens"],
+                          scale=w.DK ** -0.5, rule=w.rule, gate=w.gate, zero_init=w.zero_init,
+                          state_dtype=w.state_dtype)
+    return time.perf_counter() - t0
+
+
+def _time_oracle(w: synth.Workload, x: dict, procs: int) -> float:
+    """Wall time of the fp64 oracle over x's batch with `procs` host
+    processes: the key heads (with the value heads that read them) are split
+    into `procs` groups that run side by side, each head's recurrence being
+    separate. BLAS is held to one thread per process. Forks, so it must run
+    before anything in this process touches the GPU."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    _ORACLE_JOB.update(w=w, x=x, a=_oracle_args(w, x))
+    groups = [gr for gr in np.array_split(np.arange(w.HK), min(procs, w.HK)) if len(gr)]
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        if ctx:
-            with ctx:
-                oracle.recurrent_fp64(**args, slot_idx=x["slot_idx"], cu_seqlens=[0, tok],
-                                      scale=w.DK ** -0.5, rule=w.rule, gate=w.gate,
-                                      zero_init=w.zero_init, state_dtype=w.state_dtype)
+        if len(groups) == 1:
+            _oracle_heads(groups[0])
         else:
-            oracle.recurrent_fp64(**args, slot_idx=x["slot_idx"], cu_seqlens=[0, tok],
-                                  scale=w.DK ** -0.5, rule=w.rule, gate=w.gate,
-                                  zero_init=w.zero_init, state_dtype=w.state_dtype)
-        elapsed = time.perf_counter() - t0
-        if elapsed > budget_s / 3 or tok >= w.seqlens[0]:
-            break
-        tok = min(w.seqlens[0], tok * 4)
-    return {"value": tok / elapsed, "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 tokenwise recurrence, first {tok} tokens of sequence 0, all "
-                      f"{w.HV} value heads, one BLAS thread; {elapsed:.2f} s"}
+            with mp.get_context("fork").Pool(len(groups)) as pool:
+                pool.map(_oracle_heads, groups)
+        el = time.perf_counter() - t0
+    _ORACLE_JOB.clear()
+    return el
+
+
+def cpu_baseline(w: synth.Workload, budget_s: float = 8.0):
+    """The fp64 oracle on the host cores, on bounded samples (about 30 s of
+    CPU work in all): the headline workload's first tokens of every
+    sequence for all heads, timed with one process and with one process per
+    core (at most 16, the host share of one GPU); samples of the other
+    configurations beside it, each with the time the whole configuration
+    would take at the sampled rate (the oracle's cost is linear in tokens x
+    heads). Runs before the GPU is touched (it forks)."""
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, 16)
+
+    def sample(wl: synth.Workload, threads: int, budget: float):
+        tok, lens = 32, np.asarray(wl.seqlens)
+        while True:
+            sl = tuple(int(n) for n in np.minimum(lens, tok))
+            ws = wl.replace(seqlens=sl, steps=1)
+            el = _time_oracle(ws, synth.generate(ws), threads)
+            if el > budget / 3 or tok >= lens.max():
+                return ws, el
+            tok = min(int(lens.max()), tok * 4)
+
+    ws, el1 = sample(w, 1, budget_s)
+    elm = _time_oracle(ws, synth.generate(ws), cores)
+    full_tok = w.T_total
+    out = {"value": ws.T_total / elm, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+           "sample": f"fp64 tokenwise recurrence of {w.name}: the first {ws.seqlens[0]} tokens of each of its "
+                     f"{w.N} sequence(s), all {w.HV} value heads, the heads split over {cores} "
+                     f"processes (one per core; the host shows {affinity}) in {elm:.2f} s",
+           "single_thread": {"value": ws.T_total / el1, "seconds": el1},
+           "full_config_estimate_s": full_tok / (ws.T_total / elm),
+           "configs": {}}
+    for name in synth.CONFIGS:
+        wl = synth.workload(name)
+        if name == w.name:
+            continue
+        if wl.steps > 1:
+            # decode: one step of the whole batch
+            x = synth.generate(wl.replace(steps=1))
+            el = _time_oracle(wl.replace(steps=1), x, cores)
+            out["configs"][name] = {"steps_per_s": 1.0 / el, "unit": "decode steps/s (256 sequences)",
+                                    "sample": "one step of the full batch", "seconds": el,
+                                    "full_config_estimate_s": wl.steps * el}
+            continue
+        ws2, el = sample(wl, cores, budget_s / 2)
+        rate = ws2.T_total / el
+        out["configs"][name] = {"tokens_per_s": rate, "unit": "tokens/s/layer",
+                                "sample": f"first {max(ws2.seqlens)} tokens of each sequence, {ws2.T_total} "
+                                          f"tokens in all", "seconds": el,
+                                "full_config_estimate_s": wl.T_total / rate}
+    return out
 
 
 # ----------------------------------------------------------------------------
+
+def prefill_leg(w: synth.Workload, steps: int, warmup: int) -> dict:
+    """Time gdr_chunk_fwd on w (fp32 outputs): tokens/s, the kernel's HBM and
+    MFMA fractions, and the committed counter traffic."""
+    step_s, kernel_ms, kernel_med = bench_prefill(w, steps, warmup)
+    nbytes = prefill_bytes(w)
+    nflops = prefill_flops(w, w.chunk_size)
+    kname, ksrcs = prefill_kernel(w)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    return {"workload": w.name, "tokens": w.T_total, "tokens_per_s": w.T_total / step_s,
+            "ms_per_step": step_s * 1e3, "kernel": kname, "kernel_ms_mean": kernel_ms,
+            "kernel_ms_median": kernel_med, "algorithmic_bytes": nbytes, "algorithmic_flops": nflops,
+            "hbm_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
+            "mfma_tflops": nflops / (kernel_ms * 1e-3) / 1e12,
+            "mfma_frac": nflops / (kernel_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": committed_traffic(kname, w.name, ksrcs)}
+
+
+def decode_leg(steps: int) -> dict:
+    dw = synth.workload("decode_n256_hk16_hv32_d128")
+    d_step, d_kernel = bench_decode(dw, steps)
+    db = step_bytes(dw)
+    return {"workload": dw.name, "steps": steps, "steps_per_s": 1.0 / d_step,
+            "us_per_step": d_step * 1e6, "kernel": "recurrent_step_kernel",
+            "kernel_us_per_step": d_kernel * 1e3, "algorithmic_bytes_per_step": db,
+            "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
+            "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC)}
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -474,6 +573,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=synth.HEADLINE)
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only --workload (no other configuration legs)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--recurrent-steps", type=int, default=50)
     ap.add_argument("--no-recurrent", action="store_true")
@@ -495,6 +596,10 @@ def main():
                                    "multi-GPU runs are not part of it"}))
         sys.exit(2)
 
+    w = synth.workload(args.workload)
+    # the CPU leg forks worker processes, so it runs before the GPU is touched
+    cpu = None if (args.no_cpu_baseline or args.calibrate_copy) else cpu_baseline(w)
+
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -511,52 +616,52 @@ def main():
                           "bytes_written_per_copy": nbytes, "copies": 3}), flush=True)
         return
 
-    w = synth.workload(args.workload)
     torch.cuda.synchronize()
-    step_s, kernel_ms, kernel_med = bench_prefill(w, args.steps, args.warmup)
-    tokens_per_s = w.T_total / step_s
-    nbytes = prefill_bytes(w)
-    nflops = prefill_flops(w, w.chunk_size)
-    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-    kname, ksrcs = prefill_kernel(w)
-    traffic = committed_traffic(kname, w.name, ksrcs)
+    head = prefill_leg(w, args.steps, args.warmup)
     result = {
         "metric": "prefill tokens/s/layer + decode steps/s; % MFMA peak / % HBM BW",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
                 "g=-softplus(N(0,1)-shift))",
-        "config": {"workload": w.name, "batch": w.N, "seq_len": int(w.seqlens[0]),
+        "config": {"workload": w.name, "batch": w.N, "seq_len": int(max(w.seqlens)),
                    "tokens": w.T_total, "key_heads": w.HK, "value_heads": w.HV,
                    "head_dim": w.DK, "chunk": w.chunk_size, "gate": w.gate, "rule": w.rule,
                    "in_dtype": w.in_dtype, "out_dtype": "f32", "state_dtype": w.state_dtype},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kname, "kernel_ms_mean": kernel_ms,
-                     "kernel_ms_median": kernel_med, "algorithmic_bytes": nbytes,
-                     "algorithmic_flops": nflops,
-                     "mfma_tflops": nflops / (kernel_ms * 1e-3) / 1e12,
-                     "mfma_frac": nflops / (kernel_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": head["traffic"],
+                     "kernel": head["kernel"], "kernel_ms_mean": head["kernel_ms_mean"],
+                     "kernel_ms_median": head["kernel_ms_median"],
+                     "algorithmic_bytes": head["algorithmic_bytes"],
+                     "algorithmic_flops": head["algorithmic_flops"],
+                     "mfma_tflops": head["mfma_tflops"], "mfma_frac": head["mfma_frac"]},
     }
-    if not args.no_decode:
-        dw = synth.workload("decode_n256_hk16_hv32_d128")
-        d_step, d_kernel = bench_decode(dw, args.decode_steps)
-        db = step_bytes(dw)
-        result["decode"] = {
-            "workload": dw.name, "steps": args.decode_steps, "steps_per_s": 1.0 / d_step,
-            "us_per_step": d_step * 1e6, "kernel_us_per_step": d_kernel * 1e3,
-            "algorithmic_bytes_per_step": db,
-            "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
-            "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC)}
+    if not args.no_configs:
+        # every configuration of the pages' workloads (the headline's numbers
+        # repeated under its name), and configuration 2's linear-attention run
+        legs = {}
+        for name in synth.CONFIGS:
+            if name == w.name:
+                legs[name] = head
+            elif synth.workload(name).steps > 1:
+                if not args.no_decode:
+                    legs[name] = decode_leg(args.decode_steps)
+            else:
+                legs[name] = prefill_leg(synth.workload(name), args.steps, args.warmup)
+        if not args.no_linear:
+            legs["la_prefill_b4_t4096_h16_d128"] = prefill_leg(
+                synth.workload("la_prefill_b4_t4096_h16_d128"), args.steps, args.warmup)
+        result["configs"] = legs
+        if "decode_n256_hk16_hv32_d128" in legs:
+            result["decode"] = legs["decode_n256_hk16_hv32_d128"]
     if not args.no_recurrent:
         rw = synth.workload("short_prefill_n256_t16_hk16_hv32_d128")
         t = bench_recurrent_fwd(rw, args.recurrent_steps)
@@ -570,21 +675,7 @@ def main():
             "hbm_frac": rb / (t["recurrent_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": committed_traffic("recurrent_fwd_kernel", rw.name, RECUR_SRC),
             "chunk_fwd_kernel_us_same_batch": t["chunk_fwd"] * 1e3}
-    if not args.no_linear and w.name == synth.HEADLINE:
-        # the same shapes in linear-attention mode (alpha = 1, no delta)
-        lw = synth.workload("la_prefill_b4_t4096_h16_d128")
-        l_step, l_ms, l_med = bench_prefill(lw, args.steps, args.warmup)
-        lb = prefill_bytes(lw)
-        lf = prefill_flops(lw, lw.chunk_size)
-        lk, lsrc = prefill_kernel(lw)
-        result["linear_mode"] = {
-            "workload": lw.name, "tokens_per_s": lw.T_total / l_step, "kernel": lk,
-            "kernel_ms_mean": l_ms, "kernel_ms_median": l_med, "algorithmic_bytes": lb,
-            "hbm_gbs": lb / (l_ms * 1e-3) / 1e9, "hbm_frac": lb / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_tflops": lf / (l_ms * 1e-3) / 1e12,
-            "mfma_frac": lf / (l_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": committed_traffic(lk, lw.name, lsrc)}
-    if not args.no_backward and w.name == synth.HEADLINE:
+    if not args.no_backward:
         # gradients of the linear-attention mode (dq, dk, dv from dO)
         bw = synth.workload("la_prefill_b4_t4096_h16_d128")
         bt = bench_linear_bwd(bw, args.steps)
@@ -596,9 +687,8 @@ def main():
             "algorithmic_bytes": bb, "hbm_gbs": bb / (bt * 1e-3) / 1e9,
             "hbm_frac": bb / (bt * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_flops": bf, "mfma_tflops": bf / (bt * 1e-3) / 1e12}
-    if not args.no_backward and w.name == synth.HEADLINE:
-        # gradients of the gated delta rule on the headline batch (tokenwise)
-        gw = synth.workload(synth.HEADLINE)
+        # gradients of the gated delta rule on the GDN batch (tokenwise)
+        gw = synth.workload(synth.GDN)
         gt, gws = bench_recurrent_bwd(gw, args.backward_steps)
         T, HD, HVT = gw.T_total, gw.HV * gw.DK, gw.T_total * gw.HV
         # q, k, v, dO, g, beta and the initial states read; dq, dk, dv, dbeta,
@@ -612,7 +702,7 @@ def main():
             "hbm_frac": gb / (gt * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": gws,
             "traffic": committed_traffic("recurrent_bwd_kernel+recurrent_bwd_reduce_kernel", gw.name, RBWD_SRC)}
     if not args.no_product:
-        pw, P = synth.workload(synth.HEADLINE), 2
+        pw, P = synth.workload(synth.GDN), 2
         pt = bench_product(pw, P, args.product_steps)
         pb = product_bytes(pw, P)
         result["delta_product"] = {
@@ -624,7 +714,7 @@ def main():
                                          pw.chunk_size) / (pt * 1e-3) / 1e12,
             "traffic": committed_traffic("chunk_fwd_ws_kernel", "gdp_nh2_prefill_b4_t4096_h16_d128",
                                          prefill_kernel(pw)[1])}
-    if not args.no_speculative and not args.no_decode:
+    if not args.no_speculative and "decode" in result:
         # speculative decoding: verify 4 draft tokens per sequence, fold the
         # accepted prefix (the decode workload's pool and heads)
         sw_ = synth.workload("decode_n256_hk16_hv32_d128")
@@ -633,8 +723,8 @@ def main():
             "workload": sw_.name, "window": 4, "mean_accepted": mean_acc, "ms_per_window": sp_ms,
             "accepted_tokens_per_s": sw_.N * mean_acc / (sp_ms * 1e-3),
             "decode_steps_same_tokens_ms": result["decode"]["kernel_us_per_step"] * 1e-3 * mean_acc}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -285,20 +285,46 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-// Bound of every wait on an LDS counter (a wait that runs out goes on with
-// whatever the counter's producers have stored by then, so it cannot hang).
+// Bound of every wait on an LDS counter. A wait that runs out goes on with
+// whatever the counter's producers have stored by then, so it cannot hang;
+// it also sets g_wait_timeout, which the host clears before and reads after
+// a call made with GDR_FLAG_DEBUG_CHECKS and reports as GDR_E_DEVICE_CHECK.
+// (A wait runs out only if a producer wave never signals: a defect, never a
+// matter of timing; 2^20 polls with a sleep each last well over 10 ms.)
 constexpr int SPIN = 1 << 20;
+
+// One word per translation unit that includes this header.
+static __device__ int g_wait_timeout;
+
+__device__ __forceinline__ void note_wait_timeout() {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(&g_wait_timeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void spin_until(const int *ctr, int target) {
   // an LDS-typed pointer: a generic one compiles to a flat load, which would
   // also wait for global loads in flight
   typedef __attribute__((address_space(3))) volatile int lds_vint;
   const lds_vint *p = (const lds_vint *)ctr;
+  bool done = false;
   for (int spin = 0; spin < SPIN; ++spin) {
-    if (*p >= target) break;
+    if (*p >= target) {
+      done = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (!done) note_wait_timeout();
   asm volatile("" ::: "memory");
+}
+
+// Host side of g_wait_timeout for the including translation unit: clear it
+// (clear = true) or copy it to *out, both enqueued on `stream`.
+static inline hipError_t wait_flag_access(int *out, bool clear, hipStream_t stream) {
+  static const int zero = 0;
+  if (clear) return hipMemcpyToSymbolAsync(HIP_SYMBOL(g_wait_timeout), &zero, sizeof(int), 0,
+                                           hipMemcpyHostToDevice, stream);
+  return hipMemcpyFromSymbolAsync(out, HIP_SYMBOL(g_wait_timeout), sizeof(int), 0, hipMemcpyDeviceToHost,
+                                  stream);
 }
 
 // This wave's LDS stores land, then one lane counts the wave in.

@@ -1061,6 +1061,10 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
 
 }  // namespace
 
+hipError_t kda_wait_flag(int *out, bool clear, hipStream_t stream) {
+  return chunk::wait_flag_access(out, clear, stream);
+}
+
 bool chunk_fwd_kda_applies(const gdr_args &a) {
   return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && products_of(a) == 1;
 }

@@ -391,14 +391,18 @@ __device__ __forceinline__ void solve_col(const SM &sm, int r, int g, HoldWS &h,
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) volatile i32x4 lds_vi32x4;
     const lds_vi32x4 *q = (const lds_vi32x4 *)&sm.rcount[0];
+    bool done = false;
     for (int spin = 0; spin < SPIN; ++spin) {
       const i32x4 v = *q;
       const int n = ci + 1;
       if ((J > 0 || v[0] >= row_producers(true, NP, 0) * n) && (J > 1 || v[1] >= row_producers(true, NP, 1) * n) &&
-          (J > 2 || v[2] >= row_producers(true, NP, 2) * n) && v[3] >= row_producers(true, NP, 3) * n)
+          (J > 2 || v[2] >= row_producers(true, NP, 2) * n) && v[3] >= row_producers(true, NP, 3) * n) {
+        done = true;
         break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (!done) note_wait_timeout();
     asm volatile("" ::: "memory");
   }
   {
@@ -1101,6 +1105,10 @@ int cu_count() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+hipError_t ws_wait_flag(int *out, bool clear, hipStream_t stream) {
+  return chunk::wait_flag_access(out, clear, stream);
 }
 
 hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {

@@ -3,7 +3,9 @@
 // Validation reads only host-visible fields of gdr_args (never device memory)
 // and runs before anything is enqueued, so a rejected call has no side
 // effects. Device-side index arrays are checked only under
-// GDR_FLAG_DEBUG_CHECKS, by a small kernel whose verdict is copied back.
+// GDR_FLAG_DEBUG_CHECKS, by a small kernel whose verdict (a static device
+// word, no allocation) is copied back; the same flag reports bounded waits
+// inside the prefill kernels that ran out.
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -115,28 +117,13 @@ gdr_status validate(const gdr_args *a, Call call) {
   return GDR_OK;
 }
 
-gdr_status run_debug_checks(const gdr_args *a, bool prefill, hipStream_t stream) {
-  int *flag = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&flag), sizeof(int), stream);
-  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
-  int h = -1;
-  e = launch_index_checks(*a, prefill, flag, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  (void)hipFreeAsync(flag, stream);
-  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
-  switch (h) {
-    case 0: return GDR_OK;
-    case 1: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens[0] != 0 or cu_seqlens[N] != T_total");
-    case 2: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens is not non-decreasing");
-    case 3: return fail(GDR_E_DEVICE_CHECK, "slot_idx out of [0, num_slots)");
-    case 4: return fail(GDR_E_DEVICE_CHECK, "slot_idx has duplicates");
-    default: return fail(GDR_E_DEVICE_CHECK, "device check code %d", h);
-  }
-}
+// Verdict of the device-side index check (0: valid, else the code of the
+// first defect found), written by index_check_kernel on each device. Calls
+// that overlap on one device with GDR_FLAG_DEBUG_CHECKS share it and race.
+__device__ int g_index_check;
 
 __global__ void index_check_kernel(const int32_t *cu, const int32_t *slots, int32_t N,
-                                   int64_t T_total, int64_t num_slots, int prefill, int *flag) {
+                                   int64_t T_total, int64_t num_slots, int prefill) {
   __shared__ int code;
   if (threadIdx.x == 0) code = 0;
   __syncthreads();
@@ -154,17 +141,49 @@ __global__ void index_check_kernel(const int32_t *cu, const int32_t *slots, int3
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) *flag = code;
+  if (threadIdx.x == 0) g_index_check = code;
+}
+
+// GDR_FLAG_DEBUG_CHECKS, before the call's kernels: verify cu_seqlens and
+// slot_idx on the device (synchronising the stream) and clear the bounded
+// waits' timeout words. Allocates nothing.
+gdr_status run_debug_checks(const gdr_args *a, bool prefill, hipStream_t stream) {
+  hipLaunchKernelGGL(index_check_kernel, dim3(1), dim3(256), 0, stream, a->cu_seqlens, a->slot_idx, a->N,
+                     (int64_t)a->T_total, (int64_t)a->num_slots, prefill ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  int h = -1;
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbolAsync(&h, HIP_SYMBOL(g_index_check), sizeof(int), 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = ws_wait_flag(nullptr, true, stream);
+  if (e == hipSuccess) e = kda_wait_flag(nullptr, true, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
+  switch (h) {
+    case 0: return GDR_OK;
+    case 1: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens[0] != 0 or cu_seqlens[N] != T_total");
+    case 2: return fail(GDR_E_DEVICE_CHECK, "cu_seqlens is not non-decreasing");
+    case 3: return fail(GDR_E_DEVICE_CHECK, "slot_idx out of [0, num_slots)");
+    case 4: return fail(GDR_E_DEVICE_CHECK, "slot_idx has duplicates");
+    default: return fail(GDR_E_DEVICE_CHECK, "device check code %d", h);
+  }
+}
+
+// GDR_FLAG_DEBUG_CHECKS, after the call's kernels: wait for them and report a
+// bounded wait on an LDS counter that ran out (a producer that never
+// signalled, so the results are not to be trusted).
+gdr_status finish_debug_checks(hipStream_t stream) {
+  int ws = 0, kda = 0;
+  hipError_t e = ws_wait_flag(&ws, false, stream);
+  if (e == hipSuccess) e = kda_wait_flag(&kda, false, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "debug checks: %s", hipGetErrorString(e));
+  if (ws || kda)
+    return fail(GDR_E_DEVICE_CHECK, "a bounded wait inside the %s prefill kernel ran out; results are invalid",
+                ws ? "warp-specialised" : "channel-gate");
+  return GDR_OK;
 }
 
 }  // namespace
-
-hipError_t launch_index_checks(const gdr_args &a, bool prefill, int *flag_dev, hipStream_t stream) {
-  hipLaunchKernelGGL(index_check_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.slot_idx,
-                     a.N, (int64_t)a.T_total, (int64_t)a.num_slots, prefill ? 1 : 0, flag_dev);
-  return hipGetLastError();
-}
-
 }  // namespace gdr
 
 using namespace gdr;
@@ -297,6 +316,7 @@ GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t w
   hipError_t e = ws_path ? launch_chunk_fwd_kda(*a, workspace, ws_bytes, stream)
                          : launch_chunk_fwd(*a, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) return finish_debug_checks(stream);
   return GDR_OK;
 }
 
@@ -336,6 +356,7 @@ GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, 
   }
   hipError_t e = launch_linear_bwd(*a, dout, dq, dk, dv, workspace, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "linear_chunk_bwd launch: %s", hipGetErrorString(e));
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) return finish_debug_checks(stream);
   return GDR_OK;
 }
 

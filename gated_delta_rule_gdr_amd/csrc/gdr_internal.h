@@ -71,9 +71,10 @@ bool chunk_fwd_kda_applies(const gdr_args &a);
 size_t chunk_fwd_kda_workspace(const gdr_args &a);       // preferred bytes
 size_t chunk_fwd_kda_min_workspace(const gdr_args &a);   // fewest bytes that work
 hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hipStream_t stream);
-// Writes 0 to *flag_dev when cu_seqlens (prefill) and slot_idx are valid,
-// else a nonzero code; flag_dev is a device int.
-hipError_t launch_index_checks(const gdr_args &a, bool prefill, int *flag_dev,
-                               hipStream_t stream);
+// The wait-timeout word of the warp-specialised prefill (also run by the
+// linear-attention backward) and of the channel-gate pair: cleared
+// (clear = true) or copied to the host int *out, enqueued on `stream`.
+hipError_t ws_wait_flag(int *out, bool clear, hipStream_t stream);
+hipError_t kda_wait_flag(int *out, bool clear, hipStream_t stream);
 
 }  // namespace gdr

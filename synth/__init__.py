@@ -33,7 +33,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "generate", "widen",
-           "f64_to_bf16_bits", "bf16_bits_to_f64", "HEADLINE"]
+           "f64_to_bf16_bits", "bf16_bits_to_f64", "HEADLINE", "CONFIGS", "GDN"]
 
 
 @dataclass(frozen=True)
@@ -140,8 +140,16 @@ _reg(Workload(
     description="scalar-gated linear attention (Mamba-2; RetNet with a constant gate) on the "
                 "headline prefill's shapes"))
 
-# The prefill workload the throughput figure is quoted on.
-HEADLINE = "gdn_prefill_b4_t4096_h16_d128"
+# The five configurations of the pages' workloads, in order.
+CONFIGS = ("gdr_fp32_t256_h1_d64", "gdn_prefill_b4_t4096_h16_d128",
+           "ragged_gqa_prefill_n8_hk16_hv32_d128", "decode_n256_hk16_hv32_d128",
+           "kda_prefill_t131072_h32_d128")
+# The workload the throughput figure is quoted on: the largest configuration
+# (7.5 GB of algorithmic traffic per call).
+HEADLINE = "kda_prefill_t131072_h32_d128"
+# The Gated DeltaNet prefill on which the gradient, product and linear-mode
+# legs are measured.
+GDN = "gdn_prefill_b4_t4096_h16_d128"
 
 
 def workload(name: str, **overrides) -> Workload:

@@ -8,10 +8,12 @@ Tolerance gate (stated once, used everywhere):
   * a bf16 pool cannot hold the reference exactly: the GPU rounds its fp32
     state and the oracle its fp64 state to bf16, and two values that straddle
     a rounding midpoint land one bf16 step apart (a step is at most 2^-7 of
-    the value). A state stored m times (m chained decode steps) carries up to
-    m such steps, and the rank-one updates between stores spread an earlier
+    the value). A state stored once (every prefill) is gated elementwise by
+    |S_gpu - S_ref| <= 2^-7 |S_ref| + 3e-3 RMS(S_ref).
+    A state stored m > 1 times (m chained decode steps) carries up to m such
+    steps, and the rank-one updates between stores spread an earlier
     difference of a large entry into the small ones, at the scale of the
-    state's typical entry. Entries are gated elementwise by
+    state's typical entry:
     |S_gpu - S_ref| <= m 2^-7 (|S_ref| + RMS(S_ref)) + 3e-3 RMS(S_ref);
   * slots that no sequence names must come back bit-identical.
 """
@@ -90,8 +92,13 @@ def check_state(s_gpu: np.ndarray, s_ref: np.ndarray, in_dtype: str, state_dtype
                 roundings: int = 1):
     if state_dtype == "bf16":
         r = rms(s_ref)
-        bound = roundings * 2.0 ** -7 * (np.abs(s_ref) + r) + 3e-3 * r
-        bad = np.abs(s_gpu - s_ref) > bound
+        if roundings <= 1:
+            bound = 2.0 ** -7 * np.abs(s_ref) + 3e-3 * r
+        else:
+            bound = roundings * 2.0 ** -7 * (np.abs(s_ref) + r) + 3e-3 * r
+        diff = np.abs(s_gpu - s_ref)
+        bad = diff > bound
         assert not bad.any(), f"state: {bad.sum()} entries outside the bf16 gate"
-        return
-    check_out(s_gpu, s_ref, in_dtype, what="state")
+        return float(np.max(diff / bound)) if diff.size else 0.0
+    err, bound = check_out(s_gpu, s_ref, in_dtype, what="state")
+    return err / bound if bound else 0.0

@@ -2,6 +2,8 @@
 benchmark times. The GPU computes every sequence and head; the fp64 oracle
 recomputes a sample of (sequence, head) chains end to end and those outputs
 and final states are compared under the same gate as the small tests."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -49,9 +51,9 @@ def check_sampled(w, x, o, pool_gpu, heads):
     og = host(o[:, torch.as_tensor(heads, device=o.device)], "f32")
     err, bound = check_out(og, o_ref, w.in_dtype)
     pg = host(pool_gpu, w.state_dtype)[:, heads]
-    for s in x["slot_idx"]:
-        check_state(pg[s], pool_ref[s], w.in_dtype, w.state_dtype)
-    print(f"{w.name}: heads {list(heads)} max|err| {err:.3e} <= {bound:.3e}", flush=True)
+    smargin = max(check_state(pg[s], pool_ref[s], w.in_dtype, w.state_dtype) for s in x["slot_idx"])
+    print(f"MARGIN {w.name}: heads {list(heads)} o max|err| {err:.3e} <= {bound:.3e} "
+          f"(err/bound {err / bound:.3f}); state max err/bound {smargin:.3f}", flush=True)
 
 
 def test_gdr_fp32_t256_d64_all_outputs():
@@ -89,40 +91,75 @@ def test_ragged_gqa_prefill_bf16_pool():
     check_sampled(w, x, o, d["pool"], [0, 1, 30, 31])
 
 
-def test_decode_n256_steps():
-    """The full batch for 4 steps against the oracle on every sequence and
-    head, then 60 more steps with a 16-sequence sample followed end to end."""
+def test_decode_n256_1000_steps():
+    """The decode workload as bench.py times it: 1000 consecutive steps over the
+    256-sequence fp32 pool, step s feeding token set s mod 64 (64 distinct
+    sets of one new token per sequence). The full batch is checked against the
+    oracle at each of the first 8 steps (every output) and after step 8 (every
+    slot); a 16-sequence subset is followed for all 1000 steps (its outputs at
+    every step and its final states), the oracle running each of its
+    sequences as one 1000-token recurrence."""
     gdr = _gdr()
     w = synth.workload("decode_n256_hk16_hv32_d128")
-    steps_full, steps_more = 4, 60
-    ws = w.replace(steps=steps_full + steps_more)
+    distinct, steps, full = 64, 1000, 8
+    ws = w.replace(steps=distinct)
     x = synth.generate(ws)
     d = to_device(ws, x)
     xw = widened(ws, x)
     N = w.N
-    pool_ref = xw["pool"]
     sample = np.arange(0, N, 16)
-    sub_slots = x["slot_idx"][sample]
-    print(f"launch {w.name}", flush=True)
-    for s in range(steps_full + steps_more):
-        sl = slice(s * N, (s + 1) * N)
+    samp_t = torch.as_tensor(sample, device="cuda")
+    outs_full = []
+    outs_sample = torch.empty((steps, len(sample), w.HV, w.DV), dtype=torch.float32, device="cuda")
+    pool_full = None
+    print(f"launch {w.name}: {steps} steps", flush=True)
+    for s in range(steps):
+        sl = slice((s % distinct) * N, (s % distinct + 1) * N)
         o = gdr.recurrent_step(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["beta"][sl],
                                d["pool"], d["slot_idx"])
-        torch.cuda.synchronize()
-        if s < steps_full:
-            o_ref, pool_ref = oracle.recurrent_fp64(
-                xw["q"][sl], xw["k"][sl], xw["v"][sl], xw["g"][sl], xw["beta"][sl], pool_ref,
-                x["slot_idx"], np.arange(N + 1), scale=w.DK ** -0.5)
-            check_out(host(o, "f32"), o_ref, "bf16")
-        else:
-            idx = s * N + sample
-            o_ref, pool_ref = oracle.recurrent_fp64(
-                xw["q"][idx], xw["k"][idx], xw["v"][idx], xw["g"][idx], xw["beta"][idx],
-                pool_ref, sub_slots, np.arange(len(sample) + 1), scale=w.DK ** -0.5)
-            check_out(host(o[torch.as_tensor(sample, device=o.device)], "f32"), o_ref, "bf16")
-    pool = host(d["pool"], "f32")
-    for s in sub_slots:
-        check_state(pool[s], pool_ref[s], "bf16", "f32")
+        outs_sample[s] = o[samp_t]
+        if s < full:
+            outs_full.append(o.clone())
+        if s == full - 1:
+            pool_full = d["pool"].clone()
+    torch.cuda.synchronize()
+
+    # Oracle runs split by sequence (each sequence's recurrence is separate)
+    # over host threads; sequence n's state sits at local slot n.
+    slots = x["slot_idx"]
+    groups = np.array_split(np.arange(N), 16)
+
+    def run_group(rows_of, grp, pool_grp, T):
+        rows = np.concatenate([rows_of(n) for n in grp])
+        return oracle.recurrent_fp64(
+            xw["q"][rows], xw["k"][rows], xw["v"][rows], xw["g"][rows], xw["beta"][rows], pool_grp,
+            np.arange(len(grp)), np.arange(len(grp) + 1) * T, scale=w.DK ** -0.5)
+
+    # full batch, steps 1..8 (the pool holds fp32 after every step)
+    pool_ref = xw["pool"][slots]
+    worst = 0.0
+    with ThreadPoolExecutor(16) as ex:
+        for s in range(full):
+            res = list(ex.map(lambda grp: run_group(lambda n: [s * N + n], grp, pool_ref[grp], 1), groups))
+            o_ref = np.concatenate([r[0] for r in res])
+            pool_ref = np.concatenate([r[1] for r in res])
+            err, bound = check_out(host(outs_full[s], "f32"), o_ref, "bf16")
+            worst = max(worst, err / bound)
+        smargin = check_state(host(pool_full, "f32")[slots], pool_ref, "bf16", "f32")
+        print(f"MARGIN {w.name} full batch steps 1-{full}: o max err/bound {worst:.3f}; "
+              f"state (all {N} slots) err/bound {smargin:.3f}", flush=True)
+
+        # the subset for all 1000 steps: sequence n sees token (s mod 64) * N + n
+        # at step s, so each is one 1000-token recurrence
+        pool0 = xw["pool"][slots]
+        res = list(ex.map(lambda n: run_group(lambda m: (np.arange(steps) % distinct) * N + m, [n],
+                                              pool0[[n]], steps), sample))
+    o_ref = np.stack([r[0] for r in res], axis=1)           # [steps, 16, HV, DV]
+    pool_sub = np.concatenate([r[1] for r in res])
+    err, bound = check_out(host(outs_sample, "f32"), o_ref, "bf16")
+    smargin = check_state(host(d["pool"], "f32")[slots[sample]], pool_sub, "bf16", "f32")
+    print(f"MARGIN {w.name} {len(sample)} sequences x {steps} steps: o max|err| {err:.3e} <= {bound:.3e} "
+          f"(err/bound {err / bound:.3f}); final state err/bound {smargin:.3f}", flush=True)
 
 
 def test_kda_prefill_t131072_h32():
