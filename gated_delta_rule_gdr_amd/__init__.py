@@ -24,7 +24,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd",
            "verify_ring", "state_fold", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
@@ -94,6 +94,8 @@ def load() -> ctypes.CDLL:
     L.gdr_chunk_fwd.restype = ctypes.c_int
     L.gdr_chunk_fwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]
+    L.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+    L.gdr_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
     L.gdr_recurrent_step.restype = ctypes.c_int
     L.gdr_recurrent_step.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
     L.gdr_recurrent_fwd.restype = ctypes.c_int
@@ -248,6 +250,19 @@ def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk
     else:
         wptr, wbytes = None, 0
     _check(L.gdr_chunk_fwd(ctypes.byref(a), wptr, wbytes, _stream(q)))
+    return o
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk_size=64,
+                      rule="delta", gate=None, out_dtype=None, zero_init=False, o=None,
+                      debug_checks=False, products=1):
+    """chunk_fwd through gdr_chunk_fwd_noalloc: the library's static device
+    scratch instead of a workspace (pass ``o`` to allocate nothing at all)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    a, o = _prepare(q, k, v, g, beta, pool, slot_idx, cu_seqlens, o, scale, rule, gate,
+                    zero_init, debug_checks, chunk_size, out_dtype, products)
+    _check(load().gdr_chunk_fwd_noalloc(ctypes.byref(a), _stream(q)))
     return o
 
 

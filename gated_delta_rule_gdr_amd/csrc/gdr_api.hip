@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gdr_internal.h"
 #include "recurrent_bwd.h"
@@ -318,6 +319,66 @@ GDR_EXPORT gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t w
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
   if (a->flags & GDR_FLAG_DEBUG_CHECKS) return finish_debug_checks(stream);
   return GDR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// gdr_chunk_fwd_noalloc: the prefill with the library's own device scratch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Scratch of the allocation-free prefill: one array per device, held until
+// the process ends. In host code `scratch` names a host-side stand-in, never
+// the device memory; its device address comes from hipGetSymbolAddress, once
+// per device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of `scratch` on device `dev` (made current for the lookup,
+// the previous current device restored afterwards).
+hipError_t scratch_address(int dev, void **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+GDR_EXPORT gdr_status gdr_chunk_fwd_noalloc(const gdr_args *a, hipStream_t stream) {
+  gdr_status s = validate(a, Call::Chunk);
+  if (s != GDR_OK) return s;
+  if (!uses_workspace(a)) return gdr_chunk_fwd(a, nullptr, 0, stream);
+  const size_t need = chunk_fwd_kda_min_workspace(*a);
+  if (need > (size_t)GDR_NOALLOC_SCRATCH_BYTES)
+    return fail(GDR_E_WORKSPACE, "this call needs at least %zu bytes of scratch, more than the %zu of "
+                "gdr_chunk_fwd_noalloc (N * HV * DK * DV * 4 bytes of state carry plus one chunk's "
+                "records for every value head); pass a workspace to gdr_chunk_fwd instead",
+                need, (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  void *ptr = nullptr;
+  if (e == hipSuccess) e = scratch_address(dev, &ptr);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "scratch of gdr_chunk_fwd_noalloc: %s", hipGetErrorString(e));
+  return gdr_chunk_fwd(a, ptr, (size_t)GDR_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) {

@@ -167,6 +167,20 @@ size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a);
 gdr_status gdr_chunk_fwd(const gdr_args *a, void *workspace, size_t ws_bytes,
                          hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call, arguments and results as gdr_chunk_fwd, with the library's own
+ * static device scratch of GDR_NOALLOC_SCRATCH_BYTES in place of a caller
+ * workspace. Calls that need no workspace run exactly as gdr_chunk_fwd. A
+ * call whose minimum workspace (see gdr_chunk_fwd_workspace_bytes) exceeds
+ * the scratch returns GDR_E_WORKSPACE before enqueuing anything. Allocates
+ * nothing: the scratch is a file-scope device array, one per device, held
+ * until the process ends, and every call on a device shares it, so calls
+ * that overlap in time on one device race (serialise them, e.g. on one
+ * stream). Its contents are never read before a call writes them. */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_args *a, hipStream_t stream);
+
 /* One recurrent step: token n of q/k/v/g/beta belongs to sequence n
  * (T_total == N); reads and writes pool slot slot_idx[n] in place. */
 gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
