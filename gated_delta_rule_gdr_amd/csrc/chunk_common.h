@@ -245,6 +245,18 @@ __device__ __forceinline__ float lane_value(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
+// Sum over the four 16-lane rows of the wave (the same lane of each), with
+// gfx950's lane swaps: permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second, permlane32_swap the upper
+// half of the first with the lower half of the second; with x in both, every
+// lane receives its partner's x beside its own.
+__device__ __forceinline__ float sum_lane_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive scan across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_scan(float x) {
   const int lane = threadIdx.x & 63;

@@ -37,10 +37,12 @@
 // Scalar gate: the decay factors exp(G_i - G_j) are applied to the fp32 Gram
 // entries after the MFMA, and exp(G_i), exp(G_last - G_j) to rows of fp32
 // results, so no range restriction applies. Channel gate: decay sits inside
-// the key contraction, so the Gram operands are e^{G} (.) q, e^{G} (.) k and
-// e^{-G} (.) k with the chunk start as reference; this needs the in-chunk
-// decay of every channel to stay inside the fp32 exponent range
-// (|G_last - G_first| < ~80 per chunk and channel).
+// the key contraction. The Gram entries are summed pair by pair over the
+// channels with the factor e^{G_i - G_j} (j <= i) of each channel, the
+// token-parallel form of the diagonal interaction blocks on the KDA page
+// (section 6); the state products use e^{G} (.) q, e^{G} (.) k and the keys
+// decayed to the chunk's end, e^{G_last - G} (.) k. Every exponent is <= 0,
+// so no gate, however strong, can overflow a factor.
 //
 // MFMA fragment convention (v_mfma_f32_16x16x32_bf16, wave64, lane l,
 // r = l % 16, g = l / 16): an A fragment holds A[r][k] and a B fragment
@@ -78,9 +80,10 @@ struct Smem {
   static constexpr int PV = BV + (IN_F32 ? 4 : 8);
   static constexpr int PB = C + 8;                 // bf16 C x C planes
   Op kk[C][PK];   // keys (channel: e^{G} k) - A operand of X, rows of R
-  Op qq[C][PK];   // queries (channel: e^{G} q)
-  // Transposed keys for the state update (channel: e^{-G} k). For the channel
-  // gate the same storage first holds e^{-G} k token-major for the Grams.
+  Op qq[C][PK];   // queries (channel: e^{G} q; first the raw queries)
+  // Transposed keys for the state update (channel: the keys decayed to the
+  // chunk's end, e^{G_last - G} k). For the channel gate the same storage
+  // first holds the raw keys token-major for the Gram entries.
   union {
     Op kt[D][PT];
     Op kinv[C][PK];
@@ -257,20 +260,7 @@ __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g
     for (int rb = 0; rb < NRB; ++rb) acc[rb][J] = f32x4{0.f, 0.f, 0.f, 0.f};
     Frag fm[NS];   // keys of block J (M operand)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (GATE == GDR_GATE_CHANNEL && !DELTA) {
-        // e^{-G} k is only held transposed for the linear rule
-        float x[8];
-        const int tok = perm32(16 * J + r);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sm.kt[32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4)][tok];
-        split8(x, fm[s]);
-      } else if constexpr (GATE == GDR_GATE_CHANNEL) {
-        ldfrag(&sm.kinv[0][0], SM::PK, 16 * J + r, 32 * s, g, fm[s]);
-      } else {
-        ldfrag(&sm.kk[0][0], SM::PK, 16 * J + r, 32 * s, g, fm[s]);
-      }
-    }
+    for (int s = 0; s < NS; ++s) ldfrag(&sm.kk[0][0], SM::PK, 16 * J + r, 32 * s, g, fm[s]);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int I = rb ? IB : IA;
@@ -455,8 +445,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     } else {
-      // channel gate: stage g, prefix-sum each key channel over the chunk,
-      // then form e^{G} k, e^{G} q and e^{-G} k.
+      // channel gate: stage g, prefix-sum each key channel over the chunk;
+      // the Gram entries exactly, token pair by token pair; then e^{G} k,
+      // e^{G} q and the keys decayed to the chunk's end.
       for (int it = tid; it < C * (BV / 8); it += 256) {
         const int row = it / (BV / 8), c8 = 8 * (it % (BV / 8));
         copy8<IN_F32>(p.v, (t0 + row) * p.v_stride + (int64_t)h * D + vb * BV + c8, row < L,
@@ -469,6 +460,18 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         if (row < L && map.sub(row) == 0)
           x = *reinterpret_cast<const float4 *>(p.g + ((map.r0 + map.tok(row)) * p.HV + h) * (int64_t)D + c4);
         *reinterpret_cast<float4 *>(&sm.gstage[row][c4]) = x;
+      }
+      // raw keys (in kinv) and queries (in qq) for the Gram entries
+      for (int it = tid; it < C * (D / 8); it += 256) {
+        const int row = it / (D / 8), c8 = 8 * (it % (D / 8));
+        const bool ok = row < L;
+        float kx[8], qx[8];
+        load8<IN_F32>(p.k, (t0 + row) * p.k_stride + (int64_t)hk * D + c8, ok, kx);
+        load8<IN_F32>(p.q, (map.r0 + map.tok(row)) * p.q_stride + (int64_t)hk * D + c8, ok, qx);
+        *reinterpret_cast<float4 *>(&sm.kinv[row][perm32(c8)]) = make_float4(kx[0], kx[1], kx[2], kx[3]);
+        *reinterpret_cast<float4 *>(&sm.kinv[row][perm32(c8 + 4)]) = make_float4(kx[4], kx[5], kx[6], kx[7]);
+        *reinterpret_cast<float4 *>(&sm.qq[row][perm32(c8)]) = make_float4(qx[0], qx[1], qx[2], qx[3]);
+        *reinterpret_cast<float4 *>(&sm.qq[row][perm32(c8 + 4)]) = make_float4(qx[4], qx[5], qx[6], qx[7]);
       }
       if (w == 0) {
         sm.G[lane] = 0.f;   // decay sits inside the channel-gate operands
@@ -486,48 +489,83 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         sm.eGlastc[tid] = __expf(acc);
       }
       __syncthreads();
-      for (int it = tid; it < C * (D / 8); it += 256) {
-        const int row = it / (D / 8), c8 = 8 * (it % (D / 8));
-        const bool ok = row < L;
-        float kx[8], qx[8];
-        load8<IN_F32>(p.k, (t0 + row) * p.k_stride + (int64_t)hk * D + c8, ok, kx);
-        load8<IN_F32>(p.q, (map.r0 + map.tok(row)) * p.q_stride + (int64_t)hk * D + c8, ok, qx);
+
+      // Gram entries of row i = tid / 4 against the 16 keys of column block
+      // tid % 4 (lower blocks only): sum_c k_ic k_jc e^{G_ic - G_jc} and
+      // sum_c q_ic k_jc e^{G_ic - G_jc} for j <= i, each exponent <= 0, so
+      // no decay factor can overflow whatever the gate.
+      const int gi = tid >> 2, gjb = tid & 3;
+      float racc[16], aacc[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float Gv = sm.gstage[row][c8 + j];
-          const float e = __expf(Gv), ei = __expf(-Gv);
-          const int pc = perm32(c8 + j);
-          sm.kk[row][pc] = kx[j] * e;
-          sm.qq[row][pc] = qx[j] * e;
-          if constexpr (DELTA) sm.kinv[row][pc] = kx[j] * ei;
-          else sm.kt[c8 + j][perm32(row)] = kx[j] * ei;   // linear rule: no Gram needs kinv
+      for (int jj = 0; jj < 16; ++jj) racc[jj] = aacc[jj] = 0.f;
+      if (16 * gjb <= gi) {
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+          const float4 Gi = *reinterpret_cast<const float4 *>(&sm.gstage[gi][4 * c4]);
+          const float4 ki = *reinterpret_cast<const float4 *>(&sm.kinv[gi][perm32(4 * c4)]);
+          const float4 qi = *reinterpret_cast<const float4 *>(&sm.qq[gi][perm32(4 * c4)]);
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int j = 16 * gjb + jj;
+            if (j <= gi) {
+              const float4 Gj = *reinterpret_cast<const float4 *>(&sm.gstage[j][4 * c4]);
+              const float4 kj = *reinterpret_cast<const float4 *>(&sm.kinv[j][perm32(4 * c4)]);
+              const float e0 = __expf(Gi.x - Gj.x), e1 = __expf(Gi.y - Gj.y);
+              const float e2 = __expf(Gi.z - Gj.z), e3 = __expf(Gi.w - Gj.w);
+              const float t0_ = kj.x * e0, t1_ = kj.y * e1, t2_ = kj.z * e2, t3_ = kj.w * e3;
+              if constexpr (DELTA) racc[jj] += ((ki.x * t0_ + ki.y * t1_) + (ki.z * t2_ + ki.w * t3_));
+              aacc[jj] += ((qi.x * t0_ + qi.y * t1_) + (qi.z * t2_ + qi.w * t3_));
+            }
+          }
+        }
+      }
+
+      // the decayed operands, each thread its own elements: e^{G} k and
+      // e^{G} q in place, the keys decayed to the chunk's end kept for the
+      // transposed store below
+      constexpr int NE = C * D / 256;
+      float kend[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int idx = tid + 256 * e, row = idx / D, c = idx % D, pc = perm32(c);
+        const float Gv = sm.gstage[row][c], Gl = sm.gstage[C - 1][c];
+        const float kr = sm.kinv[row][pc], qr = sm.qq[row][pc];
+        const float eg = __expf(Gv);
+        sm.kk[row][pc] = kr * eg;
+        sm.qq[row][pc] = qr * eg;
+        kend[e] = kr * __expf(Gl - Gv);
+      }
+      __syncthreads();   // raw keys (kinv) and G (gstage) are dead from here on
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int idx = tid + 256 * e;
+        sm.kt[idx % D][perm32(idx / D)] = kend[e];
+      }
+      // Gram entries into the split planes (R's diagonal blocks in fp32)
+      if (16 * gjb <= gi) {
+        const int I = gi >> 4, r_ = gi & 15;
+        const float bi = sm.beta[gi];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int j = 16 * gjb + jj;
+          const float av = j <= gi ? p.scale * aacc[jj] : 0.f;
+          store_split(&sm.aqh[0][0], &sm.aql[0][0], gi * SM::PB + j, av);
+          if constexpr (DELTA) {
+            const float rv = j < gi ? bi * racc[jj] : 0.f;
+            if (gjb == I) sm.rd[I][r_][jj] = rv;
+            else store_split(&sm.rth[0][0], &sm.rtl[0][0], gi * SM::PB + j, rv);
+          }
         }
       }
       __syncthreads();
     }
 
-    // ================= phase 1: Gram matrices =================
-    switch (w) {
-      case 0: grams<0, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
-      case 1: grams<1, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
-      case 2: grams<2, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
-      default: grams<3, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
-    }
-
-    if constexpr (GATE == GDR_GATE_CHANNEL && DELTA) {
-      // e^{-G} k: token-major (Gram operand) -> key-major (update operand)
-      __syncthreads();
-      float tmp[C * D / 256];
-#pragma unroll
-      for (int e = 0; e < C * D / 256; ++e) {
-        const int idx = tid + 256 * e;
-        tmp[e] = sm.kinv[idx / D][perm32(idx % D)];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < C * D / 256; ++e) {
-        const int idx = tid + 256 * e;
-        sm.kt[idx % D][perm32(idx / D)] = tmp[e];
+    // ================= phase 1: Gram matrices (no or scalar gate) =================
+    if constexpr (GATE != GDR_GATE_CHANNEL) {
+      switch (w) {
+        case 0: grams<0, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+        case 1: grams<1, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+        case 2: grams<2, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
+        default: grams<3, IN_F32, GATE, DELTA, D>(sm, p, r, g); break;
       }
     }
 
@@ -721,15 +759,16 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       constexpr bool USPLIT = DELTA || IN_F32 || GATE == GDR_GATE_SCALAR;
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
+        if constexpr (GATE == GDR_GATE_CHANNEL) {
+          // S^T <- e^{G_last} (.) S^T + K_end^T Vb (key rows decay first)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[m][i] *= sm.eGlastc[16 * m + 4 * g + i];
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           Frag fa;
           ldfrag(&sm.kt[0][0], SM::PT, 16 * m + r, 32 * s, g, fa);
           st[m] = mm<OPF32, USPLIT>(fa, uf[s], st[m]);
-        }
-        if constexpr (GATE == GDR_GATE_CHANNEL) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st[m][i] *= sm.eGlastc[16 * m + 4 * g + i];
         }
       }
     }

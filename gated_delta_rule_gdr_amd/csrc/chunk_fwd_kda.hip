@@ -6,32 +6,42 @@
 // tokens with incoming state S (value-by-key) and the inclusive in-chunk
 // cumulative log-decay G_i in R^{d_k} (one value per key channel),
 //
-//   K_l = e^{G} (.) K,   K_r = e^{-G} (.) K,   Q^ = s e^{G} (.) Q     (rows i)
-//   R   = strict-lower( beta_i K_l K_r^T ),  T = (I + R)^{-1},  T' = T Diag(beta)
-//   A^  = lower( Q^ K_r^T )
-//   W   = T' K_l,  U = T' V
+//   K_l = e^{G} (.) K,   Q^ = s e^{G} (.) Q,   K_end = e^{G_last - G} (.) K
+//   R   = strict-lower( beta_i sum_c k_ic k_jc e^{G_ic - G_jc} )
+//   A^  = lower( s sum_c q_ic k_jc e^{G_ic - G_jc} )
+//   T   = (I + R)^{-1},  T' = T Diag(beta),  W = T' K_l,  U = T' V
 //   Vb  = U - W S^T                         (the solved errors e_i)
 //   O   = Q^ S^T + A^ Vb
-//   S^T <- gamma (.) (S^T + K_r^T Vb),      gamma = e^{G_last}   (per key row)
+//   S^T <- gamma (.) S^T + K_end^T Vb,      gamma = e^{G_last}   (per key row)
 //
 // Vb equals T (beta (V - K_l S^T)) of the chunk equations; forming W and U
 // ahead of time leaves two products on the serial chain from one chunk's state
-// to the next (W S^T and the update). The products use the chunk start as the
-// decay reference, so the in-chunk decay of every channel must stay inside the
-// fp32 exponent range (|G_last - G_first| < ~80 per chunk and channel).
+// to the next (W S^T and the update).
+//
+// Decay references. The Gram sums are taken over 16-token blocks (the KDA
+// page's token sub-blocks of the chunked form) with the reference at a block
+// boundary, so that no factor can overflow whatever the gate: for row block I
+// and an earlier key block J the rows are q_i e^{G_i - B_I} and the keys
+// k_j e^{B_I - G_j}, B_I being G just before block I, both factors <= 1; the
+// diagonal block I uses the keys k_j e^{B_I - G_j} >= 1 when the block's
+// strongest channel decay is at most 80 (factors <= e^{80}), and is summed
+// pair by pair in fp32 otherwise (prep_exact_diagonal). K_l, Q^, K_end and
+// gamma carry exponentials of non-positive numbers only.
 //
 // Two kernels per slice of chunks:
-//   * kda_prep_kernel, one workgroup per (chunk, value head), fully parallel:
-//     gate prefix sums, the decayed operands, the Gram matrices R and A^, the
-//     inverse T and the products W; it writes one record per (chunk, head) to
-//     the workspace with every operand the state kernel multiplies, already
-//     split into bf16 hi / lo planes and laid out as MFMA fragments;
-//   * kda_state_kernel, one workgroup per (sequence, value head, 64 value
-//     columns): four state waves (16 columns each, S^T[DK, 16] in MFMA
-//     accumulators) walk the slice's chunks in order; four loader waves copy
-//     the next chunk's record (and values) from the workspace into registers
-//     while the current one is used, and into LDS region by region as the
-//     state waves release it (LDS counters, no workgroup barrier).
+//   * kda_prep_kernel, persistent workgroups over the (chunk, value head)
+//     items, fully parallel: gate prefix sums, the decayed operands, the Gram
+//     matrices R and A^, the inverse T and the products W; it writes one
+//     record per (chunk, head) to the workspace with every operand the state
+//     kernel multiplies, already split into bf16 hi / lo planes and laid out
+//     as MFMA fragments;
+//   * kda_state_kernel, one workgroup per (sequence, value head, 16 value
+//     columns): a chain wave (S^T[DK, 16] in MFMA accumulators: Vb and the
+//     update) walks the slice's chunks in order, an output wave follows one
+//     chunk behind, and six loader waves copy the next chunks' records (and
+//     values) from the workspace into registers and into LDS region by region
+//     as the computing waves release them (LDS counters, no workgroup
+//     barrier).
 // A sequence's state crosses slice boundaries through an fp32 carry area of
 // the workspace. The workspace is sized by the caller: a larger one means
 // fewer, longer slices.
@@ -55,11 +65,11 @@ using namespace chunk;
 
 // Layout of one (chunk, value head) record, in bytes. Region 1 holds what the
 // first products of a chunk read (W, T'), region 2 the output operands (Q^,
-// A^), region 3 the update operands (K_r^T, gamma).
+// A^), region 3 the update operands (K_end^T, gamma).
 //   W(I, s):  lane (r, g) holds -W[16I + r][32s + k(j)]          (I < 4, s < DK/32)
 //   T'(p):    T'[16I + r][32s + k(j)] for the six (I, s) with s <= I/2
 //   Q^(I, s): as W;  A^(p): as T'
-//   K(m, s):  K_r[32s + k(j)][16m + r]                            (m < DK/16, s < 2)
+//   K(m, s):  K_end[32s + k(j)][16m + r]                          (m < DK/16, s < 2)
 //   gamma:    DK fp32 values
 template <int D>
 struct KdaRec {
@@ -138,15 +148,18 @@ __device__ __forceinline__ int slot_k(int g, int j) { return (j < 4 ? 4 * g + j 
 template <int D>
 struct PrepSmem {
   static constexpr int PK = D + 4;   // fp32 rows, key columns permuted (perm32)
-  float kl[C][PK];                   // K_l, token-major
+  float kl[C][PK];                   // K_l = e^{G} (.) K, token-major
   union {
-    float kr[C][PK];                 // K_r, token-major (dead once the Grams and K^T are out)
+    float kd[C][PK];                 // keys decayed to the end of their own 16-token block
     struct {
-      float tt[C][C + 4];            // T, row-major
+      float tt[C][C + 4];            // T, row-major (once the Grams are done)
       float rd[4][16][20];           // R's diagonal blocks, negated
     } t;
   };
-  float tot[4][D];                   // per 16-token block: gate sum of each channel
+  float tot[4][D];                   // per 16-token block: gate sum of each channel (<= 0)
+  float etot[4][D];                  // its exponential: the block's decay of each channel
+  float fend[4][D];                  // decay of the blocks after block b (keys to the chunk's end)
+  float dmid[3][D];                  // decay of the blocks strictly between J and w: (2,0), (3,1), (3,0)
   float beta[C];
 };
 
@@ -246,6 +259,82 @@ __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, con
   in.beta = DELTA ? p.beta[t * p.HV + it.h] : 0.f;
 }
 
+// The diagonal 16x16 block of the Gram matrices of row block w, summed pair
+// by pair (the token-parallel form of the diagonal interaction blocks on the
+// KDA page, section 6), for a block whose channel decay is too strong for
+// the factored form: lane (r, g) reloads its token's inputs, sums over its
+// own channels k_i k_j e^{G_i - G_j} and q_i k_j e^{G_i - G_j} for every row
+// j of the block (row j's key and gate fetched from lane (j, g)), and the
+// four channel groups are then summed. Every exponent is <= 0 for j <= i.
+template <int D, bool DELTA>
+__device__ __forceinline__ void prep_exact_diagonal(const KdaParams &p, const PrepItem &it, int w, int r, int g,
+                                                    float bi, f32x4 (&rv)[4], f32x4 (&av)[4]) {
+  constexpr int NS = D / 32;
+  PrepIn<D> in;
+  prep_load<D, DELTA>(in, p, it, w, r, g);
+  const bool ok = 16 * w + r < it.L;
+  float gv[NS][8], kv[NS][8], qv[NS][8];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int u = 2 * s + hf;
+      const uint32_t kw[2] = {in.k[2 * u], in.k[2 * u + 1]}, qw[2] = {in.q[2 * u], in.q[2 * u + 1]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gv[s][4 * hf + j] = ok ? __uint_as_float(in.g[4 * u + j]) : 0.f;
+        kv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1])) : 0.f;
+        qv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1])) : 0.f;
+      }
+    }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = gv[s][j];
+      x = dpp_add<0x111, 0xf>(x);
+      x = dpp_add<0x112, 0xf>(x);
+      x = dpp_add<0x114, 0xf>(x);
+      x = dpp_add<0x118, 0xf>(x);
+      gv[s][j] = x;
+    }
+  f32x4 rr = {0.f, 0.f, 0.f, 0.f}, ra = rr;
+  for (int jj = 0; jj < 16; ++jj) {
+    const int src = 16 * g + jj;
+    float sr = 0.f, sa = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float kj = __shfl(kv[s][j], src, 64), gj = __shfl(gv[s][j], src, 64);
+        const float t = kj * __expf(fminf(gv[s][j] - gj, 0.f));   // (pairs j > i are masked below)
+        if constexpr (DELTA) sr += kv[s][j] * t;
+        sa += qv[s][j] * t;
+      }
+    if constexpr (DELTA) sr = sum_lane_rows(sr);
+    sa = sum_lane_rows(sa);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (jj == 4 * g + e) {
+        rr[e] = sr;
+        ra[e] = sa;
+      }
+  }
+  f32x4 dr, da;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int jj = 4 * g + e;
+    dr[e] = jj < r ? bi * rr[e] : 0.f;
+    da[e] = jj <= r ? p.scale * ra[e] : 0.f;
+  }
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+    if (J == w) {
+      rv[J] = dr;
+      av[J] = da;
+    }
+}
+
 // Persistent: each workgroup takes items blockIdx.x, blockIdx.x + gridDim.x, ...
 // and loads the next item's inputs while it works on the current one.
 // DELTA false (the linear rule, GLA's channel-gated linear attention): no
@@ -284,18 +373,23 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
         }
       }
     if (g == 0) sm.beta[i] = ok ? in.beta : 0.f;
-    if (item + gridDim.x < items) {
-      nx = prep_item(p, item + gridDim.x);
-      prep_load<D, DELTA>(in, p, nx, w, r, g);
-    }
+    // the next item's inputs are loaded once this item's operands are formed
+    // (below), so that their registers are free meanwhile
+    auto prefetch = [&]() {
+      if (item + gridDim.x < items) {
+        nx = prep_item(p, item + gridDim.x);
+        prep_load<D, DELTA>(in, p, nx, w, r, g);
+      }
+    };
+    if (!it.valid) prefetch();
     if (it.valid) {
       const int h = it.h;
       const int L = it.L;
       char *rec = p.rec + item * (int64_t)RC::BYTES;
       (void)L;
 
-  // ---- gate prefix sums: within the 16-token block (DPP row scan over r),
-  //      then the totals of the earlier blocks ----
+  // ---- gate prefix sums within the 16-token block (DPP row scan over r):
+  //      gv becomes the log-decay from the start of the lane's block ----
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -311,71 +405,128 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        *reinterpret_cast<float4 *>(&sm.tot[w][32 * s + 16 * hf + 4 * g]) =
-            make_float4(gv[s][4 * hf], gv[s][4 * hf + 1], gv[s][4 * hf + 2], gv[s][4 * hf + 3]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = 32 * s + 16 * hf + 4 * g;
+        const float *x = &gv[s][4 * hf];
+        *reinterpret_cast<float4 *>(&sm.tot[w][c0]) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4 *>(&sm.etot[w][c0]) =
+            make_float4(__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3]));
+      }
   }
   __syncthreads();
   if (tid < D) {
     const float Gl = ((sm.tot[0][tid] + sm.tot[1][tid]) + sm.tot[2][tid]) + sm.tot[3][tid];
     reinterpret_cast<float *>(rec + RC::GAM)[tid] = __expf(Gl);
+    const float e1 = sm.etot[1][tid], e2 = sm.etot[2][tid], e3 = sm.etot[3][tid];
+    sm.fend[0][tid] = e1 * (e2 * e3);
+    sm.fend[1][tid] = e2 * e3;
+    sm.fend[2][tid] = e3;
+    sm.fend[3][tid] = 1.f;
+    sm.dmid[0][tid] = e1;
+    sm.dmid[1][tid] = e2;
+    sm.dmid[2][tid] = e1 * e2;
   }
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float4 pre = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int w2 = 0; w2 < w; ++w2) {
-        const float4 x = *reinterpret_cast<const float4 *>(&sm.tot[w2][32 * s + 16 * hf + 4 * g]);
-        pre.x += x.x; pre.y += x.y; pre.z += x.z; pre.w += x.w;
-      }
-      gv[s][4 * hf] += pre.x;
-      gv[s][4 * hf + 1] += pre.y;
-      gv[s][4 * hf + 2] += pre.z;
-      gv[s][4 * hf + 3] += pre.w;
-    }
 
-  // ---- decayed operands: K_l, K_r into LDS; this block's K_l and Q^ stay
-  //      in registers as row fragments (Q^ is also its record fragment) ----
-  Frag klf[NS], qf[NS];
+  // ---- operands of this lane's token i (G_i = B_w + gv, B_w the log-decay
+  //      before block w): every factor below but the diagonal-block one is
+  //      an exponential of a non-positive number ----
+  //   nk, nq  the Gram rows, decayed from the start of block w: k e^{gv},
+  //           s q e^{gv}
+  //   md      the diagonal block's key operand, k e^{-gv} (<= e^{span}),
+  //           multiplied into the diagonal tile right away
+  //   kd      the key decayed to the end of block w, k e^{tot_w - gv} (LDS)
+  //   kl      K_l = nk e^{B_w} (LDS); Q^ = nq e^{B_w} (record)
+  // The strongest decay of any channel over block w decides the diagonal
+  // tile's form: up to 80 the factors e^{-gv} stay far inside the fp32
+  // range and the tile is the product md^T (nk, nq) (transposed, as the
+  // other tiles below); beyond, it is summed pair by pair.
+  float span = 0.f;
+  for (int c = lane; c < D; c += 64) span = fmaxf(span, -sm.tot[w][c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) span = fmaxf(span, __shfl_xor(span, off, 64));
+  const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(span)) <= __float_as_int(80.f);
+  Frag nk[NS], nq[NS];
+  f32x4 rdiag = {0.f, 0.f, 0.f, 0.f}, adiag = rdiag;
   const float sc = p.scale;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    float a[8], b[8], c8[8];
+    float a[8], b[8], c8[8], d[8], e[8], f[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e = __expf(gv[s][j]), ei = __expf(-gv[s][j]);
-      a[j] = kv[s][j] * e;
-      b[j] = kv[s][j] * ei;
-      c8[j] = (sc * qv[s][j]) * e;
+    for (int hf = 0; hf < 2; ++hf) {
+      const int c0 = 32 * s + 16 * hf + 4 * g;
+      const float4 tw = *reinterpret_cast<const float4 *>(&sm.tot[w][c0]);
+      float4 eb = make_float4(1.f, 1.f, 1.f, 1.f);   // e^{B_w}: the decay of the earlier blocks
+      for (int w2 = 0; w2 < w; ++w2) {
+        const float4 x = *reinterpret_cast<const float4 *>(&sm.etot[w2][c0]);
+        eb.x *= x.x; eb.y *= x.y; eb.z *= x.z; eb.w *= x.w;
+      }
+      const float twv[4] = {tw.x, tw.y, tw.z, tw.w}, ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * hf + jj;
+        const float G = gv[s][j];
+        const float e1 = __expf(G);
+        a[j] = kv[s][j] * e1;                        // nk
+        c8[j] = (sc * qv[s][j]) * e1;                // nq
+        b[j] = kv[s][j] * __expf(-G);                // md
+        d[j] = kv[s][j] * __expf(twv[jj] - G);       // kd
+        e[j] = a[j] * ebv[jj];                       // K_l
+        f[j] = c8[j] * ebv[jj];                      // Q^
+      }
     }
     // slot j of step s sits at physical column 32s + 8g + j (perm32)
     float *pl = &sm.kl[i][32 * s + 8 * g];
-    float *pr = &sm.kr[i][32 * s + 8 * g];
-    *reinterpret_cast<float4 *>(pl) = make_float4(a[0], a[1], a[2], a[3]);
-    *reinterpret_cast<float4 *>(pl + 4) = make_float4(a[4], a[5], a[6], a[7]);
-    *reinterpret_cast<float4 *>(pr) = make_float4(b[0], b[1], b[2], b[3]);
-    *reinterpret_cast<float4 *>(pr + 4) = make_float4(b[4], b[5], b[6], b[7]);
-    split8(a, klf[s]);
-    split8(c8, qf[s]);
-    st_frag(rec, RC::R2 + RC::wq(w, s), lane, qf[s]);
+    float *pd = &sm.kd[i][32 * s + 8 * g];
+    *reinterpret_cast<float4 *>(pl) = make_float4(e[0], e[1], e[2], e[3]);
+    *reinterpret_cast<float4 *>(pl + 4) = make_float4(e[4], e[5], e[6], e[7]);
+    *reinterpret_cast<float4 *>(pd) = make_float4(d[0], d[1], d[2], d[3]);
+    *reinterpret_cast<float4 *>(pd + 4) = make_float4(d[4], d[5], d[6], d[7]);
+    split8(a, nk[s]);
+    split8(c8, nq[s]);
+    if (fast) {
+      Frag md;
+      split8(b, md);
+      if constexpr (DELTA) rdiag = mm<true, true>(md, nk[s], rdiag);
+      adiag = mm<true, true>(md, nq[s], adiag);
+    }
+    Frag fq;
+    split8(f, fq);
+    st_frag(rec, RC::R2 + RC::wq(w, s), lane, fq);
   }
+  prefetch();
   __syncthreads();
 
-  // ---- Grams of row block w: tile (w, J) computed transposed (K_r of block
-  //      J as the M operand), so lane (r, g) holds row 16w + r, columns
-  //      16J + 4g .. +3 ----
+  // ---- Grams of row block w: tile (w, J) computed transposed (keys of
+  //      block J as the M operand), so lane (r, g) holds row 16w + r,
+  //      columns 16J + 4g .. +3. For J < w the keys are those of block J
+  //      decayed to the start of block w (kd times the decay of the blocks
+  //      between, <= 1 per channel); tile (w, w) is the diagonal above ----
   f32x4 rv[4], av[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     f32x4 ar = {0.f, 0.f, 0.f, 0.f}, aa = ar;
-    if (J <= w) {
+    if (J == w) {
+      ar = rdiag;
+      aa = adiag;
+    } else if (J < w) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
+        const float *src = &sm.kd[16 * J + r][32 * s + 8 * g];
+        const float4 x0 = *reinterpret_cast<const float4 *>(src);
+        const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (J + 1 < w) {
+          const float *dm = sm.dmid[w == 2 ? 0 : (J == 1 ? 1 : 2)];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const float4 y = *reinterpret_cast<const float4 *>(&dm[32 * s + 16 * hf + 4 * g]);
+            x[4 * hf] *= y.x; x[4 * hf + 1] *= y.y; x[4 * hf + 2] *= y.z; x[4 * hf + 3] *= y.w;
+          }
+        }
         Frag fk;
-        ldfrag(&sm.kr[0][0], PK, 16 * J + r, 32 * s, g, fk);
-        if constexpr (DELTA) ar = mm<true, true>(fk, klf[s], ar);
-        aa = mm<true, true>(fk, qf[s], aa);
+        split8(x, fk);
+        if constexpr (DELTA) ar = mm<true, true>(fk, nk[s], ar);
+        aa = mm<true, true>(fk, nq[s], aa);
       }
     }
     const float bi = sm.beta[i];
@@ -386,6 +537,8 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       av[J][e] = (J < w || (J == w && jj <= r)) ? aa[e] : 0.f;
     }
   }
+  if (!fast) prep_exact_diagonal<D, DELTA>(p, it, w, r, g, sm.beta[i], rv, av);
+
   // A^ fragments of row block w
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -397,20 +550,24 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       st_frag(rec, RC::R2 + RC::tp(pair_index(w, s)), lane, f);
     }
   }
-  // K_r^T fragments (update operands): wave w takes fragments w, w + 4, ...
+  // K_end^T fragments (update operands): the keys decayed to the chunk's
+  // end, kd times the decay of the blocks after the key's own; wave w takes
+  // fragments w, w + 4, ...
 #pragma unroll
   for (int u = 0; u < NT / 2; ++u) {
     const int fi = w + 4 * u;
     const int m = fi >> 1, s = fi & 1;
-    const int pc = perm32(16 * m + r);
+    const int ch = 16 * m + r, pc = perm32(ch);
+    // tokens of slots 0-3 lie in block 2s, those of slots 4-7 in block 2s + 1
+    const float fe0 = sm.fend[2 * s][ch], fe1 = sm.fend[2 * s + 1][ch];
     float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = sm.kr[32 * s + slot_k(g, j)][pc];
+    for (int j = 0; j < 8; ++j) x[j] = sm.kd[32 * s + slot_k(g, j)][pc] * (j < 4 ? fe0 : fe1);
     Frag f;
     split8(x, f);
     st_frag(rec, RC::kf(m, s), lane, f);
   }
-  __syncthreads();   // K_r is dead: its storage holds T from here on
+  __syncthreads();   // kd is dead: its storage holds T from here on
 
   // (the linear rule stops here: its records need no region 1)
   if constexpr (DELTA) {
@@ -952,12 +1109,20 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
     for (int s = 0; s < 2; ++s) st_frag(xs, 2048 * (NS + s), lane, vbf[s]);
     count_in(&sm.xready[pw], lane);
 
-    // ---- region 3: S^T <- gamma (.) (S^T + K_r^T Vb), in blocks of four key
+    // ---- region 3: S^T <- gamma (.) S^T + K_end^T Vb, in blocks of four key
     //      tiles and one k step (four independent accumulators), the next
     //      block's fragments in flight ----
     spin_until(&sm.ready[2], NLW * (k + 1));
     {
       const float *gam = reinterpret_cast<const float *>(sm.rec + RC::GAM);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * m + 4 * g);
+        st[m][0] *= gm.x;
+        st[m][1] *= gm.y;
+        st[m][2] *= gm.z;
+        st[m][3] *= gm.w;
+      }
       constexpr int NB = NT / 4 * 2;   // blocks (key tile group, k step)
       Frag kf[2][4];
 #pragma unroll
@@ -979,14 +1144,6 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
         for (int j = 0; j < 4; ++j) st[4 * mg + j] = mpass<2>(kf[bk & 1][j], vbf[s], st[4 * mg + j]);
         if (bk + 1 < NB) interleave<8, 0, 1>();
         __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * m + 4 * g);
-        st[m][0] *= gm.x;
-        st[m][1] *= gm.y;
-        st[m][2] *= gm.z;
-        st[m][3] *= gm.w;
       }
     }
     count_in(&sm.freed[2], lane);

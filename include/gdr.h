@@ -38,7 +38,11 @@
  *   k           [T_total*P, HK, DK] row t*P + j (substep j of token t) starts
  *                                   at (t*P + j) * k_stride_t
  *   v           [T_total*P, HV, DV] row t*P + j starts at (t*P + j) * v_stride_t
- *   g           [T_total, HV] (SCALAR) or [T_total, HV, DK] (CHANNEL), fp32
+ *   g           [T_total, HV] (SCALAR) or [T_total, HV, DK] (CHANNEL), fp32,
+ *               finite and <= 0; any such gate is handled, however strong the
+ *               decay (the chunked forms only ever exponentiate non-positive
+ *               log-decays, or positive ones bounded by 80 where the channel
+ *               gate's 16-token blocks allow it, and sum the rest pair by pair)
  *   beta        [T_total*P, HV] fp32, in (0, 1]
  *   o           [T_total, HV, DV]   contiguous, written (never read)
  *   state_pool  [num_slots, HV, DK, DV]: S^T per slot and value head, updated

@@ -16,7 +16,8 @@ Recipe (the same for every workload):
     is bf16;
   * v ~ N(0, 1), cast the same way;
   * beta = sigmoid(N(0, 1)) and g = -softplus(N(0, 1) - shift) in fp32
-    (g = log alpha <= 0; channel gates draw one value per key channel);
+    (g = log alpha <= 0; channel gates draw one value per key channel, with
+    one shift for every channel or a repeating pattern of per-channel shifts);
   * initial states ~ N(0, 0.02^2) cast to the pool's storage type; slot indices
     are a seeded choice of distinct slots.
 Any token range reproduces the values of the whole tensor.
@@ -56,6 +57,8 @@ class Workload:
     steps: int = 1            # decode: consecutive steps (fresh token each)
     seed: int = 0
     description: str = ""
+    channel_shifts: tuple = ()  # channel gate: shift of key channel c is channel_shifts[c % len]
+                                # (empty: gate_shift for every channel)
 
     @property
     def N(self) -> int:
@@ -215,7 +218,11 @@ def _block(w: Workload, seed: int, name: str, b: int, T: int):
         b_ = rng.standard_normal((n, HV), dtype=f32)
         return (1.0 / (1.0 + np.exp(-b_))).astype(f32)
     x = rng.standard_normal((n, HV, DK) if w.gate == "channel" else (n, HV), dtype=f32)
-    z = x - f32(w.gate_shift)
+    if w.gate == "channel" and w.channel_shifts:
+        shifts = np.resize(np.asarray(w.channel_shifts, dtype=f32), DK)
+        z = x - shifts
+    else:
+        z = x - f32(w.gate_shift)
     return (-(np.maximum(z, f32(0)) + np.log1p(np.exp(-np.abs(z))))).astype(f32)
 
 

@@ -34,3 +34,19 @@ def test_bf16_cast_round_trip():
     b = synth.f64_to_bf16_bits(x)
     y = synth.bf16_bits_to_f64(b)
     assert np.all(np.abs(y - x) <= np.abs(x) * 2 ** -8)
+
+
+def test_channel_shift_pattern():
+    """Per-channel gate shifts repeat over the key channels; a single shift
+    draws the same values as a pattern of that one shift."""
+    import numpy as np
+    import synth
+    base = synth.Workload(name="t", seqlens=(40,), HK=1, HV=2, DK=64, DV=64, in_dtype="bf16",
+                          gate="channel", rule="delta", gate_shift=1.0, state_dtype="f32",
+                          num_slots=1, zero_init=True, seed=3)
+    g1 = synth.generate(base)["g"]
+    g2 = synth.generate(base.replace(channel_shifts=(1.0,)))["g"]
+    assert np.array_equal(g1, g2)
+    g3 = synth.generate(base.replace(channel_shifts=(8.0, -8.0)))["g"]
+    assert g3.shape == g1.shape and np.all(g3 <= 0)
+    assert g3[:, :, 0::2].mean() > -0.01 and g3[:, :, 1::2].mean() < -7.0
