@@ -14,6 +14,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;    // tokens per chunk
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only. __syncthreads also waits for every global load and store in flight
+// (vmcnt(0)), which puts a kernel that streams results out behind its own
+// stores at each barrier. Global memory written before it is not made
+// visible to the other waves. The memory clobbers keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A load through the scalar unit, for data no kernel writes while the
+// reader runs (sequence offsets) at a uniform address: it is waited for with
+// lgkmcnt, so it does not queue behind the vector loads and stores in flight
+// the way a vector load does (their counter drains in order).
+__device__ __forceinline__ int32_t scalar_load(const int32_t *ptr) {
+  return *(const __attribute__((address_space(4))) int32_t *)ptr;
+}
 constexpr int BV = 64;   // value columns per workgroup (16 per wave)
 
 // Substep bookkeeping for P transitions per token (Gated DeltaProduct run

@@ -335,7 +335,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int h = hk * p.ratio + j / NB;
   const int vb = j % NB;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  // (the wave index through readfirstlane: the compiler then knows it is
+  // uniform, so the role switches below are scalar branches, never
+  // exec-masked regions around MFMAs)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int col = vb * BV + 16 * w + r;   // value column this lane owns in C tiles
 
   // bos and eos count substeps: token t is rows t*P .. t*P+P-1 (P = 1 but

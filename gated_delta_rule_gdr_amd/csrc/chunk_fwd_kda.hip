@@ -35,13 +35,14 @@
 //     record per (chunk, head) to the workspace with every operand the state
 //     kernel multiplies, already split into bf16 hi / lo planes and laid out
 //     as MFMA fragments;
-//   * kda_state_kernel, one workgroup per (sequence, value head, 16 value
-//     columns): a chain wave (S^T[DK, 16] in MFMA accumulators: Vb and the
-//     update) walks the slice's chunks in order, an output wave follows one
-//     chunk behind, and six loader waves copy the next chunks' records (and
-//     values) from the workspace into registers and into LDS region by region
-//     as the computing waves release them (LDS counters, no workgroup
-//     barrier).
+//   * kda_state_kernel, one workgroup of four waves per (sequence, value
+//     head, 16 value columns) walks the slice's chunks in order: wave q
+//     holds the key rows q DK/4 .. (q+1) DK/4 - 1 of S^T[DK, 16] in MFMA
+//     accumulators and forms the Vb and output rows 16q .. 16q+15; each wave
+//     loads the record fragments it multiplies straight into registers (two
+//     register sets, the next chunk's loads in flight while this chunk is
+//     multiplied), and LDS carries only the state and Vb fragments every
+//     wave reads whole, with two LDS-only barriers per chunk.
 // A sequence's state crosses slice boundaries through an fp32 carry area of
 // the workspace. The workspace is sized by the caller: a larger one means
 // fewer, longer slices.
@@ -115,14 +116,18 @@ __device__ __forceinline__ int64_t flat_base(const int32_t *cu, int n) {
   return (int64_t)(cu[n] >> 6) + n;
 }
 
-__device__ __forceinline__ void st_frag(char *base, int off, int lane, const Frag &f) {
-  *reinterpret_cast<uint4 *>(base + off + 16 * lane) = __builtin_bit_cast(uint4, f.hi);
-  *reinterpret_cast<uint4 *>(base + off + 1024 + 16 * lane) = __builtin_bit_cast(uint4, f.lo);
-}
-
-__device__ __forceinline__ void ld_frag(const char *base, int off, int lane, Frag &f) {
-  f.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(base + off + 16 * lane));
-  f.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(base + off + 1024 + 16 * lane));
+// A record fragment stored at the record's uniform base plus the fragment's
+// offset (scalar) and a 32-bit lane offset voff = 16 x lane shared by every
+// store, so that no 64-bit address per fragment occupies vector registers.
+// (Global stores, not buffer stores: the compiler guards the data registers
+// of a 128-bit global store against being rewritten before the store has
+// read them, but assumes no such hazard for a buffer store whose scalar
+// offset is a register, and on gfx950 such stores have been seen to write
+// the registers' next contents.)
+__device__ __forceinline__ void st_frag(char *rec, uint32_t voff, int off, const Frag &f) {
+  char *base = rec + off;
+  *reinterpret_cast<u32x4 *>(base + voff) = __builtin_bit_cast(u32x4, f.hi);
+  *reinterpret_cast<u32x4 *>(base + 1024 + voff) = __builtin_bit_cast(u32x4, f.lo);
 }
 
 // Pass P of a split product: lo x hi, hi x lo, hi x hi (the products of
@@ -148,6 +153,13 @@ __device__ __forceinline__ int slot_k(int g, int j) { return (j < 4 ? 4 * g + j 
 template <int D>
 struct PrepSmem {
   static constexpr int PK = D + 4;   // fp32 rows, key columns permuted (perm32)
+  // (the small fixed-address arrays first, within the 64 KiB that an LDS
+  // instruction's immediate offset reaches, so they need no address register)
+  float tot[4][D];                   // per 16-token block: gate sum of each channel (<= 0)
+  float etot[4][D];                  // its exponential: the block's decay of each channel
+  float fend[4][D];                  // decay of the blocks after block b (keys to the chunk's end)
+  float dmid[3][D];                  // decay of the blocks strictly between J and w: (2,0), (3,1), (3,0)
+  float beta[C];
   float kl[C][PK];                   // K_l = e^{G} (.) K, token-major
   union {
     float kd[C][PK];                 // keys decayed to the end of their own 16-token block
@@ -156,11 +168,6 @@ struct PrepSmem {
       float rd[4][16][20];           // R's diagonal blocks, negated
     } t;
   };
-  float tot[4][D];                   // per 16-token block: gate sum of each channel (<= 0)
-  float etot[4][D];                  // its exponential: the block's decay of each channel
-  float fend[4][D];                  // decay of the blocks after block b (keys to the chunk's end)
-  float dmid[3][D];                  // decay of the blocks strictly between J and w: (2,0), (3,1), (3,0)
-  float beta[C];
 };
 
 // T_IJ = -T_II (sum_{K=J}^{I-1} R_IK T_KJ) for one block of T below the
@@ -197,19 +204,22 @@ struct PrepItem {
   bool valid;
 };
 
-__device__ __forceinline__ PrepItem prep_item(const KdaParams &p, int64_t item) {
+// Item jb * HV + h: flat chunk F0 + jb, value head h.
+__device__ __forceinline__ PrepItem prep_item(const KdaParams &p, int64_t jb, int h) {
   PrepItem it;
-  const int64_t jb = item / p.HV;
-  it.h = (int)(item - jb * p.HV);
+  it.h = h;
   const int64_t F = p.F0 + jb;
-  // the sequence owning flat chunk F: the last n with base(n) <= F
+  // the sequence owning flat chunk F: the last n with base(n) <= F (the
+  // offsets through scalar loads: uniform, and not queued behind the vector
+  // stores of the item in flight)
+  const int32_t *cu = p.cu_seqlens;
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (flat_base(p.cu_seqlens, mid) <= F) lo = mid;
+    if ((int64_t)(scalar_load(cu + mid) >> 6) + mid <= F) lo = mid;
     else hi = mid - 1;
   }
-  const int64_t bos = p.cu_seqlens[lo], eos = p.cu_seqlens[lo + 1];
+  const int64_t bos = scalar_load(cu + lo), eos = scalar_load(cu + lo + 1);
   it.t0 = bos + 64 * (F - flat_base(p.cu_seqlens, lo));
   it.valid = it.t0 < eos;
   it.L = it.valid ? (int)min<int64_t>(C, eos - it.t0) : 1;
@@ -232,31 +242,50 @@ template <int D, bool DELTA>
 __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, const PrepItem &it, int w,
                                           int r, int g) {
   constexpr int NS = D / 32;
-  const int i = 16 * w + r;
-  const int64_t t = it.t0 + min(i, it.L - 1);
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  // buffer loads against descriptors over the item's L token rows (scalar
+  // bases, one lane offset per tensor); a lane past the chunk's end rereads
+  // its last row
+  const int row = min(16 * w + r, it.L - 1);
   const int hk = it.h / p.ratio;
-  const float *gp = p.g + (t * p.HV + it.h) * (int64_t)D;
-  const uint16_t *kp = static_cast<const uint16_t *>(p.k) + t * p.k_stride + (int64_t)hk * D;
-  const uint16_t *qp = static_cast<const uint16_t *>(p.q) + t * p.q_stride + (int64_t)hk * D;
+  const int64_t HVD = (int64_t)p.HV * D;
+  const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(p.g + it.t0 * HVD + (int64_t)it.h * D), 0, (int)((it.L - 1) * HVD * 4 + 4 * D),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(static_cast<const uint16_t *>(p.k) + it.t0 * p.k_stride + (int64_t)hk * D), 0,
+      (int)((it.L - 1) * p.k_stride * 2 + 2 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(static_cast<const uint16_t *>(p.q) + it.t0 * p.q_stride + (int64_t)hk * D), 0,
+      (int)((it.L - 1) * p.q_stride * 2 + 2 * D), 0x00020000);
+  const uint32_t gv = (uint32_t)(row * HVD * 4) + 16u * g;
+  const uint32_t kv = (uint32_t)(row * p.k_stride * 2) + 8u * g;
+  const uint32_t qv = (uint32_t)(row * p.q_stride * 2) + 8u * g;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int col = 32 * s + 16 * hf + 4 * g;
-      const float4 g4 = *reinterpret_cast<const float4 *>(gp + col);
-      const uint2 k2 = *reinterpret_cast<const uint2 *>(kp + col);
-      const uint2 q2 = *reinterpret_cast<const uint2 *>(qp + col);
+      const int col = 32 * s + 16 * hf;
+      const u32x4 g4 = __builtin_amdgcn_raw_buffer_load_b128(gr, gv, 4 * col, 0);
+      const u32x2 k2 = __builtin_amdgcn_raw_buffer_load_b64(kr, kv, 2 * col, 0);
+      const u32x2 q2 = __builtin_amdgcn_raw_buffer_load_b64(qr, qv, 2 * col, 0);
       const int u = 2 * s + hf;
-      in.g[4 * u] = __float_as_uint(g4.x);
-      in.g[4 * u + 1] = __float_as_uint(g4.y);
-      in.g[4 * u + 2] = __float_as_uint(g4.z);
-      in.g[4 * u + 3] = __float_as_uint(g4.w);
-      in.k[2 * u] = k2.x;
-      in.k[2 * u + 1] = k2.y;
-      in.q[2 * u] = q2.x;
-      in.q[2 * u + 1] = q2.y;
+      in.g[4 * u] = g4[0];
+      in.g[4 * u + 1] = g4[1];
+      in.g[4 * u + 2] = g4[2];
+      in.g[4 * u + 3] = g4[3];
+      in.k[2 * u] = k2[0];
+      in.k[2 * u + 1] = k2[1];
+      in.q[2 * u] = q2[0];
+      in.q[2 * u + 1] = q2[1];
     }
-  in.beta = DELTA ? p.beta[t * p.HV + it.h] : 0.f;
+  if constexpr (DELTA) {
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(p.beta + it.t0 * p.HV + it.h), 0, (int)((it.L - 1) * p.HV * 4 + 4), 0x00020000);
+    in.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(row * p.HV * 4), 0, 0));
+  } else {
+    in.beta = 0.f;
+  }
 }
 
 // The diagonal 16x16 block of the Gram matrices of row block w, summed pair
@@ -348,11 +377,19 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   __shared__ SM sm;
 
   const int HV = p.HV;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  // (the wave index through readfirstlane, so that conditions on it are
+  // scalar branches)
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            g = lane >> 4;
   const int i = 16 * w + r;   // this lane's token
   const int64_t items = (p.F1 - p.F0) * HV;
   int64_t item = blockIdx.x;
-  PrepItem nx = prep_item(p, item);
+  // item = jb * HV + h, advanced by the grid stride (dj, dh) without a
+  // division per item
+  const int dj = (int)(gridDim.x / HV), dh = (int)(gridDim.x - dj * HV);
+  int64_t jb = blockIdx.x / HV;
+  int hh = (int)(blockIdx.x - jb * HV);
+  PrepItem nx = prep_item(p, jb, hh);
   PrepIn<D> in;
   prep_load<D, DELTA>(in, p, nx, w, r, g);
   for (; item < items; item += gridDim.x) {
@@ -377,7 +414,13 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
     // (below), so that their registers are free meanwhile
     auto prefetch = [&]() {
       if (item + gridDim.x < items) {
-        nx = prep_item(p, item + gridDim.x);
+        jb += dj;
+        hh += dh;
+        if (hh >= HV) {
+          hh -= HV;
+          ++jb;
+        }
+        nx = prep_item(p, jb, hh);
         prep_load<D, DELTA>(in, p, nx, w, r, g);
       }
     };
@@ -386,6 +429,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       const int h = it.h;
       const int L = it.L;
       char *rec = p.rec + item * (int64_t)RC::BYTES;
+      const uint32_t voff = 16u * (uint32_t)lane;
       (void)L;
 
   // ---- gate prefix sums within the 16-token block (DPP row scan over r):
@@ -413,10 +457,10 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
             make_float4(__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3]));
       }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     const float Gl = ((sm.tot[0][tid] + sm.tot[1][tid]) + sm.tot[2][tid]) + sm.tot[3][tid];
-    reinterpret_cast<float *>(rec + RC::GAM)[tid] = __expf(Gl);
+    *reinterpret_cast<float *>(rec + RC::GAM + 4u * (uint32_t)tid) = __expf(Gl);
     const float e1 = sm.etot[1][tid], e2 = sm.etot[2][tid], e3 = sm.etot[3][tid];
     sm.fend[0][tid] = e1 * (e2 * e3);
     sm.fend[1][tid] = e2 * e3;
@@ -445,8 +489,15 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) span = fmaxf(span, __shfl_xor(span, off, 64));
   const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(span)) <= __float_as_int(80.f);
-  Frag nk[NS], nq[NS];
-  f32x4 rdiag = {0.f, 0.f, 0.f, 0.f}, adiag = rdiag;
+  // Gram tiles of row block w, by k step s: tile (w, J) is computed
+  // transposed (keys of block J as the M operand), so lane (r, g) holds row
+  // 16w + r, columns 16J + 4g .. +3. For J < w the keys are those of block J
+  // decayed to the start of block w (kd times the decay of the blocks
+  // between, <= 1 per channel); tile (w, w) takes md. One k step's operands
+  // are live at a time; each step's kd columns are published by a barrier.
+  f32x4 ar[4], aa[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) ar[J] = aa[J] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc = p.scale;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -481,36 +532,35 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
     *reinterpret_cast<float4 *>(pl + 4) = make_float4(e[4], e[5], e[6], e[7]);
     *reinterpret_cast<float4 *>(pd) = make_float4(d[0], d[1], d[2], d[3]);
     *reinterpret_cast<float4 *>(pd + 4) = make_float4(d[4], d[5], d[6], d[7]);
-    split8(a, nk[s]);
-    split8(c8, nq[s]);
+    Frag nk, nq;
+    split8(a, nk);
+    split8(c8, nq);
+    {
+      Frag fq;
+      split8(f, fq);
+      st_frag(rec, voff, RC::R2 + RC::wq(w, s), fq);
+    }
     if (fast) {
       Frag md;
       split8(b, md);
-      if constexpr (DELTA) rdiag = mm<true, true>(md, nk[s], rdiag);
-      adiag = mm<true, true>(md, nq[s], adiag);
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J == w) {
+          if constexpr (DELTA) ar[J] = mm<true, true>(md, nk, ar[J]);
+          aa[J] = mm<true, true>(md, nq, aa[J]);
+        }
     }
-    Frag fq;
-    split8(f, fq);
-    st_frag(rec, RC::R2 + RC::wq(w, s), lane, fq);
-  }
-  prefetch();
-  __syncthreads();
-
-  // ---- Grams of row block w: tile (w, J) computed transposed (keys of
-  //      block J as the M operand), so lane (r, g) holds row 16w + r,
-  //      columns 16J + 4g .. +3. For J < w the keys are those of block J
-  //      decayed to the start of block w (kd times the decay of the blocks
-  //      between, <= 1 per channel); tile (w, w) is the diagonal above ----
-  f32x4 rv[4], av[4];
+    if (s + 1 == NS) {
+      // (fenced, so that the loads are not hoisted above the operand work and
+      // their registers stay free until here)
+      __builtin_amdgcn_sched_barrier(0);
+      prefetch();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    f32x4 ar = {0.f, 0.f, 0.f, 0.f}, aa = ar;
-    if (J == w) {
-      ar = rdiag;
-      aa = adiag;
-    } else if (J < w) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
+    for (int J = 0; J < 3; ++J) {
+      if (J < w) {
         const float *src = &sm.kd[16 * J + r][32 * s + 8 * g];
         const float4 x0 = *reinterpret_cast<const float4 *>(src);
         const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
@@ -525,18 +575,22 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
         }
         Frag fk;
         split8(x, fk);
-        if constexpr (DELTA) ar = mm<true, true>(fk, nk[s], ar);
-        aa = mm<true, true>(fk, nq[s], aa);
+        if constexpr (DELTA) ar[J] = mm<true, true>(fk, nk, ar[J]);
+        aa[J] = mm<true, true>(fk, nq, aa[J]);
       }
     }
-    const float bi = sm.beta[i];
+  }
+  // write strength and causal masks
+  f32x4 rv[4], av[4];
+  const float bi = sm.beta[i];
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jj = 4 * g + e;
-      rv[J][e] = (J < w || (J == w && jj < r)) ? bi * ar[e] : 0.f;
-      av[J][e] = (J < w || (J == w && jj <= r)) ? aa[e] : 0.f;
+      rv[J][e] = (J < w || (J == w && jj < r)) ? bi * ar[J][e] : 0.f;
+      av[J][e] = (J < w || (J == w && jj <= r)) ? aa[J][e] : 0.f;
     }
-  }
   if (!fast) prep_exact_diagonal<D, DELTA>(p, it, w, r, g, sm.beta[i], rv, av);
 
   // A^ fragments of row block w
@@ -547,17 +601,21 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
                           av[2 * s + 1][0], av[2 * s + 1][1], av[2 * s + 1][2], av[2 * s + 1][3]};
       Frag f;
       split8(x, f);
-      st_frag(rec, RC::R2 + RC::tp(pair_index(w, s)), lane, f);
+      st_frag(rec, voff, RC::R2 + RC::tp(pair_index(w, s)), f);
     }
   }
   // K_end^T fragments (update operands): the keys decayed to the chunk's
   // end, kd times the decay of the blocks after the key's own; wave w takes
-  // fragments w, w + 4, ...
+  // fragments w, w + 4, ... (the row index passes through an empty asm so
+  // that these LDS addresses are formed here, not kept live, or spilled,
+  // across the whole item loop)
+  int ro = r;
+  asm volatile("" : "+v"(ro));
 #pragma unroll
   for (int u = 0; u < NT / 2; ++u) {
     const int fi = w + 4 * u;
     const int m = fi >> 1, s = fi & 1;
-    const int ch = 16 * m + r, pc = perm32(ch);
+    const int ch = 16 * m + ro, pc = perm32(ch);
     // tokens of slots 0-3 lie in block 2s, those of slots 4-7 in block 2s + 1
     const float fe0 = sm.fend[2 * s][ch], fe1 = sm.fend[2 * s + 1][ch];
     float x[8];
@@ -565,9 +623,9 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
     for (int j = 0; j < 8; ++j) x[j] = sm.kd[32 * s + slot_k(g, j)][pc] * (j < 4 ? fe0 : fe1);
     Frag f;
     split8(x, f);
-    st_frag(rec, RC::kf(m, s), lane, f);
+    st_frag(rec, voff, RC::kf(m, s), f);
   }
-  __syncthreads();   // kd is dead: its storage holds T from here on
+  lds_barrier();   // kd is dead: its storage holds T from here on
 
   // (the linear rule stops here: its records need no region 1)
   if constexpr (DELTA) {
@@ -585,21 +643,25 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       const float4 v4 = *reinterpret_cast<const float4 *>(&sm.t.rd[w][r][4 * i4]);
       nn[4 * i4] = v4.x; nn[4 * i4 + 1] = v4.y; nn[4 * i4 + 2] = v4.z; nn[4 * i4 + 3] = v4.w;
     }
+    // (the identity from an opaque copy of the lane index: formed here
+    // rather than hoisted out of the item loop and spilled)
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tq[e] = (r == 4 * g + e) ? 1.f : 0.f;
+    for (int e = 0; e < 4; ++e) tq[e] = ((lq & 15) == 4 * (lq >> 4) + e) ? 1.f : 0.f;
     unit_lower_inverse16(tq, nn);
     *reinterpret_cast<float4 *>(&sm.t.tt[16 * w + r][16 * w + 4 * g]) = make_float4(tq[0], tq[1], tq[2], tq[3]);
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 1) t_block<1, 0, D>(sm, rv, r, g);
   if (w == 2) t_block<2, 1, D>(sm, rv, r, g);
   if (w == 3) t_block<3, 2, D>(sm, rv, r, g);
-  __syncthreads();
+  lds_barrier();
   if (w == 2) t_block<2, 0, D>(sm, rv, r, g);
   if (w == 3) t_block<3, 1, D>(sm, rv, r, g);
-  __syncthreads();
+  lds_barrier();
   if (w == 3) t_block<3, 0, D>(sm, rv, r, g);
-  __syncthreads();
+  lds_barrier();
 
   // ---- T' = T Diag(beta) fragments (all six in every wave: B operands of W) ----
   Frag tf[6];
@@ -624,7 +686,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
     }
 #pragma unroll
   for (int pr = 0; pr < 6; ++pr)
-    if (pr % 4 == w) st_frag(rec, RC::tp(pr), lane, tf[pr]);
+    if (pr % 4 == w) st_frag(rec, voff, RC::tp(pr), tf[pr]);
 
   // ---- W^T = K_l^T T'^T: wave w < NS forms key tiles m = 2w, 2w + 1, which
   //      are exactly the W fragments (I, s = w); the record holds -W ----
@@ -657,12 +719,12 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
                           -acc[1][I][0], -acc[1][I][1], -acc[1][I][2], -acc[1][I][3]};
       Frag f;
       split8(x, f);
-      st_frag(rec, RC::R1 + RC::wq(I, w), lane, f);
+      st_frag(rec, voff, RC::R1 + RC::wq(I, w), f);
     }
   }
   }   // DELTA
     }
-    __syncthreads();   // the next item reuses the LDS
+    lds_barrier();   // the next item reuses the LDS
   }
 }
 
@@ -670,129 +732,116 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 // state kernel
 // ===========================================================================
 
-constexpr int NLW = 4;   // loader waves of regions 1 and 3 (and values, gamma)
-constexpr int NLO = 2;   // loader waves of region 2
-
-// A workgroup owns 16 NSW value columns: NSW chain waves (16 columns each:
-// the state, U, Vb and the update), NSW output waves (the outputs of the same
-// columns, one chunk behind), NLW loader waves for the chain's operands and
-// NLO for the output waves'.
-template <int D, int NSW>
+// One workgroup of four waves per (sequence, value head, 16 value columns).
+// Wave q owns the chunk's token rows 16q .. 16q+15 (U, Vb and the outputs of
+// those rows) and the key rows q D/4 .. (q+1) D/4 - 1 of S^T (their state and
+// its update). Each wave loads the record fragments it multiplies straight
+// from the workspace into registers (two sets used in turn, chunk c + 1's
+// loaded while chunk c's are multiplied), so the record never passes through
+// LDS; LDS carries only what the waves exchange: the state's tiles (every
+// wave reads S^T whole), the Vb tiles (every wave reads Vb whole) and the
+// values, double-buffered by chunk parity, with two barriers per chunk that
+// wait for LDS only.
+template <int D>
 struct StateSmem {
-  static constexpr int VP = 16 * NSW + 16;  // pitch (bf16) of the value tile
-  static constexpr int XB = (KdaRec<D>::NS + 2) * 2048;   // exchange: S^T fragments, then Vb's
-  alignas(16) char rec[KdaRec<D>::BYTES];   // the current chunk's record
-  alignas(16) uint16_t vv[C][VP];           // its values: 64 tokens x 16 NSW columns
-  alignas(16) char xs[NSW][XB];             // chain wave -> output wave, per column block
-  int ready[3];                             // loader waves: regions stored (NLW, NLO, NLW per chunk)
-  int freed[3];                             // regions released (NSW per chunk; region 2 by the output waves)
-  int xready[NSW];                          // chain wave: chunks published to xs
-  int xfree[NSW];                           // output wave: chunks read from xs
+  static constexpr int NS = D / 32;
+  static constexpr int VP = 32;                   // pitch (bf16) of the value tile
+  // S^T and Vb as split B fragments, [parity][k step][lane]: the wave that
+  // holds a 16-row tile splits it once and writes its half of the fragment
+  // (words 0-1 of hi and lo for the even tile of a k step, 2-3 for the odd)
+  u32x4 sfh[2][NS][64], sfl[2][NS][64];
+  u32x4 vbh[2][2][64], vbl[2][2][64];
+  alignas(16) uint16_t vv[2][C][VP];              // values: [parity][token][column]
 };
 
-// A loader lane's share of one chunk's record and values, in registers
-// (vector types, not arrays, so that they stay there): region 1 with the
-// values (LoadR1), region 3 with gamma (LoadR3), region 2 (LoadR2).
+// Split an accumulator tile and write it as half h of split fragment slot
+// (hi, lo) of this lane.
+__device__ __forceinline__ void put_half(u32x4 *hi, u32x4 *lo, int lane, int h, const f32x4 &t) {
+  uint32_t h0, l0, h1, l1;
+  split_pair(t[0], t[1], h0, l0);
+  split_pair(t[2], t[3], h1, l1);
+  *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(&hi[lane]) + 2 * h) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(&lo[lane]) + 2 * h) = make_uint2(l0, l1);
+}
+
+__device__ __forceinline__ void get_frag(const u32x4 *hi, const u32x4 *lo, int lane, Frag &f) {
+  f.hi = __builtin_bit_cast(bf16x8, hi[lane]);
+  f.lo = __builtin_bit_cast(bf16x8, lo[lane]);
+}
+
+// Fragment at byte offset `off` of a record, through a buffer descriptor
+// over it: the lane part of the address (16 bytes per lane) is a fixed
+// register, the fragment's offset a scalar.
+__device__ __forceinline__ void buf_frag(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int off, Frag &f) {
+  f.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, off, 0));
+  f.lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, off + 1024, 0));
+}
+
+// The record fragments wave q multiplies in one chunk.
 template <int D>
-struct LoadN {
-  static constexpr int N1 = KdaRec<D>::R1_BLOCKS / NLW;   // 1 KB blocks per loader wave
-  static constexpr int N3 = KdaRec<D>::R3_BLOCKS / NLW;
+struct WaveOps {
+  static constexpr int NS = D / 32, KT = D / 64;
+  Frag w[NS];       // -W, row block q
+  Frag t[2];        // T', row block q, k steps s <= q / 2
+  Frag qh[NS];      // Q^, row block q
+  Frag a[2];        // A^, row block q, k steps s <= q / 2
+  Frag ke[KT][2];   // K_end^T, this wave's key tiles, k steps 0 and 1
+  float4 gam[KT];   // gamma of the lane's four key rows in each of those tiles
 };
-template <int NSW>
-constexpr int value_units() { return (128 * NSW + 64 * NLW - 1) / (64 * NLW); }   // 16-byte units per lane
-template <int D, int NSW>
-struct LoadR1 {
-  typename U32Vec<4 * LoadN<D>::N1>::type r1;
-  typename U32Vec<4 * value_units<NSW>()>::type v;
-};
-template <int D>
-struct LoadR3 {
-  typename U32Vec<4 * LoadN<D>::N3>::type r3;
-  typename U32Vec<4>::type gam;
-};
-template <int D>
-struct LoadR2 {
-  typename U32Vec<4 * KdaRec<D>::R1_BLOCKS / NLO>::type r2;
-};
-
-// (the linear rule needs no region 1: its corrected values are the values)
-template <int D, int NSW, bool DELTA>
-__device__ __forceinline__ void issue_r1(LoadR1<D, NSW> &l1, const KdaParams &p, const char *rec,
-                                         int64_t t0, int L, int h, int vb, int lw, int lane) {
-  const char *base = rec + 16 * lane;
-  if constexpr (DELTA) {
-#pragma unroll
-    for (int u = 0; u < LoadN<D>::N1; ++u)
-      put4(l1.r1, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)));
-  }
-  // values: 64 rows of 2 NSW 16-byte units
-  const uint16_t *vb_ = static_cast<const uint16_t *>(p.v) + (int64_t)h * D + 16 * NSW * vb;
-#pragma unroll
-  for (int u = 0; u < value_units<NSW>(); ++u) {
-    const int q = 64 * lw + lane + 64 * NLW * u;
-    const int row = min(q / (2 * NSW), C - 1);
-    const int64_t tr = t0 + min(row, L - 1);
-    const uint4 x = *reinterpret_cast<const uint4 *>(vb_ + tr * p.v_stride + 8 * (q % (2 * NSW)));
-    put4(l1.v, u, row < L ? x : make_uint4(0, 0, 0, 0));
-  }
-}
 
 template <int D>
-__device__ __forceinline__ void issue_r3(LoadR3<D> &l3, const char *rec, int lw, int lane) {
-  const char *base = rec + 16 * lane;
-#pragma unroll
-  for (int u = 0; u < LoadN<D>::N3; ++u)
-    put4(l3.r3, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R3 + 1024 * (lw + NLW * u)));
-  if (lw == 0 && lane < D / 4) put4(l3.gam, 0, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::GAM));
-}
-
-template <int D>
-__device__ __forceinline__ void issue_r2(LoadR2<D> &l2, const char *rec, int lw, int lane) {
-  const char *base = rec + 16 * lane;
-#pragma unroll
-  for (int u = 0; u < KdaRec<D>::R1_BLOCKS / NLO; ++u)
-    put4(l2.r2, u, *reinterpret_cast<const uint4 *>(base + KdaRec<D>::R2 + 1024 * (lw + NLO * u)));
-}
-
-template <int D, int NSW, bool DELTA>
-__device__ __forceinline__ void store_r1(const LoadR1<D, NSW> &l1, StateSmem<D, NSW> &sm, int lw, int lane) {
-  char *base = sm.rec + 16 * lane;
-  if constexpr (DELTA) {
-#pragma unroll
-    for (int u = 0; u < LoadN<D>::N1; ++u)
-      *reinterpret_cast<uint4 *>(base + KdaRec<D>::R1 + 1024 * (lw + NLW * u)) = get4(l1.r1, u);
-  }
-#pragma unroll
-  for (int u = 0; u < value_units<NSW>(); ++u) {
-    const int q = 64 * lw + lane + 64 * NLW * u;
-    if (q < 128 * NSW) *reinterpret_cast<uint4 *>(&sm.vv[q / (2 * NSW)][8 * (q % (2 * NSW))]) = get4(l1.v, u);
-  }
-}
-
-template <int D, int NSW>
-__device__ __forceinline__ void store_r3(const LoadR3<D> &l3, StateSmem<D, NSW> &sm, int lw, int lane) {
-  char *base = sm.rec + 16 * lane;
-#pragma unroll
-  for (int u = 0; u < LoadN<D>::N3; ++u)
-    *reinterpret_cast<uint4 *>(base + KdaRec<D>::R3 + 1024 * (lw + NLW * u)) = get4(l3.r3, u);
-  if (lw == 0 && lane < D / 4) *reinterpret_cast<uint4 *>(base + KdaRec<D>::GAM) = get4(l3.gam, 0);
-}
-
-template <int D, int NSW>
-__device__ __forceinline__ void store_r2(const LoadR2<D> &l2, StateSmem<D, NSW> &sm, int lw, int lane) {
-  char *base = sm.rec + 16 * lane;
-#pragma unroll
-  for (int u = 0; u < KdaRec<D>::R1_BLOCKS / NLO; ++u)
-    *reinterpret_cast<uint4 *>(base + KdaRec<D>::R2 + 1024 * (lw + NLO * u)) = get4(l2.r2, u);
-}
-
-// DELTA false: the linear rule (GLA), Vb = V, region 1 neither loaded nor used.
-template <int D, int NSW, bool DELTA>
-__global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(KdaParams p) {
+__device__ __forceinline__ void load_r1(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff) {
   using RC = KdaRec<D>;
-  using SM = StateSmem<D, NSW>;
-  constexpr int NS = RC::NS, NT = RC::NT;
-  constexpr int GRP = D / (16 * NSW);   // workgroups per (sequence, value head)
+#pragma unroll
+  for (int s = 0; s < RC::NS; ++s) buf_frag(rs, voff, RC::R1 + RC::wq(q, s), o.w[s]);
+  buf_frag(rs, voff, RC::tp(pair_index(q, 0)), o.t[0]);
+  if (q >= 2) buf_frag(rs, voff, RC::tp(pair_index(q, 1)), o.t[1]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_r2(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff) {
+  using RC = KdaRec<D>;
+#pragma unroll
+  for (int s = 0; s < RC::NS; ++s) buf_frag(rs, voff, RC::R2 + RC::wq(q, s), o.qh[s]);
+  buf_frag(rs, voff, RC::R2 + RC::tp(pair_index(q, 0)), o.a[0]);
+  if (q >= 2) buf_frag(rs, voff, RC::R2 + RC::tp(pair_index(q, 1)), o.a[1]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_r3(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff, int g) {
+  using RC = KdaRec<D>;
+  constexpr int KT = WaveOps<D>::KT;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int m = KT * q + t;
+    buf_frag(rs, voff, RC::kf(m, 0), o.ke[t][0]);
+    buf_frag(rs, voff, RC::kf(m, 1), o.ke[t][1]);
+    const u32x4 gm = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(16 * g), RC::GAM + 64 * m, 0);
+    o.gam[t] = make_float4(__uint_as_float(gm[0]), __uint_as_float(gm[1]), __uint_as_float(gm[2]),
+                           __uint_as_float(gm[3]));
+  }
+}
+
+// Values of the chunk starting at token t0 (L rows): wave q's 16 rows of the
+// workgroup's 16 columns, 8 bytes per lane (zeros past the chunk's end).
+__device__ __forceinline__ uint2 load_vals(const KdaParams &p, int64_t t0, int L, int h, int D, int vb, int q,
+                                           int lane) {
+  const int row = 16 * q + (lane >> 2);
+  const int64_t tr = t0 + min(row, L - 1);
+  const uint16_t *src = static_cast<const uint16_t *>(p.v) + tr * p.v_stride + (int64_t)h * D + 16 * vb + 4 * (lane & 3);
+  const uint2 x = *reinterpret_cast<const uint2 *>(src);
+  return row < L ? x : make_uint2(0, 0);
+}
+
+// DELTA false: the linear rule (GLA), Vb = V; region 1 is neither written by
+// the prep kernel nor read here.
+template <int D, bool DELTA>
+__global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
+  using RC = KdaRec<D>;
+  using SM = StateSmem<D>;
+  using OPS = WaveOps<D>;
+  constexpr int NS = RC::NS, NT = RC::NT, KT = OPS::KT;
+  constexpr int GRP = D / 16;   // workgroups per (sequence, value head)
   __shared__ SM sm;
 
   // all workgroups of one (sequence, head) get ids equal modulo 8 (one XCD,
@@ -809,21 +858,26 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
   const int64_t nc = (eos - bos + C - 1) / C;
   const int64_t cb = max<int64_t>(p.F0 - base, 0), ce = min<int64_t>(p.F1 - base, nc);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const int pw = w < NSW ? w : w - NSW;            // column block of a chain / output wave
-  const int col = 16 * NSW * vb + 16 * pw + r;    // the value column this lane owns
+  // (the wave index through readfirstlane: the compiler then knows it is
+  // uniform, so the conditions on it below are scalar branches, never
+  // exec-masked regions around MFMAs)
+  const int tid = threadIdx.x, q = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            g = lane >> 4;
+  const int col = 16 * vb + r;                    // the value column this lane owns
   const int64_t slot = p.slot_idx[n];
   const int64_t pbase = (slot * p.HV + h) * (int64_t)(D * D) + col;
+  // key row of element e of this wave's key tile t: 16 (KT q + t) + 4g + e
+  auto key_row = [&](int t, int e) { return 16 * (KT * q + t) + 4 * g + e; };
 
   if (nc == 0) {
     // a zero-length sequence writes its initial state back: zeros under
     // ZERO_INIT (once, in the slice holding its flat index), else nothing
-    if (p.zero_init && w < NSW && base >= p.F0 && base < p.F1) {
+    if (p.zero_init && base >= p.F0 && base < p.F1) {
 #pragma unroll
-      for (int m = 0; m < NT; ++m)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int64_t idx = pbase + (int64_t)(16 * m + 4 * g + e) * D;
+          const int64_t idx = pbase + (int64_t)key_row(t, e) * D;
           if (p.st_bf16) static_cast<uint16_t *>(p.pool)[idx] = 0;
           else static_cast<float *>(p.pool)[idx] = 0.f;
         }
@@ -832,345 +886,193 @@ __global__ __launch_bounds__(64 * (2 * NSW + NLW + NLO)) void kda_state_kernel(K
   }
   if (cb >= ce) return;
 
-  if (tid < 6 + 2 * NSW) {
-    int *ctr = tid < 3 ? &sm.ready[tid] : tid < 6 ? &sm.freed[tid - 3]
-             : tid < 6 + NSW ? &sm.xready[tid - 6] : &sm.xfree[tid - 6 - NSW];
-    *ctr = 0;
-  }
-  __syncthreads();
-
-  auto rec_of = [&](int64_t c) -> const char * {
-    return p.rec + ((base + c - p.F0) * p.HV + h) * (int64_t)RC::BYTES;
+  auto rec_of = [&](int64_t c) -> __amdgpu_buffer_rsrc_t {
+    const char *rec = p.rec + ((base + c - p.F0) * p.HV + h) * (int64_t)RC::BYTES;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rec), 0, RC::BYTES, 0x00020000);
   };
+  const uint32_t voff = 16u * (uint32_t)lane;
+  auto len_of = [&](int64_t c) { return (int)min<int64_t>(C, eos - (bos + C * c)); };
 
-  if (w >= 2 * NSW + NLW) {
-    // ================= region-2 loader waves: two chunks ahead =================
-    const int lw = w - 2 * NSW - NLW;
-    // (Every refill is issued, past the slice's last chunk as a reload of that
-    // chunk, so each loop trip issues the same loads and the compiler's
-    // memory-counter waits before a store cover only the loads it reads.)
-    auto last = [&](int64_t c) { return c < ce ? c : ce - 1; };
-    LoadR2<D> a0, a1;
-    issue_r2<D>(a0, rec_of(cb), lw, lane);
-    store_r2<D, NSW>(a0, sm, lw, lane);
-    count_in(&sm.ready[1], lane);
-    issue_r2<D>(a1, rec_of(last(cb + 1)), lw, lane);
-    issue_r2<D>(a0, rec_of(last(cb + 2)), lw, lane);
-    auto step = [&](LoadR2<D> &l2, int64_t c) {
-      const int k = (int)(c - cb);
-      spin_until(&sm.freed[1], NSW * (k + 1));
-      store_r2<D, NSW>(l2, sm, lw, lane);
-      count_in(&sm.ready[1], lane);
-      issue_r2<D>(l2, rec_of(last(c + 3)), lw, lane);
-    };
-    for (int64_t c = cb; c + 1 < ce; c += 2) {
-      step(a1, c);
-      if (c + 2 < ce) step(a0, c + 1);
-    }
-    return;
-  }
-  if (w >= 2 * NSW) {
-    // ================= region-1 / region-3 loader waves =================
-    // Region 1 and the values (the first operands of a chunk) are loaded
-    // two chunks ahead, alternating between two register sets; region 3 one
-    // chunk ahead (it is used at the end of its chunk).
-    const int lw = w - 2 * NSW;
-    LoadR1<D, NSW> s0, s1;
-    LoadR3<D> l3;
-    auto i1 = [&](LoadR1<D, NSW> &l1, int64_t c) {
-      const int64_t t0 = bos + C * c;
-      issue_r1<D, NSW, DELTA>(l1, p, rec_of(c), t0, (int)min<int64_t>(C, eos - t0), h, vb, lw, lane);
-    };
-    i1(s0, cb);
-    issue_r3<D>(l3, rec_of(cb), lw, lane);
-    store_r1<D, NSW, DELTA>(s0, sm, lw, lane);
-    store_r3<D, NSW>(l3, sm, lw, lane);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) {
-      atomicAdd(&sm.ready[0], 1);
-      atomicAdd(&sm.ready[2], 1);
-    }
-    auto last = [&](int64_t c) { return c < ce ? c : ce - 1; };
-    i1(s1, last(cb + 1));
-    issue_r3<D>(l3, rec_of(last(cb + 1)), lw, lane);
-    i1(s0, last(cb + 2));
-    // Store chunk c + 1's regions as chunk c releases them (region 1 early
-    // in chunk c, region 3 at its end), each followed by the loads that
-    // refill its registers.
-    auto step = [&](LoadR1<D, NSW> &l1, int64_t c) {
-      const int k = (int)(c - cb);
-      spin_until(&sm.freed[0], NSW * (k + 1));
-      store_r1<D, NSW, DELTA>(l1, sm, lw, lane);
-      count_in(&sm.ready[0], lane);
-      spin_until(&sm.freed[2], NSW * (k + 1));
-      store_r3<D, NSW>(l3, sm, lw, lane);
-      count_in(&sm.ready[2], lane);
-      issue_r3<D>(l3, rec_of(last(c + 2)), lw, lane);
-      i1(l1, last(c + 3));
-    };
-    for (int64_t c = cb; c + 1 < ce; c += 2) {
-      step(s1, c);
-      if (c + 2 < ce) step(s0, c + 1);
-    }
-    return;
-  }
-
-  char *xs = sm.xs[pw];
-  const int64_t HVD = (int64_t)p.HV * D;
-
-  if (w >= NSW) {
-    // ================= output waves: O = Q^ S^T + A^ Vb, one chunk behind the chain =================
-    for (int64_t c = cb; c < ce; ++c) {
-      const int k = (int)(c - cb);
-      const int64_t t0 = bos + C * c;
-      const int L = (int)min<int64_t>(C, eos - t0);
-      Frag sf[NS], vbf[2];
-      spin_until(&sm.xready[pw], k + 1);
+  // ---- the state's tiles: the pool (or zeros) at the sequence's start, the
+  //      carry between slices ----
+  f32x4 st[KT];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) ld_frag(xs, 2048 * s, lane, sf[s]);
+  for (int t = 0; t < KT; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) ld_frag(xs, 2048 * (NS + s), lane, vbf[s]);
-      count_in(&sm.xfree[pw], lane);
-
-      spin_until(&sm.ready[1], NLO * (k + 1));
-      f32x4 oa[4];
-      {
-        Frag qf[2][4], aa[6];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) ld_frag(sm.rec, RC::R2 + RC::wq(I, 0), lane, qf[0][I]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) oa[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          if (s + 1 < NS) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I) ld_frag(sm.rec, RC::R2 + RC::wq(I, s + 1), lane, qf[(s + 1) & 1][I]);
-          } else {
-#pragma unroll
-            for (int pr = 0; pr < 6; ++pr) ld_frag(sm.rec, RC::R2 + RC::tp(pr), lane, aa[pr]);
-          }
-#pragma unroll
-          for (int I = 0; I < 4; ++I) oa[I] = mpass<0>(qf[s & 1][I], sf[s], oa[I]);
-#pragma unroll
-          for (int I = 0; I < 4; ++I) oa[I] = mpass<1>(qf[s & 1][I], sf[s], oa[I]);
-#pragma unroll
-          for (int I = 0; I < 4; ++I) oa[I] = mpass<2>(qf[s & 1][I], sf[s], oa[I]);
-          if (s + 1 < NS) interleave<8, 0, 1>();
-          else interleave<12, 0, 1>();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // + A^ Vb (lower triangular: k steps s <= I / 2)
-        oa[0] = mpass<0>(aa[0], vbf[0], oa[0]);
-        oa[1] = mpass<0>(aa[1], vbf[0], oa[1]);
-        oa[2] = mpass<0>(aa[2], vbf[0], oa[2]);
-        oa[3] = mpass<0>(aa[4], vbf[0], oa[3]);
-        oa[0] = mpass<1>(aa[0], vbf[0], oa[0]);
-        oa[1] = mpass<1>(aa[1], vbf[0], oa[1]);
-        oa[2] = mpass<1>(aa[2], vbf[0], oa[2]);
-        oa[3] = mpass<1>(aa[4], vbf[0], oa[3]);
-        oa[0] = mpass<2>(aa[0], vbf[0], oa[0]);
-        oa[1] = mpass<2>(aa[1], vbf[0], oa[1]);
-        oa[2] = mpass<2>(aa[2], vbf[0], oa[2]);
-        oa[3] = mpass<2>(aa[4], vbf[0], oa[3]);
-        oa[2] = mpass<0>(aa[3], vbf[1], oa[2]);
-        oa[3] = mpass<0>(aa[5], vbf[1], oa[3]);
-        oa[2] = mpass<1>(aa[3], vbf[1], oa[2]);
-        oa[3] = mpass<1>(aa[5], vbf[1], oa[3]);
-        oa[2] = mpass<2>(aa[3], vbf[1], oa[2]);
-        oa[3] = mpass<2>(aa[5], vbf[1], oa[3]);
+    for (int e = 0; e < 4; ++e) {
+      const int64_t kr = key_row(t, e);
+      if (cb > 0) {
+        st[t][e] = p.carry[((int64_t)n * p.HV + h) * (int64_t)(D * D) + kr * D + col];
+      } else if (!p.zero_init) {
+        const int64_t idx = pbase + kr * D;
+        st[t][e] = p.st_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(p.pool)[idx])
+                             : static_cast<const float *>(p.pool)[idx];
       }
-      count_in(&sm.freed[1], lane);
+    }
+  }
 
-      // Buffer stores against a descriptor over this chunk's L output rows:
-      // row 16I + e is a scalar offset and the lane part (row group 4g,
-      // column) a fixed one; rows past a partial chunk's end fall outside the
-      // descriptor and are dropped by the hardware.
+  // (Barriers wait for LDS only, lds_barrier: the next chunk's operand loads
+  // stay in flight across them.)
+
+  // Operands in two register sets used in turn: chunk c + 1's are loaded
+  // while chunk c's are multiplied.
+  OPS ops0, ops1;
+  // this wave's state tiles as halves of the split S^T fragments
+  auto publish_state = [&](int par) {
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int m = KT * q + t;
+      put_half(sm.sfh[par][m >> 1], sm.sfl[par][m >> 1], lane, m & 1, st[t]);
+    }
+  };
+  {
+    const __amdgpu_buffer_rsrc_t rec = rec_of(cb);
+    if constexpr (DELTA) load_r1<D>(ops0, rec, q, voff);
+    load_r2<D>(ops0, rec, q, voff);
+    load_r3<D>(ops0, rec, q, voff, g);
+    const uint2 v0 = load_vals(p, bos + C * cb, len_of(cb), h, D, vb, q, lane);
+    const int par = (int)(cb & 1);
+    publish_state(par);
+    *reinterpret_cast<uint2 *>(&sm.vv[par][16 * q + (lane >> 2)][4 * (lane & 3)]) = v0;
+  }
+  lds_barrier();
+
+  const int64_t HVD = (int64_t)p.HV * D;
+  const int nts = q < 2 ? 1 : 2;   // k steps of row block q's lower-triangular operands
+  auto chunk = [&](OPS &cur, OPS &nxt, int64_t c) {
+    const int par = (int)(c & 1);
+    const bool more = c + 1 < ce;
+    // The next chunk's loads go out in three groups spread over this chunk's
+    // products (a compute unit's vector memory path takes ~64 B per clock,
+    // so one burst of a whole record would stall the wave that issues it).
+    uint2 vnext = make_uint2(0, 0);
+    const __amdgpu_buffer_rsrc_t nrec = rec_of(more ? c + 1 : c);
+    if (more) {
+      if constexpr (DELTA) load_r1<D>(nxt, nrec, q, voff);
+      vnext = load_vals(p, bos + C * (c + 1), len_of(c + 1), h, D, vb, q, lane);
+    }
+
+    // ---- S^T as B fragments over key rows 32s .. 32s + 31 ----
+    Frag sf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) get_frag(sm.sfh[par][s], sm.sfl[par][s], lane, sf[s]);
+
+    // ---- Vb rows of block q: U = T' V, then + (-W) S^T (the record holds
+    //      -W); even and odd k steps in two accumulators ----
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DELTA) {
+      Frag vf[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s < nts) ldfrag_tr(&sm.vv[par][0][0], SM::VP, 4 * (r & 3), s, r, g, vf[s]);
+      f32x4 a0 = acc, a1 = acc;
+      a0 = mm<true, false>(cur.t[0], vf[0], a0);
+      if (nts > 1) a1 = mm<true, false>(cur.t[1], vf[1], a1);
+#pragma unroll
+      for (int s = 0; s < NS; s += 2) {
+#pragma unroll
+        for (int ps = 0; ps < 3; ++ps) {
+          if (ps == 0) { a0 = mm_pass<0, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<0, true, true>(cur.w[s + 1], sf[s + 1], a1); }
+          if (ps == 1) { a0 = mm_pass<1, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<1, true, true>(cur.w[s + 1], sf[s + 1], a1); }
+          if (ps == 2) { a0 = mm_pass<2, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<2, true, true>(cur.w[s + 1], sf[s + 1], a1); }
+        }
+      }
+      acc = a0 + a1;
+    } else {
+      // linear rule: Vb = V, read in the accumulator layout (row 16q + 4g + i)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = bf16_to_f32(sm.vv[par][16 * q + 4 * g + i][r]);
+    }
+    put_half(sm.vbh[par][q >> 1], sm.vbl[par][q >> 1], lane, q & 1, acc);
+    if (more) load_r2<D>(nxt, nrec, q, voff);
+    lds_barrier();
+
+    // ---- Vb as B fragments over tokens 32s .. 32s + 31 ----
+    Frag vbf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) get_frag(sm.vbh[par][s], sm.vbl[par][s], lane, vbf[s]);
+
+    // ---- outputs of row block q: O = Q^ S^T + A^ Vb ----
+    {
+      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+#pragma unroll
+      for (int s = 0; s < NS; s += 2) {
+        o0 = mm_pass<0, true, true>(cur.qh[s], sf[s], o0);
+        o1 = mm_pass<0, true, true>(cur.qh[s + 1], sf[s + 1], o1);
+        o0 = mm_pass<1, true, true>(cur.qh[s], sf[s], o0);
+        o1 = mm_pass<1, true, true>(cur.qh[s + 1], sf[s + 1], o1);
+        o0 = mm_pass<2, true, true>(cur.qh[s], sf[s], o0);
+        o1 = mm_pass<2, true, true>(cur.qh[s + 1], sf[s + 1], o1);
+      }
+      o0 = mm<true, true>(cur.a[0], vbf[0], o0);
+      if (nts > 1) o1 = mm<true, true>(cur.a[1], vbf[1], o1);
+      const f32x4 oa = o0 + o1;
+      // buffer stores against a descriptor over this chunk's L output rows:
+      // rows past a partial chunk's end fall outside it and are dropped
+      const int64_t t0 = bos + C * c;
+      const int L = len_of(c);
       const uint32_t osz = p.out_bf16 ? 2u : 4u;
       const uint32_t orow = (uint32_t)HVD * osz;
       char *obase = static_cast<char *>(p.o) + (t0 * HVD + (int64_t)h * D) * osz;
       const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)(L * orow), 0x00020000);
-      const uint32_t olane = (uint32_t)(4 * g) * orow + (uint32_t)col * osz;
+      const uint32_t olane = (uint32_t)(16 * q + 4 * g) * orow + (uint32_t)col * osz;
       if (!p.out_bf16) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[I][e]), ors, olane,
-                                                  (16 * I + e) * (int)orow, 0);
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[e]), ors, olane, e * (int)orow, 0);
       } else {
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][e]), ors, olane,
-                                                  (16 * I + e) * (int)orow, 0);
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[e]), ors, olane, e * (int)orow, 0);
       }
     }
-    return;
-  }
 
-  // ================= chain waves =================
-  f32x4 st[NT];   // st[m][e] = S^T[16m + 4g + e][col]
-  if (cb == 0) {
+    if (more) load_r3<D>(nxt, nrec, q, voff, g);
+
+    // ---- this wave's key rows: S^T <- gamma (.) S^T + K_end^T Vb ----
 #pragma unroll
-    for (int m = 0; m < NT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!p.zero_init) {
+    for (int t = 0; t < KT; ++t) {
+      st[t][0] *= cur.gam[t].x;
+      st[t][1] *= cur.gam[t].y;
+      st[t][2] *= cur.gam[t].z;
+      st[t][3] *= cur.gam[t].w;
+    }
 #pragma unroll
-      for (int m = 0; m < NT; ++m)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t idx = pbase + (int64_t)(16 * m + 4 * g + e) * D;
-          st[m][e] = p.st_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(p.pool)[idx])
-                               : static_cast<const float *>(p.pool)[idx];
+      for (int ps = 0; ps < 3; ++ps)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          if (ps == 0) st[t] = mm_pass<0, true, true>(cur.ke[t][s], vbf[s], st[t]);
+          if (ps == 1) st[t] = mm_pass<1, true, true>(cur.ke[t][s], vbf[s], st[t]);
+          if (ps == 2) st[t] = mm_pass<2, true, true>(cur.ke[t][s], vbf[s], st[t]);
         }
-    }
-  } else {
-    const float *cp = p.carry + ((int64_t)n * p.HV + h) * (int64_t)(D * D) + col;
-#pragma unroll
-    for (int m = 0; m < NT; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[m][e] = cp[(16 * m + 4 * g + e) * D];
-  }
 
-  for (int64_t c = cb; c < ce; ++c) {
-    const int k = (int)(c - cb);
-
-    // S^T as B fragments over key rows 32s .. 32s + 31, also handed to the
-    // output wave once it has read the previous chunk's
-    Frag sf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) chainfrag(st[2 * s], st[2 * s + 1], sf[s]);
-    spin_until(&sm.xfree[pw], k);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) st_frag(xs, 2048 * s, lane, sf[s]);
-
-    // ---- region 1: Vb = U + (-W) S^T with U = T' V (the record holds -W) ----
-    // Each block of products issues one LDS read of the next block's
-    // fragments after each MFMA (interleave), so reads and products overlap.
-    spin_until(&sm.ready[0], NLW * (k + 1));
-    f32x4 acc[4];
-    if constexpr (!DELTA) {
-      // linear rule: Vb = V, read in the accumulator layout (row 16I + 4g + i)
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[I][i] = bf16_to_f32(sm.vv[16 * I + 4 * g + i][16 * pw + r]);
-    } else {
-      Frag vf[2], ta[6], wf[2][4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) ldfrag_tr(&sm.vv[0][0], SM::VP, 16 * pw + 4 * (r & 3), s, r, g, vf[s]);
-#pragma unroll
-      for (int pr = 0; pr < 6; ++pr) ld_frag(sm.rec, RC::tp(pr), lane, ta[pr]);
-      __builtin_amdgcn_sched_barrier(0);
-      // U = T' V: four accumulators (T' split, V exact)
-#pragma unroll
-      for (int I = 0; I < 4; ++I) ld_frag(sm.rec, RC::wq(I, 0), lane, wf[0][I]);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[0] = mpass<0, false>(ta[0], vf[0], acc[0]);
-      acc[1] = mpass<0, false>(ta[1], vf[0], acc[1]);
-      acc[2] = mpass<0, false>(ta[2], vf[0], acc[2]);
-      acc[3] = mpass<0, false>(ta[4], vf[0], acc[3]);
-      acc[0] = mpass<2, false>(ta[0], vf[0], acc[0]);
-      acc[1] = mpass<2, false>(ta[1], vf[0], acc[1]);
-      acc[2] = mpass<2, false>(ta[2], vf[0], acc[2]);
-      acc[3] = mpass<2, false>(ta[4], vf[0], acc[3]);
-      acc[2] = mpass<0, false>(ta[3], vf[1], acc[2]);
-      acc[3] = mpass<0, false>(ta[5], vf[1], acc[3]);
-      acc[2] = mpass<2, false>(ta[3], vf[1], acc[2]);
-      acc[3] = mpass<2, false>(ta[5], vf[1], acc[3]);
-      interleave<8, 0, 1>();
-      __builtin_amdgcn_sched_barrier(0);
-      // + (-W) S^T, k step by k step
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) {
-#pragma unroll
-          for (int I = 0; I < 4; ++I) ld_frag(sm.rec, RC::wq(I, s + 1), lane, wf[(s + 1) & 1][I]);
-        }
-#pragma unroll
-        for (int I = 0; I < 4; ++I) acc[I] = mpass<0>(wf[s & 1][I], sf[s], acc[I]);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) acc[I] = mpass<1>(wf[s & 1][I], sf[s], acc[I]);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) acc[I] = mpass<2>(wf[s & 1][I], sf[s], acc[I]);
-        if (s + 1 < NS) interleave<8, 0, 1>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    count_in(&sm.freed[0], lane);
-
-    // Vb to the output wave
-    Frag vbf[2];
-    chainfrag(acc[0], acc[1], vbf[0]);
-    chainfrag(acc[2], acc[3], vbf[1]);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) st_frag(xs, 2048 * (NS + s), lane, vbf[s]);
-    count_in(&sm.xready[pw], lane);
-
-    // ---- region 3: S^T <- gamma (.) S^T + K_end^T Vb, in blocks of four key
-    //      tiles and one k step (four independent accumulators), the next
-    //      block's fragments in flight ----
-    spin_until(&sm.ready[2], NLW * (k + 1));
-    {
-      const float *gam = reinterpret_cast<const float *>(sm.rec + RC::GAM);
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * m + 4 * g);
-        st[m][0] *= gm.x;
-        st[m][1] *= gm.y;
-        st[m][2] *= gm.z;
-        st[m][3] *= gm.w;
-      }
-      constexpr int NB = NT / 4 * 2;   // blocks (key tile group, k step)
-      Frag kf[2][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ld_frag(sm.rec, RC::kf(j, 0), lane, kf[0][j]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bk = 0; bk < NB; ++bk) {
-        const int mg = bk >> 1, s = bk & 1;
-        if (bk + 1 < NB) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            ld_frag(sm.rec, RC::kf(4 * ((bk + 1) >> 1) + j, (bk + 1) & 1), lane, kf[(bk + 1) & 1][j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[4 * mg + j] = mpass<0>(kf[bk & 1][j], vbf[s], st[4 * mg + j]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[4 * mg + j] = mpass<1>(kf[bk & 1][j], vbf[s], st[4 * mg + j]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[4 * mg + j] = mpass<2>(kf[bk & 1][j], vbf[s], st[4 * mg + j]);
-        if (bk + 1 < NB) interleave<8, 0, 1>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    count_in(&sm.freed[2], lane);
+    // ---- publish the next chunk's state fragments and values ----
+    publish_state(par ^ 1);
+    if (more) *reinterpret_cast<uint2 *>(&sm.vv[par ^ 1][16 * q + (lane >> 2)][4 * (lane & 3)]) = vnext;
+    lds_barrier();
+  };
+  for (int64_t c = cb; c < ce; c += 2) {
+    chunk(ops0, ops1, c);
+    if (c + 1 < ce) chunk(ops1, ops0, c + 1);
   }
 
   // ---- state out: the pool at the sequence's end, else the carry ----
-  if (ce == nc) {
-    if (p.st_bf16) {
-      uint16_t *sp = static_cast<uint16_t *>(p.pool) + pbase;
 #pragma unroll
-      for (int m = 0; m < NT; ++m)
+  for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sp[(16 * m + 4 * g + e) * D] = f32_to_bf16(st[m][e]);
-    } else {
-      float *sp = static_cast<float *>(p.pool) + pbase;
-#pragma unroll
-      for (int m = 0; m < NT; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sp[(16 * m + 4 * g + e) * D] = st[m][e];
+    for (int e = 0; e < 4; ++e) {
+      const int64_t kr = key_row(t, e);
+      if (ce == nc) {
+        const int64_t idx = pbase + kr * D;
+        if (p.st_bf16) static_cast<uint16_t *>(p.pool)[idx] = f32_to_bf16(st[t][e]);
+        else static_cast<float *>(p.pool)[idx] = st[t][e];
+      } else {
+        p.carry[((int64_t)n * p.HV + h) * (int64_t)(D * D) + kr * D + col] = st[t][e];
+      }
     }
-  } else {
-    float *cp = p.carry + ((int64_t)n * p.HV + h) * (int64_t)(D * D) + col;
-#pragma unroll
-    for (int m = 0; m < NT; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cp[(16 * m + 4 * g + e) * D] = st[m][e];
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1191,10 +1093,10 @@ int64_t flat_chunks(const gdr_args &a) { return (a.T_total + C - 1) / C + a.N; }
 // kernel reads them.
 constexpr size_t kSliceRecordBytes = (size_t)192 << 20;
 
-template <int D, int NSW>
+template <int D>
 hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStream_t stream) {
   const int cus = cu_count();
-  const int grp = D / (16 * NSW);
+  const int grp = D / 16;
   const int sblocks = ((p0.N * p0.HV + 7) / 8) * 8 * grp;
   for (int64_t F0 = 0; F0 < flat; F0 += per) {
     KdaParams p = p0;
@@ -1207,11 +1109,9 @@ hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStre
     else
       hipLaunchKernelGGL((kda_prep_kernel<D, false>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
     if (p.delta)
-      hipLaunchKernelGGL((kda_state_kernel<D, NSW, true>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0,
-                         stream, p);
+      hipLaunchKernelGGL((kda_state_kernel<D, true>), dim3(sblocks), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((kda_state_kernel<D, NSW, false>), dim3(sblocks), dim3(64 * (2 * NSW + NLW + NLO)), 0,
-                         stream, p);
+      hipLaunchKernelGGL((kda_state_kernel<D, false>), dim3(sblocks), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -1259,12 +1159,12 @@ hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hi
   int64_t per = (int64_t)((ws_bytes - cb) / row);
   if (per > flat) per = flat;
   p.F0 = p.F1 = 0;
-  // 16 value columns per workgroup: each workgroup reads the whole record of
-  // every chunk, so narrow ones spread that LDS traffic over many compute
-  // units (a batch with more (sequence, head) pairs than fit at once runs in
-  // more than one round of workgroups).
-  if (a.DK == 128) return launch_slices<128, 1>(p, flat, per, stream);
-  return launch_slices<64, 1>(p, flat, per, stream);
+  // 16 value columns per workgroup: the record's fragments are read by every
+  // workgroup of a (sequence, head) from the L2 they share; narrow workgroups
+  // spread that traffic over many compute units (a batch with more (sequence,
+  // head) pairs than fit at once runs in more than one round of workgroups).
+  if (a.DK == 128) return launch_slices<128>(p, flat, per, stream);
+  return launch_slices<64>(p, flat, per, stream);
 }
 
 }  // namespace gdr
