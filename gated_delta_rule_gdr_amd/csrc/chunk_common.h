@@ -66,6 +66,7 @@ struct ChunkParams {
   int zero_init, st_bf16, out_bf16;
   int32_t P;   // transitions per token (Gated DeltaProduct substeps); 1 otherwise
   int32_t rev; // walk each sequence's rows backwards (warp-specialised kernel only)
+  int32_t lc;  // tokens per chunk, 16, 32 or 64 (the general kernel; the others take 64)
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {

@@ -380,12 +380,17 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const LaneOffsets lo = lane_offsets<IN_F32, D>();
   if constexpr (GATE != GDR_GATE_CHANNEL) {
     if (bos < eos)
-      load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, bos, (int)min<int64_t>(C, eos - bos), h, hk, vb);
+      load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, bos, (int)min<int64_t>(p.lc, eos - bos), h, hk, vb);
   }
 
+  // Chunks of LC = 16, 32 or 64 tokens: a shorter chunk runs in the 64-row
+  // tile with its rows past LC zero, the same path as a sequence's last,
+  // partial chunk (the state is carried every LC tokens, which is the
+  // chunked algorithm at that chunk length).
+  const int LC = p.lc;
   const int64_t HVD = (int64_t)p.HV * D;
-  for (int64_t t0 = bos; t0 < eos; t0 += C) {
-    const int L = (int)((eos - t0) < C ? (eos - t0) : C);
+  for (int64_t t0 = bos; t0 < eos; t0 += LC) {
+    const int L = (int)((eos - t0) < LC ? (eos - t0) : LC);
 
     // ================= phase 0: inputs into LDS =================
     if constexpr (GATE != GDR_GATE_CHANNEL) {
@@ -423,8 +428,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         sm.beta[lane] = ok ? pf.beta : 0.f;
       }
       // next chunk's loads stay in flight while this one computes
-      if (t0 + C < eos)
-        load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, t0 + C, (int)min<int64_t>(C, eos - t0 - C), h,
+      if (t0 + LC < eos)
+        load_chunk<IN_F32, GATE, DELTA, D>(pf, p, lo, t0 + LC, (int)min<int64_t>(LC, eos - t0 - LC), h,
                                            hk, vb);
       __syncthreads();
       // transposed keys for the state update (read only at the end of the chunk)
@@ -839,8 +844,8 @@ bool prefill_force_generic() {
 hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   // bf16 inputs without a channel gate take the warp-specialised kernel;
   // GDR_PREFILL_KERNEL=generic selects this file's kernel for every case
-  // (used to compare them).
-  if (!prefill_force_generic() && a.in_dtype == GDR_BF16 && a.gate != GDR_GATE_CHANNEL)
+  // (used to compare them). Chunks of 16 or 32 tokens are this file's kernel.
+  if (!prefill_force_generic() && a.in_dtype == GDR_BF16 && a.gate != GDR_GATE_CHANNEL && a.chunk_size == 64)
     return launch_chunk_fwd_ws(a, stream);
   ChunkParams p;
   p.q = a.q; p.k = a.k; p.v = a.v;
@@ -854,6 +859,7 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   p.out_bf16 = a.out_dtype == GDR_BF16;
   p.P = products_of(a);
   p.rev = 0;   // (the reversed walk is the warp-specialised kernel's)
+  p.lc = a.chunk_size;
   if (a.in_dtype == GDR_BF16) return by_gate<false>(a, p, stream);
   return by_gate<true>(a, p, stream);
 }

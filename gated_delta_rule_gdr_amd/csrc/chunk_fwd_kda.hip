@@ -1123,7 +1123,7 @@ hipError_t kda_wait_flag(int *out, bool clear, hipStream_t stream) {
 }
 
 bool chunk_fwd_kda_applies(const gdr_args &a) {
-  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && products_of(a) == 1;
+  return a.in_dtype == GDR_BF16 && a.gate == GDR_GATE_CHANNEL && products_of(a) == 1 && a.chunk_size == 64;
 }
 
 size_t chunk_fwd_kda_min_workspace(const gdr_args &a) {

@@ -611,6 +611,25 @@ __device__ __forceinline__ void chunk_prep_role(const ChunkParams &p, SmemWS<D, 
 // GDP as GDN over a virtual sequence) and keeps each token's last output.
 // REV: each sequence's rows walked backwards (its last row first); the
 // gradients of linear attention run the forward pass this way.
+// The sequence of rank `rank` when the batch is ordered longest first (ties
+// by index), for batches of at most 64 sequences (lane i ranks sequence i
+// against all others); larger batches keep their own order. Workgroups are
+// dispatched roughly in index order and a ragged batch runs in several
+// rounds of workgroups, so starting the longest sequences first shortens the
+// tail. Called by whole waves.
+__device__ __forceinline__ int longest_first(const int32_t *cu, int N, int rank) {
+  if (N > 64) return rank;
+  const int lane = threadIdx.x & 63;
+  const int len = lane < N ? cu[lane + 1] - cu[lane] : -1;
+  int above = 0;
+  for (int i = 0; i < N; ++i) {
+    const int li = scalar_load(cu + i + 1) - scalar_load(cu + i);
+    above += (li > len || (li == len && i < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < N && above == rank);
+  return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+}
+
 template <int GATE, bool DELTA, int D, int NSW, bool PROD, bool REV>
 __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_kernel(ChunkParams p) {
   constexpr int NP = prep_waves<NSW>();
@@ -623,14 +642,16 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   constexpr int PK = SM::PK, PT = SM::PT;
   __shared__ SM sm;
 
-  // XCD-aware decomposition (see chunk_fwd.hip)
+  // XCD-aware decomposition (see chunk_fwd.hip); the sequences in
+  // longest-first order
   const int GRP = p.ratio * NB;
   const int b = blockIdx.x;
   const int gi = (b / (8 * GRP)) * 8 + (b & 7);
   if (gi >= p.N * p.HK) return;
   const int j = (b >> 3) % GRP;
-  const int n = gi / p.HK;
-  const int hk = gi - n * p.HK;
+  const int rank = gi / p.HK;
+  const int hk = gi - rank * p.HK;
+  const int n = longest_first(p.cu_seqlens, p.N, rank);
   const int h = hk * p.ratio + j / NB;
   const int vb = j % NB;
 
@@ -1124,6 +1145,7 @@ hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {
   p.out_bf16 = a.out_dtype == GDR_BF16;
   p.P = products_of(a);
   p.rev = (a.flags & kFlagReverse) ? 1 : 0;
+  p.lc = 64;
   if (a.gate == GDR_GATE_SCALAR) return ws_by_rule<GDR_GATE_SCALAR>(a, p, stream);
   return ws_by_rule<GDR_GATE_NONE>(a, p, stream);
 }

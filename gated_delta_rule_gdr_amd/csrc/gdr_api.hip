@@ -75,8 +75,8 @@ gdr_status validate(const gdr_args *a, Call call) {
   if (!prefill && a->T_total != a->N)
     return fail(GDR_E_INVALID, "recurrent step needs one token per sequence (T_total = %lld, N = %d)",
                 (long long)a->T_total, a->N);
-  if (call == Call::Chunk && a->chunk_size != 64)
-    return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: built for 64", a->chunk_size);
+  if (call == Call::Chunk && a->chunk_size != 16 && a->chunk_size != 32 && a->chunk_size != 64)
+    return fail(GDR_E_UNSUPPORTED, "chunk_size = %d: 16, 32 or 64 tokens", a->chunk_size);
   if (a->N == 0) return GDR_OK;  // nothing to do; pointers may be NULL
 
   if (!a->state_pool || !a->slot_idx) return fail(GDR_E_INVALID, "state_pool / slot_idx is NULL");

@@ -140,6 +140,7 @@ hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void
     b.o = o;
     b.state_pool = aux; b.state_dtype = GDR_F32; b.num_slots = a.N; b.slot_idx = slots;
     b.rule = GDR_RULE_LINEAR; b.gate = GDR_GATE_NONE; b.products = 1;
+    b.chunk_size = 64;
     b.flags = (zero ? GDR_FLAG_ZERO_INIT : 0u) | (rev ? kFlagReverse : 0u);
     return launch_chunk_fwd(b, stream);
   };

@@ -127,7 +127,7 @@ typedef struct gdr_args {
   int32_t DK, DV;               /* head dims, each 64 or 128                               */
   int64_t T_total;              /* tokens in q/k/v/o (the step requires T_total == N)      */
   float scale;                  /* query scale; callers normally pass DK^-1/2              */
-  int32_t chunk_size;           /* prefill tile length in tokens: 64                       */
+  int32_t chunk_size;           /* gdr_chunk_fwd: tokens per chunk, 16, 32 or 64           */
   gdr_rule rule;
   gdr_gate gate;
   uint32_t flags;               /* GDR_FLAG_*                                              */
@@ -147,7 +147,7 @@ int gdr_abi_version(void);
  * arguments that fail validation.
  *
  * Only the channel gate with bf16 inputs (KDA's delta rule or GLA's linear
- * rule, one transition per token) uses a workspace:
+ * rule, one transition per token) at chunk_size 64 uses a workspace:
  * it runs as a parallel per-chunk kernel that writes one record per (chunk,
  * value head) (the decayed keys and queries, the inverse of the chunk's unit
  * lower triangular system and the products the state recurrence needs; the
@@ -163,7 +163,13 @@ size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a);
 /* Chunkwise prefill over the ragged batch described by cu_seqlens: writes o
  * for every token and the final state of each sequence into its pool slot.
  * Zero-length sequences write their (initial) state back unchanged. N == 0 is
- * a no-op. `workspace` (device memory, 256-byte aligned, contents need not be
+ * a no-op. chunk_size is the chunk length C of the chunked algorithm ("From
+ * Attention to Learned Memory", section 4, which takes 16, 32 or 64): the
+ * results are the same recurrence whatever C, up to rounding. 64 runs the
+ * tuned kernels; 16 and 32 run the general kernel with each chunk in a
+ * 64-row tile whose rows past C are zero (as for a sequence's last, partial
+ * chunk), at the cost per chunk of a 64-token one. Other values return
+ * GDR_E_UNSUPPORTED. `workspace` (device memory, 256-byte aligned, contents need not be
  * initialised and are garbage afterwards) may be NULL when the call needs
  * none; a call that needs one and gets less than its minimum returns
  * GDR_E_WORKSPACE before enqueuing anything. Calls that share a workspace

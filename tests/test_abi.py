@@ -84,7 +84,7 @@ CASES = [
     ("HV % HK", dict(HV=3), 1),
     ("bad head dim", dict(DK=96, DV=96), 2),
     ("DK != DV", dict(DV=64), 2),
-    ("chunk size", dict(chunk_size=32), 2),
+    ("chunk size", dict(chunk_size=48), 2),
     ("null beta (delta)", dict(beta=None), 1),
     ("null g (gated)", dict(g=None), 1),
     ("null q", dict(q=None), 1),

@@ -56,6 +56,36 @@ def test_chunk_fwd_matches_oracle(D, in_dtype, gate, rule):
     assert torch.equal(d["pool"][untouched], pool_before[untouched])
 
 
+CHUNK_SIZE_COMBOS = [(16, 64, "bf16", "scalar", "delta"), (16, 128, "f32", "channel", "delta"),
+                     (16, 128, "bf16", "channel", "linear"), (16, 128, "bf16", "none", "linear"),
+                     (32, 128, "bf16", "none", "delta"), (32, 64, "f32", "scalar", "linear"),
+                     (32, 128, "bf16", "channel", "delta"), (32, 128, "bf16", "scalar", "delta")]
+
+
+@pytest.mark.parametrize("C,D,in_dtype,gate,rule", CHUNK_SIZE_COMBOS,
+                         ids=[f"c{c}-d{d}-{i}-{g}-{r}" for c, d, i, g, r in CHUNK_SIZE_COMBOS])
+def test_chunk_sizes_16_and_32(C, D, in_dtype, gate, rule):
+    """chunk_size 16 and 32 (the chunk lengths section 4 of "From Attention to
+    Learned Memory" takes beside 64) compute the same recurrence: ragged
+    sequences spanning several chunks of that length, ending in partial ones,
+    match the oracle."""
+    gdr = _gdr()
+    state_dtype = "bf16" if (D == 128 and gate == "scalar") else "f32"
+    w = small_workload(D, in_dtype, gate, rule, state_dtype, zero_init=False, seqlens=RAGGED)
+    x = synth.generate(w)
+    d = to_device(w, x)
+    scale = D ** -0.5
+    print(f"chunk_fwd C={C} D={D} in={in_dtype} gate={gate} rule={rule} lens={RAGGED}", flush=True)
+    o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                      d["cu_seqlens"], scale=scale, rule=rule, gate=gate, chunk_size=C)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], scale)
+    check_out(host(o, in_dtype), o_ref, in_dtype)
+    pool = host(d["pool"], state_dtype)
+    for s in x["slot_idx"]:
+        check_state(pool[s], pool_ref[s], in_dtype, state_dtype)
+
+
 @pytest.mark.parametrize("zero_init", [True, False])
 def test_chunk_fwd_zero_init_and_bf16_output(zero_init):
     gdr = _gdr()
