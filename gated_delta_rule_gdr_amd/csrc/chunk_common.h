@@ -84,9 +84,13 @@ struct Frag {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo) {
   const bf16x2 h = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-  hi = __builtin_bit_cast(uint32_t, h);
-  const bf16x2 l = {static_cast<__bf16>(x0 - __uint_as_float(hi << 16)),
-                    static_cast<__bf16>(x1 - __uint_as_float(hi & 0xffff0000u))};
+  uint32_t hw = __builtin_bit_cast(uint32_t, h);
+  // (the packed pair is made opaque: seen through, the compiler converts x0
+  // a second time to shift it into place, one more instruction per pair)
+  asm("" : "+v"(hw));
+  hi = hw;
+  const bf16x2 l = {static_cast<__bf16>(x0 - __uint_as_float(hw << 16)),
+                    static_cast<__bf16>(x1 - __uint_as_float(hw & 0xffff0000u))};
   lo = __builtin_bit_cast(uint32_t, l);
 }
 

@@ -836,7 +836,7 @@ __device__ __forceinline__ uint2 load_vals(const KdaParams &p, int64_t t0, int L
 // DELTA false: the linear rule (GLA), Vb = V; region 1 is neither written by
 // the prep kernel nor read here.
 template <int D, bool DELTA>
-__global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
+__global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
   using RC = KdaRec<D>;
   using SM = StateSmem<D>;
   using OPS = WaveOps<D>;
@@ -915,9 +915,12 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
   // (Barriers wait for LDS only, lds_barrier: the next chunk's operand loads
   // stay in flight across them.)
 
-  // Operands in two register sets used in turn: chunk c + 1's are loaded
-  // while chunk c's are multiplied.
-  OPS ops0, ops1;
+  // The record operands in one register set: each group of fragments is
+  // reloaded with chunk c + 1's right after chunk c's last use of it (W and
+  // T' after Vb, Q^ and A^ after the outputs, K_end and gamma after the
+  // update), so every load has about a chunk's time to land while the
+  // registers stay within what lets a prep workgroup share the compute unit.
+  OPS ops;
   // this wave's state tiles as halves of the split S^T fragments
   auto publish_state = [&](int par) {
 #pragma unroll
@@ -928,9 +931,9 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
   };
   {
     const __amdgpu_buffer_rsrc_t rec = rec_of(cb);
-    if constexpr (DELTA) load_r1<D>(ops0, rec, q, voff);
-    load_r2<D>(ops0, rec, q, voff);
-    load_r3<D>(ops0, rec, q, voff, g);
+    if constexpr (DELTA) load_r1<D>(ops, rec, q, voff);
+    load_r2<D>(ops, rec, q, voff);
+    load_r3<D>(ops, rec, q, voff, g);
     const uint2 v0 = load_vals(p, bos + C * cb, len_of(cb), h, D, vb, q, lane);
     const int par = (int)(cb & 1);
     publish_state(par);
@@ -940,18 +943,13 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
 
   const int64_t HVD = (int64_t)p.HV * D;
   const int nts = q < 2 ? 1 : 2;   // k steps of row block q's lower-triangular operands
-  auto chunk = [&](OPS &cur, OPS &nxt, int64_t c) {
+  auto chunk = [&](int64_t c) {
+    OPS &cur = ops;
     const int par = (int)(c & 1);
     const bool more = c + 1 < ce;
-    // The next chunk's loads go out in three groups spread over this chunk's
-    // products (a compute unit's vector memory path takes ~64 B per clock,
-    // so one burst of a whole record would stall the wave that issues it).
     uint2 vnext = make_uint2(0, 0);
     const __amdgpu_buffer_rsrc_t nrec = rec_of(more ? c + 1 : c);
-    if (more) {
-      if constexpr (DELTA) load_r1<D>(nxt, nrec, q, voff);
-      vnext = load_vals(p, bos + C * (c + 1), len_of(c + 1), h, D, vb, q, lane);
-    }
+    if (more) vnext = load_vals(p, bos + C * (c + 1), len_of(c + 1), h, D, vb, q, lane);
 
     // ---- S^T as B fragments over key rows 32s .. 32s + 31 ----
     Frag sf[NS];
@@ -985,7 +983,8 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
       for (int i = 0; i < 4; ++i) acc[i] = bf16_to_f32(sm.vv[par][16 * q + 4 * g + i][r]);
     }
     put_half(sm.vbh[par][q >> 1], sm.vbl[par][q >> 1], lane, q & 1, acc);
-    if (more) load_r2<D>(nxt, nrec, q, voff);
+    if constexpr (DELTA)
+      if (more) load_r1<D>(ops, nrec, q, voff);
     lds_barrier();
 
     // ---- Vb as B fragments over tokens 32s .. 32s + 31 ----
@@ -1028,7 +1027,7 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
       }
     }
 
-    if (more) load_r3<D>(nxt, nrec, q, voff, g);
+    if (more) load_r2<D>(ops, nrec, q, voff);
 
     // ---- this wave's key rows: S^T <- gamma (.) S^T + K_end^T Vb ----
 #pragma unroll
@@ -1049,15 +1048,14 @@ __global__ __launch_bounds__(256) void kda_state_kernel(KdaParams p) {
           if (ps == 2) st[t] = mm_pass<2, true, true>(cur.ke[t][s], vbf[s], st[t]);
         }
 
+    if (more) load_r3<D>(ops, nrec, q, voff, g);
+
     // ---- publish the next chunk's state fragments and values ----
     publish_state(par ^ 1);
     if (more) *reinterpret_cast<uint2 *>(&sm.vv[par ^ 1][16 * q + (lane >> 2)][4 * (lane & 3)]) = vnext;
     lds_barrier();
   };
-  for (int64_t c = cb; c < ce; c += 2) {
-    chunk(ops0, ops1, c);
-    if (c + 1 < ce) chunk(ops1, ops0, c + 1);
-  }
+  for (int64_t c = cb; c < ce; ++c) chunk(c);
 
   // ---- state out: the pool at the sequence's end, else the carry ----
 #pragma unroll
@@ -1088,30 +1086,46 @@ size_t carry_bytes(const gdr_args &a) {
 
 int64_t flat_chunks(const gdr_args &a) { return (a.T_total + C - 1) / C + a.N; }
 
-// Records per slice the preferred workspace holds: about 192 MB of them, so a
-// slice's records are still in the 256 MB last-level cache when the state
-// kernel reads them.
+// Records per slice the preferred workspace holds: about 192 MB of them.
 constexpr size_t kSliceRecordBytes = (size_t)192 << 20;
 
 template <int D>
+void launch_prep(const KdaParams &p, int64_t blocks, hipStream_t stream) {
+  if (p.delta)
+    hipLaunchKernelGGL((kda_prep_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kda_prep_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+}
+
+template <int D>
+void launch_state(const KdaParams &p, hipStream_t stream) {
+  const int blocks = ((p.N * p.HV + 7) / 8) * 8 * (D / 16);
+  if (p.delta)
+    hipLaunchKernelGGL((kda_state_kernel<D, true>), dim3(blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kda_state_kernel<D, false>), dim3(blocks), dim3(256), 0, stream, p);
+}
+
+KdaParams slice_of(const KdaParams &p0, int64_t F0, int64_t per, int64_t flat, char *rec) {
+  KdaParams p = p0;
+  p.F0 = F0;
+  p.F1 = F0 + per < flat ? F0 + per : flat;
+  p.rec = rec;
+  return p;
+}
+
+// Each slice: its prep launch (two workgroups per compute unit), then its
+// state launch. (Running the next slice's prep beside this slice's state
+// kernel, one workgroup of each per compute unit, was slower: each kernel
+// then took about twice as long.)
+template <int D>
 hipError_t launch_slices(const KdaParams &p0, int64_t flat, int64_t per, hipStream_t stream) {
-  const int cus = cu_count();
-  const int grp = D / 16;
-  const int sblocks = ((p0.N * p0.HV + 7) / 8) * 8 * grp;
+  const int64_t cap = 2 * (int64_t)cu_count();
   for (int64_t F0 = 0; F0 < flat; F0 += per) {
-    KdaParams p = p0;
-    p.F0 = F0;
-    p.F1 = F0 + per < flat ? F0 + per : flat;
+    const KdaParams p = slice_of(p0, F0, per, flat, p0.rec);
     const int64_t items = (p.F1 - p.F0) * p.HV;
-    const int64_t pblocks = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;   // two per compute unit
-    if (p.delta)
-      hipLaunchKernelGGL((kda_prep_kernel<D, true>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((kda_prep_kernel<D, false>), dim3((unsigned)pblocks), dim3(256), 0, stream, p);
-    if (p.delta)
-      hipLaunchKernelGGL((kda_state_kernel<D, true>), dim3(sblocks), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((kda_state_kernel<D, false>), dim3(sblocks), dim3(256), 0, stream, p);
+    launch_prep<D>(p, items < cap ? items : cap, stream);
+    launch_state<D>(p, stream);
   }
   return hipGetLastError();
 }
@@ -1156,13 +1170,12 @@ hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hi
   p.rec = static_cast<char *>(ws) + cb;
   const size_t row = record_bytes(a.DK) * (size_t)a.HV;
   const int64_t flat = flat_chunks(a);
+  p.F0 = p.F1 = 0;
+  // (16 value columns per state workgroup: the record's fragments are read
+  // by every workgroup of a (sequence, head) from the L2 they share; narrow
+  // workgroups spread that traffic over many compute units)
   int64_t per = (int64_t)((ws_bytes - cb) / row);
   if (per > flat) per = flat;
-  p.F0 = p.F1 = 0;
-  // 16 value columns per workgroup: the record's fragments are read by every
-  // workgroup of a (sequence, head) from the L2 they share; narrow workgroups
-  // spread that traffic over many compute units (a batch with more (sequence,
-  // head) pairs than fit at once runs in more than one round of workgroups).
   if (a.DK == 128) return launch_slices<128>(p, flat, per, stream);
   return launch_slices<64>(p, flat, per, stream);
 }

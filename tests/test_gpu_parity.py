@@ -167,15 +167,15 @@ def test_chunk_equals_repeated_steps(gate):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("rows", [1, 3])
+@pytest.mark.parametrize("rows", [1, 2, 3, 6])
 @pytest.mark.parametrize("rule", ["delta", "linear"])
 def test_channel_gate_slices(D, rows, rule):
     """The channel-gate prefill (bf16 inputs) passes per-chunk records through
     the workspace in slices of `rows` flat chunks; the state crosses slice
     boundaries through the workspace's fp32 carry. The result of a workspace
-    that holds 1 or 3 rows of records equals the oracle's, and equals the
-    result with the preferred workspace bit for bit. The linear rule (GLA)
-    takes the same records with T' = I and W = 0."""
+    that holds 1, 2, 3 or 6 rows of records equals the oracle's, and equals
+    the result with the preferred workspace (one slice here) bit for bit.
+    The linear rule (GLA) takes the same records with T' = I and W = 0."""
     gdr = _gdr()
     w = small_workload(D, "bf16", "channel", rule, "f32", zero_init=False,
                        seqlens=(130, 0, 64, 1, 200), seed=23)
