@@ -230,9 +230,12 @@ def chunk_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, chunk
               debug_checks=False, workspace=None, products=1):
     """Chunkwise prefill; returns o [T, HV, DV]; updates pool slots in place.
 
-    ``workspace`` is an optional uint8 device tensor for the calls that need
-    one (gdr_chunk_fwd_workspace_bytes > 0: the channel gate with bf16 inputs);
-    by default one of the preferred size is allocated from torch's allocator.
+    ``chunk_size`` is the chunk length, 16, 32 or 64 tokens (the same
+    recurrence up to rounding; 64 runs the tuned kernels). ``workspace`` is an
+    optional uint8 device tensor for the calls that need one
+    (gdr_chunk_fwd_workspace_bytes > 0: the channel gate with bf16 inputs at
+    chunk_size 64); by default one of the preferred size is allocated from
+    torch's allocator.
     """
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
