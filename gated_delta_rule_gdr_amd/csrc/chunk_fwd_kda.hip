@@ -56,6 +56,7 @@
 // is k = 4g + j for j < 4 and 16 + 4g + (j - 4) otherwise. A record fragment
 // is 2 KB: the hi plane (64 lanes x 16 bytes, lane-major) then the lo plane.
 #include <cstdint>
+#include <numeric>
 
 #include "chunk_common.h"
 
@@ -1086,8 +1087,26 @@ size_t carry_bytes(const gdr_args &a) {
 
 int64_t flat_chunks(const gdr_args &a) { return (a.T_total + C - 1) / C + a.N; }
 
-// Records per slice the preferred workspace holds: about 192 MB of them.
-constexpr size_t kSliceRecordBytes = (size_t)192 << 20;
+// Records per slice, at most: about 128 MB for the delta rule, 192 MB for
+// the linear rule (whose prep kernel is lighter). On the 131072-token,
+// 32-head KDA call, slices of 16, 32, 48 and 64 chunk rows (60 to 240 MB)
+// took 7.9, 7.3, 7.4 and 8.8 ms: larger slices find fewer of their records
+// still in the 256 MB last-level cache when the state kernel reads them,
+// smaller ones pay more per-slice launch and drain. GLA took 5.7 ms with 48
+// rows and 5.9 ms with 32.
+size_t slice_record_bytes(const gdr_args &a) {
+  return (size_t)(a.rule == GDR_RULE_DELTA ? 128 : 192) << 20;
+}
+
+int64_t slice_rows(const gdr_args &a) {
+  const size_t row = record_bytes(a.DK) * (size_t)a.HV;
+  int64_t per = (int64_t)(slice_record_bytes(a) / row);
+  if (per < 1) per = 1;
+  const int64_t wg = 2 * (int64_t)cu_count();
+  const int64_t q = wg / std::gcd(wg, (int64_t)a.HV);
+  if (per >= q) per = per / q * q;
+  return per;
+}
 
 template <int D>
 void launch_prep(const KdaParams &p, int64_t blocks, hipStream_t stream) {
@@ -1146,8 +1165,7 @@ size_t chunk_fwd_kda_min_workspace(const gdr_args &a) {
 
 size_t chunk_fwd_kda_workspace(const gdr_args &a) {
   const size_t row = record_bytes(a.DK) * (size_t)a.HV;   // one flat chunk of every head
-  int64_t per = (int64_t)(kSliceRecordBytes / row);
-  if (per < 1) per = 1;
+  int64_t per = slice_rows(a);
   const int64_t flat = flat_chunks(a);
   if (per > flat) per = flat;
   return carry_bytes(a) + row * (size_t)per;
@@ -1175,6 +1193,8 @@ hipError_t launch_chunk_fwd_kda(const gdr_args &a, void *ws, size_t ws_bytes, hi
   // by every workgroup of a (sequence, head) from the L2 they share; narrow
   // workgroups spread that traffic over many compute units)
   int64_t per = (int64_t)((ws_bytes - cb) / row);
+  const int64_t cap = slice_rows(a);   // (a larger workspace does not make larger slices)
+  if (per > cap) per = cap;
   if (per > flat) per = flat;
   if (a.DK == 128) return launch_slices<128>(p, flat, per, stream);
   return launch_slices<64>(p, flat, per, stream);

@@ -156,8 +156,9 @@ int gdr_abi_version(void);
  * N * HV * DK * DV values plus records for a slice of flat chunks; the call
  * runs as many slices as it needs, so any size from the carry plus one
  * chunk's records for every value head (HV * 123392 bytes at DK = 128,
- * HV * 73984 at DK = 64) up works, a larger one with fewer launches. The
- * preferred size keeps a slice's records within the 256 MB last-level cache. */
+ * HV * 73984 at DK = 64) up works. The preferred size holds up to about
+ * 128 MB (KDA) or 192 MB (GLA) of records per slice, the fastest measured;
+ * a larger workspace makes no larger slices. */
 size_t gdr_chunk_fwd_workspace_bytes(const gdr_args *a);
 
 /* Chunkwise prefill over the ragged batch described by cu_seqlens: writes o
