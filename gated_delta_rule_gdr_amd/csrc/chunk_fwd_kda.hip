@@ -39,10 +39,10 @@
 //     head, 16 value columns) walks the slice's chunks in order: wave q
 //     holds the key rows q DK/4 .. (q+1) DK/4 - 1 of S^T[DK, 16] in MFMA
 //     accumulators and forms the Vb and output rows 16q .. 16q+15; each wave
-//     loads the record fragments it multiplies straight into registers (two
-//     register sets, the next chunk's loads in flight while this chunk is
-//     multiplied), and LDS carries only the state and Vb fragments every
-//     wave reads whole, with two LDS-only barriers per chunk.
+//     loads the record fragments it multiplies straight into registers (one
+//     set, each group reloaded with the next chunk's right after its last
+//     use), and LDS carries only the state and Vb fragments every wave reads
+//     whole, with two LDS-only barriers per chunk.
 // A sequence's state crosses slice boundaries through an fp32 carry area of
 // the workspace. The workspace is sized by the caller: a larger one means
 // fewer, longer slices.
@@ -737,12 +737,12 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
 // Wave q owns the chunk's token rows 16q .. 16q+15 (U, Vb and the outputs of
 // those rows) and the key rows q D/4 .. (q+1) D/4 - 1 of S^T (their state and
 // its update). Each wave loads the record fragments it multiplies straight
-// from the workspace into registers (two sets used in turn, chunk c + 1's
-// loaded while chunk c's are multiplied), so the record never passes through
-// LDS; LDS carries only what the waves exchange: the state's tiles (every
-// wave reads S^T whole), the Vb tiles (every wave reads Vb whole) and the
-// values, double-buffered by chunk parity, with two barriers per chunk that
-// wait for LDS only.
+// from the workspace into registers (one set, each group of fragments
+// reloaded with chunk c + 1's right after chunk c's last use of it), so the
+// record never passes through LDS; LDS carries only what the waves exchange:
+// the state's tiles (every wave reads S^T whole), the Vb tiles (every wave
+// reads Vb whole) and the values, double-buffered by chunk parity, with two
+// barriers per chunk that wait for LDS only.
 template <int D>
 struct StateSmem {
   static constexpr int NS = D / 32;
@@ -790,22 +790,29 @@ struct WaveOps {
   float4 gam[KT];   // gamma of the lane's four key rows in each of those tiles
 };
 
+// voff2 is the lane offset for the second k step of the lower-triangular
+// operands: voff for row blocks 2 and 3, beyond the record for blocks 0 and 1
+// (whose fragment is zero), so that such a load returns zeros and reads
+// nothing. Every wave then issues the same loads and the compiler's wait
+// counts stay exact.
 template <int D>
-__device__ __forceinline__ void load_r1(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff) {
+__device__ __forceinline__ void load_r1(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff,
+                                        uint32_t voff2) {
   using RC = KdaRec<D>;
 #pragma unroll
   for (int s = 0; s < RC::NS; ++s) buf_frag(rs, voff, RC::R1 + RC::wq(q, s), o.w[s]);
   buf_frag(rs, voff, RC::tp(pair_index(q, 0)), o.t[0]);
-  if (q >= 2) buf_frag(rs, voff, RC::tp(pair_index(q, 1)), o.t[1]);
+  buf_frag(rs, voff2, RC::tp(pair_index(max(q, 2), 1)), o.t[1]);
 }
 
 template <int D>
-__device__ __forceinline__ void load_r2(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff) {
+__device__ __forceinline__ void load_r2(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs, int q, uint32_t voff,
+                                        uint32_t voff2) {
   using RC = KdaRec<D>;
 #pragma unroll
   for (int s = 0; s < RC::NS; ++s) buf_frag(rs, voff, RC::R2 + RC::wq(q, s), o.qh[s]);
   buf_frag(rs, voff, RC::R2 + RC::tp(pair_index(q, 0)), o.a[0]);
-  if (q >= 2) buf_frag(rs, voff, RC::R2 + RC::tp(pair_index(q, 1)), o.a[1]);
+  buf_frag(rs, voff2, RC::R2 + RC::tp(pair_index(max(q, 2), 1)), o.a[1]);
 }
 
 template <int D>
@@ -824,14 +831,17 @@ __device__ __forceinline__ void load_r3(WaveOps<D> &o, __amdgpu_buffer_rsrc_t rs
 }
 
 // Values of the chunk starting at token t0 (L rows): wave q's 16 rows of the
-// workgroup's 16 columns, 8 bytes per lane (zeros past the chunk's end).
-__device__ __forceinline__ uint2 load_vals(const KdaParams &p, int64_t t0, int L, int h, int D, int vb, int q,
-                                           int lane) {
-  const int row = 16 * q + (lane >> 2);
-  const int64_t tr = t0 + min(row, L - 1);
-  const uint16_t *src = static_cast<const uint16_t *>(p.v) + tr * p.v_stride + (int64_t)h * D + 16 * vb + 4 * (lane & 3);
-  const uint2 x = *reinterpret_cast<const uint2 *>(src);
-  return row < L ? x : make_uint2(0, 0);
+// workgroup's 16 columns, 8 bytes per lane, through a buffer descriptor over
+// the chunk's L rows of this head's columns: rows past the chunk's end fall
+// outside it and read as zeros. vlane = row x (row pitch in bytes) + 8 (lane
+// mod 4), the same for every chunk.
+__device__ __forceinline__ uint2 load_vals(const KdaParams &p, int64_t t0, int L, int h, int D, int vb,
+                                           uint32_t vlane) {
+  const char *base = static_cast<const char *>(p.v) + (t0 * p.v_stride + (int64_t)h * D + 16 * vb) * 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)(L * p.v_stride * 2), 0x00020000);
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, vlane, 0, 0);
+  return make_uint2(x[0], x[1]);
 }
 
 // DELTA false: the linear rule (GLA), Vb = V; region 1 is neither written by
@@ -840,8 +850,7 @@ template <int D, bool DELTA>
 __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
   using RC = KdaRec<D>;
   using SM = StateSmem<D>;
-  using OPS = WaveOps<D>;
-  constexpr int NS = RC::NS, NT = RC::NT, KT = OPS::KT;
+  constexpr int NS = RC::NS, KT = WaveOps<D>::KT;
   constexpr int GRP = D / 16;   // workgroups per (sequence, value head)
   __shared__ SM sm;
 
@@ -892,6 +901,8 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rec), 0, RC::BYTES, 0x00020000);
   };
   const uint32_t voff = 16u * (uint32_t)lane;
+  uint32_t voff2 = q >= 2 ? voff : 0x80000000u;
+  asm volatile("" : "+v"(voff2));
   auto len_of = [&](int64_t c) { return (int)min<int64_t>(C, eos - (bos + C * c)); };
 
   // ---- the state's tiles: the pool (or zeros) at the sequence's start, the
@@ -920,8 +931,8 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
   // reloaded with chunk c + 1's right after chunk c's last use of it (W and
   // T' after Vb, Q^ and A^ after the outputs, K_end and gamma after the
   // update), so every load has about a chunk's time to land while the
-  // registers stay within what lets a prep workgroup share the compute unit.
-  OPS ops;
+  // registers stay within two workgroups per compute unit.
+  WaveOps<D> ops;
   // this wave's state tiles as halves of the split S^T fragments
   auto publish_state = [&](int par) {
 #pragma unroll
@@ -930,12 +941,18 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
       put_half(sm.sfh[par][m >> 1], sm.sfl[par][m >> 1], lane, m & 1, st[t]);
     }
   };
+  // values of the next chunk, loaded two chunks ahead of their use;
+  // vlane = row x (row pitch in bytes) + 8 (lane mod 4)
+  const uint32_t vlane = (uint32_t)((16 * q + (lane >> 2)) * p.v_stride * 2) + 8u * (uint32_t)(lane & 3);
+  uint2 vq;
   {
     const __amdgpu_buffer_rsrc_t rec = rec_of(cb);
-    if constexpr (DELTA) load_r1<D>(ops, rec, q, voff);
-    load_r2<D>(ops, rec, q, voff);
+    if constexpr (DELTA) load_r1<D>(ops, rec, q, voff, voff2);
+    load_r2<D>(ops, rec, q, voff, voff2);
     load_r3<D>(ops, rec, q, voff, g);
-    const uint2 v0 = load_vals(p, bos + C * cb, len_of(cb), h, D, vb, q, lane);
+    const uint2 v0 = load_vals(p, bos + C * cb, len_of(cb), h, D, vb, vlane);
+    const int64_t c1 = min(cb + 1, ce - 1);
+    vq = load_vals(p, bos + C * c1, len_of(c1), h, D, vb, vlane);
     const int par = (int)(cb & 1);
     publish_state(par);
     *reinterpret_cast<uint2 *>(&sm.vv[par][16 * q + (lane >> 2)][4 * (lane & 3)]) = v0;
@@ -943,14 +960,27 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
   lds_barrier();
 
   const int64_t HVD = (int64_t)p.HV * D;
+  // output rows of this lane: 16q + 4g + e, at e row pitches past the lane
+  // offset, which is the same for every chunk; both widths are issued, the
+  // other one at a lane offset beyond the chunk's descriptor, so that no
+  // branch makes the compiler's wait counts assume fewer stores in flight
+  const uint32_t osz = p.out_bf16 ? 2u : 4u;
+  const uint32_t orow = (uint32_t)HVD * osz;
+  const uint32_t olane = (uint32_t)(16 * q + 4 * g) * orow + (uint32_t)col * osz;
+  uint32_t olane32 = p.out_bf16 ? 0x80000000u : olane, olane16 = p.out_bf16 ? olane : 0x80000000u;
+  asm volatile("" : "+v"(olane32), "+v"(olane16));
   const int nts = q < 2 ? 1 : 2;   // k steps of row block q's lower-triangular operands
   auto chunk = [&](int64_t c) {
-    OPS &cur = ops;
     const int par = (int)(c & 1);
+    // The next chunk's loads are issued on every chunk, the last one
+    // reloading its own record (unused): with loads under a branch the
+    // compiler's wait counts must assume the branch that issued none, and a
+    // wait for one group of operands then also waits for every load issued
+    // after it.
     const bool more = c + 1 < ce;
-    uint2 vnext = make_uint2(0, 0);
     const __amdgpu_buffer_rsrc_t nrec = rec_of(more ? c + 1 : c);
-    if (more) vnext = load_vals(p, bos + C * (c + 1), len_of(c + 1), h, D, vb, q, lane);
+    const int64_t c2 = min(c + 2, ce - 1);
+    const uint2 vload = load_vals(p, bos + C * c2, len_of(c2), h, D, vb, vlane);
 
     // ---- S^T as B fragments over key rows 32s .. 32s + 31 ----
     Frag sf[NS];
@@ -966,15 +996,15 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
       for (int s = 0; s < 2; ++s)
         if (s < nts) ldfrag_tr(&sm.vv[par][0][0], SM::VP, 4 * (r & 3), s, r, g, vf[s]);
       f32x4 a0 = acc, a1 = acc;
-      a0 = mm<true, false>(cur.t[0], vf[0], a0);
-      if (nts > 1) a1 = mm<true, false>(cur.t[1], vf[1], a1);
+      a0 = mm<true, false>(ops.t[0], vf[0], a0);
+      if (nts > 1) a1 = mm<true, false>(ops.t[1], vf[1], a1);
 #pragma unroll
       for (int s = 0; s < NS; s += 2) {
 #pragma unroll
         for (int ps = 0; ps < 3; ++ps) {
-          if (ps == 0) { a0 = mm_pass<0, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<0, true, true>(cur.w[s + 1], sf[s + 1], a1); }
-          if (ps == 1) { a0 = mm_pass<1, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<1, true, true>(cur.w[s + 1], sf[s + 1], a1); }
-          if (ps == 2) { a0 = mm_pass<2, true, true>(cur.w[s], sf[s], a0); a1 = mm_pass<2, true, true>(cur.w[s + 1], sf[s + 1], a1); }
+          if (ps == 0) { a0 = mm_pass<0, true, true>(ops.w[s], sf[s], a0); a1 = mm_pass<0, true, true>(ops.w[s + 1], sf[s + 1], a1); }
+          if (ps == 1) { a0 = mm_pass<1, true, true>(ops.w[s], sf[s], a0); a1 = mm_pass<1, true, true>(ops.w[s + 1], sf[s + 1], a1); }
+          if (ps == 2) { a0 = mm_pass<2, true, true>(ops.w[s], sf[s], a0); a1 = mm_pass<2, true, true>(ops.w[s + 1], sf[s + 1], a1); }
         }
       }
       acc = a0 + a1;
@@ -984,8 +1014,7 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
       for (int i = 0; i < 4; ++i) acc[i] = bf16_to_f32(sm.vv[par][16 * q + 4 * g + i][r]);
     }
     put_half(sm.vbh[par][q >> 1], sm.vbl[par][q >> 1], lane, q & 1, acc);
-    if constexpr (DELTA)
-      if (more) load_r1<D>(ops, nrec, q, voff);
+    if constexpr (DELTA) load_r1<D>(ops, nrec, q, voff, voff2);
     lds_barrier();
 
     // ---- Vb as B fragments over tokens 32s .. 32s + 31 ----
@@ -998,45 +1027,48 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
       f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
 #pragma unroll
       for (int s = 0; s < NS; s += 2) {
-        o0 = mm_pass<0, true, true>(cur.qh[s], sf[s], o0);
-        o1 = mm_pass<0, true, true>(cur.qh[s + 1], sf[s + 1], o1);
-        o0 = mm_pass<1, true, true>(cur.qh[s], sf[s], o0);
-        o1 = mm_pass<1, true, true>(cur.qh[s + 1], sf[s + 1], o1);
-        o0 = mm_pass<2, true, true>(cur.qh[s], sf[s], o0);
-        o1 = mm_pass<2, true, true>(cur.qh[s + 1], sf[s + 1], o1);
+        o0 = mm_pass<0, true, true>(ops.qh[s], sf[s], o0);
+        o1 = mm_pass<0, true, true>(ops.qh[s + 1], sf[s + 1], o1);
+        o0 = mm_pass<1, true, true>(ops.qh[s], sf[s], o0);
+        o1 = mm_pass<1, true, true>(ops.qh[s + 1], sf[s + 1], o1);
+        o0 = mm_pass<2, true, true>(ops.qh[s], sf[s], o0);
+        o1 = mm_pass<2, true, true>(ops.qh[s + 1], sf[s + 1], o1);
       }
-      o0 = mm<true, true>(cur.a[0], vbf[0], o0);
-      if (nts > 1) o1 = mm<true, true>(cur.a[1], vbf[1], o1);
+      o0 = mm<true, true>(ops.a[0], vbf[0], o0);
+      if (nts > 1) o1 = mm<true, true>(ops.a[1], vbf[1], o1);
       const f32x4 oa = o0 + o1;
       // buffer stores against a descriptor over this chunk's L output rows:
       // rows past a partial chunk's end fall outside it and are dropped
       const int64_t t0 = bos + C * c;
       const int L = len_of(c);
-      const uint32_t osz = p.out_bf16 ? 2u : 4u;
-      const uint32_t orow = (uint32_t)HVD * osz;
       char *obase = static_cast<char *>(p.o) + (t0 * HVD + (int64_t)h * D) * osz;
       const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)(L * orow), 0x00020000);
-      const uint32_t olane = (uint32_t)(16 * q + 4 * g) * orow + (uint32_t)col * osz;
-      if (!p.out_bf16) {
+      const bf16x2 b01 = {static_cast<__bf16>(oa[0]), static_cast<__bf16>(oa[1])};
+      const bf16x2 b23 = {static_cast<__bf16>(oa[2]), static_cast<__bf16>(oa[3])};
+      const uint32_t w01 = __builtin_bit_cast(uint32_t, b01), w23 = __builtin_bit_cast(uint32_t, b23);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[e]), ors, olane, e * (int)orow, 0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[e]), ors, olane, e * (int)orow, 0);
-      }
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(oa[e]), ors, olane32, e * (int)orow, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w01, ors, olane16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w01 >> 16), ors, olane16, (int)orow, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w23, ors, olane16, 2 * (int)orow, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w23 >> 16), ors, olane16, 3 * (int)orow, 0);
     }
 
-    if (more) load_r2<D>(ops, nrec, q, voff);
+    load_r2<D>(ops, nrec, q, voff, voff2);
 
     // ---- this wave's key rows: S^T <- gamma (.) S^T + K_end^T Vb ----
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      st[t][0] *= cur.gam[t].x;
-      st[t][1] *= cur.gam[t].y;
-      st[t][2] *= cur.gam[t].z;
-      st[t][3] *= cur.gam[t].w;
+      // (gamma through an opaque copy here: hoisted into the Vb products
+      // instead, its wait would stall them on loads issued at the end of
+      // the previous chunk)
+      float4 gm = ops.gam[t];
+      asm volatile("" : "+v"(gm.x), "+v"(gm.y), "+v"(gm.z), "+v"(gm.w));
+      st[t][0] *= gm.x;
+      st[t][1] *= gm.y;
+      st[t][2] *= gm.z;
+      st[t][3] *= gm.w;
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -1044,19 +1076,23 @@ __global__ __launch_bounds__(256, 2) void kda_state_kernel(KdaParams p) {
       for (int ps = 0; ps < 3; ++ps)
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          if (ps == 0) st[t] = mm_pass<0, true, true>(cur.ke[t][s], vbf[s], st[t]);
-          if (ps == 1) st[t] = mm_pass<1, true, true>(cur.ke[t][s], vbf[s], st[t]);
-          if (ps == 2) st[t] = mm_pass<2, true, true>(cur.ke[t][s], vbf[s], st[t]);
+          if (ps == 0) st[t] = mm_pass<0, true, true>(ops.ke[t][s], vbf[s], st[t]);
+          if (ps == 1) st[t] = mm_pass<1, true, true>(ops.ke[t][s], vbf[s], st[t]);
+          if (ps == 2) st[t] = mm_pass<2, true, true>(ops.ke[t][s], vbf[s], st[t]);
         }
 
-    if (more) load_r3<D>(ops, nrec, q, voff, g);
+    load_r3<D>(ops, nrec, q, voff, g);
 
     // ---- publish the next chunk's state fragments and values ----
     publish_state(par ^ 1);
-    if (more) *reinterpret_cast<uint2 *>(&sm.vv[par ^ 1][16 * q + (lane >> 2)][4 * (lane & 3)]) = vnext;
+    if (more) *reinterpret_cast<uint2 *>(&sm.vv[par ^ 1][16 * q + (lane >> 2)][4 * (lane & 3)]) = vq;
+    vq = vload;
     lds_barrier();
   };
-  for (int64_t c = cb; c < ce; ++c) chunk(c);
+  // (the first chunk peeled: the loop's first wait then follows a chunk's
+  // loads, as on every later iteration, not the prologue's different order)
+  chunk(cb);
+  for (int64_t c = cb + 1; c < ce; ++c) chunk(c);
 
   // ---- state out: the pool at the sequence's end, else the carry ----
 #pragma unroll

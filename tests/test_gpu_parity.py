@@ -87,13 +87,17 @@ def test_chunk_sizes_16_and_32(C, D, in_dtype, gate, rule):
 
 
 @pytest.mark.parametrize("zero_init", [True, False])
-def test_chunk_fwd_zero_init_and_bf16_output(zero_init):
+@pytest.mark.parametrize("gate,rule", [("scalar", "delta"), ("channel", "delta"), ("channel", "linear")])
+def test_chunk_fwd_zero_init_and_bf16_output(zero_init, gate, rule):
+    """bf16 outputs on ragged partial chunks (100 = 64 + 36 tokens, 7, an
+    empty sequence), from the scalar-gate kernel and the channel-gate pair."""
     gdr = _gdr()
-    w = small_workload(128, "bf16", "scalar", "delta", "f32", zero_init, seqlens=(100, 0, 7, 64))
+    w = small_workload(128, "bf16", gate, rule, "f32", zero_init, seqlens=(100, 0, 7, 64))
     x = synth.generate(w)
     d = to_device(w, x)
+    print(f"chunk_fwd bf16 out gate={gate} rule={rule} zero_init={zero_init}", flush=True)
     o = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
-                      d["cu_seqlens"], zero_init=zero_init, out_dtype=torch.bfloat16)
+                      d["cu_seqlens"], zero_init=zero_init, out_dtype=torch.bfloat16, rule=rule, gate=gate)
     torch.cuda.synchronize()
     o_ref, pool_ref = oracle_run(w, widened(w, x), x["slot_idx"], x["cu_seqlens"], 128 ** -0.5)
     # a bf16 output carries its own rounding (2^-9 relative); gate it elementwise
