@@ -60,7 +60,11 @@ template <int NSW> constexpr int prep_waves() { return NSW == 2 ? 6 : 4; }
 // The solves follow R row by row (a counter per row), so they overlap the
 // long rows. A, which is needed only after the end-of-chunk barrier, goes to
 // the waves with the shortest chains: the two with short T columns (before
-// their solve) and the two R waves (after R).
+// their solve) and the two R waves (after R). With four prep waves wave w
+// forms row 3 - w of R, inverts its diagonal block and solves T column 3 - w
+// (every row of R is waited for before any solve), and forms row w of A: the
+// longest solve (column 0) falls to the wave with the shortest R row, and each
+// wave forms five Gram tiles.
 struct SegWS {
   int kind, row, j0, j1;
 };
@@ -80,7 +84,7 @@ constexpr RoleWS role_ws(bool delta, int np, int w) {
       default: return {{NOSEG, NOSEG, NOSEG, NOSEG}, -1, -1, -1};
     }
   }
-  if (np == 4) return {{{1, 3 - w, 0, 3 - w}, {2, w ^ 2, 0, w ^ 2}, NOSEG, NOSEG}, 3 - w, w, w};
+  if (np == 4) return {{{1, 3 - w, 0, 3 - w}, {2, w, 0, w}, NOSEG, NOSEG}, 3 - w, 3 - w, w};
   switch (w) {
     case 0: return {{{1, 0, 0, 0}, {2, 0, 0, 0}, {2, 1, 0, 1}, NOSEG}, 0, 3, 0};
     case 1: return {{{1, 1, 1, 1}, {2, 2, 0, 2}, NOSEG, NOSEG}, 1, 2, 1};
