@@ -233,7 +233,18 @@ def bench_decode(w: synth.Workload, steps: int, warmup: int = 10):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / steps, e0.elapsed_time(e1) / steps
+    kernel_ms = e0.elapsed_time(e1) / steps
+    # For comparison, the same pool streamed in place by torch's elementwise
+    # multiply: each element read and written once, as by the step.
+    for _ in range(3):
+        pool.mul_(1.0)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        pool.mul_(1.0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return wall / steps, kernel_ms, e0.elapsed_time(e1) / reps
 
 
 def bench_recurrent_fwd(w: synth.Workload, steps: int, warmup: int = 5):
@@ -556,14 +567,20 @@ def prefill_leg(w: synth.Workload, steps: int, warmup: int) -> dict:
 
 def decode_leg(steps: int) -> dict:
     dw = synth.workload("decode_n256_hk16_hv32_d128")
-    d_step, d_kernel = bench_decode(dw, steps)
+    d_step, d_kernel, d_rmw = bench_decode(dw, steps)
     db = step_bytes(dw)
+    pool_bytes = 2 * dw.num_slots * dw.HV * dw.DK * dw.DV * (2 if dw.state_dtype == "bf16" else 4)
     return {"workload": dw.name, "steps": steps, "steps_per_s": 1.0 / d_step,
             "us_per_step": d_step * 1e6, "kernel": "recurrent_step_kernel",
             "kernel_us_per_step": d_kernel * 1e3, "algorithmic_bytes_per_step": db,
             "hbm_gbs": db / (d_kernel * 1e-3) / 1e9,
             "hbm_frac": db / (d_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC)}
+            "traffic": committed_traffic("recurrent_step_kernel", dw.name, STEP_SRC),
+            # torch's in-place multiply over the whole pool (read + write), the
+            # same stream without the step's arithmetic: a reference for the
+            # rate an in-place state stream reaches on this device
+            "pool_inplace_stream_us": d_rmw * 1e3,
+            "pool_inplace_stream_gbs": pool_bytes / (d_rmw * 1e-3) / 1e9}
 
 
 def main():
