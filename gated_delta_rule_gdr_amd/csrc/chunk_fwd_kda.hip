@@ -144,6 +144,11 @@ __device__ __forceinline__ f32x4 mpass(const Frag &a, const Frag &b, f32x4 c) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The prep kernel keeps the gate in base-2 units (g log2 e), so that every
+// decay factor is one v_exp_f32 (2^x) of a prefix-sum difference.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Slot j of lane group g: offset of its k inside a 32-wide step.
 __device__ __forceinline__ int slot_k(int g, int j) { return (j < 4 ? 4 * g + j : 12 + 4 * g + j); }
 
@@ -245,9 +250,9 @@ __device__ __forceinline__ void prep_load(PrepIn<D> &in, const KdaParams &p, con
   constexpr int NS = D / 32;
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   // buffer loads against descriptors over the item's L token rows (scalar
-  // bases, one lane offset per tensor); a lane past the chunk's end rereads
-  // its last row
-  const int row = min(16 * w + r, it.L - 1);
+  // bases, one lane offset per tensor); a lane past the chunk's end falls
+  // outside them (its row offset alone passes the range) and reads zeros
+  const int row = 16 * w + r;
   const int hk = it.h / p.ratio;
   const int64_t HVD = (int64_t)p.HV * D;
   const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
@@ -302,7 +307,6 @@ __device__ __forceinline__ void prep_exact_diagonal(const KdaParams &p, const Pr
   constexpr int NS = D / 32;
   PrepIn<D> in;
   prep_load<D, DELTA>(in, p, it, w, r, g);
-  const bool ok = 16 * w + r < it.L;
   float gv[NS][8], kv[NS][8], qv[NS][8];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -312,9 +316,9 @@ __device__ __forceinline__ void prep_exact_diagonal(const KdaParams &p, const Pr
       const uint32_t kw[2] = {in.k[2 * u], in.k[2 * u + 1]}, qw[2] = {in.q[2 * u], in.q[2 * u + 1]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        gv[s][4 * hf + j] = ok ? __uint_as_float(in.g[4 * u + j]) : 0.f;
-        kv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1])) : 0.f;
-        qv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1])) : 0.f;
+        gv[s][4 * hf + j] = __uint_as_float(in.g[4 * u + j]) * LOG2E;
+        kv[s][4 * hf + j] = (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
+        qv[s][4 * hf + j] = (j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1]);
       }
     }
 #pragma unroll
@@ -337,7 +341,7 @@ __device__ __forceinline__ void prep_exact_diagonal(const KdaParams &p, const Pr
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float kj = __shfl(kv[s][j], src, 64), gj = __shfl(gv[s][j], src, 64);
-        const float t = kj * __expf(fminf(gv[s][j] - gj, 0.f));   // (pairs j > i are masked below)
+        const float t = kj * exp2_(fminf(gv[s][j] - gj, 0.f));   // (pairs j > i are masked below)
         if constexpr (DELTA) sr += kv[s][j] * t;
         sa += qv[s][j] * t;
       }
@@ -395,7 +399,6 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   prep_load<D, DELTA>(in, p, nx, w, r, g);
   for (; item < items; item += gridDim.x) {
     const PrepItem it = nx;
-    const bool ok = i < it.L;
     float gv[NS][8], kv[NS][8], qv[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -405,12 +408,13 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
         const uint32_t kw[2] = {in.k[2 * u], in.k[2 * u + 1]}, qw[2] = {in.q[2 * u], in.q[2 * u + 1]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          gv[s][4 * hf + j] = ok ? __uint_as_float(in.g[4 * u + j]) : 0.f;
-          kv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1])) : 0.f;
-          qv[s][4 * hf + j] = ok ? ((j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1])) : 0.f;
+          // (rows past the chunk's end were read as zeros)
+          gv[s][4 * hf + j] = __uint_as_float(in.g[4 * u + j]) * LOG2E;
+          kv[s][4 * hf + j] = (j & 1) ? bf_hi(kw[j >> 1]) : bf_lo(kw[j >> 1]);
+          qv[s][4 * hf + j] = (j & 1) ? bf_hi(qw[j >> 1]) : bf_lo(qw[j >> 1]);
         }
       }
-    if (g == 0) sm.beta[i] = ok ? in.beta : 0.f;
+    if (g == 0) sm.beta[i] = in.beta;
     // the next item's inputs are loaded once this item's operands are formed
     // (below), so that their registers are free meanwhile
     auto prefetch = [&]() {
@@ -434,7 +438,8 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       (void)L;
 
   // ---- gate prefix sums within the 16-token block (DPP row scan over r):
-  //      gv becomes the log-decay from the start of the lane's block ----
+  //      gv becomes the log-decay (base 2) from the start of the lane's
+  //      block ----
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -455,13 +460,13 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
         const float *x = &gv[s][4 * hf];
         *reinterpret_cast<float4 *>(&sm.tot[w][c0]) = make_float4(x[0], x[1], x[2], x[3]);
         *reinterpret_cast<float4 *>(&sm.etot[w][c0]) =
-            make_float4(__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3]));
+            make_float4(exp2_(x[0]), exp2_(x[1]), exp2_(x[2]), exp2_(x[3]));
       }
   }
   lds_barrier();
   if (tid < D) {
     const float Gl = ((sm.tot[0][tid] + sm.tot[1][tid]) + sm.tot[2][tid]) + sm.tot[3][tid];
-    *reinterpret_cast<float *>(rec + RC::GAM + 4u * (uint32_t)tid) = __expf(Gl);
+    *reinterpret_cast<float *>(rec + RC::GAM + 4u * (uint32_t)tid) = exp2_(Gl);
     const float e1 = sm.etot[1][tid], e2 = sm.etot[2][tid], e3 = sm.etot[3][tid];
     sm.fend[0][tid] = e1 * (e2 * e3);
     sm.fend[1][tid] = e2 * e3;
@@ -482,14 +487,14 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
   //   kd      the key decayed to the end of block w, k e^{tot_w - gv} (LDS)
   //   kl      K_l = nk e^{B_w} (LDS); Q^ = nq e^{B_w} (record)
   // The strongest decay of any channel over block w decides the diagonal
-  // tile's form: up to 80 the factors e^{-gv} stay far inside the fp32
-  // range and the tile is the product md^T (nk, nq) (transposed, as the
+  // tile's form: up to 80 (in natural-log units; 80 log2 e in the kernel's
+  // base-2 units) the factors e^{-gv} stay far inside the fp32 range and the tile is the product md^T (nk, nq) (transposed, as the
   // other tiles below); beyond, it is summed pair by pair.
   float span = 0.f;
   for (int c = lane; c < D; c += 64) span = fmaxf(span, -sm.tot[w][c]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) span = fmaxf(span, __shfl_xor(span, off, 64));
-  const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(span)) <= __float_as_int(80.f);
+  const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(span)) <= __float_as_int(80.f * LOG2E);
   // Gram tiles of row block w, by k step s: tile (w, J) is computed
   // transposed (keys of block J as the M operand), so lane (r, g) holds row
   // 16w + r, columns 16J + 4g .. +3. For J < w the keys are those of block J
@@ -517,11 +522,11 @@ __global__ __launch_bounds__(256, 2) void kda_prep_kernel(KdaParams p) {
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * hf + jj;
         const float G = gv[s][j];
-        const float e1 = __expf(G);
+        const float e1 = exp2_(G);
         a[j] = kv[s][j] * e1;                        // nk
         c8[j] = (sc * qv[s][j]) * e1;                // nq
-        b[j] = kv[s][j] * __expf(-G);                // md
-        d[j] = kv[s][j] * __expf(twv[jj] - G);       // kd
+        b[j] = kv[s][j] * exp2_(-G);                 // md
+        d[j] = kv[s][j] * exp2_(twv[jj] - G);        // kd
         e[j] = a[j] * ebv[jj];                       // K_l
         f[j] = c8[j] * ebv[jj];                      // Q^
       }
