@@ -22,7 +22,8 @@ HBM bandwidth (its binding roofline), with its MFMA fraction alongside;
 `configs` holds the same figures for each of the five configurations (and
 configuration 2's linear-attention run), the decode step's as steps/s and HBM
 fraction; `linear_backward` and `gdn_backward` time the gradients on the
-Gated DeltaNet batch; `recurrent_fwd` the tokenwise recurrence on a short
+Gated DeltaNet batch, `gated_linear_backward` those of gated linear attention
+on the ragged grouped-head batch (chunkwise, the tokenwise backward beside it); `recurrent_fwd` the tokenwise recurrence on a short
 batch; `delta_product` the chunkwise prefill of Gated DeltaProduct (2
 transitions per token); `speculative` a 4-token verify window per sequence and
 the fold of its accepted prefix on the decode pool; `cpu_baseline` times the
@@ -326,9 +327,11 @@ def bench_product(w: synth.Workload, P: int, steps: int, warmup: int = 3):
 
 
 def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
-    """Mean time (ms) of gdr_linear_chunk_bwd on w's batch (all of its
-    kernels: the input reversals, three chunkwise passes, the output
-    reversals), with a workspace allocated once."""
+    """Mean time (ms) of gdr_linear_chunk_bwd (w.gate "none") or
+    gdr_gated_linear_chunk_bwd (w.gate "scalar") on w's batch (all of its
+    kernels: the gate shifts, input reversals or head repeats, three chunkwise
+    passes, the output reversals, group sums and the gate's gradient), with a
+    workspace allocated once."""
     import torch
     import gated_delta_rule_gdr_amd as gdr
     dev = torch.device("cuda", 0)
@@ -337,18 +340,19 @@ def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
     a = dict(q=_dev(x["q"], w.in_dtype, dev), k=_dev(x["k"], w.in_dtype, dev),
              v=_dev(x["v"], w.in_dtype, dev), do=_dev(do, w.in_dtype, dev),
              pool=_dev(x["pool"], w.state_dtype, dev), slot_idx=_dev(x["slot_idx"], "i32", dev),
-             cu_seqlens=_dev(x["cu_seqlens"], "i32", dev))
+             cu_seqlens=_dev(x["cu_seqlens"], "i32", dev),
+             g=_dev(x["g"], "f32", dev) if w.gate == "scalar" else None)
     del x, do
     L = gdr.load()
     ws = None
 
     def run():
         return gdr.linear_chunk_bwd(a["q"], a["k"], a["v"], a["do"], a["pool"], a["slot_idx"],
-                                    a["cu_seqlens"], zero_init=w.zero_init, workspace=ws)
+                                    a["cu_seqlens"], g=a["g"], zero_init=w.zero_init, workspace=ws)
     run()
     import ctypes
-    args, _ = gdr._prepare(a["q"], a["k"], a["v"], None, None, a["pool"], a["slot_idx"],
-                           a["cu_seqlens"], None, None, "linear", "none", w.zero_init, False, 64,
+    args, _ = gdr._prepare(a["q"], a["k"], a["v"], a["g"], None, a["pool"], a["slot_idx"],
+                           a["cu_seqlens"], None, None, "linear", w.gate, w.zero_init, False, 64,
                            torch.float32)
     ws = torch.empty(L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(args)), dtype=torch.uint8,
                      device=dev)
@@ -704,6 +708,22 @@ def main():
             "algorithmic_bytes": bb, "hbm_gbs": bb / (bt * 1e-3) / 1e9,
             "hbm_frac": bb / (bt * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_flops": bf, "mfma_tflops": bf / (bt * 1e-3) / 1e12}
+        # gradients of gated linear attention (dq, dk, dv, dg) on the ragged
+        # grouped-head batch, chunkwise, and tokenwise beside it
+        lw = synth.workload("ragged_gqa_prefill_n8_hk16_hv32_d128").replace(rule="linear")
+        lt = bench_linear_bwd(lw, args.steps)
+        lrt, _ = bench_recurrent_bwd(lw, args.backward_steps)
+        T, HKD, HVD = lw.T_total, lw.HK * lw.DK, lw.HV * lw.DV
+        # q, k, v, dO, g and the initial states read; dq, dk, dv, dg written (fp32)
+        sb = lw.N * lw.HV * lw.DK * lw.DV
+        lb = ((2 * HKD + 2 * HVD) * T * _isz(lw.in_dtype) + T * lw.HV * 4 + sb * _isz(lw.state_dtype)
+              + (2 * HKD + HVD) * T * 4 + T * lw.HV * 4)
+        lf = 3 * prefill_flops(lw, lw.chunk_size)   # one linear pass per gradient
+        result["gated_linear_backward"] = {
+            "workload": lw.name + " (linear rule)", "steps": args.steps, "ms": lt,
+            "tokens_per_s": T / (lt * 1e-3), "algorithmic_bytes": lb, "hbm_gbs": lb / (lt * 1e-3) / 1e9,
+            "hbm_frac": lb / (lt * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_flops": lf,
+            "mfma_tflops": lf / (lt * 1e-3) / 1e12, "tokenwise_ms_same_batch": lrt}
         # gradients of the gated delta rule on the GDN batch (tokenwise)
         gw = synth.workload(synth.GDN)
         gt, gws = bench_recurrent_bwd(gw, args.backward_steps)

@@ -41,7 +41,7 @@ FLAG_QK_L2NORM = 4
 
 
 # GDR_ABI_VERSION of include/gdr.h that Args mirrors.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class GdrError(RuntimeError):
@@ -105,6 +105,9 @@ def load() -> ctypes.CDLL:
     L.gdr_linear_chunk_bwd.restype = ctypes.c_int
     L.gdr_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.gdr_gated_linear_chunk_bwd.restype = ctypes.c_int
+    L.gdr_gated_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t,
+                                                                                            ctypes.c_void_p]
     L.gdr_recurrent_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdr_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
     L.gdr_recurrent_bwd.restype = ctypes.c_int
@@ -310,30 +313,41 @@ def recurrent_fwd(q, k, v, g, beta, pool, slot_idx, cu_seqlens, *, scale=None, r
     return o
 
 
-def linear_chunk_bwd(q, k, v, do, pool, slot_idx, cu_seqlens, *, scale=None, zero_init=False,
+def linear_chunk_bwd(q, k, v, do, pool, slot_idx, cu_seqlens, *, g=None, scale=None, zero_init=False,
                      out_dtype=None, workspace=None, debug_checks=False):
-    """Gradients (dq, dk, dv) of causal linear attention (no gate, no delta)
-    for the forward call with these arguments and upstream gradient do
-    [T, HV, DV] (contiguous, q's dtype). The pool supplies the initial state
-    (read only) unless zero_init. ``workspace`` is an optional uint8 device
-    tensor of at least the size the library asks for (allocated from torch
-    by default)."""
+    """Gradients of causal linear attention (no delta), plain or with a
+    scalar gate g (the log-decay, fp32 [T, HV]), with grouped key heads
+    (HV a multiple of HK), for the forward call with these arguments and
+    upstream gradient do [T, HV, DV] (contiguous, q's dtype). The pool
+    supplies the initial state (read only) unless zero_init. Returns
+    (dq, dk, dv), and with g also dg (fp32 [T, HV], the gradient of the
+    log-decays). ``workspace`` is an optional uint8 device tensor of at least
+    the size the library asks for (allocated from torch by default)."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     T, HK, DK = q.shape
-    dq = torch.empty((T, HK, DK), dtype=out_dtype, device=q.device)
-    a, _ = _prepare(q, k, v, None, None, pool, slot_idx, cu_seqlens, dq, scale, "linear", "none",
-                    zero_init, debug_checks, 64, out_dtype)
+    gated = g is not None
+    if gated and g.dim() != 2:
+        raise ValueError("the backward takes the scalar gate, g [T, HV]")
+    dv = torch.empty(tuple(v.shape), dtype=out_dtype, device=q.device)
+    a, _ = _prepare(q, k, v, g, None, pool, slot_idx, cu_seqlens, dv, scale, "linear",
+                    "scalar" if gated else "none", zero_init, debug_checks, 64, out_dtype)
     if do.dtype != q.dtype or not do.is_contiguous() or tuple(do.shape) != tuple(v.shape) or do.device != q.device:
         raise ValueError("do must be a contiguous tensor shaped like v, in q's dtype, on q's device")
+    dq = torch.empty((T, HK, DK), dtype=out_dtype, device=q.device)
     dk = torch.empty_like(dq)
-    dv = torch.empty(tuple(v.shape), dtype=out_dtype, device=q.device)
+    dg = torch.empty(tuple(g.shape), dtype=torch.float32, device=q.device) if gated else None
     L = load()
     if workspace is None:
         nbytes = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
         raise TypeError(f"workspace must be a contiguous uint8 tensor on {q.device}")
+    if gated:
+        _check(L.gdr_gated_linear_chunk_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                            dv.data_ptr(), dg.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel(), _stream(q)))
+        return dq, dk, dv, dg
     _check(L.gdr_linear_chunk_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv

@@ -1084,8 +1084,9 @@ hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, true, false>), dim3(blocks),
                        dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
   else if (p.rev) {
-    // (the reversed walk serves the linear-attention gradients only)
-    if constexpr (GATE == GDR_GATE_NONE && !DELTA)
+    // (the reversed walk serves the linear-attention gradients only, plain
+    // or with a scalar gate)
+    if constexpr (!DELTA)
       hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, DELTA, D, NSW, false, true>), dim3(blocks),
                          dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
     else

@@ -195,43 +195,53 @@ namespace {
 // The channel-gate prefill for bf16 inputs runs as two kernels that pass
 // per-chunk records through the workspace; every other prefill is one fused
 // kernel and needs none.
-// What the linear-attention backward covers (the plain linear rule of the
-// page that derives it), on top of the forward's checks of the arguments.
-gdr_status validate_bwd_shape(const gdr_args *a) {
-  if (a->rule != GDR_RULE_LINEAR || a->gate != GDR_GATE_NONE)
-    return fail(GDR_E_UNSUPPORTED, "the backward covers the linear rule without a gate");
-  if (a->HV != a->HK)
-    return fail(GDR_E_UNSUPPORTED, "the backward takes one value head per key head (HV = %d, HK = %d)", a->HV, a->HK);
+// What the linear-attention backward covers (the linear rule of the page
+// that derives it, plain or with a scalar gate, with grouped key heads), on
+// top of the forward's checks of the arguments. `gated` says whether the
+// caller takes the gate's gradient.
+gdr_status validate_bwd_shape(const gdr_args *a, bool gated) {
+  if (a->rule != GDR_RULE_LINEAR) return fail(GDR_E_UNSUPPORTED, "the backward covers the linear rule");
+  if (a->gate == GDR_GATE_CHANNEL) return fail(GDR_E_UNSUPPORTED, "the backward takes no channel gate");
+  if (gated && a->gate != GDR_GATE_SCALAR)
+    return fail(GDR_E_UNSUPPORTED, "gdr_gated_linear_chunk_bwd takes the scalar gate");
+  if (!gated && a->gate != GDR_GATE_NONE)
+    return fail(GDR_E_UNSUPPORTED, "a gated backward is gdr_gated_linear_chunk_bwd (it forms the gate's gradient)");
   if (products_of(*a) > 1) return fail(GDR_E_UNSUPPORTED, "the backward takes one transition per token");
   return GDR_OK;
 }
 
-gdr_status validate_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv) {
+gdr_status validate_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dg, bool gated) {
   if (!a) return fail(GDR_E_INVALID, "args is NULL");
   gdr_args b = *a;
-  b.o = dq;   // the forward's checks then cover dq as its output
-  if (a->T_total > 0 && a->N > 0 && !dq) return fail(GDR_E_INVALID, "dq is NULL");
+  b.o = dv;   // the forward's checks then cover dv as its output
+  if (a->T_total > 0 && a->N > 0 && !dv) return fail(GDR_E_INVALID, "dv is NULL");
   gdr_status st = validate(&b, Call::Chunk);
   if (st != GDR_OK) return st;
-  if ((st = validate_bwd_shape(a)) != GDR_OK) return st;
+  if ((st = validate_bwd_shape(a, gated)) != GDR_OK) return st;
   if (a->N == 0 || a->T_total == 0) return GDR_OK;
-  if (!dout || !dk || !dv) return fail(GDR_E_INVALID, "dout / dk / dv is NULL");
-  const void *ptrs[] = {dout, dk, dv};
+  if (!dout || !dq || !dk) return fail(GDR_E_INVALID, "dout / dq / dk is NULL");
+  if (gated && !dg) return fail(GDR_E_INVALID, "dg is NULL");
+  const void *ptrs[] = {dout, dq, dk};
   for (const void *ptr : ptrs)
-    if (reinterpret_cast<uintptr_t>(ptr) % 16) return fail(GDR_E_INVALID, "dout, dk and dv must be 16-byte aligned");
-  const int64_t row = (int64_t)a->HV * a->DV;
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return fail(GDR_E_INVALID, "dout, dq and dk must be 16-byte aligned");
+  if (gated && reinterpret_cast<uintptr_t>(dg) % 4) return fail(GDR_E_INVALID, "dg must be 4-byte aligned");
+  const int64_t vrow = (int64_t)a->HV * a->DV, krow = (int64_t)a->HK * a->DK;
   const size_t ie = dtype_bytes(a->in_dtype), oe = dtype_bytes(a->out_dtype);
-  const Range outs[] = {span(dq, a->T_total, row, row, oe), span(dk, a->T_total, row, row, oe),
-                        span(dv, a->T_total, row, row, oe)};
-  const Range ins[] = {span(a->q, a->T_total, a->q_stride_t, row, ie), span(a->k, a->T_total, a->k_stride_t, row, ie),
-                       span(a->v, a->T_total, a->v_stride_t, row, ie), span(dout, a->T_total, row, row, ie),
+  const Range outs[] = {span(dq, a->T_total, krow, krow, oe), span(dk, a->T_total, krow, krow, oe),
+                        span(dv, a->T_total, vrow, vrow, oe),
+                        gated ? span(dg, a->T_total, a->HV, a->HV, 4) : Range{}};
+  const Range ins[] = {span(a->q, a->T_total, a->q_stride_t, krow, ie),
+                       span(a->k, a->T_total, a->k_stride_t, krow, ie),
+                       span(a->v, a->T_total, a->v_stride_t, vrow, ie), span(dout, a->T_total, vrow, vrow, ie),
+                       gated ? span(a->g, a->T_total, a->HV, a->HV, 4) : Range{},
                        span(a->state_pool, 1, 0, a->num_slots * a->HV * (int64_t)a->DK * a->DV,
                             dtype_bytes(a->state_dtype))};
-  for (int i = 0; i < 3; ++i) {
+  const int nout = gated ? 4 : 3;
+  for (int i = 0; i < nout; ++i) {
     for (const Range &r : ins)
-      if (overlap(outs[i], r)) return fail(GDR_E_INVALID, "dq / dk / dv overlaps an input or the state pool");
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], outs[j])) return fail(GDR_E_INVALID, "dq, dk and dv overlap each other");
+      if (overlap(outs[i], r)) return fail(GDR_E_INVALID, "a gradient overlaps an input or the state pool");
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDR_E_INVALID, "the gradients overlap each other");
   }
   return GDR_OK;
 }
@@ -397,14 +407,15 @@ GDR_EXPORT gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream) 
 GDR_EXPORT size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a) {
   if (!a) return 0;
   g_last_error[0] = '\0';
-  if (validate_bwd_shape(a) != GDR_OK || a->N <= 0 || a->T_total <= 0) return 0;
-  if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK)) return 0;
+  if (validate_bwd_shape(a, a->gate == GDR_GATE_SCALAR) != GDR_OK || a->N <= 0 || a->T_total <= 0) return 0;
+  if (!((a->DK == 64 || a->DK == 128) && a->DV == a->DK) || a->HK <= 0 || a->HV % a->HK) return 0;
   return linear_bwd_workspace(*a);
 }
 
-GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
-                                           void *workspace, size_t ws_bytes, hipStream_t stream) {
-  gdr_status s = validate_bwd(a, dout, dq, dk, dv);
+namespace {
+gdr_status linear_bwd_call(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dg, bool gated,
+                           void *workspace, size_t ws_bytes, hipStream_t stream) {
+  gdr_status s = validate_bwd(a, dout, dq, dk, dv, dg, gated);
   if (s != GDR_OK) return s;
   if (a->N == 0 || a->T_total == 0) return GDR_OK;
   const size_t need = linear_bwd_workspace(*a);
@@ -415,10 +426,21 @@ GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, 
     s = run_debug_checks(a, true, stream);
     if (s != GDR_OK) return s;
   }
-  hipError_t e = launch_linear_bwd(*a, dout, dq, dk, dv, workspace, stream);
+  hipError_t e = launch_linear_bwd(*a, dout, dq, dk, dv, dg, workspace, stream);
   if (e != hipSuccess) return fail(GDR_E_HIP, "linear_chunk_bwd launch: %s", hipGetErrorString(e));
   if (a->flags & GDR_FLAG_DEBUG_CHECKS) return finish_debug_checks(stream);
   return GDR_OK;
+}
+}  // namespace
+
+GDR_EXPORT gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                           void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_call(a, dout, dq, dk, dv, nullptr, false, workspace, ws_bytes, stream);
+}
+
+GDR_EXPORT gdr_status gdr_gated_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                                 float *dg, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_call(a, dout, dq, dk, dv, dg, true, workspace, ws_bytes, stream);
 }
 
 GDR_EXPORT int gdr_ring_record_elements(const gdr_args *a) { return a ? ring_record_elements(*a) : 0; }

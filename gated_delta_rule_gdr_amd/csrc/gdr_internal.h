@@ -57,8 +57,8 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
 // Linear-attention backward: three chunkwise forward passes with exchanged
 // roles (linear_bwd.hip); its workspace in bytes.
 size_t linear_bwd_workspace(const gdr_args &a);
-hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, void *ws,
-                             hipStream_t stream);
+hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, float *dg,
+                             void *ws, hipStream_t stream);
 // True when GDR_PREFILL_KERNEL=generic asks for the general prefill kernel in
 // every case (used to compare kernels).
 bool prefill_force_generic();

@@ -21,7 +21,8 @@
  *   gdr_recurrent_fwd   the tokenwise recurrence over a ragged batch, the
  *                       state in registers across each sequence (the
  *                       "gated_delta" Mojo page's kernel).
- * gdr_linear_chunk_bwd gives the gradients of the plain linear rule;
+ * gdr_linear_chunk_bwd and gdr_gated_linear_chunk_bwd give the gradients of
+ * the linear rule, plain or with a scalar gate, chunkwise;
  * gdr_recurrent_bwd gives the gradients of the gated delta and gated linear
  * rules, tokenwise;
  * gdr_verify_ring and gdr_state_fold split a speculative-decode window into a
@@ -77,7 +78,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 6
+#define GDR_ABI_VERSION 7
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -207,11 +208,15 @@ gdr_status gdr_recurrent_step(const gdr_args *a, hipStream_t stream);
  * workspace. */
 gdr_status gdr_recurrent_fwd(const gdr_args *a, hipStream_t stream);
 
-/* Bytes of device workspace gdr_linear_chunk_bwd needs with these arguments
- * (0 for arguments it does not cover, or when there is no work): an fp32
- * scratch pool of N * H * D * D values and N slot indices; with fp32 inputs
- * also four reversed input copies and one output copy of T_total * H * D
- * elements. */
+/* Bytes of device workspace gdr_linear_chunk_bwd or gdr_gated_linear_chunk_bwd
+ * needs with these arguments (0 for arguments they do not cover, or when
+ * there is no work): an fp32 scratch pool of N * HV * D * D values and N
+ * slot indices; with fp32 inputs also reversed copies of q, k (T_total * HK
+ * * D elements each), v and dout (T_total * HV * D each) and an fp32 output
+ * copy of T_total * HV * D; with grouped key heads (HV > HK) q and k
+ * repeated over each group (T_total * HV * D elements each); with a gate or
+ * grouped key heads two fp32 buffers of T_total * HV * D (dq and dk per value
+ * head); with a gate two fp32 arrays of T_total * HV. */
 size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
 
 /* Gradients of causal linear attention ("From Attention to Learned Memory",
@@ -220,18 +225,34 @@ size_t gdr_linear_chunk_bwd_workspace_bytes(const gdr_args *a);
  * and a loss with upstream gradient dout (= dL/do), writes
  *   dq [T_total, HK, DK], dk [T_total, HK, DK], dv [T_total, HV, DV]
  * (contiguous, out_dtype). `a` describes the forward call: q, k, v, their
- * strides and in_dtype, cu_seqlens, the initial state S_0 read from
- * state_pool[slot_idx[n]] (never written) unless GDR_FLAG_ZERO_INIT, scale,
- * chunk_size 64; `a->o` is ignored. dout is [T_total, HV, DV], contiguous, in
- * in_dtype. Covered: the linear rule with gate NONE, HV == HK, one transition
+ * strides and in_dtype, cu_seqlens, HK and HV (HV a multiple of HK: value
+ * head h reads key head h / (HV / HK), and dq, dk sum over each group), the
+ * initial state S_0 read from state_pool[slot_idx[n]] (never written) unless
+ * GDR_FLAG_ZERO_INIT, scale, chunk_size 64; `a->o` is ignored. dout is
+ * [T_total, HV, DV], contiguous, in in_dtype. Covered: the linear rule with
+ * gate NONE (a scalar gate is gdr_gated_linear_chunk_bwd), one transition
  * per token (else GDR_E_UNSUPPORTED). The final state's gradient is taken as
  * zero and the initial state's is not formed. `workspace` (device memory,
- * 256-byte aligned, at least gdr_linear_chunk_bwd_workspace_bytes) is scratch;
- * calls sharing one must not overlap. Each gradient runs as one chunkwise
- * forward pass with the roles of q, k, v and dout exchanged (dk and dv walk
- * every sequence's tokens backwards). */
+ * 256-byte aligned, at least gdr_linear_chunk_bwd_workspace_bytes) is
+ * scratch; calls sharing one must not overlap. Each gradient runs as one
+ * chunkwise forward pass with the roles of q, k, v and dout exchanged (dk and
+ * dv walk every sequence's tokens backwards). */
 gdr_status gdr_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* The same gradients for the linear rule with a scalar gate (same page and
+ * section; the state decays as S_t = alpha_t S_{t-1} + v_t k_t^T with
+ * a->g = log alpha, fp32 [T_total, HV]), plus the log-decays' gradient
+ *   dg [T_total, HV] fp32:  dg_t = sum over the tokens i >= t of t's
+ *   sequence of (q_i . dq_i - k_i . dk_i), dq_i and dk_i taken per value head
+ * (each pair's decay exponent is the sum of the log-decays between them, so
+ * a log-decay's gradient collects every pair that spans it). Requires gate
+ * SCALAR (else GDR_E_UNSUPPORTED); dg is device memory, 4-byte aligned, not
+ * overlapping any input or gradient. Everything else as gdr_linear_chunk_bwd;
+ * the passes that walk backwards take each token's decay from the token
+ * after it. */
+gdr_status gdr_gated_linear_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                      float *dg, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace gdr_recurrent_bwd needs with these arguments
  * (0 when N == 0 or the arguments are invalid): fp32 checkpoints of the state

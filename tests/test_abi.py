@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                             "gdr_linear_chunk_bwd", "gdr_ring_record_elements",
                             "gdr_ring_record_stride", "gdr_verify_ring", "gdr_state_fold",
                             "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd",
-                            "gdr_chunk_fwd_noalloc"])
+                            "gdr_chunk_fwd_noalloc", "gdr_gated_linear_chunk_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(L, name)
-    assert L.gdr_abi_version() == gdr.ABI_VERSION == 6
+    assert L.gdr_abi_version() == gdr.ABI_VERSION == 7
 
 
 def test_args_struct_matches_header_field_order():
@@ -213,8 +213,10 @@ def test_binding_checks_product_rows():
 
 
 def test_linear_backward_rejects_on_host():
-    """The backward covers the linear rule without a gate and HV == HK; it
-    checks its outputs, their overlaps and the workspace before any launch."""
+    """The backward covers the linear rule, plain (gdr_linear_chunk_bwd) or
+    with a scalar gate (gdr_gated_linear_chunk_bwd), with grouped key heads;
+    it checks its outputs, their overlaps and the workspace before any
+    launch."""
     gdr, L = _lib()
     a = _valid_args(gdr)
     a.rule, a.gate, a.HV, a.beta, a.g = 1, 0, 2, None, None
@@ -225,10 +227,13 @@ def test_linear_backward_rejects_on_host():
     a.in_dtype = 0                                     # fp32 inputs: reversed copies as well
     assert L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a)) >= 4 * rows * 4 + rows * 4 + need
     a.in_dtype = 1
-    dout, dq, dk, dv, ws = 0x7000000, 0x8000000, 0x8100000, 0x8200000, 0x10000000
+    dout, dq, dk, dv, dg, ws = 0x7000000, 0x8000000, 0x8100000, 0x8200000, 0x8300000, 0x10000000
     call = lambda aa, **kw: L.gdr_linear_chunk_bwd(
         ctypes.byref(aa), kw.get("dout", dout), kw.get("dq", dq), kw.get("dk", dk), kw.get("dv", dv),
         kw.get("ws", ws), kw.get("wsb", need), None)
+    gcall = lambda aa, **kw: L.gdr_gated_linear_chunk_bwd(
+        ctypes.byref(aa), kw.get("dout", dout), kw.get("dq", dq), kw.get("dk", dk), kw.get("dv", dv),
+        kw.get("dg", dg), kw.get("ws", ws), kw.get("wsb", need), None)
     assert call(a, ws=None) == 3                      # no workspace
     assert call(a, wsb=need - 1) == 3                 # short workspace
     assert call(a, ws=ws + 16) == 1                   # misaligned workspace
@@ -236,12 +241,35 @@ def test_linear_backward_rejects_on_host():
     assert call(a, dv=dq + 64) == 1                   # outputs overlap
     assert call(a, dq=0x1000) == 1                    # dq overlaps q
     assert call(a, dout=dout + 4) == 1                # misaligned dout
+    assert gcall(a) == 2                              # the gated entry wants a gate
     b = _valid_args(gdr)                              # delta rule, scalar gate
     assert L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(b)) == 0
     assert call(b) == 2
-    a.HV, a.v_stride_t = 4, 4 * 128                   # grouped heads
-    assert call(a) == 2
-
+    assert gcall(b) == 2
+    # grouped heads (HV = 2 HK): q and k repeated per value head, fp32 dq, dk
+    # per value head
+    a.HV, a.v_stride_t = 4, 4 * 128
+    grouped = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    vrows = a.T_total * 4 * 128
+    assert grouped >= need + 2 * vrows * 2 + 2 * vrows * 4
+    assert call(a, wsb=grouped - 1) == 3
+    assert call(a, dq=dv + 64, wsb=grouped) == 1      # dq overlaps dv
+    # the scalar gate: the plain entry refuses it (it has no dg), the gated
+    # one checks dg
+    a.gate, a.g = 1, 0x2000
+    gated = L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    assert gated >= grouped + 2 * a.T_total * 4 * 4
+    assert call(a, wsb=gated) == 2
+    assert gcall(a, dg=None, wsb=gated) == 1
+    assert gcall(a, dg=dg + 2, wsb=gated) == 1        # misaligned dg
+    assert gcall(a, dg=0x2000 + 4, wsb=gated) == 1    # dg overlaps g
+    assert gcall(a, dg=dv, wsb=gated) == 1            # dg overlaps dv
+    assert gcall(a, wsb=gated - 1) == 3
+    a.gate = 2                                        # channel gate
+    assert L.gdr_linear_chunk_bwd_workspace_bytes(ctypes.byref(a)) == 0
+    assert gcall(a, wsb=gated) == 2
+    a.gate, a.products = 1, 2                         # several transitions per token
+    assert gcall(a, wsb=gated) == 2
 
 
 def test_recurrent_backward_rejects_on_host():
