@@ -22,7 +22,8 @@ HBM bandwidth (its binding roofline), with its MFMA fraction alongside;
 `configs` holds the same figures for each of the five configurations (and
 configuration 2's linear-attention run), the decode step's as steps/s and HBM
 fraction; `linear_backward` and `gdn_backward` time the gradients on the
-Gated DeltaNet batch, `gated_linear_backward` those of gated linear attention
+Gated DeltaNet batch (`gdn_chunk_backward` the delta rule's chunkwise),
+`gated_linear_backward` those of gated linear attention
 on the ragged grouped-head batch (chunkwise, the tokenwise backward beside it); `recurrent_fwd` the tokenwise recurrence on a short
 batch; `delta_product` the chunkwise prefill of Gated DeltaProduct (2
 transitions per token); `speculative` a 4-token verify window per sequence and
@@ -369,10 +370,12 @@ def bench_linear_bwd(w: synth.Workload, steps: int, warmup: int = 3):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_recurrent_bwd(w: synth.Workload, steps: int, warmup: int = 2):
-    """Mean time (ms) of gdr_recurrent_bwd on w's batch (the checkpointing
-    walk and the reduction of the partial sums), with a workspace allocated
-    once; also its workspace bytes."""
+def bench_recurrent_bwd(w: synth.Workload, steps: int, warmup: int = 2, entry: str = "recurrent_bwd"):
+    """Mean time (ms) of gdr_recurrent_bwd (the checkpointing walk and the
+    reduction of the partial sums) or, with entry "chunk_bwd", of
+    gdr_chunk_bwd (the forward walk, the reverse maps, the reverse walk, the
+    per-chunk gradients and the group sums) on w's batch, with a workspace
+    allocated once; also its workspace bytes."""
     import ctypes
     import torch
     import gated_delta_rule_gdr_amd as gdr
@@ -390,13 +393,13 @@ def bench_recurrent_bwd(w: synth.Workload, steps: int, warmup: int = 2):
     args, _ = gdr._prepare(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["slot_idx"],
                            a["cu_seqlens"], None, None, w.rule, w.gate, w.zero_init, False, 64,
                            torch.float32)
-    nbytes = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(args))
+    nbytes = getattr(L, "gdr_" + entry + "_workspace_bytes")(ctypes.byref(args))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    kw = dict(rule=w.rule) if entry == "recurrent_bwd" else {}
 
     def run():
-        return gdr.recurrent_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"], a["pool"], a["slot_idx"],
-                                 a["cu_seqlens"], rule=w.rule, gate=w.gate, zero_init=w.zero_init,
-                                 workspace=ws)
+        return getattr(gdr, entry)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"], a["pool"], a["slot_idx"],
+                                   a["cu_seqlens"], gate=w.gate, zero_init=w.zero_init, workspace=ws, **kw)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -738,6 +741,14 @@ def main():
             "algorithmic_bytes": gb, "hbm_gbs": gb / (gt * 1e-3) / 1e9,
             "hbm_frac": gb / (gt * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": gws,
             "traffic": committed_traffic("recurrent_bwd_kernel+recurrent_bwd_reduce_kernel", gw.name, RBWD_SRC)}
+        # the same gradients chunkwise (forward walk, reverse maps, reverse
+        # walk, per-chunk gradients, group sums)
+        ct, cws = bench_recurrent_bwd(gw, args.steps, entry="chunk_bwd")
+        result["gdn_chunk_backward"] = {
+            "workload": gw.name, "steps": args.steps, "ms": ct, "tokens_per_s": T / (ct * 1e-3),
+            "algorithmic_bytes": gb, "hbm_gbs": gb / (ct * 1e-3) / 1e9,
+            "hbm_frac": gb / (ct * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": cws,
+            "speedup_vs_tokenwise": gt / ct}
     if not args.no_product:
         pw, P = synth.workload(synth.GDN), 2
         pt = bench_product(pw, P, args.product_steps)

@@ -24,7 +24,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_workspace_bytes", "recurrent_step", "recurrent_fwd", "linear_chunk_bwd", "chunk_bwd", "recurrent_bwd",
            "verify_ring", "state_fold", "lib", "lib_path", "GdrError",
            "abi_version", "Args", "load"]
 
@@ -108,6 +108,12 @@ def load() -> ctypes.CDLL:
     L.gdr_gated_linear_chunk_bwd.restype = ctypes.c_int
     L.gdr_gated_linear_chunk_bwd.argtypes = [ctypes.POINTER(Args)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t,
                                                                                             ctypes.c_void_p]
+    for name in ("gdr_recurrent_bwd", "gdr_chunk_bwd"):
+        getattr(L, name + "_workspace_bytes").restype = ctypes.c_size_t
+        getattr(L, name + "_workspace_bytes").argtypes = [ctypes.POINTER(Args)]
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = [ctypes.POINTER(Args)] + [ctypes.c_void_p] * 8 + [ctypes.c_size_t,
+                                                                                     ctypes.c_void_p]
     L.gdr_recurrent_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdr_recurrent_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Args)]
     L.gdr_recurrent_bwd.restype = ctypes.c_int
@@ -363,6 +369,22 @@ def recurrent_bwd(q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, *, scale=Non
     (gated calls) and dstate0 [N, HV, DK, DV] fp32 (the initial state's
     gradient, transposed like the pool) unless ``dstate0`` is False; absent
     entries are None. The pool is read, never written."""
+    return _grads("gdr_recurrent_bwd", q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, scale, rule, gate,
+                  zero_init, out_dtype, dstate0, workspace, debug_checks)
+
+
+def chunk_bwd(q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, *, scale=None, gate=None, zero_init=False,
+              out_dtype=None, dstate0=True, workspace=None, debug_checks=False):
+    """The same gradients as recurrent_bwd for the delta rule with gate
+    "none" or "scalar", computed chunkwise (gdr_chunk_bwd): a scan of the
+    state's gradient over the chunk boundaries, then every chunk on its
+    own. Same arguments and result."""
+    return _grads("gdr_chunk_bwd", q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, scale, "delta", gate,
+                  zero_init, out_dtype, dstate0, workspace, debug_checks)
+
+
+def _grads(entry, q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, scale, rule, gate, zero_init, out_dtype,
+           dstate0, workspace, debug_checks):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     T, HK, DK = q.shape
@@ -379,14 +401,13 @@ def recurrent_bwd(q, k, v, g, beta, do, pool, slot_idx, cu_seqlens, *, scale=Non
     ds = torch.empty((slot_idx.shape[0], v.shape[1], DK, v.shape[2]), **f32) if dstate0 else None
     L = load()
     if workspace is None:
-        nbytes = L.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(a))
+        nbytes = getattr(L, entry + "_workspace_bytes")(ctypes.byref(a))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
         raise TypeError(f"workspace must be a contiguous uint8 tensor on {q.device}")
     ptr = lambda x: None if x is None else x.data_ptr()
-    _check(L.gdr_recurrent_bwd(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                               ptr(dbeta), ptr(dg), ptr(ds), workspace.data_ptr(), workspace.numel(),
-                               _stream(q)))
+    _check(getattr(L, entry)(ctypes.byref(a), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             ptr(dbeta), ptr(dg), ptr(ds), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dstate0=ds)
 
 

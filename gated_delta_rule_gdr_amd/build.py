@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
 SOURCES = ["gdr_api.hip", "recurrent_step.hip", "recurrent_fwd.hip", "chunk_fwd.hip", "chunk_fwd_ws.hip",
-           "chunk_fwd_kda.hip", "linear_bwd.hip", "recurrent_bwd.hip"]
+           "chunk_fwd_kda.hip", "linear_bwd.hip", "recurrent_bwd.hip", "chunk_bwd.hip"]
 ARCH = "gfx950"
 
 

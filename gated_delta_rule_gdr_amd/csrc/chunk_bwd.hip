@@ -1,0 +1,782 @@
+// Chunkwise backward of the gated delta rule (scalar gate or none): the
+// reverse-mode gradient of the chunk equations, regrouped the way "From
+// Attention to Learned Memory" regroups the linear-attention backward
+// (section "Backward: reverse the boundary scan, then differentiate each
+// chunk"): one scan of the state's gradient over the chunk boundaries, from
+// the last chunk back, then every chunk differentiated on its own.
+//
+// Forward chunk (C = 64 tokens, incoming state S_c as S^T [DK, DV], G the
+// in-chunk cumulative log-decay, gamma_i = e^{G_i}, Gamma_ij = e^{G_i - G_j}
+// for j <= i, s the query scale; the chunk equations of "You Could Have Come
+// Up With Kimi Delta Attention", section 6, with a scalar gate):
+//   K_l = gamma (.) K,  Q_l = gamma (.) Q,  K_e = e^{G_last - G} (.) K
+//   R  = strict-lower( beta_i Gamma_ij k_i.k_j ),  T = (I + R)^{-1}
+//   A  = lower( s Gamma_ij q_i.k_j )
+//   X  = K_l S^T,  Rv = beta (.) (V - X),  E = T Rv
+//   O  = s Q_l S^T + A E
+//   S^T_{c+1} = e^{G_last} S^T_c + K_e^T E
+// Backward, with dS^T_{c+1} the gradient of the state after the chunk and
+// dO the outputs' gradient:
+//   dE  = A^T dO + K_e dS^T_{c+1},  dRv = T^T dE,  dV = beta (.) dRv
+//   dX  = -beta (.) dRv,  dA = dO E^T (lower),  dR = -dRv E^T (strict lower)
+//   dQ_l = s dO S,  dK_l = dX S,  dK_e = E dS_{c+1}
+//   dS^T_c = e^{G_last} dS^T_{c+1} + K_l^T dX + s Q_l^T dO = M dS^T_{c+1} + Y
+// with W = T Diag(beta) K_l, M = e^{G_last} I - W^T K_e (the transpose of
+// the linear part of the forward map S^T_c -> S^T_{c+1}, as the adjoint of a
+// linear map must be) and Y = (s Q_l - A W)^T dO. Through the Gram matrices (KK = K K^T, QK = Q K^T):
+//   P_R = dR (.) beta_i Gamma_ij,  P_A = dA (.) s Gamma_ij
+//   dk = P_R K + P_R^T K + P_A^T Q + gamma (.) dK_l + e^{G_last - G} (.) dK_e
+//   dq = P_A K + gamma (.) dQ_l
+//   dbeta_i = sum_v (V - X)_iv dRv_iv + sum_j dR_ij Gamma_ij k_i.k_j
+//   dG_i = rowsum_i(N) - colsum_i(N) + gamma_i (k_i.dK_l,i + q_i.dQ_l,i)
+//          - e^{G_last - G_i} k_i.dK_e,i   (N = dR (.) R + dA (.) A)
+//   dG_last += sum_j e^{G_last - G_j} k_j.dK_e,j + e^{G_last} <dS_{c+1}, S_c>
+//   dg_t = sum_{i >= t} dG_i over the chunk (G is a prefix sum of g).
+//
+// Kernels, in order:
+//   1. the general prefill kernel in its checkpointing form (chunk_fwd.hip):
+//      S^T_c at every chunk start (no outputs, the pool untouched);
+//   2. bwd_prep_kernel, one workgroup per (chunk, value head): the Grams, T,
+//      W and the reverse map's M and Y, written as fp32 [DK, DK] / [DK, DV];
+//   3. bwd_walk_kernel, one workgroup per (sequence, value head, 16 value
+//      columns): dS^T from zero at the sequence end back to the start,
+//      dS^T_{c+1} stored per chunk; the last one is the initial state's
+//      gradient;
+//   4. bwd_grad_kernel, one workgroup per (chunk, value head): the formulas
+//      above, over 16-column blocks of the value dimension, dq and dk per
+//      value head in fp32;
+//   5. bwd_group_sum_kernel: dq and dk summed over each key head's group of
+//      value heads, in the output dtype.
+// Everything is fp32: the matrix products on v_mfma_f32_16x16x4_f32 with
+// operands from LDS (or, in the walk, from memory), fp32 accumulation.
+#include <cstdint>
+
+#include "chunk_common.h"
+
+namespace gdr {
+namespace {
+
+using chunk::f32x4;
+constexpr int CB = 64;        // tokens per chunk
+constexpr int PC = CB + 4;    // pitch of the C x C matrices in LDS
+constexpr int BW = 16;        // value columns per block of the gradient kernel
+constexpr int PB = BW + 4;    // pitch of those blocks
+
+__device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc (one 16 x 16 tile) += A (16 x 4n) B (4n x 16), n a multiple of 4.
+// A's element (i, k) is a[i * ai + k * ak], B's element (k, j) is
+// b[k * bk + j * bj]. The k range is taken in blocks of 16, four MFMAs each:
+// at step j of a block lane (r, g) supplies A(r, k) and B(k, r) for
+// k = 16 blk + 4g + j (any assignment of the k's to steps gives the same
+// sum as long as A and B agree), so that a lane's four A values (four B
+// values) of a block are adjacent in memory when ak == 1 (bk == 1): one
+// 16-byte read. The tile's element (4g + e, r) is acc[e].
+template <bool AK1, bool BK1>
+__device__ __forceinline__ f32x4 mm(const float *a, int ai, int ak, const float *b, int bk, int bj, int n,
+                                    f32x4 acc, int r, int g) {
+  const float *pa = a + r * ai + 4 * g * (AK1 ? 1 : ak);
+  const float *pb = b + 4 * g * (BK1 ? 1 : bk) + r * bj;
+  const int sa = 16 * (AK1 ? 1 : ak), sb = 16 * (BK1 ? 1 : bk);
+#pragma unroll 2
+  for (int s = 0; s < n; s += 4) {
+    float av[4], bv[4];
+    if constexpr (AK1) {
+      const float4 x = *reinterpret_cast<const float4 *>(pa);
+      av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = pa[j * ak];
+    }
+    if constexpr (BK1) {
+      const float4 x = *reinterpret_cast<const float4 *>(pb);
+      bv[0] = x.x; bv[1] = x.y; bv[2] = x.z; bv[3] = x.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = pb[j * bk];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mf(av[j], bv[j], acc);
+    pa += sa;
+    pb += sb;
+  }
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <bool BF16>
+__device__ __forceinline__ float ld_in(const void *p, int64_t i) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+  else return static_cast<const float *>(p)[i];
+}
+
+struct BwdParams {
+  const void *q, *k, *v, *dout;
+  int64_t q_stride, k_stride, v_stride;   // elements between tokens (dout: HV * D)
+  const float *g, *beta;
+  const int32_t *cu_seqlens;
+  int32_t N, HK, HV, ratio;
+  float scale;
+  int gated, out_bf16;
+  int64_t flat;                           // flat chunk indices: [0, flat)
+  const float *ckf;                       // S^T_c per (flat chunk, value head)
+  float *ckb;                             // dS^T_{c+1} per (flat chunk, value head)
+  float *M, *Y;                           // the reverse map per (flat chunk, value head)
+  float *dqh, *dkh;                       // [T, HV, D] fp32
+  void *dv;                               // [T, HV, D] out dtype
+  float *dbeta, *dg;                      // [T, HV]
+  float *dstate0;                         // [N, HV, D, D] or NULL
+};
+
+// The chunk of flat index F: sequence n (the last with base(n) <= F, base(n)
+// = floor(cu[n] / 64) + n) and its first token t0; valid is false for an
+// index between two sequences' ranges.
+struct ChunkAt {
+  int64_t t0;
+  int n, L;
+  bool valid;
+};
+
+__device__ __forceinline__ ChunkAt chunk_at(const int32_t *cu, int N, int64_t F) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)(cu[mid] >> 6) + mid <= F) lo = mid;
+    else hi = mid - 1;
+  }
+  ChunkAt c;
+  c.n = lo;
+  const int64_t bos = cu[lo], eos = cu[lo + 1];
+  c.t0 = bos + (int64_t)CB * (F - ((int64_t)(bos >> 6) + lo));
+  c.valid = c.t0 < eos;
+  c.L = c.valid ? (int)min<int64_t>(CB, eos - c.t0) : 0;
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// shared chunk set-up: inputs into LDS, the gate's prefix sums, the Gram
+// matrices and T = (I + R)^{-1}
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct ChunkSm {
+  static constexpr int PD = D + 4;
+  // (16-byte aligned arrays: their rows are read 16 bytes at a time)
+  alignas(16) float kk[CB][PD];   // keys (fp32), rows >= L zero
+  alignas(16) float kg[CB][PC];   // Gamma (.) K K^T, strictly lower
+  alignas(16) float ag[CB][PC];   // A = s Gamma (.) Q K^T, lower
+  alignas(16) float tt[CB][PC];   // T
+  float G[CB], eG[CB], eGl[CB], beta[CB];
+  float gl;                       // e^{G_last}
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ void load_rows(float (*dst)[D + 4], const void *src, int64_t stride, int64_t off0,
+                                          int L, int tid) {
+  constexpr int Q4 = D / 4;
+  for (int it = tid; it < CB * Q4; it += 256) {
+    const int row = it / Q4, c = 4 * (it - row * Q4);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < L) {
+      const int64_t e = off0 + row * stride + c;
+      if constexpr (BF16) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(src) + e);
+        x = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+      } else {
+        x = *reinterpret_cast<const float4 *>(static_cast<const float *>(src) + e);
+      }
+    }
+    *reinterpret_cast<float4 *>(&dst[row][c]) = x;
+  }
+}
+
+// Keys and queries (into qq), beta and the gate; then the Grams and T. Ends
+// with a barrier.
+template <bool BF16, int D>
+__device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams &p, const ChunkAt &ck, int h,
+                            int tid) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int hk = h / p.ratio;
+  load_rows<BF16, D>(sm.kk, p.k, p.k_stride, ck.t0 * p.k_stride + (int64_t)hk * D, ck.L, tid);
+  load_rows<BF16, D>(qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
+  if (w == 0) {
+    const bool ok = lane < ck.L;
+    const float gv = (ok && p.gated) ? p.g[(ck.t0 + lane) * p.HV + h] : 0.f;
+    const float G = chunk::wave_scan(gv);
+    const float Gl = __shfl(G, 63, 64);
+    sm.G[lane] = G;
+    sm.eG[lane] = __expf(G);
+    sm.eGl[lane] = __expf(Gl - G);
+    sm.beta[lane] = ok ? p.beta[(ck.t0 + lane) * p.HV + h] : 0.f;
+    if (lane == 0) sm.gl = __expf(Gl);
+  }
+  __syncthreads();
+  // Grams: wave w forms row block w against column blocks J <= w
+  for (int J = 0; J <= w; ++J) {
+    f32x4 a = mm<true, true>(&sm.kk[16 * w][0], D + 4, 1, &sm.kk[16 * J][0], 1, D + 4, D / 4, zero4(), r, g);
+    f32x4 b = mm<true, true>(&qq[16 * w][0], D + 4, 1, &sm.kk[16 * J][0], 1, D + 4, D / 4, zero4(), r, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e, j = 16 * J + r;
+      const float gm = j <= i ? __expf(sm.G[i] - sm.G[j]) : 0.f;
+      sm.kg[i][j] = j < i ? a[e] * gm : 0.f;
+      sm.ag[i][j] = p.scale * b[e] * gm;
+    }
+  }
+  for (int J = w + 1; J < 4; ++J)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e, j = 16 * J + r;
+      sm.kg[i][j] = 0.f;
+      sm.ag[i][j] = 0.f;
+    }
+  __syncthreads();
+  // diagonal blocks of T: lane b < 16 of wave w solves column b of
+  // (I + R_ww) T_ww = I by forward substitution, R = beta_i kg
+  if (lane < 16) {
+    float t[16];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int i = 16 * w + a;
+      float x = a == lane ? 1.f : 0.f;
+      const float bi = sm.beta[i];
+#pragma unroll
+      for (int c = 0; c < a; ++c) x -= bi * sm.kg[i][16 * w + c] * t[c];
+      t[a] = x;
+    }
+#pragma unroll
+    for (int a = 0; a < 16; ++a) sm.tt[16 * w + a][16 * w + lane] = t[a];
+  }
+  // the blocks above the diagonal are zero
+  for (int J = w + 1; J < 4; ++J)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.tt[16 * w + 4 * g + e][16 * J + r] = 0.f;
+  __syncthreads();
+  // blocks below: T_IJ = -T_II sum_{K=J}^{I-1} R_IK T_KJ, by distance I - J
+  for (int d = 1; d < 4; ++d) {
+    const int I = w, J = w - d;
+    if (J >= 0) {
+      f32x4 y = mm<true, false>(&sm.kg[16 * I][16 * J], PC, 1, &sm.tt[16 * J][16 * J], PC, 1, 4 * d, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] *= sm.beta[16 * I + 4 * g + e];
+      // Y through the block's own slot (this wave alone reads and writes it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.tt[16 * I + 4 * g + e][16 * J + r] = y[e];
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot holds Y
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 t = mm<true, false>(&sm.tt[16 * I][16 * I], PC, 1, &sm.tt[16 * I][16 * J], PC, 1, 4, zero4(), r, g);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.tt[16 * I + 4 * g + e][16 * J + r] = -t[e];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. the reverse map of each chunk: M = e^{G_last} I - W^T K_e,
+//    Y = (s Q_l - A W)^T dO, W = T Diag(beta) K_l
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct PrepBwdSm {
+  ChunkSm<D> c;
+  alignas(16) float qq[CB][D + 4];   // queries, then Z = s Q_l - A W
+  alignas(16) float ww[CB][D + 4];   // W, then dO
+};
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  __shared__ PrepBwdSm<D> sm;
+  constexpr int PD = D + 4;
+  const int64_t F = blockIdx.x / p.HV;
+  const int h = blockIdx.x - (int)F * p.HV;
+  const ChunkAt ck = chunk_at(p.cu_seqlens, p.N, F);
+  if (!ck.valid) return;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            g = lane >> 4;
+  chunk_setup<BF16, D>(sm.c, sm.qq, p, ck, h, tid);
+  // T <- T Diag(beta gamma), so that T K = W
+  for (int it = tid; it < CB * CB; it += 256) {
+    const int i = it / CB, j = it - i * CB;
+    sm.c.tt[i][j] *= sm.c.beta[j] * sm.c.eG[j];
+  }
+  __syncthreads();
+  // W, row block w (T lower: k < 16 (w + 1))
+  for (int m = 0; m < D / 16; ++m) {
+    const f32x4 a = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), zero4(), r, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.ww[16 * w + 4 * g + e][16 * m + r] = a[e];
+  }
+  __syncthreads();
+  // keys decayed to the chunk's end, in place
+  for (int it = tid; it < CB * D; it += 256) {
+    const int i = it / D, j = it - i * D;
+    sm.c.kk[i][j] *= sm.c.eGl[i];
+  }
+  __syncthreads();
+  const int64_t mbase = (F * p.HV + h) * (int64_t)(D * D);
+  // M = gl I - W^T K_e: wave w takes rows (D / 4) w ..
+  constexpr int RT = D / 64;   // 16-row tiles per wave
+  for (int ti = 0; ti < RT; ++ti) {
+    const int a0 = (D / 4) * w + 16 * ti;
+    for (int m = 0; m < D / 16; ++m) {
+      const f32x4 a = mm<false, false>(&sm.ww[0][a0], 1, PD, &sm.c.kk[0][16 * m], PD, 1, CB / 4, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = a0 + 4 * g + e, col = 16 * m + r;
+        p.M[mbase + (int64_t)row * D + col] = (row == col ? sm.c.gl : 0.f) - a[e];
+      }
+    }
+  }
+  // Z = s Q_l - A W, row block w, in place of this wave's query rows
+  for (int m = 0; m < D / 16; ++m) {
+    const f32x4 a = mm<true, false>(&sm.c.ag[16 * w][0], PC, 1, &sm.ww[0][16 * m], PD, 1, 4 * (w + 1), zero4(), r, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e, j = 16 * m + r;
+      sm.qq[i][j] = p.scale * sm.c.eG[i] * sm.qq[i][j] - a[e];
+    }
+  }
+  __syncthreads();
+  // dO into W's place
+  load_rows<BF16, D>(sm.ww, p.dout, (int64_t)p.HV * D, ck.t0 * (int64_t)p.HV * D + (int64_t)h * D, ck.L, tid);
+  __syncthreads();
+  // Y = Z^T dO
+  for (int ti = 0; ti < RT; ++ti) {
+    const int a0 = (D / 4) * w + 16 * ti;
+    for (int m = 0; m < D / 16; ++m) {
+      const f32x4 a = mm<false, false>(&sm.qq[0][a0], 1, PD, &sm.ww[0][16 * m], PD, 1, CB / 4, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.Y[mbase + (int64_t)(a0 + 4 * g + e) * D + 16 * m + r] = a[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. the reverse walk: dS^T_c = M_c dS^T_{c+1} + Y_c from dS^T = 0 at the
+//    sequence's end; dS^T_{c+1} stored for chunk c; dS^T_0 to dstate0
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_walk_kernel(BwdParams p) {
+  __shared__ alignas(16) float xs[2][D][PB];   // the state gradient's 16 columns, by parity
+  constexpr int GRP = D / 16;
+  constexpr int RT = D / 64;       // 16-row tiles per wave
+  constexpr int KB = D / 16;       // 16-wide k blocks
+  // all workgroups of one (sequence, head) get ids equal modulo 8: one XCD,
+  // whose L2 serves them each chunk's M
+  const int b = blockIdx.x;
+  const int gi = (b / (8 * GRP)) * 8 + (b & 7), vb = (b >> 3) % GRP;
+  if (gi >= p.N * p.HV) return;
+  const int n = gi / p.HV, h = gi - n * p.HV;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            g = lane >> 4;
+  const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  const int64_t nc = (eos - bos + CB - 1) / CB;
+  const int64_t base = (int64_t)(p.cu_seqlens[n] >> 6) + n;
+  const int col0 = 16 * vb;
+  // A operands of M (rows (D/4) w + 16 t + r, k = 16 kb + 4g + j) and the
+  // accumulators' Y, loaded one chunk ahead
+  auto load_ops = [&](int64_t c, float4 (&am)[RT][KB], f32x4 (&ya)[RT]) {
+    const int64_t mb = ((base + c) * p.HV + h) * (int64_t)(D * D);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int a0 = (D / 4) * w + 16 * t;
+      const float *mr = p.M + mb + (int64_t)(a0 + r) * D + 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) am[t][kb] = *reinterpret_cast<const float4 *>(mr + 16 * kb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ya[t][e] = p.Y[mb + (int64_t)(a0 + 4 * g + e) * D + col0 + r];
+    }
+  };
+  f32x4 x[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) x[t] = zero4();
+  float4 am[RT][KB];
+  f32x4 ya[RT];
+  if (nc > 0) load_ops(nc - 1, am, ya);
+  int par = 0;
+  for (int64_t c = nc - 1; c >= 0; --c) {
+    const int64_t mb = ((base + c) * p.HV + h) * (int64_t)(D * D);
+    // dS^T_{c+1}: to the checkpoint and to LDS
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = (D / 4) * w + 16 * t + 4 * g + e;
+        p.ckb[mb + (int64_t)row * D + col0 + r] = x[t][e];
+        xs[par][row][r] = x[t][e];
+      }
+    // the next chunk's operands (chunk 0 reloads its own: every iteration
+    // issues the same loads)
+    float4 an[RT][KB];
+    f32x4 yn[RT];
+    load_ops(c > 0 ? c - 1 : 0, an, yn);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      f32x4 acc = ya[t];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float av[4] = {am[t][kb].x, am[t][kb].y, am[t][kb].z, am[t][kb].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mf(av[j], xs[par][16 * kb + 4 * g + j][r], acc);
+      }
+      x[t] = acc;
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      ya[t] = yn[t];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) am[t][kb] = an[t][kb];
+    }
+    par ^= 1;
+  }
+  if (p.dstate0) {
+    float *d0 = p.dstate0 + ((int64_t)n * p.HV + h) * (int64_t)(D * D);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d0[(int64_t)((D / 4) * w + 16 * t + 4 * g + e) * D + col0 + r] = x[t][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. per-chunk gradients
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct GradSm {
+  ChunkSm<D> c;
+  union alignas(16) {
+    float qq[CB][D + 4];        // queries (set-up, and again for the last step)
+    struct {
+      float sb[D][PB];          // S^T_c, this block's columns
+      float db[D][PB];          // dS^T_{c+1}, this block's columns
+      float vb[CB][PB];         // V
+      float ob[CB][PB];         // dO
+      float rv[CB][PB];         // Rv
+      float eb[CB][PB];         // E
+      float de[CB][PB];         // dE
+      float dr[CB][PB];         // dRv
+      float dx[CB][PB];         // dX
+    } b;
+  } u;
+  float dG[CB], dbeta[CB];
+  float sds;                    // <dS_{c+1}, S_c>
+};
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
+  __shared__ GradSm<D> sm;
+  constexpr int PD = D + 4;
+  constexpr int NT = D / 16;
+  const int64_t F = blockIdx.x / p.HV;
+  const int h = blockIdx.x - (int)F * p.HV;
+  const ChunkAt ck = chunk_at(p.cu_seqlens, p.N, F);
+  if (!ck.valid) return;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            g = lane >> 4;
+  const int hk = h / p.ratio;
+  chunk_setup<BF16, D>(sm.c, sm.u.qq, p, ck, h, tid);
+  if (tid < CB) {
+    sm.dG[tid] = 0.f;
+    sm.dbeta[tid] = 0.f;
+  }
+  if (tid == 0) sm.sds = 0.f;
+
+  const int64_t mb = (F * p.HV + h) * (int64_t)(D * D);
+  const int64_t HVD = (int64_t)p.HV * D;
+  f32x4 dA[4], dR[4], dQl[NT], dKl[NT], dKe[NT];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) dA[J] = dR[J] = zero4();
+#pragma unroll
+  for (int m = 0; m < NT; ++m) dQl[m] = dKl[m] = dKe[m] = zero4();
+  float dbl[4] = {0.f, 0.f, 0.f, 0.f};   // sum over columns of (V - X) dRv, rows 16w + 4g + e
+  float sds = 0.f;
+  float beta_r[4], eG_r[4], eGl_r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 16 * w + 4 * g + e;
+    beta_r[e] = sm.c.beta[i];
+    eG_r[e] = sm.c.eG[i];
+    eGl_r[e] = sm.c.eGl[i];
+  }
+
+  for (int vb = 0; vb < D / BW; ++vb) {
+    const int col0 = BW * vb;
+    __syncthreads();   // the previous block (or the queries) is no longer read
+    for (int it = tid; it < D * BW; it += 256) {
+      const int row = it / BW, c = it - row * BW;
+      const float s = p.ckf[mb + (int64_t)row * D + col0 + c];
+      const float d = p.ckb[mb + (int64_t)row * D + col0 + c];
+      sm.u.b.sb[row][c] = s;
+      sm.u.b.db[row][c] = d;
+      sds += s * d;
+    }
+    for (int it = tid; it < CB * BW; it += 256) {
+      const int row = it / BW, c = it - row * BW;
+      const bool ok = row < ck.L;
+      const int64_t e = (ck.t0 + row) * HVD + (int64_t)h * D + col0 + c;
+      sm.u.b.vb[row][c] = ok ? ld_in<BF16>(p.v, (ck.t0 + row) * p.v_stride + (int64_t)h * D + col0 + c) : 0.f;
+      sm.u.b.ob[row][c] = ok ? ld_in<BF16>(p.dout, e) : 0.f;
+    }
+    __syncthreads();
+    // X = K_l S^T, Rv = beta (V - X)
+    float vx[4];
+    {
+      const f32x4 x = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.sb[0][0], PB, 1, D / 4, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e;
+        vx[e] = sm.u.b.vb[i][r] - eG_r[e] * x[e];
+        sm.u.b.rv[i][r] = beta_r[e] * vx[e];
+      }
+    }
+    __syncthreads();
+    // E = T Rv;  dE = A^T dO + K_e dS^T
+    f32x4 ev = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.u.b.rv[0][0], PB, 1, 4 * (w + 1), zero4(), r, g);
+    {
+      f32x4 a = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.b.ob[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
+      const f32x4 k = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.db[0][0], PB, 1, D / 4, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e;
+        a[e] += eGl_r[e] * k[e];
+        sm.u.b.eb[i][r] = ev[e];
+        sm.u.b.de[i][r] = a[e];
+      }
+    }
+    __syncthreads();
+    // dRv = T^T dE; dV = beta dRv; dX = -beta dRv
+    {
+      const f32x4 d = mm<false, false>(&sm.c.tt[16 * w][16 * w], 1, PC, &sm.u.b.de[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e;
+        dbl[e] += vx[e] * d[e];
+        sm.u.b.dr[i][r] = d[e];
+        sm.u.b.dx[i][r] = -beta_r[e] * d[e];
+        if (i < ck.L) {
+          const int64_t o = (ck.t0 + i) * HVD + (int64_t)h * D + col0 + r;
+          const float dvv = beta_r[e] * d[e];
+          if (p.out_bf16) static_cast<uint16_t *>(p.dv)[o] = f32_to_bf16(dvv);
+          else static_cast<float *>(p.dv)[o] = dvv;
+        }
+      }
+    }
+    __syncthreads();
+    // dA += dO E^T, dR += dRv E^T (negated at the end), blocks J <= w
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J <= w) {
+        dA[J] = mm<true, true>(&sm.u.b.ob[16 * w][0], PB, 1, &sm.u.b.eb[16 * J][0], 1, PB, BW / 4, dA[J], r, g);
+        dR[J] = mm<true, true>(&sm.u.b.dr[16 * w][0], PB, 1, &sm.u.b.eb[16 * J][0], 1, PB, BW / 4, dR[J], r, g);
+      }
+    }
+    // dQ_l += dO S, dK_l += dX S, dK_e += E dS (S's element (v, j) is sb[j][v])
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      dQl[m] = mm<true, true>(&sm.u.b.ob[16 * w][0], PB, 1, &sm.u.b.sb[16 * m][0], 1, PB, BW / 4, dQl[m], r, g);
+      dKl[m] = mm<true, true>(&sm.u.b.dx[16 * w][0], PB, 1, &sm.u.b.sb[16 * m][0], 1, PB, BW / 4, dKl[m], r, g);
+      dKe[m] = mm<true, true>(&sm.u.b.eb[16 * w][0], PB, 1, &sm.u.b.db[16 * m][0], 1, PB, BW / 4, dKe[m], r, g);
+    }
+  }
+  __syncthreads();   // the blocks are dead: the queries return
+  load_rows<BF16, D>(sm.u.qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
+  atomicAdd(&sm.sds, sds);
+  // dbeta from Rv; the Gram terms of dG and dbeta; P_R, P_A in place of
+  // kg and ag
+  {
+    float rowp[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > w) continue;
+      float colp = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, j = 16 * J + r;
+        const float kgv = sm.c.kg[i][j], agv = sm.c.ag[i][j];
+        const float dr = -dR[J][e], da = dA[J][e];
+        const float gm = j <= i ? __expf(sm.c.G[i] - sm.c.G[j]) : 0.f;
+        const float nn = dr * beta_r[e] * kgv + da * agv;
+        rowp[e] += nn;
+        colp += nn;
+        rowb[e] += dr * kgv;
+        sm.c.kg[i][j] = j < i ? dr * beta_r[e] * gm : 0.f;
+        sm.c.ag[i][j] = j <= i ? da * p.scale * gm : 0.f;
+      }
+      atomicAdd(&sm.dG[16 * J + r], -colp);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e;
+      atomicAdd(&sm.dG[i], rowp[e]);
+      atomicAdd(&sm.dbeta[i], rowb[e] + dbl[e]);
+    }
+  }
+  __syncthreads();   // queries loaded, P_R and P_A written
+  // row terms of dG; dk, dq start from the decayed-operand terms
+  {
+    float rowp[4] = {0.f, 0.f, 0.f, 0.f}, last = 0.f;
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, j = 16 * m + r;
+        const float kv = sm.c.kk[i][j], qv = sm.u.qq[i][j];
+        const float ke = eGl_r[e] * kv * dKe[m][e];
+        rowp[e] += eG_r[e] * (kv * dKl[m][e] + p.scale * qv * dQl[m][e]) - ke;
+        last += ke;
+        dKl[m][e] = eG_r[e] * dKl[m][e] + eGl_r[e] * dKe[m][e];   // dk
+        dQl[m][e] = p.scale * eG_r[e] * dQl[m][e];                 // dq
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&sm.dG[16 * w + 4 * g + e], rowp[e]);
+    atomicAdd(&sm.dG[CB - 1], last);
+  }
+  // dk += P_R K + P_R^T K + P_A^T Q;  dq += P_A K
+#pragma unroll
+  for (int m = 0; m < NT; ++m) {
+    dKl[m] = mm<true, false>(&sm.c.kg[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), dKl[m], r, g);
+    dKl[m] = mm<false, false>(&sm.c.kg[16 * w][16 * w], 1, PC, &sm.c.kk[16 * w][16 * m], PD, 1, 4 * (4 - w), dKl[m], r, g);
+    dKl[m] = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.qq[16 * w][16 * m], PD, 1, 4 * (4 - w), dKl[m], r, g);
+    dQl[m] = mm<true, false>(&sm.c.ag[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), dQl[m], r, g);
+  }
+#pragma unroll
+  for (int m = 0; m < NT; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e;
+      if (i < ck.L) {
+        const int64_t o = (ck.t0 + i) * HVD + (int64_t)h * D + 16 * m + r;
+        p.dkh[o] = dKl[m][e];
+        p.dqh[o] = dQl[m][e];
+      }
+    }
+  __syncthreads();   // dG, dbeta, sds complete
+  if (tid == 0) atomicAdd(&sm.dG[CB - 1], sm.c.gl * sm.sds);
+  __syncthreads();
+  if (tid < ck.L) {
+    const int64_t o = (ck.t0 + tid) * p.HV + h;
+    p.dbeta[o] = sm.dbeta[tid];
+    if (p.gated) {
+      float s = 0.f;
+      for (int i = tid; i < CB; ++i) s += sm.dG[i];
+      p.dg[o] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5. dq, dk of a key head: the sum over its value heads
+// ---------------------------------------------------------------------------
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *dqh, const float *dkh, void *dq, void *dk,
+                                                            int HK, int R, int D) {
+  const int64_t t = blockIdx.x;
+  const int HV = HK * R;
+  for (int e = threadIdx.x; e < HK * D; e += 256) {
+    const int hk = e / D, d = e - hk * D;
+    float sq = 0.f, sk = 0.f;
+    for (int j = 0; j < R; ++j) {
+      const int64_t s = (t * HV + hk * R + j) * (int64_t)D + d;
+      sq += dqh[s];
+      sk += dkh[s];
+    }
+    const int64_t o = t * HK * (int64_t)D + e;
+    if constexpr (OUT_BF16) {
+      static_cast<uint16_t *>(dq)[o] = f32_to_bf16(sq);
+      static_cast<uint16_t *>(dk)[o] = f32_to_bf16(sk);
+    } else {
+      static_cast<float *>(dq)[o] = sq;
+      static_cast<float *>(dk)[o] = sk;
+    }
+  }
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdWs {
+  size_t ckf, ckb, M, Y, dqh, dkh, total;
+};
+
+BwdWs ws_layout(const gdr_args &a) {
+  const size_t flat = (size_t)((a.T_total + CB - 1) / CB + a.N);
+  const size_t mat = flat * a.HV * (size_t)a.DK * a.DK * 4;
+  const size_t rows = (size_t)a.T_total * a.HV * a.DK * 4;
+  BwdWs l;
+  size_t o = 0;
+  l.ckf = o; o += al256(mat);
+  l.ckb = o; o += al256(mat);
+  l.M = o; o += al256(mat);
+  l.Y = o; o += al256(mat);
+  l.dqh = o; o += al256(rows);
+  l.dkh = o; o += al256(rows);
+  l.total = o;
+  return l;
+}
+
+template <bool BF16, int D>
+hipError_t launch_bwd(const BwdParams &p, const gdr_args &a, void *dq, void *dk, hipStream_t stream) {
+  const unsigned items = (unsigned)(p.flat * p.HV);
+  hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(items), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_walk_kernel<D>), dim3((unsigned)(((p.N * p.HV + 7) / 8) * 8 * (D / 16))), dim3(256), 0,
+                     stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_grad_kernel<BF16, D>), dim3(items), dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.T_total == 0) return hipSuccess;
+  if (p.out_bf16)
+    hipLaunchKernelGGL((bwd_group_sum_kernel<true>), dim3((unsigned)a.T_total), dim3(256), 0, stream, p.dqh, p.dkh,
+                       dq, dk, a.HK, p.ratio, D);
+  else
+    hipLaunchKernelGGL((bwd_group_sum_kernel<false>), dim3((unsigned)a.T_total), dim3(256), 0, stream, p.dqh,
+                       p.dkh, dq, dk, a.HK, p.ratio, D);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace(const gdr_args &a) { return ws_layout(a).total; }
+
+hipError_t launch_chunk_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
+                            float *dg, float *dstate0, void *ws, hipStream_t stream) {
+  const BwdWs l = ws_layout(a);
+  char *w = static_cast<char *>(ws);
+  hipError_t e = launch_chunk_states(a, reinterpret_cast<float *>(w + l.ckf), stream);
+  if (e != hipSuccess) return e;
+  BwdParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.dout = dout;
+  p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
+  p.g = a.g; p.beta = a.beta;
+  p.cu_seqlens = a.cu_seqlens;
+  p.N = a.N; p.HK = a.HK; p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.scale = a.scale;
+  p.gated = a.gate == GDR_GATE_SCALAR;
+  p.out_bf16 = a.out_dtype == GDR_BF16;
+  p.flat = (a.T_total + CB - 1) / CB + a.N;
+  p.ckf = reinterpret_cast<const float *>(w + l.ckf);
+  p.ckb = reinterpret_cast<float *>(w + l.ckb);
+  p.M = reinterpret_cast<float *>(w + l.M);
+  p.Y = reinterpret_cast<float *>(w + l.Y);
+  p.dqh = reinterpret_cast<float *>(w + l.dqh);
+  p.dkh = reinterpret_cast<float *>(w + l.dkh);
+  p.dv = dv;
+  p.dbeta = dbeta;
+  p.dg = dg;
+  p.dstate0 = dstate0;
+  const bool bf = a.in_dtype == GDR_BF16;
+  if (a.DK == 128) return bf ? launch_bwd<true, 128>(p, a, dq, dk, stream) : launch_bwd<false, 128>(p, a, dq, dk, stream);
+  return bf ? launch_bwd<true, 64>(p, a, dq, dk, stream) : launch_bwd<false, 64>(p, a, dq, dk, stream);
+}
+
+}  // namespace gdr

@@ -67,6 +67,7 @@ struct ChunkParams {
   int32_t P;   // transitions per token (Gated DeltaProduct substeps); 1 otherwise
   int32_t rev; // walk each sequence's rows backwards (warp-specialised kernel only)
   int32_t lc;  // tokens per chunk, 16, 32 or 64 (the general kernel; the others take 64)
+  float *ckpt; // chunk-start states of the backward's forward walk (general kernel), or NULL
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {

@@ -310,7 +310,11 @@ __device__ __forceinline__ void grams(SM &sm, const ChunkParams &p, int r, int g
   }
 }
 
-template <bool IN_F32, int GATE, bool DELTA, int D>
+// CKPT: the forward walk of the chunkwise backward. The state at the start
+// of every chunk goes to p.ckpt (fp32 S^T, [flat chunk][HV][DK][DV], flat
+// chunk base(n) + c with base(n) = floor(cu[n] / 64) + n), and neither the
+// outputs nor the final state are written.
+template <bool IN_F32, int GATE, bool DELTA, int D, bool CKPT = false>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using SM = Smem<IN_F32, GATE, DELTA, D>;
   using In = typename SM::In;
@@ -391,6 +395,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int64_t HVD = (int64_t)p.HV * D;
   for (int64_t t0 = bos; t0 < eos; t0 += LC) {
     const int L = (int)((eos - t0) < LC ? (eos - t0) : LC);
+    if constexpr (CKPT) {
+      const int64_t F = (int64_t)(p.cu_seqlens[n] >> 6) + n + (t0 - bos) / C;
+      float *cp = p.ckpt + (F * p.HV + h) * (int64_t)(D * D) + col;
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cp[(16 * m + 4 * g + i) * D] = st[m][i];
+    }
 
     // ================= phase 0: inputs into LDS =================
     if constexpr (GATE != GDR_GATE_CHANNEL) {
@@ -698,7 +710,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
       oa[I] = acc;
     }
-    {
+    if constexpr (!CKPT) {
       // row (16I + 4g + i) of this chunk, column col: 32-bit offsets from the
       // chunk's first output row
       const uint32_t HVDu = (uint32_t)HVD;
@@ -784,7 +796,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 
   // ---- final state back to the pool slot ----
-  {
+  if constexpr (!CKPT) {
     const int64_t sbase = (slot * p.HV + h) * (int64_t)(D * D) + col;
     if (p.st_bf16) {
       uint16_t *sp = static_cast<uint16_t *>(p.pool) + sbase;
@@ -831,7 +843,46 @@ hipError_t by_gate(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
   }
 }
 
+template <bool IN_F32, int GATE, int D>
+hipError_t launch_ckpt(const ChunkParams &p, int N, hipStream_t stream) {
+  const int grp = p.ratio * (D / BV);
+  const int blocks = ((N * p.HK + 7) / 8) * 8 * grp;
+  hipLaunchKernelGGL((chunk_fwd_kernel<IN_F32, GATE, true, D, true>), dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool IN_F32, int GATE>
+hipError_t ckpt_by_dim(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
+  if (a.DK == 128) return launch_ckpt<IN_F32, GATE, 128>(p, a.N, s);
+  return launch_ckpt<IN_F32, GATE, 64>(p, a.N, s);
+}
+
+template <bool IN_F32>
+hipError_t ckpt_by_gate(const gdr_args &a, const ChunkParams &p, hipStream_t s) {
+  if (a.gate == GDR_GATE_SCALAR) return ckpt_by_dim<IN_F32, GDR_GATE_SCALAR>(a, p, s);
+  return ckpt_by_dim<IN_F32, GDR_GATE_NONE>(a, p, s);
+}
+
 }  // namespace
+
+hipError_t launch_chunk_states(const gdr_args &a, float *ckpt, hipStream_t stream) {
+  ChunkParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v;
+  p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
+  p.g = a.g; p.beta = a.beta; p.o = nullptr; p.pool = a.state_pool;
+  p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
+  p.N = a.N; p.HK = a.HK; p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.scale = a.scale;
+  p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
+  p.st_bf16 = a.state_dtype == GDR_BF16;
+  p.out_bf16 = 0;
+  p.P = 1;
+  p.rev = 0;
+  p.lc = 64;
+  p.ckpt = ckpt;
+  if (a.in_dtype == GDR_BF16) return ckpt_by_gate<false>(a, p, stream);
+  return ckpt_by_gate<true>(a, p, stream);
+}
 
 bool prefill_force_generic() {
   static const bool force = [] {
@@ -860,6 +911,7 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream) {
   p.P = products_of(a);
   p.rev = 0;   // (the reversed walk is the warp-specialised kernel's)
   p.lc = a.chunk_size;
+  p.ckpt = nullptr;
   if (a.in_dtype == GDR_BF16) return by_gate<false>(a, p, stream);
   return by_gate<true>(a, p, stream);
 }

@@ -1151,6 +1151,7 @@ hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {
   p.P = products_of(a);
   p.rev = (a.flags & kFlagReverse) ? 1 : 0;
   p.lc = 64;
+  p.ckpt = nullptr;
   if (a.gate == GDR_GATE_SCALAR) return ws_by_rule<GDR_GATE_SCALAR>(a, p, stream);
   return ws_by_rule<GDR_GATE_NONE>(a, p, stream);
 }

@@ -524,6 +524,44 @@ GDR_EXPORT const char *gdr_status_string(gdr_status s) {
 
 GDR_EXPORT const char *gdr_last_error(void) { return g_last_error; }
 
+// What the chunkwise backward covers, on top of the tokenwise backward's
+// checks: the delta rule, gate NONE or SCALAR.
+gdr_status chunk_bwd_covers(const gdr_args *a) {
+  if (a->rule != GDR_RULE_DELTA)
+    return fail(GDR_E_UNSUPPORTED, "the chunkwise backward covers the delta rule (the linear rule: "
+                "gdr_linear_chunk_bwd / gdr_gated_linear_chunk_bwd)");
+  if (a->gate == GDR_GATE_CHANNEL)
+    return fail(GDR_E_UNSUPPORTED, "the chunkwise backward takes gate NONE or SCALAR");
+  return GDR_OK;
+}
+
+GDR_EXPORT size_t gdr_chunk_bwd_workspace_bytes(const gdr_args *a) {
+  if (validate(a, Call::Recur) != GDR_OK || a->N == 0) return 0;
+  if (chunk_bwd_covers(a) != GDR_OK) return 0;
+  return chunk_bwd_workspace(*a);
+}
+
+GDR_EXPORT gdr_status gdr_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv,
+                                    float *dbeta, float *dg, float *dstate0, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  gdr_status s = validate_rbwd(a, dout, dq, dk, dv, dbeta, dg, dstate0);
+  if (s != GDR_OK) return s;
+  if ((s = chunk_bwd_covers(a)) != GDR_OK) return s;
+  if (a->N == 0) return GDR_OK;
+  const size_t need = chunk_bwd_workspace(*a);
+  if (!workspace || ws_bytes < need)
+    return fail(GDR_E_WORKSPACE, "workspace of %zu bytes at %p: this call needs %zu "
+                "(gdr_chunk_bwd_workspace_bytes)", ws_bytes, workspace, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_E_INVALID, "workspace is not 256-byte aligned");
+  if (a->flags & GDR_FLAG_DEBUG_CHECKS) {
+    s = run_debug_checks(a, true, stream);
+    if (s != GDR_OK) return s;
+  }
+  hipError_t e = launch_chunk_bwd(*a, dout, dq, dk, dv, dbeta, dg, dstate0, workspace, stream);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "chunk_bwd launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
 GDR_EXPORT size_t gdr_recurrent_bwd_workspace_bytes(const gdr_args *a) {
   if (validate(a, Call::Recur) != GDR_OK || a->N == 0) return 0;
   return recurrent_bwd_workspace(*a);

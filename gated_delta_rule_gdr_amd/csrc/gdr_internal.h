@@ -59,6 +59,16 @@ hipError_t launch_chunk_fwd(const gdr_args &a, hipStream_t stream);
 size_t linear_bwd_workspace(const gdr_args &a);
 hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, float *dg,
                              void *ws, hipStream_t stream);
+// The backward's forward walk: the general prefill kernel storing S^T at the
+// start of every chunk to ckpt ([flat chunk][HV][DK][DV] fp32, flat chunk
+// floor(cu[n] / 64) + n + c), writing neither outputs nor the pool
+// (chunk_fwd.hip; delta rule, gate NONE or SCALAR, chunks of 64).
+hipError_t launch_chunk_states(const gdr_args &a, float *ckpt, hipStream_t stream);
+// Chunkwise backward of the gated delta rule (chunk_bwd.hip): its workspace
+// in bytes, and the launch.
+size_t chunk_bwd_workspace(const gdr_args &a);
+hipError_t launch_chunk_bwd(const gdr_args &a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
+                            float *dg, float *dstate0, void *ws, hipStream_t stream);
 // True when GDR_PREFILL_KERNEL=generic asks for the general prefill kernel in
 // every case (used to compare kernels).
 bool prefill_force_generic();

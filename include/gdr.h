@@ -24,7 +24,8 @@
  * gdr_linear_chunk_bwd and gdr_gated_linear_chunk_bwd give the gradients of
  * the linear rule, plain or with a scalar gate, chunkwise;
  * gdr_recurrent_bwd gives the gradients of the gated delta and gated linear
- * rules, tokenwise;
+ * rules, tokenwise; gdr_chunk_bwd those of the delta rule (gate NONE or
+ * SCALAR), chunkwise;
  * gdr_verify_ring and gdr_state_fold split a speculative-decode window into a
  * verify that writes no state and a fold of the accepted tokens.
  *
@@ -286,6 +287,30 @@ size_t gdr_recurrent_bwd_workspace_bytes(const gdr_args *a);
  * gdr_recurrent_bwd_workspace_bytes) is scratch. */
 gdr_status gdr_recurrent_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
                              float *dg, float *dstate0, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gdr_chunk_bwd needs with these arguments (0 when
+ * N == 0 or the arguments are invalid or not covered): four fp32 arrays of
+ * (ceil(T_total / 64) + N) * HV * DK * DV values (the state at every chunk
+ * start, its gradient after every chunk, and each chunk's reverse map M and
+ * Y) and two of T_total * HV * DK (dq and dk per value head). */
+size_t gdr_chunk_bwd_workspace_bytes(const gdr_args *a);
+
+/* The gradients of gdr_recurrent_bwd (same arguments, outputs, layouts and
+ * readings) for the delta rule with gate NONE or SCALAR, computed chunkwise
+ * in the manner of "From Attention to Learned Memory", section "Backward:
+ * reverse the boundary scan, then differentiate each chunk", applied to the
+ * delta rule's chunk equations ("You Could Have Come Up With Kimi Delta
+ * Attention", section 6): a forward walk stores the state at every chunk
+ * start; a reverse walk carries the state's gradient from the sequence end
+ * back over the chunk boundaries (each chunk's map is the transpose of the
+ * forward chunk map's linear part, plus a term from the chunk's output
+ * gradients); then every chunk's gradients are formed independently. fp32
+ * arithmetic throughout (matrix products on fp32 MFMA). Other rules and gates
+ * return GDR_E_UNSUPPORTED. `workspace` (device, 256-byte aligned, at least
+ * gdr_chunk_bwd_workspace_bytes) is scratch; calls sharing one must not
+ * overlap. */
+gdr_status gdr_chunk_bwd(const gdr_args *a, const void *dout, void *dq, void *dk, void *dv, float *dbeta,
+                         float *dg, float *dstate0, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Speculative decoding ("gated_delta" Mojo page, its verify-ring, record and
  * fold functions, which it names without detail; the reading taken here):

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
                             "gdr_linear_chunk_bwd", "gdr_ring_record_elements",
                             "gdr_ring_record_stride", "gdr_verify_ring", "gdr_state_fold",
                             "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd",
-                            "gdr_chunk_fwd_noalloc", "gdr_gated_linear_chunk_bwd"])
+                            "gdr_chunk_fwd_noalloc", "gdr_gated_linear_chunk_bwd",
+                            "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
