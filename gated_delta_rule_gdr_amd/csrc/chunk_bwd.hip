@@ -42,9 +42,9 @@
 //      columns): dS^T from zero at the sequence end back to the start,
 //      dS^T_{c+1} stored per chunk; the last one is the initial state's
 //      gradient;
-//   4. bwd_grad_kernel, one workgroup per (chunk, value head): the formulas
-//      above, over 16-column blocks of the value dimension, dq and dk per
-//      value head in fp32;
+//   4. bwd_grad_kernel, one workgroup of eight waves per (chunk, value head):
+//      the formulas above, over 16-column blocks of the value dimension, dq
+//      and dk per value head in fp32;
 //   5. bwd_group_sum_kernel: dq and dk summed over each key head's group of
 //      value heads, in the output dtype.
 // Everything is fp32: the matrix products on v_mfma_f32_16x16x4_f32 with
@@ -173,11 +173,11 @@ struct ChunkSm {
   float gl;                       // e^{G_last}
 };
 
-template <bool BF16, int D>
+template <bool BF16, int D, int NTH>
 __device__ __forceinline__ void load_rows(float (*dst)[D + 4], const void *src, int64_t stride, int64_t off0,
                                           int L, int tid) {
   constexpr int Q4 = D / 4;
-  for (int it = tid; it < CB * Q4; it += 256) {
+  for (int it = tid; it < CB * Q4; it += NTH) {
     const int row = it / Q4, c = 4 * (it - row * Q4);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row < L) {
@@ -194,16 +194,20 @@ __device__ __forceinline__ void load_rows(float (*dst)[D + 4], const void *src, 
   }
 }
 
-// Keys and queries (into qq), beta and the gate; then the Grams and T. Ends
-// with a barrier.
-template <bool BF16, int D>
+// Keys and queries (into qq), beta and the gate; then the Grams and T, with
+// NW = 4 or 8 waves: wave w forms Gram row block w & 3, column blocks J of
+// parity w >> 2 when NW = 8; the inverse runs on waves 0-3. Ends with a
+// barrier.
+template <bool BF16, int D, int NW>
 __device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams &p, const ChunkAt &ck, int h,
                             int tid) {
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6), w = w8 & 3, hf = w8 >> 2, lane = tid & 63,
+            r = lane & 15, g = lane >> 4;
+  constexpr int JS = NW / 4;   // column-block stride of one wave
   const int hk = h / p.ratio;
-  load_rows<BF16, D>(sm.kk, p.k, p.k_stride, ck.t0 * p.k_stride + (int64_t)hk * D, ck.L, tid);
-  load_rows<BF16, D>(qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
-  if (w == 0) {
+  load_rows<BF16, D, 64 * NW>(sm.kk, p.k, p.k_stride, ck.t0 * p.k_stride + (int64_t)hk * D, ck.L, tid);
+  load_rows<BF16, D, 64 * NW>(qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
+  if (w8 == 0) {
     const bool ok = lane < ck.L;
     const float gv = (ok && p.gated) ? p.g[(ck.t0 + lane) * p.HV + h] : 0.f;
     const float G = chunk::wave_scan(gv);
@@ -215,8 +219,8 @@ __device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams 
     if (lane == 0) sm.gl = __expf(Gl);
   }
   __syncthreads();
-  // Grams: wave w forms row block w against column blocks J <= w
-  for (int J = 0; J <= w; ++J) {
+  // Grams: row block w against column blocks J <= w
+  for (int J = hf; J <= w; J += JS) {
     f32x4 a = mm<true, true>(&sm.kk[16 * w][0], D + 4, 1, &sm.kk[16 * J][0], 1, D + 4, D / 4, zero4(), r, g);
     f32x4 b = mm<true, true>(&qq[16 * w][0], D + 4, 1, &sm.kk[16 * J][0], 1, D + 4, D / 4, zero4(), r, g);
 #pragma unroll
@@ -227,7 +231,7 @@ __device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams 
       sm.ag[i][j] = p.scale * b[e] * gm;
     }
   }
-  for (int J = w + 1; J < 4; ++J)
+  for (int J = w + 1 + hf; J < 4; J += JS)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e, j = 16 * J + r;
@@ -237,7 +241,7 @@ __device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams 
   __syncthreads();
   // diagonal blocks of T: lane b < 16 of wave w solves column b of
   // (I + R_ww) T_ww = I by forward substitution, R = beta_i kg
-  if (lane < 16) {
+  if (hf == 0 && lane < 16) {
     float t[16];
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
@@ -252,14 +256,14 @@ __device__ void chunk_setup(ChunkSm<D> &sm, float (*qq)[D + 4], const BwdParams 
     for (int a = 0; a < 16; ++a) sm.tt[16 * w + a][16 * w + lane] = t[a];
   }
   // the blocks above the diagonal are zero
-  for (int J = w + 1; J < 4; ++J)
+  for (int J = w + 1 + hf; J < 4; J += JS)
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.tt[16 * w + 4 * g + e][16 * J + r] = 0.f;
   __syncthreads();
   // blocks below: T_IJ = -T_II sum_{K=J}^{I-1} R_IK T_KJ, by distance I - J
   for (int d = 1; d < 4; ++d) {
     const int I = w, J = w - d;
-    if (J >= 0) {
+    if (hf == 0 && J >= 0) {
       f32x4 y = mm<true, false>(&sm.kg[16 * I][16 * J], PC, 1, &sm.tt[16 * J][16 * J], PC, 1, 4 * d, zero4(), r, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] *= sm.beta[16 * I + 4 * g + e];
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   if (!ck.valid) return;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
             g = lane >> 4;
-  chunk_setup<BF16, D>(sm.c, sm.qq, p, ck, h, tid);
+  chunk_setup<BF16, D, 4>(sm.c, sm.qq, p, ck, h, tid);
   // T <- T Diag(beta gamma), so that T K = W
   for (int it = tid; it < CB * CB; it += 256) {
     const int i = it / CB, j = it - i * CB;
@@ -344,7 +348,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
   __syncthreads();
   // dO into W's place
-  load_rows<BF16, D>(sm.ww, p.dout, (int64_t)p.HV * D, ck.t0 * (int64_t)p.HV * D + (int64_t)h * D, ck.L, tid);
+  load_rows<BF16, D, 256>(sm.ww, p.dout, (int64_t)p.HV * D, ck.t0 * (int64_t)p.HV * D + (int64_t)h * D, ck.L,
+                          tid);
   __syncthreads();
   // Y = Z^T dO
   for (int ti = 0; ti < RT; ++ti) {
@@ -465,25 +470,32 @@ struct GradSm {
       float de[CB][PB];         // dE
       float dr[CB][PB];         // dRv
       float dx[CB][PB];         // dX
+      float kd[CB][PB];         // K dS^T
     } b;
   } u;
   float dG[CB], dbeta[CB];
   float sds;                    // <dS_{c+1}, S_c>
 };
 
+// Eight waves: wave w8 = 4 hf + w. The products over a block's 16 value
+// columns along the chain (X, E, dE, dRv: one 16 x 16 tile per row block)
+// run on waves hf = 0; the Gram-side products (dA, dR: column blocks J of
+// parity hf) and those over the key dimension (dQ_l, dK_l, dK_e, and dq, dk
+// at the end: key tiles m of parity hf) are shared by all eight. Waves w and
+// w + 4 share a SIMD.
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
   __shared__ GradSm<D> sm;
   constexpr int PD = D + 4;
-  constexpr int NT = D / 16;
+  constexpr int NH = D / 32;   // key tiles per wave
   const int64_t F = blockIdx.x / p.HV;
   const int h = blockIdx.x - (int)F * p.HV;
   const ChunkAt ck = chunk_at(p.cu_seqlens, p.N, F);
   if (!ck.valid) return;
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
-            g = lane >> 4;
+  const int tid = threadIdx.x, w8 = __builtin_amdgcn_readfirstlane(tid >> 6), w = w8 & 3, hf = w8 >> 2,
+            lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int hk = h / p.ratio;
-  chunk_setup<BF16, D>(sm.c, sm.u.qq, p, ck, h, tid);
+  chunk_setup<BF16, D, 8>(sm.c, sm.u.qq, p, ck, h, tid);
   if (tid < CB) {
     sm.dG[tid] = 0.f;
     sm.dbeta[tid] = 0.f;
@@ -492,11 +504,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
 
   const int64_t mb = (F * p.HV + h) * (int64_t)(D * D);
   const int64_t HVD = (int64_t)p.HV * D;
-  f32x4 dA[4], dR[4], dQl[NT], dKl[NT], dKe[NT];
+  f32x4 dA[2], dR[2], dQl[NH], dKl[NH], dKe[NH];   // column blocks hf, hf + 2; key tiles 2 mm + hf
 #pragma unroll
-  for (int J = 0; J < 4; ++J) dA[J] = dR[J] = zero4();
+  for (int J = 0; J < 2; ++J) dA[J] = dR[J] = zero4();
 #pragma unroll
-  for (int m = 0; m < NT; ++m) dQl[m] = dKl[m] = dKe[m] = zero4();
+  for (int m = 0; m < NH; ++m) dQl[m] = dKl[m] = dKe[m] = zero4();
   float dbl[4] = {0.f, 0.f, 0.f, 0.f};   // sum over columns of (V - X) dRv, rows 16w + 4g + e
   float sds = 0.f;
   float beta_r[4], eG_r[4], eGl_r[4];
@@ -508,28 +520,51 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
     eGl_r[e] = sm.c.eGl[i];
   }
 
+  // a block's S^T, dS^T, V and dO columns, fetched into registers one block
+  // ahead
+  constexpr int NSB = D * BW / 512, NVB = CB * BW / 512;
+  float ps[NSB], pd[NSB], pv[NVB], po[NVB];
+  auto fetch = [&](int vb) {
+    const int col0 = BW * vb;
+#pragma unroll
+    for (int u = 0; u < NSB; ++u) {
+      const int it = tid + 512 * u, row = it / BW, c = it - row * BW;
+      ps[u] = p.ckf[mb + (int64_t)row * D + col0 + c];
+      pd[u] = p.ckb[mb + (int64_t)row * D + col0 + c];
+    }
+#pragma unroll
+    for (int u = 0; u < NVB; ++u) {
+      const int it = tid + 512 * u, row = it / BW, c = it - row * BW;
+      const bool ok = row < ck.L;
+      const int64_t tr = ck.t0 + (ok ? row : 0);
+      const float v = ld_in<BF16>(p.v, tr * p.v_stride + (int64_t)h * D + col0 + c);
+      const float o = ld_in<BF16>(p.dout, tr * HVD + (int64_t)h * D + col0 + c);
+      pv[u] = ok ? v : 0.f;
+      po[u] = ok ? o : 0.f;
+    }
+  };
+  fetch(0);
   for (int vb = 0; vb < D / BW; ++vb) {
     const int col0 = BW * vb;
     __syncthreads();   // the previous block (or the queries) is no longer read
-    for (int it = tid; it < D * BW; it += 256) {
-      const int row = it / BW, c = it - row * BW;
-      const float s = p.ckf[mb + (int64_t)row * D + col0 + c];
-      const float d = p.ckb[mb + (int64_t)row * D + col0 + c];
-      sm.u.b.sb[row][c] = s;
-      sm.u.b.db[row][c] = d;
-      sds += s * d;
+#pragma unroll
+    for (int u = 0; u < NSB; ++u) {
+      const int it = tid + 512 * u, row = it / BW, c = it - row * BW;
+      sm.u.b.sb[row][c] = ps[u];
+      sm.u.b.db[row][c] = pd[u];
+      sds += ps[u] * pd[u];
     }
-    for (int it = tid; it < CB * BW; it += 256) {
-      const int row = it / BW, c = it - row * BW;
-      const bool ok = row < ck.L;
-      const int64_t e = (ck.t0 + row) * HVD + (int64_t)h * D + col0 + c;
-      sm.u.b.vb[row][c] = ok ? ld_in<BF16>(p.v, (ck.t0 + row) * p.v_stride + (int64_t)h * D + col0 + c) : 0.f;
-      sm.u.b.ob[row][c] = ok ? ld_in<BF16>(p.dout, e) : 0.f;
+#pragma unroll
+    for (int u = 0; u < NVB; ++u) {
+      const int it = tid + 512 * u, row = it / BW, c = it - row * BW;
+      sm.u.b.vb[row][c] = pv[u];
+      sm.u.b.ob[row][c] = po[u];
     }
+    fetch(vb + 1 < D / BW ? vb + 1 : vb);   // (the last block fetches itself again)
     __syncthreads();
-    // X = K_l S^T, Rv = beta (V - X)
-    float vx[4];
-    {
+    // X = K_l S^T, Rv = beta (V - X) on waves hf = 0; K dS^T on the others
+    float vx[4] = {0.f, 0.f, 0.f, 0.f};
+    if (hf == 0) {
       const f32x4 x = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.sb[0][0], PB, 1, D / 4, zero4(), r, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -537,24 +572,26 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         vx[e] = sm.u.b.vb[i][r] - eG_r[e] * x[e];
         sm.u.b.rv[i][r] = beta_r[e] * vx[e];
       }
+    } else {
+      const f32x4 k = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.db[0][0], PB, 1, D / 4, zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.b.kd[16 * w + 4 * g + e][r] = k[e];
     }
     __syncthreads();
     // E = T Rv;  dE = A^T dO + K_e dS^T
-    f32x4 ev = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.u.b.rv[0][0], PB, 1, 4 * (w + 1), zero4(), r, g);
-    {
-      f32x4 a = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.b.ob[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
-      const f32x4 k = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.db[0][0], PB, 1, D / 4, zero4(), r, g);
+    if (hf == 0) {
+      const f32x4 ev = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.u.b.rv[0][0], PB, 1, 4 * (w + 1), zero4(), r, g);
+      const f32x4 a = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.b.ob[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * w + 4 * g + e;
-        a[e] += eGl_r[e] * k[e];
         sm.u.b.eb[i][r] = ev[e];
-        sm.u.b.de[i][r] = a[e];
+        sm.u.b.de[i][r] = a[e] + eGl_r[e] * sm.u.b.kd[i][r];
       }
     }
     __syncthreads();
     // dRv = T^T dE; dV = beta dRv; dX = -beta dRv
-    {
+    if (hf == 0) {
       const f32x4 d = mm<false, false>(&sm.c.tt[16 * w][16 * w], 1, PC, &sm.u.b.de[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -571,38 +608,70 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    // dA += dO E^T, dR += dRv E^T (negated at the end), blocks J <= w
+    // over the block's 16 columns k (lane (r, g) holds k = 4g .. 4g + 3):
+    // dA += dO E^T, dR += dRv E^T (negated at the end) for blocks J <= w;
+    // dQ_l += dO S, dK_l += dX S, dK_e += E dS for the wave's key tiles
+    // (S's element (v, j) is sb[j][v]); every product of the step shares its
+    // operand loads and runs as an independent accumulator chain
+    {
+      const float4 aob = *reinterpret_cast<const float4 *>(&sm.u.b.ob[16 * w + r][4 * g]);
+      const float4 adr = *reinterpret_cast<const float4 *>(&sm.u.b.dr[16 * w + r][4 * g]);
+      const float4 adx = *reinterpret_cast<const float4 *>(&sm.u.b.dx[16 * w + r][4 * g]);
+      const float4 aeb = *reinterpret_cast<const float4 *>(&sm.u.b.eb[16 * w + r][4 * g]);
+      float4 be[2], bs[NH], bd[NH];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      if (J <= w) {
-        dA[J] = mm<true, true>(&sm.u.b.ob[16 * w][0], PB, 1, &sm.u.b.eb[16 * J][0], 1, PB, BW / 4, dA[J], r, g);
-        dR[J] = mm<true, true>(&sm.u.b.dr[16 * w][0], PB, 1, &sm.u.b.eb[16 * J][0], 1, PB, BW / 4, dR[J], r, g);
+      for (int jj = 0; jj < 2; ++jj) {
+        const int J = min(hf + 2 * jj, 3);
+        be[jj] = *reinterpret_cast<const float4 *>(&sm.u.b.eb[16 * J + r][4 * g]);
       }
-    }
-    // dQ_l += dO S, dK_l += dX S, dK_e += E dS (S's element (v, j) is sb[j][v])
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-      dQl[m] = mm<true, true>(&sm.u.b.ob[16 * w][0], PB, 1, &sm.u.b.sb[16 * m][0], 1, PB, BW / 4, dQl[m], r, g);
-      dKl[m] = mm<true, true>(&sm.u.b.dx[16 * w][0], PB, 1, &sm.u.b.sb[16 * m][0], 1, PB, BW / 4, dKl[m], r, g);
-      dKe[m] = mm<true, true>(&sm.u.b.eb[16 * w][0], PB, 1, &sm.u.b.db[16 * m][0], 1, PB, BW / 4, dKe[m], r, g);
+      for (int mm_ = 0; mm_ < NH; ++mm_) {
+        const int m = 2 * mm_ + hf;
+        bs[mm_] = *reinterpret_cast<const float4 *>(&sm.u.b.sb[16 * m + r][4 * g]);
+        bd[mm_] = *reinterpret_cast<const float4 *>(&sm.u.b.db[16 * m + r][4 * g]);
+      }
+      const bool j0 = hf <= w, j1 = hf + 2 <= w;
+      const float a_ob[4] = {aob.x, aob.y, aob.z, aob.w}, a_dr[4] = {adr.x, adr.y, adr.z, adr.w};
+      const float a_dx[4] = {adx.x, adx.y, adx.z, adx.w}, a_eb[4] = {aeb.x, aeb.y, aeb.z, aeb.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const float b = jj == 0 ? (j == 0 ? be[0].x : j == 1 ? be[0].y : j == 2 ? be[0].z : be[0].w)
+                                  : (j == 0 ? be[1].x : j == 1 ? be[1].y : j == 2 ? be[1].z : be[1].w);
+          if (jj == 0 ? j0 : j1) {
+            dA[jj] = mf(a_ob[j], b, dA[jj]);
+            dR[jj] = mf(a_dr[j], b, dR[jj]);
+          }
+        }
+#pragma unroll
+        for (int mm_ = 0; mm_ < NH; ++mm_) {
+          const float b1 = j == 0 ? bs[mm_].x : j == 1 ? bs[mm_].y : j == 2 ? bs[mm_].z : bs[mm_].w;
+          const float b2 = j == 0 ? bd[mm_].x : j == 1 ? bd[mm_].y : j == 2 ? bd[mm_].z : bd[mm_].w;
+          dQl[mm_] = mf(a_ob[j], b1, dQl[mm_]);
+          dKl[mm_] = mf(a_dx[j], b1, dKl[mm_]);
+          dKe[mm_] = mf(a_eb[j], b2, dKe[mm_]);
+        }
+      }
     }
   }
   __syncthreads();   // the blocks are dead: the queries return
-  load_rows<BF16, D>(sm.u.qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
+  load_rows<BF16, D, 512>(sm.u.qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
   atomicAdd(&sm.sds, sds);
   // dbeta from Rv; the Gram terms of dG and dbeta; P_R, P_A in place of
   // kg and ag
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int jj = 0; jj < 2; ++jj) {
+      const int J = hf + 2 * jj;
       if (J > w) continue;
       float colp = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * w + 4 * g + e, j = 16 * J + r;
         const float kgv = sm.c.kg[i][j], agv = sm.c.ag[i][j];
-        const float dr = -dR[J][e], da = dA[J][e];
+        const float dr = -dR[jj][e], da = dA[jj][e];
         const float gm = j <= i ? __expf(sm.c.G[i] - sm.c.G[j]) : 0.f;
         const float nn = dr * beta_r[e] * kgv + da * agv;
         rowp[e] += nn;
@@ -625,38 +694,73 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f}, last = 0.f;
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int mm_ = 0; mm_ < NH; ++mm_)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e, j = 16 * m + r;
+        const int i = 16 * w + 4 * g + e, j = 16 * (2 * mm_ + hf) + r;
         const float kv = sm.c.kk[i][j], qv = sm.u.qq[i][j];
-        const float ke = eGl_r[e] * kv * dKe[m][e];
-        rowp[e] += eG_r[e] * (kv * dKl[m][e] + p.scale * qv * dQl[m][e]) - ke;
+        const float ke = eGl_r[e] * kv * dKe[mm_][e];
+        rowp[e] += eG_r[e] * (kv * dKl[mm_][e] + p.scale * qv * dQl[mm_][e]) - ke;
         last += ke;
-        dKl[m][e] = eG_r[e] * dKl[m][e] + eGl_r[e] * dKe[m][e];   // dk
-        dQl[m][e] = p.scale * eG_r[e] * dQl[m][e];                 // dq
+        dKl[mm_][e] = eG_r[e] * dKl[mm_][e] + eGl_r[e] * dKe[mm_][e];   // dk
+        dQl[mm_][e] = p.scale * eG_r[e] * dQl[mm_][e];                  // dq
       }
 #pragma unroll
     for (int e = 0; e < 4; ++e) atomicAdd(&sm.dG[16 * w + 4 * g + e], rowp[e]);
     atomicAdd(&sm.dG[CB - 1], last);
   }
-  // dk += P_R K + P_R^T K + P_A^T Q;  dq += P_A K
+  // dk += P_R K + P_R^T K + P_A^T Q;  dq += P_A K, over 16-token blocks kb
+  // of the contraction (lane (r, g) holds tokens 16 kb + 4g .. + 3), every
+  // key tile of the wave at once: P_R and P_A rows for kb <= w, their
+  // columns for kb >= w
+  for (int kb = 0; kb <= w; ++kb) {
+    const float4 pr = *reinterpret_cast<const float4 *>(&sm.c.kg[16 * w + r][16 * kb + 4 * g]);
+    const float4 pa = *reinterpret_cast<const float4 *>(&sm.c.ag[16 * w + r][16 * kb + 4 * g]);
+    const float a_pr[4] = {pr.x, pr.y, pr.z, pr.w}, a_pa[4] = {pa.x, pa.y, pa.z, pa.w};
+    float bk[NH][4];
 #pragma unroll
-  for (int m = 0; m < NT; ++m) {
-    dKl[m] = mm<true, false>(&sm.c.kg[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), dKl[m], r, g);
-    dKl[m] = mm<false, false>(&sm.c.kg[16 * w][16 * w], 1, PC, &sm.c.kk[16 * w][16 * m], PD, 1, 4 * (4 - w), dKl[m], r, g);
-    dKl[m] = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.qq[16 * w][16 * m], PD, 1, 4 * (4 - w), dKl[m], r, g);
-    dQl[m] = mm<true, false>(&sm.c.ag[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), dQl[m], r, g);
+    for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bk[mm_][j] = sm.c.kk[16 * kb + 4 * g + j][16 * (2 * mm_ + hf) + r];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mm_ = 0; mm_ < NH; ++mm_) {
+        dKl[mm_] = mf(a_pr[j], bk[mm_][j], dKl[mm_]);
+        dQl[mm_] = mf(a_pa[j], bk[mm_][j], dQl[mm_]);
+      }
+  }
+  for (int kb = w; kb < 4; ++kb) {
+    float a_pr[4], a_pa[4], bk[NH][4], bq[NH][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a_pr[j] = sm.c.kg[16 * kb + 4 * g + j][16 * w + r];
+      a_pa[j] = sm.c.ag[16 * kb + 4 * g + j][16 * w + r];
+    }
+#pragma unroll
+    for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bk[mm_][j] = sm.c.kk[16 * kb + 4 * g + j][16 * (2 * mm_ + hf) + r];
+        bq[mm_][j] = sm.u.qq[16 * kb + 4 * g + j][16 * (2 * mm_ + hf) + r];
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mm_ = 0; mm_ < NH; ++mm_) {
+        dKl[mm_] = mf(a_pr[j], bk[mm_][j], dKl[mm_]);
+        dKl[mm_] = mf(a_pa[j], bq[mm_][j], dKl[mm_]);
+      }
   }
 #pragma unroll
-  for (int m = 0; m < NT; ++m)
+  for (int mm_ = 0; mm_ < NH; ++mm_)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e;
       if (i < ck.L) {
-        const int64_t o = (ck.t0 + i) * HVD + (int64_t)h * D + 16 * m + r;
-        p.dkh[o] = dKl[m][e];
-        p.dqh[o] = dQl[m][e];
+        const int64_t o = (ck.t0 + i) * HVD + (int64_t)h * D + 16 * (2 * mm_ + hf) + r;
+        p.dkh[o] = dKl[mm_][e];
+        p.dqh[o] = dQl[mm_][e];
       }
     }
   __syncthreads();   // dG, dbeta, sds complete
@@ -732,7 +836,7 @@ hipError_t launch_bwd(const BwdParams &p, const gdr_args &a, void *dq, void *dk,
   hipLaunchKernelGGL((bwd_walk_kernel<D>), dim3((unsigned)(((p.N * p.HV + 7) / 8) * 8 * (D / 16))), dim3(256), 0,
                      stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_grad_kernel<BF16, D>), dim3(items), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_grad_kernel<BF16, D>), dim3(items), dim3(512), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.T_total == 0) return hipSuccess;
   if (p.out_bf16)
