@@ -34,10 +34,13 @@
 //   dg_t = sum_{i >= t} dG_i over the chunk (G is a prefix sum of g).
 //
 // Kernels, in order:
-//   1. the general prefill kernel in its checkpointing form (chunk_fwd.hip):
-//      S^T_c at every chunk start (no outputs, the pool untouched);
-//   2. bwd_prep_kernel, one workgroup per (chunk, value head): the Grams, T,
-//      W and the reverse map's M and Y, written as fp32 [DK, DK] / [DK, DV];
+//   1. a prefill kernel in its checkpointing form: S^T_c at every chunk start
+//      (bf16 inputs: the warp-specialised kernel, on a scratch copy of the
+//      initial states and with scratch outputs; fp32 inputs: the general
+//      kernel, which writes neither);
+//   2. bwd_prep_kernel, one workgroup of eight waves per (chunk, value head):
+//      the Grams, T, W and the reverse map's M and Y, written as fp32
+//      [DK, DK] / [DK, DV];
 //   3. bwd_walk_kernel, one workgroup per (sequence, value head, 16 value
 //      columns): dS^T from zero at the sequence end back to the start,
 //      dS^T_{c+1} stored per chunk; the last one is the initial state's
@@ -293,72 +296,134 @@ struct PrepBwdSm {
   alignas(16) float ww[CB][D + 4];   // W, then dO
 };
 
+// Eight waves (w8 = 4 hf + w). Every product runs over 16-token blocks kb of
+// its contraction with all of a wave's output tiles at once (one operand
+// load feeds several independent accumulator chains): W and Z by row block
+// w and key tiles of parity hf; M and Y (D x D) by 16-row tiles of the key
+// dimension, D / 16 of them over the eight waves.
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_prep_kernel(BwdParams p) {
   __shared__ PrepBwdSm<D> sm;
-  constexpr int PD = D + 4;
+  constexpr int NH = D / 32;               // key tiles per wave in W and Z
+  constexpr int RTT = D / 16;              // row tiles of M and Y
+  constexpr int CT = RTT * RTT / 8;        // M / Y tiles per wave
+  constexpr int WPR = 8 / RTT;             // waves per row tile of M / Y
   const int64_t F = blockIdx.x / p.HV;
   const int h = blockIdx.x - (int)F * p.HV;
   const ChunkAt ck = chunk_at(p.cu_seqlens, p.N, F);
   if (!ck.valid) return;
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
-            g = lane >> 4;
-  chunk_setup<BF16, D, 4>(sm.c, sm.qq, p, ck, h, tid);
+  const int tid = threadIdx.x, w8 = __builtin_amdgcn_readfirstlane(tid >> 6), w = w8 & 3, hf = w8 >> 2,
+            lane = tid & 63, r = lane & 15, g = lane >> 4;
+  chunk_setup<BF16, D, 8>(sm.c, sm.qq, p, ck, h, tid);
   // T <- T Diag(beta gamma), so that T K = W
-  for (int it = tid; it < CB * CB; it += 256) {
+  for (int it = tid; it < CB * CB; it += 512) {
     const int i = it / CB, j = it - i * CB;
     sm.c.tt[i][j] *= sm.c.beta[j] * sm.c.eG[j];
   }
   __syncthreads();
-  // W, row block w (T lower: k < 16 (w + 1))
-  for (int m = 0; m < D / 16; ++m) {
-    const f32x4 a = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.c.kk[0][16 * m], PD, 1, 4 * (w + 1), zero4(), r, g);
+  // W, row block w, key tiles 2 mm + hf (T lower: tokens < 16 (w + 1))
+  {
+    f32x4 acc[NH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.ww[16 * w + 4 * g + e][16 * m + r] = a[e];
+    for (int mm_ = 0; mm_ < NH; ++mm_) acc[mm_] = zero4();
+    for (int kb = 0; kb <= w; ++kb) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(&sm.c.tt[16 * w + r][16 * kb + 4 * g]);
+      const float a[4] = {t4.x, t4.y, t4.z, t4.w};
+      float b[NH][4];
+#pragma unroll
+      for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[mm_][j] = sm.c.kk[16 * kb + 4 * g + j][16 * (2 * mm_ + hf) + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mm_ = 0; mm_ < NH; ++mm_) acc[mm_] = mf(a[j], b[mm_][j], acc[mm_]);
+    }
+#pragma unroll
+    for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.ww[16 * w + 4 * g + e][16 * (2 * mm_ + hf) + r] = acc[mm_][e];
   }
   __syncthreads();
   // keys decayed to the chunk's end, in place
-  for (int it = tid; it < CB * D; it += 256) {
+  for (int it = tid; it < CB * D; it += 512) {
     const int i = it / D, j = it - i * D;
     sm.c.kk[i][j] *= sm.c.eGl[i];
   }
   __syncthreads();
   const int64_t mbase = (F * p.HV + h) * (int64_t)(D * D);
-  // M = gl I - W^T K_e: wave w takes rows (D / 4) w ..
-  constexpr int RT = D / 64;   // 16-row tiles per wave
-  for (int ti = 0; ti < RT; ++ti) {
-    const int a0 = (D / 4) * w + 16 * ti;
-    for (int m = 0; m < D / 16; ++m) {
-      const f32x4 a = mm<false, false>(&sm.ww[0][a0], 1, PD, &sm.c.kk[0][16 * m], PD, 1, CB / 4, zero4(), r, g);
+  // X^T Y' over the chunk's 64 tokens for one row tile (a0) and CT column
+  // tiles c0 + WPR u: A(a, k) = xa[k][a0 + a], B(k, b) = xb[k][16 (c0 + WPR u) + b]
+  const int a0 = 16 * (w8 / WPR), c0 = w8 % WPR;
+  auto tprod = [&](const float (*xa)[D + 4], const float (*xb)[D + 4], f32x4 (&acc)[CT]) {
+#pragma unroll
+    for (int u = 0; u < CT; ++u) acc[u] = zero4();
+    for (int kb = 0; kb < CB / 16; ++kb) {
+      float a[4], b[CT][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = xa[16 * kb + 4 * g + j][a0 + r];
+#pragma unroll
+      for (int u = 0; u < CT; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[u][j] = xb[16 * kb + 4 * g + j][16 * (c0 + WPR * u) + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < CT; ++u) acc[u] = mf(a[j], b[u][j], acc[u]);
+    }
+  };
+  // M = gl I - W^T K_e
+  {
+    f32x4 acc[CT];
+    tprod(sm.ww, sm.c.kk, acc);
+#pragma unroll
+    for (int u = 0; u < CT; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = a0 + 4 * g + e, col = 16 * m + r;
-        p.M[mbase + (int64_t)row * D + col] = (row == col ? sm.c.gl : 0.f) - a[e];
+        const int row = a0 + 4 * g + e, col = 16 * (c0 + WPR * u) + r;
+        p.M[mbase + (int64_t)row * D + col] = (row == col ? sm.c.gl : 0.f) - acc[u][e];
       }
-    }
   }
-  // Z = s Q_l - A W, row block w, in place of this wave's query rows
-  for (int m = 0; m < D / 16; ++m) {
-    const f32x4 a = mm<true, false>(&sm.c.ag[16 * w][0], PC, 1, &sm.ww[0][16 * m], PD, 1, 4 * (w + 1), zero4(), r, g);
+  // Z = s Q_l - A W, row block w, key tiles 2 mm + hf, in place of the queries
+  {
+    f32x4 acc[NH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, j = 16 * m + r;
-      sm.qq[i][j] = p.scale * sm.c.eG[i] * sm.qq[i][j] - a[e];
+    for (int mm_ = 0; mm_ < NH; ++mm_) acc[mm_] = zero4();
+    for (int kb = 0; kb <= w; ++kb) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(&sm.c.ag[16 * w + r][16 * kb + 4 * g]);
+      const float a[4] = {t4.x, t4.y, t4.z, t4.w};
+      float b[NH][4];
+#pragma unroll
+      for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[mm_][j] = sm.ww[16 * kb + 4 * g + j][16 * (2 * mm_ + hf) + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mm_ = 0; mm_ < NH; ++mm_) acc[mm_] = mf(a[j], b[mm_][j], acc[mm_]);
     }
+#pragma unroll
+    for (int mm_ = 0; mm_ < NH; ++mm_)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, j = 16 * (2 * mm_ + hf) + r;
+        sm.qq[i][j] = p.scale * sm.c.eG[i] * sm.qq[i][j] - acc[mm_][e];
+      }
   }
   __syncthreads();
   // dO into W's place
-  load_rows<BF16, D, 256>(sm.ww, p.dout, (int64_t)p.HV * D, ck.t0 * (int64_t)p.HV * D + (int64_t)h * D, ck.L,
+  load_rows<BF16, D, 512>(sm.ww, p.dout, (int64_t)p.HV * D, ck.t0 * (int64_t)p.HV * D + (int64_t)h * D, ck.L,
                           tid);
   __syncthreads();
   // Y = Z^T dO
-  for (int ti = 0; ti < RT; ++ti) {
-    const int a0 = (D / 4) * w + 16 * ti;
-    for (int m = 0; m < D / 16; ++m) {
-      const f32x4 a = mm<false, false>(&sm.qq[0][a0], 1, PD, &sm.ww[0][16 * m], PD, 1, CB / 4, zero4(), r, g);
+  {
+    f32x4 acc[CT];
+    tprod(sm.qq, sm.ww, acc);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.Y[mbase + (int64_t)(a0 + 4 * g + e) * D + 16 * m + r] = a[e];
-    }
+    for (int u = 0; u < CT; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p.Y[mbase + (int64_t)(a0 + 4 * g + e) * D + 16 * (c0 + WPR * u) + r] = acc[u][e];
   }
 }
 
@@ -369,7 +434,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_walk_kernel(BwdParams p) {
-  __shared__ alignas(16) float xs[2][D][PB];   // the state gradient's 16 columns, by parity
+  // the state gradient's 16 columns, column-major (a lane's four k of a
+  // 16-wide k block are one 16-byte read), by parity
+  __shared__ alignas(16) float xs[2][16][D + 4];
   constexpr int GRP = D / 16;
   constexpr int RT = D / 64;       // 16-row tiles per wave
   constexpr int KB = D / 16;       // 16-wide k blocks
@@ -402,46 +469,51 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(BwdParams p) {
   f32x4 x[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) x[t] = zero4();
-  float4 am[RT][KB];
-  f32x4 ya[RT];
-  if (nc > 0) load_ops(nc - 1, am, ya);
-  int par = 0;
-  for (int64_t c = nc - 1; c >= 0; --c) {
+  // chunk c with operands in (am, ya), loading chunk c - 1's into (an, yn)
+  // (chunk 0 loads its own again: every step issues the same loads); two
+  // register sets used in turn, so that no copy waits for loads in flight
+  auto step = [&](int64_t c, int par, const float4 (&am)[RT][KB], const f32x4 (&ya)[RT], float4 (&an)[RT][KB],
+                  f32x4 (&yn)[RT]) {
     const int64_t mb = ((base + c) * p.HV + h) * (int64_t)(D * D);
     // dS^T_{c+1}: to the checkpoint and to LDS
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < RT; ++t) {
+      const int row0 = (D / 4) * w + 16 * t + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = (D / 4) * w + 16 * t + 4 * g + e;
-        p.ckb[mb + (int64_t)row * D + col0 + r] = x[t][e];
-        xs[par][row][r] = x[t][e];
-      }
-    // the next chunk's operands (chunk 0 reloads its own: every iteration
-    // issues the same loads)
-    float4 an[RT][KB];
-    f32x4 yn[RT];
+      for (int e = 0; e < 4; ++e) p.ckb[mb + (int64_t)(row0 + e) * D + col0 + r] = x[t][e];
+      *reinterpret_cast<float4 *>(&xs[par][r][row0]) = make_float4(x[t][0], x[t][1], x[t][2], x[t][3]);
+    }
     load_ops(c > 0 ? c - 1 : 0, an, yn);
     __syncthreads();
+    float4 bx[KB];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      f32x4 acc = ya[t];
+    for (int kb = 0; kb < KB; ++kb) bx[kb] = *reinterpret_cast<const float4 *>(&xs[par][r][16 * kb + 4 * g]);
+    f32x4 acc[RT];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const float av[4] = {am[t][kb].x, am[t][kb].y, am[t][kb].z, am[t][kb].w};
+    for (int t = 0; t < RT; ++t) acc[t] = ya[t];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mf(av[j], xs[par][16 * kb + 4 * g + j][r], acc);
-      }
-      x[t] = acc;
+    for (int kb = 0; kb < KB; ++kb) {
+      const float bv[4] = {bx[kb].x, bx[kb].y, bx[kb].z, bx[kb].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const float a = j == 0 ? am[t][kb].x : j == 1 ? am[t][kb].y : j == 2 ? am[t][kb].z : am[t][kb].w;
+          acc[t] = mf(a, bv[j], acc[t]);
+        }
     }
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      ya[t] = yn[t];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) am[t][kb] = an[t][kb];
-    }
-    par ^= 1;
+    for (int t = 0; t < RT; ++t) x[t] = acc[t];
+  };
+  float4 a0[RT][KB], a1[RT][KB];
+  f32x4 y0[RT], y1[RT];
+  if (nc > 0) load_ops(nc - 1, a0, y0);
+  int64_t c = nc - 1;
+  for (; c >= 1; c -= 2) {
+    step(c, 0, a0, y0, a1, y1);
+    step(c - 1, 1, a1, y1, a0, y0);
   }
+  if (c == 0) step(0, 0, a0, y0, a1, y1);
   if (p.dstate0) {
     float *d0 = p.dstate0 + ((int64_t)n * p.HV + h) * (int64_t)(D * D);
 #pragma unroll
@@ -805,6 +877,21 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *dqh, co
   }
 }
 
+// dst[n][h] = pool[slot_idx[n]][h] in fp32 (D x D values), and slots[n] = n:
+// the initial states as a scratch pool the warp-specialised walk may write.
+// (COPY false: the slots alone, for a walk from zero states)
+template <bool ST_BF16, bool COPY = true>
+__global__ __launch_bounds__(256) void copy_states_kernel(const void *pool, const int32_t *slot_idx, float *dst,
+                                                          int32_t *slots, int HV, int DD) {
+  const int nh = blockIdx.x, n = nh / HV, h = nh - n * HV;
+  const int64_t src = ((int64_t)slot_idx[n] * HV + h) * DD, o = (int64_t)nh * DD;
+  for (int e = threadIdx.x; COPY && e < DD; e += 256) {
+    if constexpr (ST_BF16) dst[o + e] = bf16_to_f32(static_cast<const uint16_t *>(pool)[src + e]);
+    else dst[o + e] = static_cast<const float *>(pool)[src + e];
+  }
+  if (h == 0 && threadIdx.x == 0) slots[n] = n;
+}
+
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
@@ -830,7 +917,7 @@ BwdWs ws_layout(const gdr_args &a) {
 template <bool BF16, int D>
 hipError_t launch_bwd(const BwdParams &p, const gdr_args &a, void *dq, void *dk, hipStream_t stream) {
   const unsigned items = (unsigned)(p.flat * p.HV);
-  hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(items), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(items), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_walk_kernel<D>), dim3((unsigned)(((p.N * p.HV + 7) / 8) * 8 * (D / 16))), dim3(256), 0,
@@ -856,7 +943,35 @@ hipError_t launch_chunk_bwd(const gdr_args &a, const void *dout, void *dq, void 
                             float *dg, float *dstate0, void *ws, hipStream_t stream) {
   const BwdWs l = ws_layout(a);
   char *w = static_cast<char *>(ws);
-  hipError_t e = launch_chunk_states(a, reinterpret_cast<float *>(w + l.ckf), stream);
+  hipError_t e;
+  if (a.in_dtype == GDR_BF16 && !prefill_force_generic()) {
+    // the warp-specialised kernel, on a scratch copy of the initial states
+    // (in M's place) with its outputs in dq's fp32 scratch (both rewritten
+    // later)
+    gdr_args b = a;
+    b.state_pool = w + l.M;
+    b.state_dtype = GDR_F32;
+    b.num_slots = a.N;
+    b.slot_idx = reinterpret_cast<const int32_t *>(w + l.Y);
+    b.o = w + l.dqh;
+    b.out_dtype = GDR_F32;
+    if (a.flags & GDR_FLAG_ZERO_INIT)
+      hipLaunchKernelGGL((copy_states_kernel<false, false>), dim3((unsigned)(a.N * a.HV)), dim3(256), 0, stream,
+                         a.state_pool, a.slot_idx, reinterpret_cast<float *>(w + l.M),
+                         reinterpret_cast<int32_t *>(w + l.Y), a.HV, a.DK * a.DK);
+    else if (a.state_dtype == GDR_BF16)
+      hipLaunchKernelGGL(copy_states_kernel<true>, dim3((unsigned)(a.N * a.HV)), dim3(256), 0, stream, a.state_pool,
+                         a.slot_idx, reinterpret_cast<float *>(w + l.M), reinterpret_cast<int32_t *>(w + l.Y), a.HV,
+                         a.DK * a.DK);
+    else
+      hipLaunchKernelGGL(copy_states_kernel<false>, dim3((unsigned)(a.N * a.HV)), dim3(256), 0, stream,
+                         a.state_pool, a.slot_idx, reinterpret_cast<float *>(w + l.M),
+                         reinterpret_cast<int32_t *>(w + l.Y), a.HV, a.DK * a.DK);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_chunk_states_ws(b, reinterpret_cast<float *>(w + l.ckf), stream);
+  } else {
+    e = launch_chunk_states(a, reinterpret_cast<float *>(w + l.ckf), stream);
+  }
   if (e != hipSuccess) return e;
   BwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = dout;

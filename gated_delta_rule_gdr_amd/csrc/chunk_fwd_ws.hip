@@ -634,7 +634,10 @@ __device__ __forceinline__ int longest_first(const int32_t *cu, int N, int rank)
   return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
 }
 
-template <int GATE, bool DELTA, int D, int NSW, bool PROD, bool REV>
+// CKPT: the forward walk of the chunkwise backward; the state waves also
+// store S^T at the start of every chunk to p.ckpt ([flat chunk][HV][DK][DV]
+// fp32, flat chunk floor(cu[n] / 64) + n + c).
+template <int GATE, bool DELTA, int D, int NSW, bool PROD, bool REV, bool CKPT = false>
 __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_kernel(ChunkParams p) {
   constexpr int NP = prep_waves<NSW>();
   constexpr int NTH = 64 * (NSW + NP);
@@ -747,6 +750,14 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   }
 
   for (int c = 0; c < nc; ++c) {
+    if constexpr (CKPT) {
+      const int64_t F = (int64_t)(p.cu_seqlens[n] >> 6) + n + c;
+      float *cp = p.ckpt + (F * p.HV + h) * (int64_t)(D * D) + col;
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cp[(16 * m + 4 * g + i) * D] = st[m][i];
+    }
     {
       const auto &S = sm.set[c & 1];
       const int64_t t0 = bos + (int64_t)c * C;
@@ -1097,6 +1108,21 @@ hipError_t launch_ws(const ChunkParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int GATE, int D>
+hipError_t launch_ws_ckpt(const ChunkParams &p, hipStream_t stream) {
+  const int64_t wide = (int64_t)p.N * p.HV * (D / 64);
+  auto go = [&](auto nsw) {
+    constexpr int NSW = decltype(nsw)::value;
+    const int grp = p.ratio * (D / (16 * NSW));
+    const int blocks = ((p.N * p.HK + 7) / 8) * 8 * grp;
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<GATE, true, D, NSW, false, false, true>), dim3(blocks),
+                       dim3(64 * (NSW + prep_waves<NSW>())), 0, stream, p);
+    return hipGetLastError();
+  };
+  if (wide >= cu_count()) return go(std::integral_constant<int, 4>());
+  return go(std::integral_constant<int, 2>());
+}
+
 // 64 value columns per workgroup when that already gives every compute unit
 // a workgroup, else 32 (twice the workgroups, each with half the state work).
 template <int GATE, bool DELTA, int D>
@@ -1135,6 +1161,30 @@ int cu_count() {
 
 hipError_t ws_wait_flag(int *out, bool clear, hipStream_t stream) {
   return chunk::wait_flag_access(out, clear, stream);
+}
+
+// The backward's forward walk on this kernel (bf16 inputs, delta rule, gate
+// NONE or SCALAR): outputs to a.o and the final state to a.state_pool as
+// usual (the caller passes scratch for both), and S^T at every chunk start
+// to ckpt.
+hipError_t launch_chunk_states_ws(const gdr_args &a, float *ckpt, hipStream_t stream) {
+  ChunkParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v;
+  p.q_stride = a.q_stride_t; p.k_stride = a.k_stride_t; p.v_stride = a.v_stride_t;
+  p.g = a.g; p.beta = a.beta; p.o = a.o; p.pool = a.state_pool;
+  p.slot_idx = a.slot_idx; p.cu_seqlens = a.cu_seqlens;
+  p.N = a.N; p.HK = a.HK; p.HV = a.HV; p.ratio = a.HV / a.HK;
+  p.scale = a.scale;
+  p.zero_init = (a.flags & GDR_FLAG_ZERO_INIT) ? 1 : 0;
+  p.st_bf16 = a.state_dtype == GDR_BF16;
+  p.out_bf16 = a.out_dtype == GDR_BF16;
+  p.P = 1;
+  p.rev = 0;
+  p.lc = 64;
+  p.ckpt = ckpt;
+  if (a.gate == GDR_GATE_SCALAR)
+    return a.DK == 128 ? launch_ws_ckpt<GDR_GATE_SCALAR, 128>(p, stream) : launch_ws_ckpt<GDR_GATE_SCALAR, 64>(p, stream);
+  return a.DK == 128 ? launch_ws_ckpt<GDR_GATE_NONE, 128>(p, stream) : launch_ws_ckpt<GDR_GATE_NONE, 64>(p, stream);
 }
 
 hipError_t launch_chunk_fwd_ws(const gdr_args &a, hipStream_t stream) {

@@ -64,6 +64,10 @@ hipError_t launch_linear_bwd(const gdr_args &a, const void *dout, void *dq, void
 // floor(cu[n] / 64) + n + c), writing neither outputs nor the pool
 // (chunk_fwd.hip; delta rule, gate NONE or SCALAR, chunks of 64).
 hipError_t launch_chunk_states(const gdr_args &a, float *ckpt, hipStream_t stream);
+// The same walk on the warp-specialised kernel (bf16 inputs), which also
+// writes the outputs to a.o and the final states to a.state_pool: the caller
+// points both at scratch.
+hipError_t launch_chunk_states_ws(const gdr_args &a, float *ckpt, hipStream_t stream);
 // Chunkwise backward of the gated delta rule (chunk_bwd.hip): its workspace
 // in bytes, and the launch.
 size_t chunk_bwd_workspace(const gdr_args &a);

@@ -273,6 +273,37 @@ def test_linear_backward_rejects_on_host():
     assert gcall(a, wsb=gated) == 2
 
 
+def test_chunk_backward_rejects_on_host():
+    """gdr_chunk_bwd takes the delta rule with gate NONE or SCALAR (the
+    tokenwise backward's other checks apply too) and checks its workspace
+    before any launch."""
+    gdr, L = _lib()
+    a = _valid_args(gdr)                              # delta rule, scalar gate, HV = 2 HK
+    need = L.gdr_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    flat = (a.T_total + 63) // 64 + a.N
+    mat = flat * a.HV * 128 * 128 * 4
+    rows = a.T_total * a.HV * 128 * 4
+    assert need >= 4 * mat + 2 * rows
+    dout, dq, dk, dv, db, dg, ds, ws = (0x7000000, 0x8000000, 0x8100000, 0x8200000, 0x8300000, 0x8400000,
+                                        0x9000000, 0x10000000)
+    call = lambda aa, **kw: L.gdr_chunk_bwd(
+        ctypes.byref(aa), dout, dq, dk, dv, kw.get("db", db), kw.get("dg", dg), ds, kw.get("ws", ws),
+        kw.get("wsb", need), None)
+    assert call(a, ws=None) == 3
+    assert call(a, wsb=need - 1) == 3
+    assert call(a, ws=ws + 16) == 1
+    assert call(a, db=None) == 1                      # dbeta is required for the delta rule
+    assert call(a, dg=None) == 1                      # dg is required for a gated call
+    b = _valid_args(gdr)
+    b.rule, b.beta = 1, None                          # the linear rule has its own chunkwise backward
+    assert L.gdr_chunk_bwd_workspace_bytes(ctypes.byref(b)) == 0
+    assert call(b) == 2
+    c = _valid_args(gdr)
+    c.gate = 2                                        # channel gate
+    assert L.gdr_chunk_bwd_workspace_bytes(ctypes.byref(c)) == 0
+    assert call(c) == 2
+
+
 def test_recurrent_backward_rejects_on_host():
     """The tokenwise backward takes any rule and gate; it checks the gradients'
     buffers, their overlaps, the workspace, L2 norm and products before any
