@@ -542,7 +542,6 @@ struct GradSm {
       float de[CB][PB];         // dE
       float dr[CB][PB];         // dRv
       float dx[CB][PB];         // dX
-      float kd[CB][PB];         // K dS^T
     } b;
   } u;
   float dG[CB], dbeta[CB];
@@ -550,8 +549,9 @@ struct GradSm {
 };
 
 // Eight waves: wave w8 = 4 hf + w. The products over a block's 16 value
-// columns along the chain (X, E, dE, dRv: one 16 x 16 tile per row block)
-// run on waves hf = 0; the Gram-side products (dA, dR: column blocks J of
+// columns along the chain (one 16 x 16 tile per row block) are split
+// between the two wave sets: X and E on hf = 0, K dS^T and dE on hf = 1,
+// dRv on hf = 0; the Gram-side products (dA, dR: column blocks J of
 // parity hf) and those over the key dimension (dQ_l, dK_l, dK_e, and dq, dk
 // at the end: key tiles m of parity hf) are shared by all eight. Waves w and
 // w + 4 share a SIMD.
@@ -634,8 +634,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
     }
     fetch(vb + 1 < D / BW ? vb + 1 : vb);   // (the last block fetches itself again)
     __syncthreads();
-    // X = K_l S^T, Rv = beta (V - X) on waves hf = 0; K dS^T on the others
+    // X = K_l S^T, Rv = beta (V - X) on waves hf = 0; K dS^T (kept) on the others
     float vx[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 kds = zero4();
     if (hf == 0) {
       const f32x4 x = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.sb[0][0], PB, 1, D / 4, zero4(), r, g);
 #pragma unroll
@@ -645,21 +646,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
         sm.u.b.rv[i][r] = beta_r[e] * vx[e];
       }
     } else {
-      const f32x4 k = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.db[0][0], PB, 1, D / 4, zero4(), r, g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.u.b.kd[16 * w + 4 * g + e][r] = k[e];
+      kds = mm<true, false>(&sm.c.kk[16 * w][0], PD, 1, &sm.u.b.db[0][0], PB, 1, D / 4, zero4(), r, g);
     }
     __syncthreads();
-    // E = T Rv;  dE = A^T dO + K_e dS^T
+    // E = T Rv on waves hf = 0;  dE = A^T dO + K_e dS^T on the others
     if (hf == 0) {
       const f32x4 ev = mm<true, false>(&sm.c.tt[16 * w][0], PC, 1, &sm.u.b.rv[0][0], PB, 1, 4 * (w + 1), zero4(), r, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.b.eb[16 * w + 4 * g + e][r] = ev[e];
+    } else {
       const f32x4 a = mm<false, false>(&sm.c.ag[16 * w][16 * w], 1, PC, &sm.u.b.ob[16 * w][0], PB, 1, 4 * (4 - w), zero4(), r, g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e;
-        sm.u.b.eb[i][r] = ev[e];
-        sm.u.b.de[i][r] = a[e] + eGl_r[e] * sm.u.b.kd[i][r];
-      }
+      for (int e = 0; e < 4; ++e) sm.u.b.de[16 * w + 4 * g + e][r] = a[e] + eGl_r[e] * kds[e];
     }
     __syncthreads();
     // dRv = T^T dE; dV = beta dRv; dX = -beta dRv
