@@ -81,6 +81,10 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: the library then binds to the HIP runtime torch has already
+    # loaded, the one that owns the streams and memory it is handed (loaded
+    # first, it could bind another copy, on which torch's streams mean nothing)
+    import torch  # noqa: F401
     if not os.path.exists(lib_path):
         raise ImportError(
             f"{lib_path} is missing: build it with `python -m gated_delta_rule_gdr_amd.build`")
