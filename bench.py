@@ -53,6 +53,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_delta_rule_gdr_amd", "csrc")
 STEP_SRC = [os.path.join(CSRC, "recurrent_step.hip"), os.path.join(CSRC, "gdr_internal.h")]
 RECUR_SRC = [os.path.join(CSRC, "recurrent_fwd.hip"), os.path.join(CSRC, "gdr_internal.h")]
+CBWD_SRC = [os.path.join(CSRC, "chunk_bwd.hip"), os.path.join(CSRC, "chunk_fwd_ws.hip"),
+            os.path.join(CSRC, "chunk_common.h"), os.path.join(CSRC, "gdr_internal.h")]
 RBWD_SRC = [os.path.join(CSRC, "recurrent_bwd.hip"), os.path.join(CSRC, "recurrent_bwd.h"),
             os.path.join(CSRC, "gdr_internal.h")]
 
@@ -748,7 +750,7 @@ def main():
             "workload": gw.name, "steps": args.steps, "ms": ct, "tokens_per_s": T / (ct * 1e-3),
             "algorithmic_bytes": gb, "hbm_gbs": gb / (ct * 1e-3) / 1e9,
             "hbm_frac": gb / (ct * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": cws,
-            "speedup_vs_tokenwise": gt / ct}
+            "speedup_vs_tokenwise": gt / ct, "traffic": committed_traffic("chunk_bwd", gw.name, CBWD_SRC)}
     if not args.no_product:
         pw, P = synth.workload(synth.GDN), 2
         pt = bench_product(pw, P, args.product_steps)
