@@ -122,6 +122,14 @@ def test_chunk_bwd_zero_init_and_one_head_group(gate):
     compare(run(gdr, w, x), reference(w, x), w)
 
 
+def test_chunk_bwd_four_value_heads_per_key_head():
+    gdr = _gdr()
+    w = small(64, "bf16", "scalar", HK=1, HV=4, seqlens=(150, 64, 1), seed=94)
+    x = inputs(w)
+    print("chunk_bwd HK=1 HV=4", flush=True)
+    compare(run(gdr, w, x), reference(w, x), w)
+
+
 def test_chunk_bwd_strong_gate():
     """A strong decay (g = -softplus(x + 2): about -2.1 per token, spans of
     -130 over a chunk): every factor stays an exponential of a non-positive
