@@ -544,8 +544,11 @@ struct GradSm {
       float dx[CB][PB];         // dX
     } b;
   } u;
-  float dG[CB], dbeta[CB];
-  float sds;                    // <dS_{c+1}, S_c>
+  // per-wave partial sums of dG (by row and by column), dbeta and the last
+  // row's scalar terms, each written by one wave and summed in wave order
+  // (so the results do not depend on the order in which waves finish)
+  float pr[8][CB], pc[8][CB], pb[8][CB], pl[8];
+  float dG[CB];
 };
 
 // Eight waves: wave w8 = 4 hf + w. The products over a block's 16 value
@@ -568,11 +571,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
             lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int hk = h / p.ratio;
   chunk_setup<BF16, D, 8>(sm.c, sm.u.qq, p, ck, h, tid);
-  if (tid < CB) {
-    sm.dG[tid] = 0.f;
-    sm.dbeta[tid] = 0.f;
+  for (int i = tid; i < 8 * CB; i += 512) {
+    (&sm.pr[0][0])[i] = 0.f;
+    (&sm.pc[0][0])[i] = 0.f;
+    (&sm.pb[0][0])[i] = 0.f;
   }
-  if (tid == 0) sm.sds = 0.f;
 
   const int64_t mb = (F * p.HV + h) * (int64_t)(D * D);
   const int64_t HVD = (int64_t)p.HV * D;
@@ -727,11 +730,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
   }
   __syncthreads();   // the blocks are dead: the queries return
   load_rows<BF16, D, 512>(sm.u.qq, p.q, p.q_stride, ck.t0 * p.q_stride + (int64_t)hk * D, ck.L, tid);
-  atomicAdd(&sm.sds, sds);
   // dbeta from Rv; the Gram terms of dG and dbeta; P_R, P_A in place of
   // kg and ag
+  // (sums over the 16 lanes of a row group, or over the four row groups of
+  // a column, by xor shuffles: a fixed order)
+  auto sum16 = [](float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+  };
+  auto sum_g = [](float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+  };
+  float rowp[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
   {
-    float rowp[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int J = hf + 2 * jj;
@@ -750,19 +763,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
         sm.c.kg[i][j] = j < i ? dr * beta_r[e] * gm : 0.f;
         sm.c.ag[i][j] = j <= i ? da * p.scale * gm : 0.f;
       }
-      atomicAdd(&sm.dG[16 * J + r], -colp);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e;
-      atomicAdd(&sm.dG[i], rowp[e]);
-      atomicAdd(&sm.dbeta[i], rowb[e] + dbl[e]);
+      colp = sum_g(colp);
+      if (g == 0) sm.pc[w8][16 * J + r] = -colp;
     }
   }
   __syncthreads();   // queries loaded, P_R and P_A written
   // row terms of dG; dk, dq start from the decayed-operand terms
   {
-    float rowp[4] = {0.f, 0.f, 0.f, 0.f}, last = 0.f;
+    float last = 0.f;
 #pragma unroll
     for (int mm_ = 0; mm_ < NH; ++mm_)
 #pragma unroll
@@ -776,8 +784,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
         dQl[mm_][e] = p.scale * eG_r[e] * dQl[mm_][e];                  // dq
       }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) atomicAdd(&sm.dG[16 * w + 4 * g + e], rowp[e]);
-    atomicAdd(&sm.dG[CB - 1], last);
+    for (int e = 0; e < 4; ++e) {
+      const float rs = sum16(rowp[e]), bs = sum16(rowb[e] + dbl[e]);
+      if (r == 0) {
+        sm.pr[w8][16 * w + 4 * g + e] = rs;
+        sm.pb[w8][16 * w + 4 * g + e] = bs;
+      }
+    }
+    // the last row's scalar terms: sum_j e^{G_last - G_j} k_j . dK_e,j and
+    // e^{G_last} <dS_{c+1}, S_c> (this thread's share of both)
+    float lt = last + sm.c.gl * sds;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lt += __shfl_xor(lt, off, 64);
+    if (lane == 0) sm.pl[w8] = lt;
   }
   // dk += P_R K + P_R^T K + P_A^T Q;  dq += P_A K, over 16-token blocks kb
   // of the contraction (lane (r, g) holds tokens 16 kb + 4g .. + 3), every
@@ -833,12 +852,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
         p.dqh[o] = dQl[mm_][e];
       }
     }
-  __syncthreads();   // dG, dbeta, sds complete
-  if (tid == 0) atomicAdd(&sm.dG[CB - 1], sm.c.gl * sm.sds);
+  __syncthreads();   // the partial sums are complete
+  if (tid < CB) {
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x += sm.pr[u][tid] + sm.pc[u][tid];
+    if (tid == CB - 1)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x += sm.pl[u];
+    sm.dG[tid] = x;
+  }
   __syncthreads();
   if (tid < ck.L) {
     const int64_t o = (ck.t0 + tid) * p.HV + h;
-    p.dbeta[o] = sm.dbeta[tid];
+    float b = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b += sm.pb[u][tid];
+    p.dbeta[o] = b;
     if (p.gated) {
       float s = 0.f;
       for (int i = tid; i < CB; ++i) s += sm.dG[i];

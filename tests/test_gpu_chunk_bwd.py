@@ -155,6 +155,18 @@ def test_chunk_bwd_bf16_gradients_and_no_dstate():
     compare(got, ref, w, names=("dbeta", "dg"))
 
 
+def test_chunk_bwd_is_deterministic():
+    """Two calls give bit-identical gradients (no summation order depends on
+    which wave finishes first)."""
+    gdr = _gdr()
+    w = small(128, "bf16", "scalar", seed=93)
+    x = inputs(w)
+    print("chunk_bwd twice", flush=True)
+    a, b = run(gdr, w, x), run(gdr, w, x)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
+
+
 def test_chunk_bwd_agrees_with_tokenwise():
     """Both backwards of the same call, fp32 inputs: equal to fp32
     rounding."""
