@@ -685,7 +685,14 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
 
   // Both roles pass the same barriers: one after the prologue and one at the
   // end of every chunk (nc + 1 in all when nc > 0, none when nc == 0).
+  // Issue priority for the role that sets the pace: with six prep waves
+  // (NSW = 2) the state waves' chain, with four (NSW = 4) the prep waves.
+  // Each SIMD runs one wave of each kind side by side; the other fills the
+  // first one's stalls. (Measured: Gated DeltaNet shapes 0.223 -> 0.216 ms
+  // with the state waves first; the ragged GQA batch 1.34 -> 1.30 ms with
+  // the prep waves first; the opposite choices gain nothing.)
   if (w >= NSW) {
+    if constexpr (NSW == 4) __builtin_amdgcn_s_setprio(2);
 #define GDR_PREP(PW) chunk_prep_role<PW, NP, GATE, DELTA, D, NSW, PROD, REV>(p, sm, lane, r, g, h, hk, bos, eos, nc)
     switch (w - NSW) {
       case 0: GDR_PREP(0); break;
@@ -700,6 +707,7 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
   }
 
   // state waves: this lane's value column and resident state
+  if constexpr (NSW == 2) __builtin_amdgcn_s_setprio(2);
   const int col = vb * BVW + 16 * w + r;
   f32x4 st[NT];
 #pragma unroll
