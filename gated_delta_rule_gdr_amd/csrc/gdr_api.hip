@@ -3,7 +3,7 @@
 // Validation reads only host-visible fields of gdr_args (never device memory)
 // and runs before anything is enqueued, so a rejected call has no side
 // effects. Device-side index arrays are checked only under
-// GDR_FLAG_DEBUG_CHECKS, by a small kernel whose verdict (a static device
+// GDR_FLAG_DEBUG_CHECKS, by a small kernel whose result (a static device
 // word, no allocation) is copied back; the same flag reports bounded waits
 // inside the prefill kernels that ran out.
 #include <cmath>
@@ -118,7 +118,7 @@ gdr_status validate(const gdr_args *a, Call call) {
   return GDR_OK;
 }
 
-// Verdict of the device-side index check (0: valid, else the code of the
+// Result of the device-side index check (0: valid, else the code of the
 // first defect found), written by index_check_kernel on each device. Calls
 // that overlap on one device with GDR_FLAG_DEBUG_CHECKS share it and race.
 __device__ int g_index_check;
