@@ -130,6 +130,30 @@ def test_chunk_bwd_four_value_heads_per_key_head():
     compare(run(gdr, w, x), reference(w, x), w)
 
 
+def test_chunk_bwd_all_sequences_empty():
+    """Sequences of no tokens: nothing to differentiate but the initial
+    states, whose gradient is zero (the final state's is taken as zero)."""
+    gdr = _gdr()
+    w = small(128, "bf16", "scalar", seqlens=(0, 0, 0), seed=92)
+    x = inputs(w)
+    print("chunk_bwd empty batch", flush=True)
+    got = run(gdr, w, x)
+    assert got["dq"].shape[0] == 0 and got["dv"].shape[0] == 0
+    assert np.array_equal(got["dstate0"], np.zeros_like(got["dstate0"]))
+
+
+def test_chunk_bwd_with_debug_checks():
+    """GDR_FLAG_DEBUG_CHECKS validates the index arrays on the device first;
+    the gradients are unchanged."""
+    gdr = _gdr()
+    w = small(64, "bf16", "scalar", seed=91)
+    x = inputs(w)
+    print("chunk_bwd debug checks", flush=True)
+    a, b = run(gdr, w, x), run(gdr, w, x, debug_checks=True)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
+
+
 def test_chunk_bwd_strong_gate():
     """A strong decay (g = -softplus(x + 2): about -2.1 per token, spans of
     -130 over a chunk): every factor stays an exponential of a non-positive
