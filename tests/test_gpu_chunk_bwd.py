@@ -191,6 +191,29 @@ def test_chunk_bwd_is_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
+def test_chunk_bwd_on_fused_qkv_views():
+    """q, k, v as views into one fused [T, (2 HK + HV) D] buffer: the same
+    gradients, bit for bit, as from contiguous tensors."""
+    gdr = _gdr()
+    w = small(128, "bf16", "scalar", seqlens=(90, 0, 33, 130), seed=90)
+    x = inputs(w)
+    d = {n: dev(x[n], w.in_dtype) for n in ("q", "k", "v", "do")}
+    pool = dev(x["pool"], w.state_dtype)
+    g, beta = dev(x["g"], "f32"), dev(x["beta"], "f32")
+    slot, cu = dev(x["slot_idx"], "i32"), dev(x["cu_seqlens"], "i32")
+    T, KD, VD = w.T_total, w.HK * w.DK, w.HV * w.DV
+    fused = torch.cat([d["q"].reshape(T, KD), d["k"].reshape(T, KD), d["v"].reshape(T, VD)], 1)
+    q = fused[:, :KD].view(T, w.HK, w.DK)
+    k = fused[:, KD:2 * KD].view(T, w.HK, w.DK)
+    v = fused[:, 2 * KD:].view(T, w.HV, w.DV)
+    print("chunk_bwd on fused views", flush=True)
+    a = gdr.chunk_bwd(d["q"], d["k"], d["v"], g, beta, d["do"], pool, slot, cu, gate="scalar")
+    b = gdr.chunk_bwd(q, k, v, g, beta, d["do"], pool, slot, cu, gate="scalar")
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
 def test_chunk_bwd_agrees_with_tokenwise():
     """Both backwards of the same call, fp32 inputs: equal to fp32
     rounding."""
