@@ -617,7 +617,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the gated delta rule "
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; the gated delta rule "
                                    "shards by (sequence, head) with no communication and "
                                    "multi-GPU runs are not part of it"}))
         sys.exit(2)
