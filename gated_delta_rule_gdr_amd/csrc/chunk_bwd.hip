@@ -49,7 +49,8 @@
 //      the formulas above, over 16-column blocks of the value dimension, dq
 //      and dk per value head in fp32;
 //   5. bwd_group_sum_kernel: dq and dk summed over each key head's group of
-//      value heads, in the output dtype.
+//      value heads, in the output dtype (with one value head per key head
+//      the gradient kernel writes them directly instead).
 // Everything is fp32: the matrix products on v_mfma_f32_16x16x4_f32 with
 // operands from LDS (or, in the walk, from memory), fp32 accumulation.
 #include <cstdint>
@@ -129,6 +130,7 @@ struct BwdParams {
   float *ckb;                             // dS^T_{c+1} per (flat chunk, value head)
   float *M, *Y;                           // the reverse map per (flat chunk, value head)
   float *dqh, *dkh;                       // [T, HV, D] fp32
+  void *dq, *dk;                          // [T, HK, D] out dtype (written here when HV == HK)
   void *dv;                               // [T, HV, D] out dtype
   float *dbeta, *dg;                      // [T, HV]
   float *dstate0;                         // [N, HV, D, D] or NULL
@@ -848,8 +850,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p) {
       const int i = 16 * w + 4 * g + e;
       if (i < ck.L) {
         const int64_t o = (ck.t0 + i) * HVD + (int64_t)h * D + 16 * (2 * mm_ + hf) + r;
-        p.dkh[o] = dKl[mm_][e];
-        p.dqh[o] = dQl[mm_][e];
+        if (p.ratio > 1) {
+          p.dkh[o] = dKl[mm_][e];
+          p.dqh[o] = dQl[mm_][e];
+        } else if (p.out_bf16) {   // one value head per key head: the final dq, dk
+          static_cast<uint16_t *>(p.dk)[o] = f32_to_bf16(dKl[mm_][e]);
+          static_cast<uint16_t *>(p.dq)[o] = f32_to_bf16(dQl[mm_][e]);
+        } else {
+          static_cast<float *>(p.dk)[o] = dKl[mm_][e];
+          static_cast<float *>(p.dq)[o] = dQl[mm_][e];
+        }
       }
     }
   __syncthreads();   // the partial sums are complete
@@ -953,7 +963,7 @@ hipError_t launch_bwd(const BwdParams &p, const gdr_args &a, void *dq, void *dk,
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<BF16, D>), dim3(items), dim3(512), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.T_total == 0) return hipSuccess;
+  if (a.T_total == 0 || p.ratio == 1) return hipSuccess;   // (HV == HK: dq, dk already final)
   if (p.out_bf16)
     hipLaunchKernelGGL((bwd_group_sum_kernel<true>), dim3((unsigned)a.T_total), dim3(256), 0, stream, p.dqh, p.dkh,
                        dq, dk, a.HK, p.ratio, D);
@@ -1017,6 +1027,8 @@ hipError_t launch_chunk_bwd(const gdr_args &a, const void *dout, void *dq, void 
   p.Y = reinterpret_cast<float *>(w + l.Y);
   p.dqh = reinterpret_cast<float *>(w + l.dqh);
   p.dkh = reinterpret_cast<float *>(w + l.dkh);
+  p.dq = dq;
+  p.dk = dk;
   p.dv = dv;
   p.dbeta = dbeta;
   p.dg = dg;

@@ -165,11 +165,14 @@ def test_chunk_bwd_strong_gate():
     compare(run(gdr, w, x), reference(w, x), w)
 
 
-def test_chunk_bwd_bf16_gradients_and_no_dstate():
+@pytest.mark.parametrize("HK,HV", [(2, 4), (3, 3)])
+def test_chunk_bwd_bf16_gradients_and_no_dstate(HK, HV):
+    """bf16 dq, dk, dv: summed over each key head's group (HV > HK) or
+    written by the gradient kernel itself (HV == HK)."""
     gdr = _gdr()
-    w = small(128, "bf16", "scalar", seqlens=(33, 5, 64), seed=98)
+    w = small(128, "bf16", "scalar", HK=HK, HV=HV, seqlens=(33, 5, 64), seed=98)
     x = inputs(w)
-    print("chunk_bwd bf16 gradients, dstate0 off", flush=True)
+    print(f"chunk_bwd bf16 gradients, dstate0 off, HK={HK} HV={HV}", flush=True)
     got = run(gdr, w, x, out_dtype=torch.bfloat16, dstate0=False)
     assert got["dstate0"] is None
     ref = reference(w, x)
