@@ -1062,13 +1062,20 @@ __global__ __launch_bounds__(64 * (NSW + prep_waves<NSW>())) void chunk_fwd_ws_k
                                                         (16 * I + i) * (int)orow, 0);
           }
         } else {
+          // (pairs converted by one packed instruction; the high half stored
+          // from the same register)
 #pragma unroll
           for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; i += 2) {
+              const bf16x2 pr = {static_cast<__bf16>(oa[I][i]), static_cast<__bf16>(oa[I][i + 1])};
+              const uint32_t u = __builtin_bit_cast(uint32_t, pr);
               if (L == C || 16 * I + 4 * g + i < L)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(oa[I][i]), ors, olane,
-                                                      (16 * I + i) * (int)orow, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)u, ors, olane, (16 * I + i) * (int)orow, 0);
+              if (L == C || 16 * I + 4 * g + i + 1 < L)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(u >> 16), ors, olane,
+                                                      (16 * I + i + 1) * (int)orow, 0);
+            }
         }
       }
     }

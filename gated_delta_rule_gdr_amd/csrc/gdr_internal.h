@@ -17,12 +17,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
+// fp32 -> bf16, round to nearest even; NaN stays NaN. (One hardware
+// conversion, v_cvt_pk_bf16_f32, with the other half unused.)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // hi = bf16(x), lo = bf16(x - hi): hi + lo carries 16 significant bits of x.
