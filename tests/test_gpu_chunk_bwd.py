@@ -265,3 +265,49 @@ def test_chunk_bwd_full_size_ragged_grouped():
     for name, hh in (("dq", kh), ("dk", kh), ("dv", vh), ("dbeta", vh), ("dg", vh)):
         check(got[name][rows][:, hh], ref[name], "bf16", name)
     check(got["dstate0"][n][vh], ref["dstate0"][0], "bf16", "dstate0")
+
+
+def _degenerate(x, kind):
+    """Inputs with one degenerate feature of the update imposed: beta = 0 (no
+    write: dv is exactly zero), beta = 1, zero keys on every other token,
+    complete forgetting (log-decay -60 per token) or a gate of exactly zero."""
+    x = dict(x)
+    if kind == "beta0":
+        x["beta"] = np.zeros_like(x["beta"])
+    elif kind == "beta1":
+        x["beta"] = np.ones_like(x["beta"])
+    elif kind == "zero_k":
+        k = np.array(x["k"], copy=True)
+        k[::2] = 0
+        x["k"] = k
+    elif kind == "forget":
+        x["g"] = np.full_like(x["g"], -60.0)
+    elif kind == "zero_g":
+        x["g"] = np.zeros_like(x["g"])
+    return x
+
+
+DEGEN = list(itertools.product(["beta0", "beta1", "zero_k", "forget", "zero_g"], ["bf16", "f32"],
+                               ["chunk_bwd", "recurrent_bwd"]))
+
+
+@pytest.mark.parametrize("kind,in_dtype,fn", DEGEN, ids=["-".join(c) for c in DEGEN])
+def test_backward_degenerate_cases(kind, in_dtype, fn):
+    """Both delta-rule backwards on the update's degenerate cases (scalar
+    gate, ragged grouped batch). Under complete forgetting the log-decays'
+    and the initial states' gradients are of order e^{-60} times the others:
+    they are checked against an absolute bound of 1e-6 times the scale of the
+    key gradients, below which fp32 cannot resolve them."""
+    gdr = _gdr()
+    w = small(128, in_dtype, "scalar", seed=97)
+    x = _degenerate(inputs(w), kind)
+    print(f"{fn} degenerate {kind} in={in_dtype}", flush=True)
+    got, ref = run(gdr, w, x, fn=fn), reference(w, x)
+    tiny = ("dg", "dstate0") if kind == "forget" else ()
+    compare(got, ref, w, names=tuple(n for n in NAMES if n not in tiny))
+    for n in tiny:
+        assert np.all(np.isfinite(got[n])), n
+        err = float(np.max(np.abs(got[n] - ref[n])))
+        assert err <= 1e-6 * max(1.0, rms(ref["dk"])), f"{n}: max|err| {err:.3e}"
+    if kind == "beta0":
+        assert not np.any(got["dv"]), "beta = 0: dv must be exactly zero"
