@@ -282,3 +282,35 @@ def test_gated_linear_backward_full_size_ragged_grouped():
     ref = reference_rec(w, x, kh, [n])
     for name, a, b, hh in zip(("dq", "dk", "dv", "dg"), got, ref, (kh, kh, vh, vh)):
         check(a[rows][:, hh], b, "bf16", name)
+
+
+LDEGEN = list(itertools.product(["zero_k", "forget", "zero_g"], ["bf16", "f32"]))
+
+
+@pytest.mark.parametrize("kind,in_dtype", LDEGEN, ids=["-".join(c) for c in LDEGEN])
+def test_gated_linear_backward_degenerate_cases(kind, in_dtype):
+    """The gated linear backward (scalar gate, grouped key heads) on zero keys
+    for every other token, complete forgetting (log-decay -60 per token) and a
+    gate of exactly zero. Under complete forgetting the exact dg is of order
+    e^{-60} times the other gradients, while the kernels form it as
+    q.dq - k.dk (a difference of terms of the gradients' own scale, summed
+    over the tokens after it): it is checked against fp32's absolute bound at
+    that scale, 1e-4 times the scale of dk."""
+    gdr = _gdr()
+    w = small_gated(128, in_dtype, "scalar", 2, 4, seed=88)
+    x = inputs(w)
+    if kind == "zero_k":
+        k = np.array(x["k"], copy=True)
+        k[::2] = 0
+        x["k"] = k
+    else:
+        x["g"] = np.full_like(x["g"], -60.0 if kind == "forget" else 0.0)
+    print(f"linear_chunk_bwd degenerate {kind} in={in_dtype}", flush=True)
+    got = run_gated(gdr, w, x)
+    ref = reference_rec(w, x)
+    for name, a, b in zip(("dq", "dk", "dv", "dg"), got, ref):
+        if name == "dg" and kind == "forget":
+            assert np.all(np.isfinite(a))
+            assert float(np.max(np.abs(a - b))) <= 1e-4 * max(1.0, rms(ref[1]))
+            continue
+        check(a, b, in_dtype, name)
