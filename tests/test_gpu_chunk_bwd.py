@@ -311,3 +311,15 @@ def test_backward_degenerate_cases(kind, in_dtype, fn):
         assert err <= 1e-6 * max(1.0, rms(ref["dk"])), f"{n}: max|err| {err:.3e}"
     if kind == "beta0":
         assert not np.any(got["dv"]), "beta = 0: dv must be exactly zero"
+
+
+@pytest.mark.parametrize("HK,HV", [(1, 8), (3, 6), (5, 5)])
+def test_chunk_bwd_head_layouts(HK, HV):
+    """Eight value heads per key head (the group sums of dq and dk over eight
+    heads), an odd number of key heads, and five heads with one value head
+    each (the direct dq/dk write), against the oracle."""
+    gdr = _gdr()
+    w = small(64, "bf16", "scalar", HK=HK, HV=HV, seqlens=(70, 0, 129), seed=98 + HV)
+    x = inputs(w)
+    print(f"chunk_bwd HK={HK} HV={HV}", flush=True)
+    compare(run(gdr, w, x), reference(w, x), w)
