@@ -214,3 +214,27 @@ def test_chunk_fwd_products_equal_recurrent_fwd(out_dtype):
         assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 3e-3 * r)
     for s in x["slot_idx"]:
         check_state(host(d["pool"], "f32")[s], host(p2, "f32")[s], "bf16", "f32")
+
+
+@pytest.mark.parametrize("HK,HV", [(1, 8), (3, 6)])
+@pytest.mark.parametrize("entry", ["chunk_fwd", "recurrent_fwd"])
+def test_products_head_layouts(HK, HV, entry):
+    """Gated DeltaProduct (two transitions per token) with eight value heads
+    per key head and with an odd number of key heads, on the warp-specialised
+    prefill and the tokenwise recurrence."""
+    gdr = _gdr()
+    P, D = 2, 128
+    w = synth.Workload(name="small", seqlens=(1, 40, 0, 97), HK=HK, HV=HV, DK=D, DV=D, in_dtype="bf16",
+                       gate="scalar", rule="delta", gate_shift=2.0, state_dtype="f32", num_slots=6,
+                       zero_init=False, seed=66 + HV)
+    x = product_inputs(w, P)
+    d = to_dev(w, x)
+    print(f"{entry} products={P} HK={HK} HV={HV}", flush=True)
+    o = getattr(gdr, entry)(d["q"], d["k"], d["v"], d["g"], d["beta"], d["pool"], d["slot_idx"],
+                            d["cu_seqlens"], scale=D ** -0.5, rule="delta", gate="scalar", products=P)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = reference(w, x, P, D ** -0.5)
+    check_out(host(o, "bf16"), o_ref, "bf16")
+    pool = host(d["pool"], "f32")
+    for s in x["slot_idx"]:
+        check_state(pool[s], pool_ref[s], "bf16", "f32")
